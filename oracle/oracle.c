@@ -1,0 +1,484 @@
+/*
+ * CPU oracle for the SpMV library -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, serial, obviously-correct C with fp64 accumulation.  It is called
+ * only by the tests, by the smoke check and by the bench's CPU-baseline leg;
+ * the library (HIP kernels + C-ABI) never links, includes or calls it, and it
+ * shares no source with the library.
+ *
+ * Each function follows one passage of the source pages (cited by page title
+ * and section) or the plain mathematical definition of the operation.  Where
+ * a page is silent or garbled, the reading taken is stated at the function.
+ *
+ * Value outputs come with a per-row error scale
+ *     scale_i = |alpha| * sum_k |a_ik * x_k| + |beta * y_in_i|
+ * so that a tolerance of the form |y_gpu - y_ref| <= tau * scale_i can be
+ * checked by the caller.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+
+/* ------------------------------------------------------------------------ */
+/* IEEE-754 binary16 -> binary64, decoded field by field (exact).           */
+/* ------------------------------------------------------------------------ */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int mant = h & 0x3ff;
+    double v;
+    if (expo == 0)            /* zero or subnormal: mant * 2^-24 */
+        v = ldexp((double)mant, -24);
+    else if (expo == 31)      /* inf or nan */
+        v = mant ? NAN : INFINITY;
+    else                      /* normal: (1024 + mant) * 2^(expo - 25) */
+        v = ldexp((double)(1024 + mant), expo - 25);
+    return sign ? -v : v;
+}
+
+/* ------------------------------------------------------------------------ */
+/* CSR SpMV.  "Why SpMV needs CUDA optimisation", section 2.1 (scalar CSR   */
+/* kernel: dot += values[i] * x[col_idx[i]] over the row's range) and       */
+/* section 4.1 (warp-per-row form computes the same sum).  The product is   */
+/* y = alpha*A*x + beta*y; y_in is not read when beta == 0.                 */
+/* Duplicate columns are summed; the sum runs in storage order.             */
+/* ------------------------------------------------------------------------ */
+void oracle_csr_spmv(int n_rows, const int32_t *rp, const int32_t *ci,
+                     const float *v, const float *x, double alpha, double beta,
+                     const float *y_in, double *y_out, double *scale)
+{
+    for (int i = 0; i < n_rows; ++i) {
+        double s = 0.0, a = 0.0;
+        for (int32_t k = rp[i]; k < rp[i + 1]; ++k) {
+            double p = (double)v[k] * (double)x[ci[k]];
+            s += p;
+            a += fabs(p);
+        }
+        double yi = alpha * s;
+        double sc = fabs(alpha) * a;
+        if (beta != 0.0) {
+            yi += beta * (double)y_in[i];
+            sc += fabs(beta * (double)y_in[i]);
+        }
+        y_out[i] = yi;
+        if (scale) scale[i] = sc;
+    }
+}
+
+/* Same definition with fp64 matrix values (used for the assembled FE form). */
+void oracle_csr_spmv_f64(int n_rows, const int32_t *rp, const int32_t *ci,
+                         const double *v, const float *x, double alpha, double beta,
+                         const float *y_in, double *y_out, double *scale)
+{
+    for (int i = 0; i < n_rows; ++i) {
+        double s = 0.0, a = 0.0;
+        for (int32_t k = rp[i]; k < rp[i + 1]; ++k) {
+            double p = v[k] * (double)x[ci[k]];
+            s += p;
+            a += fabs(p);
+        }
+        double yi = alpha * s, sc = fabs(alpha) * a;
+        if (beta != 0.0) {
+            yi += beta * (double)y_in[i];
+            sc += fabs(beta * (double)y_in[i]);
+        }
+        y_out[i] = yi;
+        if (scale) scale[i] = sc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Row statistics: max row length, sum and sum of squares (int64).          */
+/* ------------------------------------------------------------------------ */
+void oracle_row_stats(int n_rows, const int32_t *rp, int32_t *max_len,
+                      int64_t *sum_len, int64_t *sum_len_sq)
+{
+    int32_t m = 0;
+    int64_t s = 0, q = 0;
+    for (int i = 0; i < n_rows; ++i) {
+        int32_t len = rp[i + 1] - rp[i];
+        if (len > m) m = len;
+        s += len;
+        q += (int64_t)len * len;
+    }
+    *max_len = m;
+    *sum_len = s;
+    *sum_len_sq = q;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Row grouping ("Sparse matrix multiplication acceleration", section 2.1.1 */
+/* grouping table and the Map[] indirection of section 2.2.1).  For SpMV    */
+/* the dense operand is an n x 1 vector, so a row's count of intermediate   */
+/* products equals its nonzero count.  Group g holds rows with             */
+/* t[g-1] <= len < t[g] (t[-1] = 0, t[3] = infinity); the page's table      */
+/* gives t = {32, 512, 8192}.  perm lists rows group by group, ascending     */
+/* row id inside a group (a stable counting sort); bin_offsets[g] is the    */
+/* position of group g's first row in perm, bin_offsets[4] = n_rows.        */
+/* ------------------------------------------------------------------------ */
+int oracle_row_bin(int32_t len, const int32_t *t)
+{
+    if (len < t[0]) return 0;
+    if (len < t[1]) return 1;
+    if (len < t[2]) return 2;
+    return 3;
+}
+
+void oracle_bins(int n_rows, const int32_t *rp, const int32_t *t,
+                 int32_t *bin_offsets, int32_t *perm)
+{
+    int32_t count[4] = {0, 0, 0, 0};
+    for (int i = 0; i < n_rows; ++i)
+        count[oracle_row_bin(rp[i + 1] - rp[i], t)]++;
+    bin_offsets[0] = 0;
+    for (int g = 0; g < 4; ++g)
+        bin_offsets[g + 1] = bin_offsets[g] + count[g];
+    int32_t next[4];
+    for (int g = 0; g < 4; ++g) next[g] = bin_offsets[g];
+    for (int i = 0; i < n_rows; ++i) {
+        int g = oracle_row_bin(rp[i + 1] - rp[i], t);
+        perm[next[g]++] = i;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Format choice by coefficient of variation of row lengths ("Why SpMV     */
+/* needs CUDA optimisation", section 2.2): CV < 0.3 -> ELL,                 */
+/* 0.3 <= CV <= 0.7 -> HYB, CV > 0.7 -> CSR with row reordering.            */
+/* Reading: population standard deviation; the comparisons are done         */
+/* exactly in integers, CV^2 = (n*S2 - S1^2) / S1^2; an undefined CV        */
+/* (n == 0 or S1 == 0) picks CSR.  Returns 0 = ELL, 1 = HYB, 2 = CSR.       */
+/* ------------------------------------------------------------------------ */
+int oracle_format_choice(int64_t n, int64_t s1, int64_t s2)
+{
+    if (n <= 0 || s1 <= 0) return 2;
+    __int128 num = (__int128)n * s2 - (__int128)s1 * s1;
+    __int128 den = (__int128)s1 * s1;
+    if (100 * num < 9 * den) return 0;
+    if (100 * num <= 49 * den) return 1;
+    return 2;
+}
+
+/* ------------------------------------------------------------------------ */
+/* ELL ("Why SpMV needs CUDA optimisation", section 2.1 table: fixed width, */
+/* zero padding).  Reading: width W >= the longest row, slot-major layout   */
+/* ell[k*n + i]; a padding slot holds column -1 and value +0.0f and is       */
+/* skipped by the product.  Returns 0, or -1 when a row is longer than W.   */
+/* ------------------------------------------------------------------------ */
+int oracle_ell_from_csr(int n_rows, const int32_t *rp, const int32_t *ci,
+                        const float *v, int W, int32_t *ell_col, float *ell_val)
+{
+    for (int i = 0; i < n_rows; ++i)
+        if (rp[i + 1] - rp[i] > W) return -1;
+    for (int k = 0; k < W; ++k) {
+        for (int i = 0; i < n_rows; ++i) {
+            int32_t len = rp[i + 1] - rp[i];
+            size_t slot = (size_t)k * (size_t)n_rows + (size_t)i;
+            if (k < len) {
+                ell_col[slot] = ci[rp[i] + k];
+                ell_val[slot] = v[rp[i] + k];
+            } else {
+                ell_col[slot] = -1;
+                ell_val[slot] = 0.0f;
+            }
+        }
+    }
+    return 0;
+}
+
+void oracle_ell_spmv(int n_rows, int W, const int32_t *ell_col, const float *ell_val,
+                     const float *x, double alpha, double beta, const float *y_in,
+                     double *y_out, double *scale)
+{
+    for (int i = 0; i < n_rows; ++i) {
+        double s = 0.0, a = 0.0;
+        for (int k = 0; k < W; ++k) {
+            size_t slot = (size_t)k * (size_t)n_rows + (size_t)i;
+            if (ell_col[slot] < 0) continue;
+            double p = (double)ell_val[slot] * (double)x[ell_col[slot]];
+            s += p;
+            a += fabs(p);
+        }
+        double yi = alpha * s, sc = fabs(alpha) * a;
+        if (beta != 0.0) {
+            yi += beta * (double)y_in[i];
+            sc += fabs(beta * (double)y_in[i]);
+        }
+        y_out[i] = yi;
+        if (scale) scale[i] = sc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* MACKO format ("MACKO-SpMV: GPU acceleration and storage optimisation at  */
+/* low sparsity", section 2.1: delta coding, dynamic zero padding, 4-bit     */
+/* packing 8 per 32-bit word, aligned loads).  Readings taken where the      */
+/* page is silent or self-contradictory:                                     */
+/*  - a row starts at previous column -1, every stored entry has a column    */
+/*    gap g = col - prev in 1..16 and code g-1 in 0..15 (the page: a 4-bit   */
+/*    delta spans at most 16);                                               */
+/*  - a gap larger than 16 is bridged by zero-valued padding entries placed  */
+/*    16 columns after the previous entry (code 15, value +0);               */
+/*  - each row is then padded with (code 0, value +0) entries to a multiple  */
+/*    of 256 entries, so 128 B of codes and 512 B of values are aligned per  */
+/*    256 entries;                                                           */
+/*  - entry e's code is nibble (e % 8) of word e / 8, least significant      */
+/*    nibble first.                                                          */
+/* Columns must be strictly increasing in each row and lie in [0, n_cols).  */
+/* ------------------------------------------------------------------------ */
+#define ORACLE_MACKO_SPAN 16
+#define ORACLE_MACKO_ALIGN 256
+
+static int64_t oracle_macko_row_entries(const int32_t *cols, int32_t len)
+{
+    int64_t count = 0;
+    int64_t prev = -1;
+    for (int32_t k = 0; k < len; ++k) {
+        int64_t g = (int64_t)cols[k] - prev;
+        while (g > ORACLE_MACKO_SPAN) {       /* one padding entry per 16 columns */
+            count++;
+            prev += ORACLE_MACKO_SPAN;
+            g -= ORACLE_MACKO_SPAN;
+        }
+        count++;
+        prev = cols[k];
+    }
+    int64_t rem = count % ORACLE_MACKO_ALIGN;
+    if (rem) count += ORACLE_MACKO_ALIGN - rem;
+    return count;
+}
+
+/* Total encoded entries, or -1 for unsorted/duplicate/out-of-range columns. */
+int64_t oracle_macko_size(int n_rows, int n_cols, const int32_t *rp, const int32_t *ci)
+{
+    int64_t total = 0;
+    for (int i = 0; i < n_rows; ++i) {
+        for (int32_t k = rp[i]; k < rp[i + 1]; ++k) {
+            if (ci[k] < 0 || ci[k] >= n_cols) return -1;
+            if (k > rp[i] && ci[k] <= ci[k - 1]) return -1;
+        }
+        total += oracle_macko_row_entries(ci + rp[i], rp[i + 1] - rp[i]);
+    }
+    return total;
+}
+
+static void oracle_macko_put(uint32_t *codes, uint16_t *mvals, int64_t e,
+                             uint32_t code, uint16_t val)
+{
+    codes[e / 8] |= (code & 0xfu) << (4 * (e % 8));
+    mvals[e] = val;
+}
+
+/* Fills mrow_ptr[n_rows+1] (entry offsets), codes[E/8] and mvals[E] (fp16
+ * bits).  Returns 0, or -1 on invalid columns. */
+int oracle_macko_encode(int n_rows, int n_cols, const int32_t *rp, const int32_t *ci,
+                        const uint16_t *vals, int32_t *mrow_ptr, uint32_t *codes,
+                        uint16_t *mvals)
+{
+    int64_t total = oracle_macko_size(n_rows, n_cols, rp, ci);
+    if (total < 0 || total > INT32_MAX) return -1;
+    memset(codes, 0, (size_t)(total / 8) * sizeof(uint32_t));
+    int64_t e = 0;
+    for (int i = 0; i < n_rows; ++i) {
+        mrow_ptr[i] = (int32_t)e;
+        int64_t row_begin = e;
+        int64_t prev = -1;
+        for (int32_t k = rp[i]; k < rp[i + 1]; ++k) {
+            int64_t g = (int64_t)ci[k] - prev;
+            while (g > ORACLE_MACKO_SPAN) {
+                oracle_macko_put(codes, mvals, e++, ORACLE_MACKO_SPAN - 1, 0);
+                prev += ORACLE_MACKO_SPAN;
+                g -= ORACLE_MACKO_SPAN;
+            }
+            oracle_macko_put(codes, mvals, e++, (uint32_t)(g - 1), vals[k]);
+            prev = ci[k];
+        }
+        while ((e - row_begin) % ORACLE_MACKO_ALIGN)
+            oracle_macko_put(codes, mvals, e++, 0, 0);
+    }
+    mrow_ptr[n_rows] = (int32_t)e;
+    return 0;
+}
+
+/* Column of every stored entry: restart at -1 per row, col = prev + code + 1. */
+void oracle_macko_decode(int n_rows, const int32_t *mrow_ptr, const uint32_t *codes,
+                         int32_t *cols)
+{
+    for (int i = 0; i < n_rows; ++i) {
+        int64_t prev = -1;
+        for (int64_t e = mrow_ptr[i]; e < mrow_ptr[i + 1]; ++e) {
+            uint32_t code = (codes[e / 8] >> (4 * (e % 8))) & 0xfu;
+            prev = prev + (int64_t)code + 1;
+            cols[e] = (int32_t)prev;
+        }
+    }
+}
+
+/* MACKO SpMV (section 2.2): y_i = alpha * sum over the row's stored entries
+ * of value * x[col] + beta * y_i, with fp16 values and fp16 x taken exactly
+ * into fp64.  Trailing alignment entries may decode to a column >= n_cols;
+ * they hold +0 and are skipped. */
+void oracle_macko_spmv(int n_rows, int n_cols, const int32_t *mrow_ptr,
+                       const uint32_t *codes, const uint16_t *mvals,
+                       const uint16_t *x, double alpha, double beta,
+                       const float *y_in, double *y_out, double *scale)
+{
+    for (int i = 0; i < n_rows; ++i) {
+        double s = 0.0, a = 0.0;
+        int64_t prev = -1;
+        for (int64_t e = mrow_ptr[i]; e < mrow_ptr[i + 1]; ++e) {
+            uint32_t code = (codes[e / 8] >> (4 * (e % 8))) & 0xfu;
+            prev = prev + (int64_t)code + 1;
+            if (prev >= n_cols) continue;
+            double p = oracle_half_to_double(mvals[e]) * oracle_half_to_double(x[prev]);
+            s += p;
+            a += fabs(p);
+        }
+        double yi = alpha * s, sc = fabs(alpha) * a;
+        if (beta != 0.0) {
+            yi += beta * (double)y_in[i];
+            sc += fabs(beta * (double)y_in[i]);
+        }
+        y_out[i] = yi;
+        if (scale) scale[i] = sc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dense fp16 GEMV, the dense comparator of the MACKO-SpMV page's section    */
+/* 3.1 table: y = alpha * W x + beta * y, W row-major m x n fp16.            */
+/* ------------------------------------------------------------------------ */
+void oracle_gemv_f16(int m, int n, const uint16_t *W, const uint16_t *x,
+                     double alpha, double beta, const float *y_in,
+                     double *y_out, double *scale)
+{
+    for (int i = 0; i < m; ++i) {
+        double s = 0.0, a = 0.0;
+        for (int j = 0; j < n; ++j) {
+            double p = oracle_half_to_double(W[(size_t)i * n + j]) * oracle_half_to_double(x[j]);
+            s += p;
+            a += fabs(p);
+        }
+        double yi = alpha * s, sc = fabs(alpha) * a;
+        if (beta != 0.0) {
+            yi += beta * (double)y_in[i];
+            sc += fabs(beta * (double)y_in[i]);
+        }
+        y_out[i] = yi;
+        if (scale) scale[i] = sc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Finite-element stiffness matvec ("Fused GPU SpMV kernel optimisation:     */
+/* from bandwidth bottleneck to BF16 precision", sections 2.1-2.2 and 5.1):  */
+/* for every element gather the 24 local DOFs through edof, multiply by the  */
+/* element matrix, and add the result into the global vector.  Readings:     */
+/* one shared Ke scaled by rho_e^p (the SIMP interpolation the page's         */
+/* topology-optimisation setting uses; section 5.2 notes a shared Ke), and   */
+/* edof = -1 marks a constrained DOF that is neither gathered nor written.   */
+/* y = alpha * sum_e rho_e^p P_e^T Ke P_e x + beta * y.                      */
+/* scale_a = |alpha| sum_e sum_b |rho_e^p Ke_ab x_b| + |beta y_a|.           */
+/* ------------------------------------------------------------------------ */
+static double oracle_ipow(double r, int p)
+{
+    double s = 1.0;
+    for (int k = 0; k < p; ++k) s *= r;
+    return s;
+}
+
+void oracle_fe_matvec(int n_elem, int n_dof, const int32_t *edof, const float *rho,
+                      int penalty, const float *Ke, const float *x, double alpha,
+                      double beta, const float *y_in, double *y_out, double *scale)
+{
+    for (int d = 0; d < n_dof; ++d) {
+        y_out[d] = (beta != 0.0) ? beta * (double)y_in[d] : 0.0;
+        if (scale) scale[d] = (beta != 0.0) ? fabs(beta * (double)y_in[d]) : 0.0;
+    }
+    for (int e = 0; e < n_elem; ++e) {
+        const int32_t *dof = edof + (size_t)e * 24;
+        double s = oracle_ipow((double)rho[e], penalty);
+        double u[24];
+        for (int b = 0; b < 24; ++b)
+            u[b] = dof[b] >= 0 ? (double)x[dof[b]] : 0.0;
+        for (int a = 0; a < 24; ++a) {
+            if (dof[a] < 0) continue;
+            double f = 0.0, fa = 0.0;
+            for (int b = 0; b < 24; ++b) {
+                double p = s * (double)Ke[a * 24 + b] * u[b];
+                f += p;
+                fa += fabs(p);
+            }
+            y_out[dof[a]] += alpha * f;
+            if (scale) scale[dof[a]] += fabs(alpha) * fa;
+        }
+    }
+}
+
+/* Assembled form of the same operator: every element contributes
+ * (edof[a], edof[b], rho^p Ke_ab) for unconstrained a, b; entries are sorted
+ * by (row, column) and equal positions are summed in fp64, giving CSR.
+ * Two calls: with rp_out == NULL it returns the number of distinct entries;
+ * otherwise it fills rp_out[n_dof+1], ci_out[nnz], v_out[nnz] and returns
+ * nnz.  Returns -1 on allocation failure. */
+typedef struct { int32_t r, c; int64_t order; double v; } oracle_coo_t;
+
+static int oracle_coo_cmp(const void *pa, const void *pb)
+{
+    const oracle_coo_t *a = (const oracle_coo_t *)pa, *b = (const oracle_coo_t *)pb;
+    if (a->r != b->r) return a->r < b->r ? -1 : 1;
+    if (a->c != b->c) return a->c < b->c ? -1 : 1;
+    if (a->order != b->order) return a->order < b->order ? -1 : 1;
+    return 0;
+}
+
+int64_t oracle_fe_assemble(int n_elem, int n_dof, const int32_t *edof, const float *rho,
+                           int penalty, const float *Ke, int32_t *rp_out,
+                           int32_t *ci_out, double *v_out)
+{
+    size_t cap = (size_t)n_elem * 576;
+    oracle_coo_t *coo = (oracle_coo_t *)malloc(cap * sizeof(oracle_coo_t) + 1);
+    if (!coo) return -1;
+    size_t m = 0;
+    for (int e = 0; e < n_elem; ++e) {
+        const int32_t *dof = edof + (size_t)e * 24;
+        double s = oracle_ipow((double)rho[e], penalty);
+        for (int a = 0; a < 24; ++a) {
+            if (dof[a] < 0) continue;
+            for (int b = 0; b < 24; ++b) {
+                if (dof[b] < 0) continue;
+                coo[m].r = dof[a];
+                coo[m].c = dof[b];
+                coo[m].order = (int64_t)m;
+                coo[m].v = s * (double)Ke[a * 24 + b];
+                m++;
+            }
+        }
+    }
+    qsort(coo, m, sizeof(oracle_coo_t), oracle_coo_cmp);
+    int64_t nnz = 0;
+    for (size_t k = 0; k < m; ++k) {
+        int fresh = (k == 0) || coo[k].r != coo[k - 1].r || coo[k].c != coo[k - 1].c;
+        if (fresh) {
+            if (rp_out) {
+                ci_out[nnz] = coo[k].c;
+                v_out[nnz] = coo[k].v;
+            }
+            nnz++;
+        } else if (rp_out) {
+            v_out[nnz - 1] += coo[k].v;
+        }
+    }
+    if (rp_out) {
+        for (int d = 0; d <= n_dof; ++d) rp_out[d] = 0;
+        for (size_t k = 0; k < m; ++k) {
+            int fresh = (k == 0) || coo[k].r != coo[k - 1].r || coo[k].c != coo[k - 1].c;
+            if (fresh) rp_out[coo[k].r + 1]++;
+        }
+        for (int d = 0; d < n_dof; ++d) rp_out[d + 1] += rp_out[d];
+    }
+    free(coo);
+    return nnz;
+}
