@@ -1,0 +1,240 @@
+/*
+ * spmv.h -- C ABI of the MI355X (gfx950) sparse matrix-vector library.
+ *
+ * Every entry point computes (a step of) y = alpha * A * x + beta * y, the
+ * operation all four source pages turn on:
+ *   - "Why SpMV needs CUDA optimisation" (codechina.net): CSR scalar and
+ *     warp-per-row kernels (sections 2.1, 4.1), ELL and the CV-based format
+ *     rule (sections 2.1-2.2);
+ *   - "Sparse matrix multiplication acceleration" (mlqm.cn, hash-based
+ *     multi-phase SpGEMM): row grouping by work per row (section 2.1.1) and
+ *     the group-ordered row map (section 2.2.1);
+ *   - "MACKO-SpMV: GPU acceleration and storage optimisation at low sparsity"
+ *     (maplevalley.com.cn): the MACKO format and its kernel (section 2);
+ *   - "Fused GPU SpMV kernel optimisation: from bandwidth bottleneck to BF16
+ *     precision" (bbs.csdn.net): the fused gather / element product / atomic
+ *     scatter finite-element matvec (sections 2 and 5.1).
+ *
+ * Conventions shared by all calls
+ *   - Indices are int32, as on the pages.  Counts that do not fit int32 return
+ *     SPMV_ERR_OVERFLOW.
+ *   - "device" pointers point to GPU memory (hipMalloc / torch CUDA tensors),
+ *     "host" pointers to CPU memory.  All memory is owned by the caller; the
+ *     library never frees what it is given.  A CSR handle *borrows* the
+ *     matrix arrays: they must stay allocated and structurally unchanged until
+ *     spmv_csr_destroy (values may be rewritten in place between applies).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls that launch kernels are asynchronous on that stream unless their
+ *     comment says "synchronises".
+ *   - beta == 0 means y is write-only: it is not read, so it may hold NaN.
+ *   - Every call returns an spmv_status.  On failure nothing was launched
+ *     (validation runs first, on the host) unless the status is SPMV_ERR_HIP,
+ *     and spmv_last_error() gives a message (per calling thread).
+ *   - fp16 data is passed as its IEEE binary16 bit pattern (uint16_t).
+ */
+#ifndef SPMV_AMD_H
+#define SPMV_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPMV_OK = 0,
+    SPMV_ERR_INVALID_VALUE = 1,   /* bad size, null pointer, workspace too small */
+    SPMV_ERR_INVALID_MATRIX = 2,  /* row_ptr not monotone / inconsistent, column out of range */
+    SPMV_ERR_UNSORTED = 3,        /* MACKO input: columns not strictly increasing in a row */
+    SPMV_ERR_OVERFLOW = 4,        /* a count does not fit int32 */
+    SPMV_ERR_UNSUPPORTED = 5,     /* valid request this build does not support */
+    SPMV_ERR_HIP = 6              /* a HIP runtime call failed */
+} spmv_status;
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *spmv_last_error(void);
+
+/* ======================================================================== */
+/* Row statistics and format choice                                         */
+/* ======================================================================== */
+
+/* Longest row, sum and sum of squares of the row lengths of a CSR row_ptr.
+ * row_ptr: device int32[n_rows+1].  Outputs: host.  Synchronises `stream`.
+ * SPMV_ERR_INVALID_MATRIX if some row has negative length. */
+spmv_status spmv_csr_row_stats(int32_t n_rows, const int32_t *row_ptr,
+                               int32_t *max_len, int64_t *sum_len,
+                               int64_t *sum_len_sq, void *stream);
+
+/* Format recommendation by the coefficient of variation (CV) of the row
+ * lengths ("Why SpMV needs CUDA optimisation", section 2.2): CV < 0.3 -> ELL,
+ * 0.3 <= CV <= 0.7 -> HYB, CV > 0.7 -> CSR with row reordering (the binned
+ * CSR path).  CV uses the population standard deviation; the comparison is
+ * exact integer arithmetic on (n, sum_len, sum_len_sq).  No rows or no
+ * nonzeros -> CSR.  Host only, no GPU call. */
+typedef enum { SPMV_FORMAT_ELL = 0, SPMV_FORMAT_HYB = 1, SPMV_FORMAT_CSR = 2 } spmv_format;
+spmv_status spmv_format_recommend(int64_t n_rows, int64_t sum_len, int64_t sum_len_sq,
+                                  int32_t *format);
+
+/* ======================================================================== */
+/* CSR: y = alpha * A * x + beta * y                                        */
+/* ("Why SpMV needs CUDA optimisation", sections 2.1 and 4.1; row grouping  */
+/*  from "Sparse matrix multiplication acceleration", section 2.1.1)        */
+/* ======================================================================== */
+
+typedef enum {
+    SPMV_CSR_AUTO = 0,     /* = BINNED */
+    SPMV_CSR_SCALAR = 1,   /* one lane per row, rows in natural order */
+    SPMV_CSR_VECTOR = 2,   /* G lanes per row (G = power of two >= mean row length, 2..64) */
+    SPMV_CSR_BINNED = 3    /* rows grouped by length, one kernel shape per group */
+} spmv_csr_variant;
+
+typedef struct spmv_csr_plan *spmv_csr_t;
+
+/* Bytes of device workspace spmv_csr_create needs for a matrix of this size.
+ * thresholds: host int32[3] or NULL for the page's {32, 512, 8192}; valid
+ * thresholds satisfy 1 <= t0 < t1 < t2 and t0 <= 256. */
+spmv_status spmv_csr_plan_size(int32_t n_rows, int32_t nnz, const int32_t *thresholds,
+                               size_t *bytes);
+
+/* Validates the matrix on the GPU (row_ptr[0] == 0, row_ptr[n_rows] == nnz,
+ * non-decreasing row_ptr, 0 <= col < n_cols) and, for BINNED/AUTO, builds
+ * the row-grouping plan in `workspace` (device, >= spmv_csr_plan_size bytes,
+ * owned by the caller, kept until destroy).  The grouping: group g holds rows
+ * with t[g-1] <= length < t[g]; `perm` lists rows group by group in
+ * ascending row order.  row_ptr, col_idx: device int32; vals: device fp32.
+ * Column order inside a row is free (duplicates are summed).  Synchronises
+ * `stream`.  *h receives a handle (host memory owned by the library until
+ * spmv_csr_destroy). */
+spmv_status spmv_csr_create(spmv_csr_t *h, int32_t n_rows, int32_t n_cols, int32_t nnz,
+                            const int32_t *row_ptr, const int32_t *col_idx,
+                            const float *vals, int32_t variant,
+                            const int32_t *thresholds, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* y = alpha * A * x + beta * y with fp32 products summed in fp32.
+ * x: device fp32[n_cols]; y: device fp32[n_rows].  x and y must not overlap.
+ * Asynchronous; no synchronisation and no allocation. */
+spmv_status spmv_csr_apply(spmv_csr_t h, float alpha, const float *x, float beta,
+                           float *y, void *stream);
+
+/* Test hook: copies the grouping plan.  h_bin_offsets: host int32[5] (group
+ * g occupies perm[bin_offsets[g] .. bin_offsets[g+1]-1]); d_perm: device
+ * int32[n_rows] or NULL.  Synchronises `stream`.  SPMV_ERR_INVALID_VALUE for
+ * a handle without a plan (SCALAR / VECTOR). */
+spmv_status spmv_csr_get_plan(spmv_csr_t h, int32_t *h_bin_offsets, int32_t *d_perm,
+                              void *stream);
+
+/* Resolved variant, lanes per row of the VECTOR variant (0 otherwise) and the
+ * number of short-row blocks of the BINNED plan (0 otherwise).  Host only. */
+spmv_status spmv_csr_info(spmv_csr_t h, int32_t *variant, int32_t *group_lanes,
+                          int32_t *n_short_blocks);
+
+/* Releases the handle (not the borrowed arrays or the workspace). */
+spmv_status spmv_csr_destroy(spmv_csr_t h);
+
+/* ======================================================================== */
+/* ELL ("Why SpMV needs CUDA optimisation", section 2.1 table)               */
+/* Layout: slot-major, entry k of row i at [k * n_rows + i]; a padding slot */
+/* holds column -1 and value +0.0f and is skipped.                          */
+/* ======================================================================== */
+
+/* Converts CSR (device arrays) to ELL of the given width (device outputs
+ * int32 / fp32 [width * n_rows]).  width must be >= the longest row
+ * (SPMV_ERR_INVALID_VALUE otherwise).  Row order of entries is kept.
+ * Synchronises `stream` (it checks the width and the matrix first). */
+spmv_status spmv_ell_from_csr(int32_t n_rows, int32_t n_cols, int32_t nnz,
+                              const int32_t *row_ptr, const int32_t *col_idx,
+                              const float *vals, int32_t width, int32_t *ell_col,
+                              float *ell_val, void *stream);
+
+/* y = alpha * A * x + beta * y for an ELL matrix; slots are summed in slot
+ * order in fp32.  ell_col entries must be -1 or in [0, n_cols) (as written
+ * by spmv_ell_from_csr).  Asynchronous. */
+spmv_status spmv_ell_apply(int32_t n_rows, int32_t n_cols, int32_t width,
+                           const int32_t *ell_col, const float *ell_val, float alpha,
+                           const float *x, float beta, float *y, void *stream);
+
+/* ======================================================================== */
+/* MACKO ("MACKO-SpMV: GPU acceleration and storage optimisation at low      */
+/* sparsity", section 2)                                                    */
+/* Format: per row, entries in column order; each entry has a 4-bit code c  */
+/* meaning "column = previous column + c + 1" (the previous column starts   */
+/* at -1 in each row) and an fp16 value.  A gap larger than 16 is bridged by */
+/* padding entries (code 15, value +0) placed 16 columns after the previous */
+/* entry; each row is padded with (code 0, value +0) to a multiple of 256   */
+/* entries.  codes: entry e in bits [4(e%8), 4(e%8)+3] of word e/8.         */
+/* mrow_ptr[i] is the first entry of row i; mrow_ptr[n_rows] = total.       */
+/* ======================================================================== */
+
+/* Number of encoded entries (host inputs).  SPMV_ERR_UNSORTED if a row's
+ * columns are not strictly increasing, SPMV_ERR_INVALID_MATRIX for a column
+ * outside [0, n_cols) or a bad row_ptr, SPMV_ERR_OVERFLOW past int32. */
+spmv_status macko_encode_size(int32_t n_rows, int32_t n_cols, const int32_t *h_row_ptr,
+                              const int32_t *h_col, int64_t *n_entries);
+
+/* Encodes on the host into caller buffers: h_mrow_ptr int32[n_rows+1],
+ * h_codes uint32[n_entries/8], h_mvals uint16[n_entries] (fp16 bits).  Same
+ * errors as macko_encode_size. */
+spmv_status macko_encode(int32_t n_rows, int32_t n_cols, const int32_t *h_row_ptr,
+                         const int32_t *h_col, const uint16_t *h_vals_f16,
+                         int32_t *h_mrow_ptr, uint32_t *h_codes, uint16_t *h_mvals);
+
+/* y = alpha * A * x + beta * y: fp16 values times fp16 x, fp32 accumulate,
+ * fp32 y.  Columns are rebuilt on the GPU from the codes by a wave-wide
+ * prefix sum (section 2.2.2).  All pointers are device; mvals and codes must
+ * be 16-byte and 4-byte aligned (SPMV_ERR_UNSUPPORTED otherwise).
+ * Asynchronous. */
+spmv_status macko_spmv(int32_t n_rows, int32_t n_cols, const int32_t *mrow_ptr,
+                       const uint32_t *codes, const uint16_t *mvals, float alpha,
+                       const uint16_t *x_f16, float beta, float *y, void *stream);
+
+/* Test hook: the column of every stored entry (device int32[total entries]),
+ * rebuilt by the same on-GPU decoder.  Asynchronous. */
+spmv_status macko_decode_columns(int32_t n_rows, const int32_t *mrow_ptr,
+                                 const uint32_t *codes, int32_t *cols_out, void *stream);
+
+/* ======================================================================== */
+/* Dense fp16 GEMV, the dense comparator of the MACKO page's section 3.1    */
+/* y = alpha * W x + beta * y; W device fp16[m * n] row-major, x fp16[n],   */
+/* y fp32[m]; fp32 accumulation.  Asynchronous.                             */
+/* ======================================================================== */
+spmv_status dense_gemv_f16(int32_t m, int32_t n, const uint16_t *W, const uint16_t *x_f16,
+                           float alpha, float beta, float *y, void *stream);
+
+/* ======================================================================== */
+/* Finite-element stiffness matvec ("Fused GPU SpMV kernel optimisation",   */
+/* sections 2.1-2.2 and 5.1-5.2)                                             */
+/* y = alpha * sum_e rho_e^penalty * P_e^T Ke P_e x + beta * y               */
+/* edof: device int32[n_elem * 24], element e's 24 global DOFs; -1 (or any   */
+/* value outside [0, n_dof)) marks a constrained DOF, neither gathered nor   */
+/* written.  rho: device fp32[n_elem]; Ke: device fp32[24 * 24] row-major,   */
+/* shared by all elements; x, y: device fp32[n_dof]; 0 <= penalty <= 8.      */
+/* The scatter uses fp32 atomics, so the order of additions (and the last   */
+/* bits of y) may differ from call to call.                                 */
+/* ======================================================================== */
+
+/* One fused kernel (after a y = beta * y pass): gather, 24x24 product,
+ * atomic scatter.  Asynchronous. */
+spmv_status fem_matvec_apply(int32_t n_elem, int32_t n_dof, const int32_t *edof,
+                             const float *rho, int32_t penalty, const float *Ke,
+                             float alpha, const float *x, float beta, float *y,
+                             void *stream);
+
+/* Workspace bytes of the three-stage comparator (2 * n_elem * 24 floats). */
+spmv_status fem_threestage_size(int32_t n_elem, size_t *bytes);
+
+/* The unfused comparator the page measures against (section 2.1): a gather
+ * kernel writing per-element vectors to the workspace, an element-product
+ * kernel, and an atomic scatter kernel.  Same result as fem_matvec_apply up
+ * to rounding order.  Asynchronous. */
+spmv_status fem_matvec_threestage(int32_t n_elem, int32_t n_dof, const int32_t *edof,
+                                  const float *rho, int32_t penalty, const float *Ke,
+                                  float alpha, const float *x, float beta, float *y,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPMV_AMD_H */

@@ -1,0 +1,309 @@
+"""Python binding of the MI355X SpMV library (libspmv_amd.so, C ABI in
+include/spmv.h).
+
+Each function has the name of the C entry point it calls and only marshals
+arguments: torch tensors (or NumPy arrays for the host-side MACKO encoder)
+become pointers, ``stream=None`` becomes torch's current stream on the
+tensors' device.  Every step of the computation runs in the library's HIP
+kernels; nothing here computes.  A non-zero status raises ``SpmvError`` with
+the library's message.
+
+``CSRMatrix`` is a small convenience wrapper that owns the plan workspace and
+the handle of ``spmv_csr_create``.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+
+__all__ = [
+    "SpmvError", "STATUS", "CSR_AUTO", "CSR_SCALAR", "CSR_VECTOR", "CSR_BINNED",
+    "FORMAT_ELL", "FORMAT_HYB", "FORMAT_CSR", "lib",
+    "spmv_csr_row_stats", "spmv_format_recommend", "spmv_csr_plan_size", "spmv_csr_create",
+    "spmv_csr_apply", "spmv_csr_get_plan", "spmv_csr_info", "spmv_csr_destroy",
+    "spmv_ell_from_csr", "spmv_ell_apply", "macko_encode_size", "macko_encode", "macko_spmv",
+    "macko_decode_columns", "dense_gemv_f16", "fem_matvec_apply", "fem_threestage_size",
+    "fem_matvec_threestage", "CSRMatrix",
+]
+
+STATUS = {0: "SPMV_OK", 1: "SPMV_ERR_INVALID_VALUE", 2: "SPMV_ERR_INVALID_MATRIX",
+          3: "SPMV_ERR_UNSORTED", 4: "SPMV_ERR_OVERFLOW", 5: "SPMV_ERR_UNSUPPORTED", 6: "SPMV_ERR_HIP"}
+CSR_AUTO, CSR_SCALAR, CSR_VECTOR, CSR_BINNED = 0, 1, 2, 3
+FORMAT_ELL, FORMAT_HYB, FORMAT_CSR = 0, 1, 2
+
+
+class SpmvError(RuntimeError):
+    def __init__(self, status: int, func: str, message: str):
+        self.status = status
+        super().__init__(f"{func}: {STATUS.get(status, status)}: {message}")
+
+
+def lib():
+    return _lib.load()
+
+
+def _check(status: int, func: str):
+    if status != 0:
+        msg = lib().spmv_last_error().decode(errors="replace")
+        raise SpmvError(status, func, msg)
+
+
+def _call(name: str, *args):
+    _check(getattr(lib(), name)(*args), name)
+
+
+def _dev(t, dtype, name, allow_none=False):
+    """Device pointer of a contiguous CUDA tensor of the given dtype."""
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    ok = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in ok:
+        raise TypeError(f"{name} must be one of {ok}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _host(a, dtype, name):
+    a = np.asarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"{name} must be {np.dtype(dtype)}, got {a.dtype}")
+    if not a.flags.c_contiguous:
+        raise ValueError(f"{name} must be C-contiguous")
+    return a
+
+
+def _stream(stream, like=None):
+    if stream is None:
+        import torch
+        dev = like.device if like is not None else None
+        return torch.cuda.current_stream(dev).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _i32_dtype():
+    import torch
+    return torch.int32
+
+
+def _f32_dtype():
+    import torch
+    return torch.float32
+
+
+def _u16_dtype():
+    """fp16 data may come as float16 or as its raw bits (uint16 / int16)."""
+    import torch
+    return (torch.float16, torch.uint16, torch.int16)
+
+
+def _u32_dtype():
+    """Packed code words: uint32 or int32 with the same bits."""
+    import torch
+    return (torch.uint32, torch.int32)
+
+
+# ---------------------------------------------------------------------------
+# Row statistics and format choice
+# ---------------------------------------------------------------------------
+def spmv_csr_row_stats(row_ptr, stream=None):
+    """(max_len, sum_len, sum_len_sq) of a device int32 row_ptr."""
+    n = row_ptr.numel() - 1
+    m, s, q = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    _call("spmv_csr_row_stats", n, _dev(row_ptr, _i32_dtype(), "row_ptr"), ctypes.byref(m),
+          ctypes.byref(s), ctypes.byref(q), _stream(stream, row_ptr))
+    return m.value, s.value, q.value
+
+
+def spmv_format_recommend(n_rows, sum_len, sum_len_sq) -> int:
+    f = ctypes.c_int32()
+    _call("spmv_format_recommend", int(n_rows), int(sum_len), int(sum_len_sq), ctypes.byref(f))
+    return f.value
+
+
+# ---------------------------------------------------------------------------
+# CSR
+# ---------------------------------------------------------------------------
+def _thr(thresholds):
+    if thresholds is None:
+        return None, None
+    a = (ctypes.c_int32 * 3)(*[int(t) for t in thresholds])
+    return a, ctypes.addressof(a)
+
+
+def spmv_csr_plan_size(n_rows, nnz, thresholds=None) -> int:
+    keep, p = _thr(thresholds)
+    out = ctypes.c_size_t()
+    _call("spmv_csr_plan_size", int(n_rows), int(nnz), p, ctypes.byref(out))
+    return out.value
+
+
+def spmv_csr_create(n_rows, n_cols, row_ptr, col_idx, vals, variant=CSR_AUTO, thresholds=None,
+                    workspace=None, stream=None):
+    """Returns an opaque handle (int).  workspace: a CUDA uint8 tensor of at
+    least spmv_csr_plan_size() bytes (needed by BINNED / AUTO)."""
+    keep, p = _thr(thresholds)
+    h = ctypes.c_void_p()
+    nnz = col_idx.numel()
+    ws = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("spmv_csr_create", ctypes.byref(h), int(n_rows), int(n_cols), int(nnz),
+          _dev(row_ptr, _i32_dtype(), "row_ptr"), _dev(col_idx, _i32_dtype(), "col_idx"),
+          _dev(vals, _f32_dtype(), "vals"), int(variant), p, ws, ws_bytes, _stream(stream, row_ptr))
+    return h.value
+
+
+def spmv_csr_apply(h, alpha, x, beta, y, stream=None):
+    _call("spmv_csr_apply", h, float(alpha), _dev(x, _f32_dtype(), "x"), float(beta),
+          _dev(y, _f32_dtype(), "y"), _stream(stream, y))
+
+
+def spmv_csr_get_plan(h, perm_out=None, stream=None):
+    """bin_offsets (list of 5 ints); fills perm_out (CUDA int32 [n_rows]) if given."""
+    off = (ctypes.c_int32 * 5)()
+    _call("spmv_csr_get_plan", h, off, _dev(perm_out, _i32_dtype(), "perm_out", allow_none=True),
+          _stream(stream, perm_out))
+    return list(off)
+
+
+def spmv_csr_info(h):
+    v, g, b = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _call("spmv_csr_info", h, ctypes.byref(v), ctypes.byref(g), ctypes.byref(b))
+    return {"variant": v.value, "group_lanes": g.value, "n_short_blocks": b.value}
+
+
+def spmv_csr_destroy(h):
+    _call("spmv_csr_destroy", h)
+
+
+class CSRMatrix:
+    """Owns the plan workspace and handle of one CSR matrix (device tensors)."""
+
+    def __init__(self, n_rows, n_cols, row_ptr, col_idx, vals, variant=CSR_AUTO, thresholds=None,
+                 stream=None):
+        import torch
+        self.n_rows, self.n_cols = int(n_rows), int(n_cols)
+        self._arrays = (row_ptr, col_idx, vals)          # borrowed by the handle: keep alive
+        self.workspace = None
+        if variant in (CSR_AUTO, CSR_BINNED):
+            nb = spmv_csr_plan_size(n_rows, col_idx.numel(), thresholds)
+            self.workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=row_ptr.device)
+        self.handle = spmv_csr_create(n_rows, n_cols, row_ptr, col_idx, vals, variant, thresholds,
+                                      self.workspace, stream)
+
+    def apply(self, x, y, alpha=1.0, beta=0.0, stream=None):
+        spmv_csr_apply(self.handle, alpha, x, beta, y, stream)
+        return y
+
+    def plan(self, perm_out=None):
+        return spmv_csr_get_plan(self.handle, perm_out)
+
+    def info(self):
+        return spmv_csr_info(self.handle)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            spmv_csr_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------------------------------
+# ELL
+# ---------------------------------------------------------------------------
+def spmv_ell_from_csr(n_rows, n_cols, row_ptr, col_idx, vals, width, ell_col, ell_val, stream=None):
+    _call("spmv_ell_from_csr", int(n_rows), int(n_cols), int(col_idx.numel()),
+          _dev(row_ptr, _i32_dtype(), "row_ptr"), _dev(col_idx, _i32_dtype(), "col_idx"),
+          _dev(vals, _f32_dtype(), "vals"), int(width), _dev(ell_col, _i32_dtype(), "ell_col"),
+          _dev(ell_val, _f32_dtype(), "ell_val"), _stream(stream, row_ptr))
+
+
+def spmv_ell_apply(n_rows, n_cols, width, ell_col, ell_val, alpha, x, beta, y, stream=None):
+    _call("spmv_ell_apply", int(n_rows), int(n_cols), int(width),
+          _dev(ell_col, _i32_dtype(), "ell_col"), _dev(ell_val, _f32_dtype(), "ell_val"),
+          float(alpha), _dev(x, _f32_dtype(), "x"), float(beta), _dev(y, _f32_dtype(), "y"),
+          _stream(stream, y))
+
+
+# ---------------------------------------------------------------------------
+# MACKO (encoder on the host, kernels on the device)
+# ---------------------------------------------------------------------------
+def macko_encode_size(n_rows, n_cols, row_ptr, col_idx) -> int:
+    rp = _host(row_ptr, np.int32, "row_ptr")
+    ci = _host(col_idx, np.int32, "col_idx")
+    out = ctypes.c_int64()
+    _call("macko_encode_size", int(n_rows), int(n_cols), rp.ctypes.data, ci.ctypes.data, ctypes.byref(out))
+    return out.value
+
+
+def macko_encode(n_rows, n_cols, row_ptr, col_idx, vals_f16):
+    """Host encode: returns (mrow_ptr int32[R+1], codes uint32[E/8], mvals uint16[E])."""
+    rp = _host(row_ptr, np.int32, "row_ptr")
+    ci = _host(col_idx, np.int32, "col_idx")
+    vv = _host(vals_f16, np.uint16, "vals_f16")
+    E = macko_encode_size(n_rows, n_cols, rp, ci)
+    mrp = np.empty(n_rows + 1, np.int32)
+    codes = np.empty(max(E // 8, 1), np.uint32)[:E // 8]
+    mv = np.empty(max(E, 1), np.uint16)[:E]
+    _call("macko_encode", int(n_rows), int(n_cols), rp.ctypes.data, ci.ctypes.data, vv.ctypes.data,
+          mrp.ctypes.data, codes.ctypes.data, mv.ctypes.data)
+    return mrp, codes, mv
+
+
+def macko_spmv(n_rows, n_cols, mrow_ptr, codes, mvals, alpha, x_f16, beta, y, stream=None):
+    _call("macko_spmv", int(n_rows), int(n_cols), _dev(mrow_ptr, _i32_dtype(), "mrow_ptr"),
+          _dev(codes, _u32_dtype(), "codes"), _dev(mvals, _u16_dtype(), "mvals"), float(alpha),
+          _dev(x_f16, _u16_dtype(), "x_f16"), float(beta), _dev(y, _f32_dtype(), "y"), _stream(stream, y))
+
+
+def macko_decode_columns(n_rows, mrow_ptr, codes, cols_out, stream=None):
+    _call("macko_decode_columns", int(n_rows), _dev(mrow_ptr, _i32_dtype(), "mrow_ptr"),
+          _dev(codes, _u32_dtype(), "codes"), _dev(cols_out, _i32_dtype(), "cols_out"),
+          _stream(stream, cols_out))
+
+
+# ---------------------------------------------------------------------------
+# Dense fp16 GEMV
+# ---------------------------------------------------------------------------
+def dense_gemv_f16(m, n, W, x_f16, alpha, beta, y, stream=None):
+    _call("dense_gemv_f16", int(m), int(n), _dev(W, _u16_dtype(), "W"), _dev(x_f16, _u16_dtype(), "x_f16"),
+          float(alpha), float(beta), _dev(y, _f32_dtype(), "y"), _stream(stream, y))
+
+
+# ---------------------------------------------------------------------------
+# Finite-element matvec
+# ---------------------------------------------------------------------------
+def fem_matvec_apply(n_elem, n_dof, edof, rho, penalty, Ke, alpha, x, beta, y, stream=None):
+    _call("fem_matvec_apply", int(n_elem), int(n_dof), _dev(edof, _i32_dtype(), "edof"),
+          _dev(rho, _f32_dtype(), "rho"), int(penalty), _dev(Ke, _f32_dtype(), "Ke"), float(alpha),
+          _dev(x, _f32_dtype(), "x"), float(beta), _dev(y, _f32_dtype(), "y"), _stream(stream, y))
+
+
+def fem_threestage_size(n_elem) -> int:
+    out = ctypes.c_size_t()
+    _call("fem_threestage_size", int(n_elem), ctypes.byref(out))
+    return out.value
+
+
+def fem_matvec_threestage(n_elem, n_dof, edof, rho, penalty, Ke, alpha, x, beta, y, workspace,
+                          stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _call("fem_matvec_threestage", int(n_elem), int(n_dof), _dev(edof, _i32_dtype(), "edof"),
+          _dev(rho, _f32_dtype(), "rho"), int(penalty), _dev(Ke, _f32_dtype(), "Ke"), float(alpha),
+          _dev(x, _f32_dtype(), "x"), float(beta), _dev(y, _f32_dtype(), "y"), workspace.data_ptr(),
+          ws_bytes, _stream(stream, y))

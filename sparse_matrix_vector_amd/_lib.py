@@ -1,0 +1,61 @@
+"""ctypes loader and signatures of libspmv_amd.so (the C ABI in include/spmv.h).
+
+The library must have been built (``__graft_entry__.build()`` or
+``python -m sparse_matrix_vector_amd.csrc.build``); loading fails loudly
+otherwise.  There is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspmv_amd.so")
+
+c_i32, c_i64, c_f32, c_sz, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+P_i32 = ctypes.POINTER(ctypes.c_int32)
+P_i64 = ctypes.POINTER(ctypes.c_int64)
+P_sz = ctypes.POINTER(ctypes.c_size_t)
+P_vp = ctypes.POINTER(ctypes.c_void_p)
+
+# name -> argument types (every function returns spmv_status, an int)
+SIGNATURES = {
+    "spmv_csr_row_stats": [c_i32, vp, P_i32, P_i64, P_i64, vp],
+    "spmv_format_recommend": [c_i64, c_i64, c_i64, P_i32],
+    "spmv_csr_plan_size": [c_i32, c_i32, vp, P_sz],
+    "spmv_csr_create": [P_vp, c_i32, c_i32, c_i32, vp, vp, vp, c_i32, vp, vp, c_sz, vp],
+    "spmv_csr_apply": [vp, c_f32, vp, c_f32, vp, vp],
+    "spmv_csr_get_plan": [vp, P_i32, vp, vp],
+    "spmv_csr_info": [vp, P_i32, P_i32, P_i32],
+    "spmv_csr_destroy": [vp],
+    "spmv_ell_from_csr": [c_i32, c_i32, c_i32, vp, vp, vp, c_i32, vp, vp, vp],
+    "spmv_ell_apply": [c_i32, c_i32, c_i32, vp, vp, c_f32, vp, c_f32, vp, vp],
+    "macko_encode_size": [c_i32, c_i32, vp, vp, P_i64],
+    "macko_encode": [c_i32, c_i32, vp, vp, vp, vp, vp, vp],
+    "macko_spmv": [c_i32, c_i32, vp, vp, vp, c_f32, vp, c_f32, vp, vp],
+    "macko_decode_columns": [c_i32, vp, vp, vp, vp],
+    "dense_gemv_f16": [c_i32, c_i32, vp, vp, c_f32, c_f32, vp, vp],
+    "fem_matvec_apply": [c_i32, c_i32, vp, vp, c_i32, vp, c_f32, vp, c_f32, vp, vp],
+    "fem_threestage_size": [c_i32, P_sz],
+    "fem_matvec_threestage": [c_i32, c_i32, vp, vp, c_i32, vp, c_f32, vp, c_f32, vp, vp, c_sz, vp],
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -m sparse_matrix_vector_amd.csrc.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.spmv_last_error.restype = ctypes.c_char_p
+        L.spmv_last_error.argtypes = []
+        for name, args in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = args
+        _lib = L
+    return _lib

@@ -1,0 +1,107 @@
+// Shared host helpers (status / error text / launch checks) and wave64
+// device primitives for the gfx950 SpMV kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "spmv.h"
+
+namespace spmv {
+
+// ---------------------------------------------------------------------------
+// Host: thread-local error message and status helpers.
+// ---------------------------------------------------------------------------
+void set_error(const char *fmt, ...);
+void clear_error();
+
+inline spmv_status fail(spmv_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    set_error("%s", buf);
+    return s;
+}
+
+#define SPMV_HIP(call)                                                          \
+    do {                                                                        \
+        hipError_t e_ = (call);                                                 \
+        if (e_ != hipSuccess)                                                   \
+            return ::spmv::fail(SPMV_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+#define SPMV_LAUNCHED(name)                                                     \
+    do {                                                                        \
+        hipError_t e_ = hipGetLastError();                                      \
+        if (e_ != hipSuccess)                                                   \
+            return ::spmv::fail(SPMV_ERR_HIP, "launch of %s: %s", name, hipGetErrorString(e_)); \
+    } while (0)
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Number of compute units of the current device (cached per device id).
+int device_cu_count();
+
+// ---------------------------------------------------------------------------
+// Device: wave64 primitives.
+//
+// DPP controls of the GFX9-family data-parallel-primitives encoding (CDNA
+// keeps the row broadcasts that RDNA dropped).
+// ---------------------------------------------------------------------------
+constexpr int DPP_ROW_SHR1 = 0x111;
+constexpr int DPP_ROW_SHR2 = 0x112;
+constexpr int DPP_ROW_SHR4 = 0x114;
+constexpr int DPP_ROW_SHR8 = 0x118;
+constexpr int DPP_ROW_BCAST15 = 0x142;
+constexpr int DPP_ROW_BCAST31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active).
+// Rows of 16 lanes are scanned with shifted adds, then row totals are
+// propagated with the two row broadcasts.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, DPP_ROW_SHR1, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, DPP_ROW_SHR2, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, DPP_ROW_SHR4, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, DPP_ROW_SHR8, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, DPP_ROW_BCAST15, 0xa, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, DPP_ROW_BCAST31, 0xc, 0xf, false);
+    return v;
+}
+
+// One scan step on floats: v += (v of the lane selected by `ctrl`), lanes
+// without a source (or outside `row_mask`) add +0.
+#define SPMV_DPP_FADD(v, ctrl, row_mask)                                              \
+    (v) += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), (ctrl),     \
+                                                      (row_mask), 0xf, false))
+
+// Sum over the 64 lanes (all lanes active); the total is returned in every
+// lane.  Fixed order, so the result is bit-reproducible.
+__device__ __forceinline__ float wave_sum(float v) {
+    SPMV_DPP_FADD(v, DPP_ROW_SHR1, 0xf);
+    SPMV_DPP_FADD(v, DPP_ROW_SHR2, 0xf);
+    SPMV_DPP_FADD(v, DPP_ROW_SHR4, 0xf);
+    SPMV_DPP_FADD(v, DPP_ROW_SHR8, 0xf);
+    SPMV_DPP_FADD(v, DPP_ROW_BCAST15, 0xa);
+    SPMV_DPP_FADD(v, DPP_ROW_BCAST31, 0xc);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Non-temporal loads for streamed matrix data: read once, so keep them from
+// evicting the gathered vector from the caches.
+template <typename T>
+__device__ __forceinline__ T stream_load(const T *p) {
+    return __builtin_nontemporal_load(p);
+}
+
+}  // namespace spmv

@@ -1,0 +1,175 @@
+// ELL on gfx950: CSR -> ELL conversion and the ELL product.
+//
+// "Why SpMV needs CUDA optimisation" (section 2.1 table) names ELL as the
+// fixed-width, zero-padded format that suits rows of equal length and is
+// sensitive to padding.  Layout here: slot-major, entry k of row i at
+// [k * n_rows + i], so lane i of a wave reads row i's k-th entry and
+// consecutive lanes read consecutive words.  A padding slot holds column -1
+// and value +0.0f and is skipped (x is never read for it).
+//
+// Apply: when n_rows % 4 == 0 and the arrays are 16-byte aligned, each lane
+// owns four consecutive rows and reads each slot as one 16-byte load of
+// columns and one of values; otherwise one lane per row with 4-byte loads.
+// Products are summed in slot order in fp32.
+#include "common.hpp"
+
+#include <algorithm>
+
+namespace spmv {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WG = 256;
+
+// Copies row i's entries into its slots and pads the rest.  Columns outside
+// [0, n_cols) and an inconsistent row_ptr raise `err` (the caller reports it).
+__global__ __launch_bounds__(WG) void k_ell_from_csr(int n, int n_cols, int nnz, int width,
+                                                     const int *__restrict__ rp, const int *__restrict__ ci,
+                                                     const float *__restrict__ v, int *__restrict__ ec,
+                                                     float *__restrict__ ev, int *__restrict__ err) {
+    const int i = blockIdx.x * WG + threadIdx.x;
+    if (i >= n) return;
+    const int s = rp[i], len = rp[i + 1] - s;
+    bool bad = (i == 0 && s != 0) || (i == n - 1 && rp[n] != nnz) || len < 0 || len > width;
+    for (int k = 0; k < width; ++k) {
+        const size_t slot = (size_t)k * (size_t)n + (size_t)i;
+        const bool real = !bad && k < len;
+        const int c = real ? ci[s + k] : -1;
+        bad |= real && (unsigned)c >= (unsigned)n_cols;
+        ec[slot] = c;
+        ev[slot] = real ? v[s + k] : 0.0f;
+    }
+    if (bad) atomicOr(err, 1);
+}
+
+// Same XCD grouping as the CSR kernels: the workgroups dispatched to one XCD
+// take a contiguous range of rows.
+__device__ __forceinline__ int xcd_contiguous(int w, int nw) {
+    constexpr int NX = 8;
+    const int q = nw / NX, r = nw % NX;
+    const int xcd = w % NX, idx = w / NX;
+    return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
+__device__ __forceinline__ float finish(float acc, float alpha, float beta, float yold) {
+    float r = alpha * acc;
+    if (beta != 0.0f) r = fmaf(beta, yold, r);
+    return r;
+}
+
+// Four rows per lane, 16-byte slot loads.
+__global__ __launch_bounds__(WG) void k_ell_apply4(int n, int width, const int *__restrict__ ec,
+                                                   const float *__restrict__ ev, float alpha,
+                                                   const float *__restrict__ x, float beta, float *__restrict__ y) {
+    const int w = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int quad = w * WG + threadIdx.x;
+    const int i0 = 4 * quad;
+    if (i0 >= n) return;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = 0; k < width; ++k) {
+        const size_t slot = (size_t)k * (size_t)n + (size_t)i0;
+        const i32x4 c = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(ec + slot));
+        const f32x4 f = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(ev + slot));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (c[t] >= 0) acc[t] = fmaf(f[t], x[c[t]], acc[t]);
+    }
+    f32x4 yo = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (beta != 0.0f) yo = *reinterpret_cast<const f32x4 *>(y + i0);
+    f32x4 r;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) r[t] = finish(acc[t], alpha, beta, yo[t]);
+    *reinterpret_cast<f32x4 *>(y + i0) = r;
+}
+
+// One row per lane.
+__global__ __launch_bounds__(WG) void k_ell_apply1(int n, int width, const int *__restrict__ ec,
+                                                   const float *__restrict__ ev, float alpha,
+                                                   const float *__restrict__ x, float beta, float *__restrict__ y) {
+    const int w = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int i = w * WG + threadIdx.x;
+    if (i >= n) return;
+    float acc = 0.0f;
+    for (int k = 0; k < width; ++k) {
+        const size_t slot = (size_t)k * (size_t)n + (size_t)i;
+        const int c = ec[slot];
+        if (c >= 0) acc = fmaf(ev[slot], x[c], acc);
+    }
+    y[i] = finish(acc, alpha, beta, beta != 0.0f ? y[i] : 0.0f);
+}
+
+__global__ void k_scale(int n, float beta, float *__restrict__ y) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) y[i] = beta != 0.0f ? beta * y[i] : 0.0f;
+}
+
+}  // namespace
+}  // namespace spmv
+
+using namespace spmv;
+
+extern "C" spmv_status spmv_ell_from_csr(int32_t n_rows, int32_t n_cols, int32_t nnz, const int32_t *row_ptr,
+                                         const int32_t *col_idx, const float *vals, int32_t width,
+                                         int32_t *ell_col, float *ell_val, void *stream) {
+    if (n_rows < 0 || n_cols < 0 || nnz < 0 || width < 0) return fail(SPMV_ERR_INVALID_VALUE, "negative size");
+    if ((int64_t)n_rows * width > INT32_MAX)
+        return fail(SPMV_ERR_OVERFLOW, "width * n_rows = %lld exceeds int32", (long long)n_rows * width);
+    if (n_rows == 0 || width == 0) {
+        if (n_rows > 0 && nnz > 0) return fail(SPMV_ERR_INVALID_VALUE, "width 0 cannot hold %d nonzeros", nnz);
+        return SPMV_OK;
+    }
+    if (!row_ptr || !ell_col || !ell_val || (nnz > 0 && (!col_idx || !vals)))
+        return fail(SPMV_ERR_INVALID_VALUE, "NULL pointer");
+    int32_t max_len = 0;
+    int64_t s1 = 0, s2 = 0;
+    spmv_status s = spmv_csr_row_stats(n_rows, row_ptr, &max_len, &s1, &s2, stream);
+    if (s != SPMV_OK) return s;
+    if (s1 != nnz) return fail(SPMV_ERR_INVALID_MATRIX, "row lengths sum to %lld, not nnz = %d", (long long)s1, nnz);
+    if (max_len > width) return fail(SPMV_ERR_INVALID_VALUE, "width %d is shorter than the longest row (%d)", width, max_len);
+    hipStream_t st = as_stream(stream);
+    // with row_ptr[0] == 0, non-decreasing rows and lengths summing to nnz,
+    // every entry the conversion reads lies in [0, nnz)
+    int rp0 = -1;
+    SPMV_HIP(hipMemcpyAsync(&rp0, row_ptr, sizeof(int), hipMemcpyDeviceToHost, st));
+    SPMV_HIP(hipStreamSynchronize(st));
+    if (rp0 != 0) return fail(SPMV_ERR_INVALID_MATRIX, "row_ptr[0] != 0");
+    int *d_err = nullptr;
+    SPMV_HIP(hipMallocAsync(reinterpret_cast<void **>(&d_err), sizeof(int), st));
+    SPMV_HIP(hipMemsetAsync(d_err, 0, sizeof(int), st));
+    k_ell_from_csr<<<(int)ceil_div(n_rows, WG), WG, 0, st>>>(n_rows, n_cols, nnz, width, row_ptr, col_idx, vals,
+                                                             ell_col, ell_val, d_err);
+    SPMV_LAUNCHED("k_ell_from_csr");
+    int err = 0;
+    SPMV_HIP(hipMemcpyAsync(&err, d_err, sizeof(int), hipMemcpyDeviceToHost, st));
+    SPMV_HIP(hipFreeAsync(d_err, st));
+    SPMV_HIP(hipStreamSynchronize(st));
+    if (err) return fail(SPMV_ERR_INVALID_MATRIX, "row_ptr inconsistent or a column outside [0, n_cols)");
+    return SPMV_OK;
+}
+
+extern "C" spmv_status spmv_ell_apply(int32_t n_rows, int32_t n_cols, int32_t width, const int32_t *ell_col,
+                                      const float *ell_val, float alpha, const float *x, float beta, float *y,
+                                      void *stream) {
+    if (n_rows < 0 || n_cols < 0 || width < 0) return fail(SPMV_ERR_INVALID_VALUE, "negative size");
+    if ((int64_t)n_rows * width > INT32_MAX) return fail(SPMV_ERR_OVERFLOW, "width * n_rows exceeds int32");
+    if (n_rows == 0) return SPMV_OK;
+    if (!y) return fail(SPMV_ERR_INVALID_VALUE, "y is NULL");
+    hipStream_t st = as_stream(stream);
+    if (width == 0) {
+        k_scale<<<(int)ceil_div(n_rows, WG), WG, 0, st>>>(n_rows, beta, y);
+        SPMV_LAUNCHED("k_scale");
+        return SPMV_OK;
+    }
+    if (!ell_col || !ell_val || !x) return fail(SPMV_ERR_INVALID_VALUE, "NULL pointer");
+    const bool quad = (n_rows % 4 == 0) && aligned16(ell_col) && aligned16(ell_val) && aligned16(y);
+    if (quad) {
+        k_ell_apply4<<<(int)ceil_div(n_rows / 4, WG), WG, 0, st>>>(n_rows, width, ell_col, ell_val, alpha, x, beta, y);
+        SPMV_LAUNCHED("k_ell_apply4");
+    } else {
+        k_ell_apply1<<<(int)ceil_div(n_rows, WG), WG, 0, st>>>(n_rows, width, ell_col, ell_val, alpha, x, beta, y);
+        SPMV_LAUNCHED("k_ell_apply1");
+    }
+    return SPMV_OK;
+}

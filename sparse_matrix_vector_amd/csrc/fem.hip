@@ -1,0 +1,212 @@
+// Finite-element stiffness matvec on gfx950.
+//
+// "Fused GPU SpMV kernel optimisation: from bandwidth bottleneck to BF16
+// precision", section 2.1: the unfused form gathers every element's 24 DOFs
+// into a per-element vector, multiplies by the element matrix, and scatters
+// the result with atomic adds, one kernel per stage with the intermediates
+// in DRAM.  Section 2.2: the fused form keeps the gathered vector and the
+// product in registers and issues one launch.  Section 5.1 gives the fused
+// kernel's shape (one thread per element), section 5.2 notes that a Ke shared
+// by all elements belongs in fast on-chip memory.
+//
+// Operator: y = alpha * sum_e rho_e^p * P_e^T Ke P_e x + beta * y, with one
+// shared Ke (24 x 24, row-major) scaled per element by the SIMP factor
+// rho_e^p.  An edof entry outside [0, n_dof) (the mesh uses -1 for a
+// clamped DOF) contributes no gather and no scatter.
+//
+// gfx950 shape of the fused kernel: one lane per element, Ke staged in LDS
+// once per workgroup and read with broadcast (same-address) LDS reads, the
+// element's 24 DOF indices read with six 16-byte loads, 24 gathers of x,
+// 576 FMAs, and 24 fp32 atomic adds (hardware global_atomic_add_f32).  The
+// beta pass runs first as a separate small kernel, because atomics only add.
+#include "common.hpp"
+
+#include <algorithm>
+
+namespace spmv {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int FE_WG = 256;
+constexpr int NDOF_E = 24;
+constexpr int MAX_PENALTY = 8;
+
+__device__ __forceinline__ float simp(float r, int p) {
+    float s = 1.0f;
+    for (int k = 0; k < p; ++k) s *= r;
+    return s;
+}
+
+__global__ void k_fe_beta(int n, float beta, float *__restrict__ y) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) y[i] = beta != 0.0f ? beta * y[i] : 0.0f;
+}
+
+__device__ __forceinline__ void load_edof(const int *__restrict__ edof, int e, int (&d)[NDOF_E]) {
+    const i32x4 *p = reinterpret_cast<const i32x4 *>(edof + (size_t)e * NDOF_E);
+#pragma unroll
+    for (int k = 0; k < NDOF_E / 4; ++k) {
+        const i32x4 q = __builtin_nontemporal_load(p + k);
+        d[4 * k + 0] = q.x;
+        d[4 * k + 1] = q.y;
+        d[4 * k + 2] = q.z;
+        d[4 * k + 3] = q.w;
+    }
+}
+
+__global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const int *__restrict__ edof,
+                                                    const float *__restrict__ rho, int penalty,
+                                                    const float *__restrict__ Ke, float alpha,
+                                                    const float *__restrict__ x, float *__restrict__ y) {
+    __shared__ __attribute__((aligned(16))) float ke[NDOF_E * NDOF_E];
+    for (int k = threadIdx.x; k < NDOF_E * NDOF_E; k += FE_WG) ke[k] = Ke[k];
+    __syncthreads();
+    const int e = blockIdx.x * FE_WG + threadIdx.x;
+    if (e >= n_elem) return;
+    int d[NDOF_E];
+    load_edof(edof, e, d);
+    float u[NDOF_E];
+#pragma unroll
+    for (int b = 0; b < NDOF_E; ++b) u[b] = (unsigned)d[b] < (unsigned)n_dof ? x[d[b]] : 0.0f;
+    const float s = alpha * simp(rho[e], penalty);
+#pragma unroll
+    for (int a = 0; a < NDOF_E; ++a) {
+        float f = 0.0f;
+#pragma unroll
+        for (int b = 0; b < NDOF_E; b += 4) {
+            const f32x4 k4 = *reinterpret_cast<const f32x4 *>(ke + a * NDOF_E + b);
+            f = fmaf(k4.x, u[b], f);
+            f = fmaf(k4.y, u[b + 1], f);
+            f = fmaf(k4.z, u[b + 2], f);
+            f = fmaf(k4.w, u[b + 3], f);
+        }
+        if ((unsigned)d[a] < (unsigned)n_dof) atomicAdd(y + d[a], s * f);
+    }
+}
+
+// ---- three-stage comparator ----
+
+// U[e][b] = x[edof[e][b]] (0 for a constrained DOF); one thread per entry.
+__global__ void k_fe_gather(int n_elem, int n_dof, const int *__restrict__ edof, const float *__restrict__ x,
+                            float *__restrict__ U) {
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= (int64_t)n_elem * NDOF_E) return;
+    const int d = edof[k];
+    U[k] = (unsigned)d < (unsigned)n_dof ? x[d] : 0.0f;
+}
+
+// F[e] = alpha * rho_e^p * Ke U[e]; one thread per element.
+__global__ __launch_bounds__(FE_WG) void k_fe_elem(int n_elem, const float *__restrict__ rho, int penalty,
+                                                   const float *__restrict__ Ke, float alpha,
+                                                   const float *__restrict__ U, float *__restrict__ F) {
+    __shared__ __attribute__((aligned(16))) float ke[NDOF_E * NDOF_E];
+    for (int k = threadIdx.x; k < NDOF_E * NDOF_E; k += FE_WG) ke[k] = Ke[k];
+    __syncthreads();
+    const int e = blockIdx.x * FE_WG + threadIdx.x;
+    if (e >= n_elem) return;
+    float u[NDOF_E];
+    const f32x4 *up = reinterpret_cast<const f32x4 *>(U + (size_t)e * NDOF_E);
+#pragma unroll
+    for (int k = 0; k < NDOF_E / 4; ++k) {
+        const f32x4 q = up[k];
+        u[4 * k] = q.x;
+        u[4 * k + 1] = q.y;
+        u[4 * k + 2] = q.z;
+        u[4 * k + 3] = q.w;
+    }
+    const float s = alpha * simp(rho[e], penalty);
+    f32x4 *fp = reinterpret_cast<f32x4 *>(F + (size_t)e * NDOF_E);
+#pragma unroll
+    for (int a4 = 0; a4 < NDOF_E; a4 += 4) {
+        f32x4 o;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float f = 0.0f;
+#pragma unroll
+            for (int b = 0; b < NDOF_E; ++b) f = fmaf(ke[(a4 + t) * NDOF_E + b], u[b], f);
+            o[t] = s * f;
+        }
+        fp[a4 / 4] = o;
+    }
+}
+
+// y[edof[e][a]] += F[e][a]; one thread per entry.
+__global__ void k_fe_scatter(int n_elem, int n_dof, const int *__restrict__ edof, const float *__restrict__ F,
+                             float *__restrict__ y) {
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= (int64_t)n_elem * NDOF_E) return;
+    const int d = edof[k];
+    if ((unsigned)d < (unsigned)n_dof) atomicAdd(y + d, F[k]);
+}
+
+spmv_status check_fe(int32_t n_elem, int32_t n_dof, const int32_t *edof, const float *rho, int32_t penalty,
+                     const float *Ke, const float *x, float *y) {
+    if (n_elem < 0 || n_dof < 0) return fail(SPMV_ERR_INVALID_VALUE, "negative size");
+    if ((int64_t)n_elem * NDOF_E > INT32_MAX) return fail(SPMV_ERR_OVERFLOW, "n_elem * 24 exceeds int32");
+    if (penalty < 0 || penalty > MAX_PENALTY) return fail(SPMV_ERR_INVALID_VALUE, "penalty must be in [0, %d]", MAX_PENALTY);
+    if (n_dof > 0 && !y) return fail(SPMV_ERR_INVALID_VALUE, "y is NULL");
+    if (n_elem > 0 && (!edof || !rho || !Ke || !x)) return fail(SPMV_ERR_INVALID_VALUE, "NULL pointer");
+    if (n_elem > 0 && (!aligned16(edof) || !aligned16(Ke)))
+        return fail(SPMV_ERR_UNSUPPORTED, "edof and Ke must be 16-byte aligned");
+    return SPMV_OK;
+}
+
+}  // namespace
+}  // namespace spmv
+
+using namespace spmv;
+
+extern "C" spmv_status fem_matvec_apply(int32_t n_elem, int32_t n_dof, const int32_t *edof, const float *rho,
+                                        int32_t penalty, const float *Ke, float alpha, const float *x, float beta,
+                                        float *y, void *stream) {
+    spmv_status s = check_fe(n_elem, n_dof, edof, rho, penalty, Ke, x, y);
+    if (s != SPMV_OK) return s;
+    if (n_dof == 0) return SPMV_OK;
+    hipStream_t st = as_stream(stream);
+    if (beta != 1.0f) {
+        k_fe_beta<<<(int)ceil_div(n_dof, 256), 256, 0, st>>>(n_dof, beta, y);
+        SPMV_LAUNCHED("k_fe_beta");
+    }
+    if (n_elem == 0) return SPMV_OK;
+    k_fe_fused<<<(int)ceil_div(n_elem, FE_WG), FE_WG, 0, st>>>(n_elem, n_dof, edof, rho, penalty, Ke, alpha, x, y);
+    SPMV_LAUNCHED("k_fe_fused");
+    return SPMV_OK;
+}
+
+extern "C" spmv_status fem_threestage_size(int32_t n_elem, size_t *bytes) {
+    if (!bytes) return fail(SPMV_ERR_INVALID_VALUE, "bytes is NULL");
+    if (n_elem < 0) return fail(SPMV_ERR_INVALID_VALUE, "negative size");
+    *bytes = 2 * (size_t)n_elem * NDOF_E * sizeof(float);
+    return SPMV_OK;
+}
+
+extern "C" spmv_status fem_matvec_threestage(int32_t n_elem, int32_t n_dof, const int32_t *edof, const float *rho,
+                                             int32_t penalty, const float *Ke, float alpha, const float *x,
+                                             float beta, float *y, void *workspace, size_t workspace_bytes,
+                                             void *stream) {
+    spmv_status s = check_fe(n_elem, n_dof, edof, rho, penalty, Ke, x, y);
+    if (s != SPMV_OK) return s;
+    const size_t need = 2 * (size_t)n_elem * NDOF_E * sizeof(float);
+    if (n_elem > 0 && (!workspace || workspace_bytes < need))
+        return fail(SPMV_ERR_INVALID_VALUE, "workspace of %zu bytes is smaller than %zu", workspace_bytes, need);
+    if (n_elem > 0 && !aligned16(workspace)) return fail(SPMV_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+    if (n_dof == 0) return SPMV_OK;
+    hipStream_t st = as_stream(stream);
+    if (beta != 1.0f) {
+        k_fe_beta<<<(int)ceil_div(n_dof, 256), 256, 0, st>>>(n_dof, beta, y);
+        SPMV_LAUNCHED("k_fe_beta");
+    }
+    if (n_elem == 0) return SPMV_OK;
+    float *U = static_cast<float *>(workspace);
+    float *F = U + (size_t)n_elem * NDOF_E;
+    const int entries = n_elem * NDOF_E;
+    k_fe_gather<<<(int)ceil_div(entries, 256), 256, 0, st>>>(n_elem, n_dof, edof, x, U);
+    SPMV_LAUNCHED("k_fe_gather");
+    k_fe_elem<<<(int)ceil_div(n_elem, FE_WG), FE_WG, 0, st>>>(n_elem, rho, penalty, Ke, alpha, U, F);
+    SPMV_LAUNCHED("k_fe_elem");
+    k_fe_scatter<<<(int)ceil_div(entries, 256), 256, 0, st>>>(n_elem, n_dof, edof, F, y);
+    SPMV_LAUNCHED("k_fe_scatter");
+    return SPMV_OK;
+}

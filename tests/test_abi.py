@@ -1,0 +1,137 @@
+"""CPU-side checks of the C-ABI library (no GPU kernel is launched here).
+
+* the library loads and exports every entry point declared in include/spmv.h;
+* the host-only format rule matches the oracle's rule on the golden CV cases
+  and on random statistics;
+* the host MACKO encoder is bit-exact with the oracle encoder (mrow_ptr,
+  codes, values) and rejects unsorted / duplicate / out-of-range columns;
+* argument validation that runs before any HIP call returns the documented
+  status.
+"""
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gen
+import oracle
+import sparse_matrix_vector_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLD = os.path.join(ROOT, "tests", "golden")
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "spmv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:spmv_status|const char \*)\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 19
+    L = S.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # and the binding exposes the same names
+    for n in names:
+        if n != "spmv_last_error":
+            assert callable(getattr(S, n)), n
+
+
+def test_format_recommend_matches_oracle():
+    g = json.load(open(os.path.join(GOLD, "cv_rule.json")))
+    for case in g["cases"]:
+        lens = np.asarray(case["row_lengths"], dtype=np.int64)
+        n, s1, s2 = len(lens), int(lens.sum()), int((lens * lens).sum())
+        assert S.spmv_format_recommend(n, s1, s2) == case["choice"]
+    rng = np.random.default_rng(0)
+    for _ in range(3000):
+        n = int(rng.integers(0, 40))
+        lens = rng.integers(0, 60, n)
+        s1, s2 = int(lens.sum()), int((lens * lens).sum())
+        assert S.spmv_format_recommend(n, s1, s2) == oracle.format_choice(n, s1, s2)
+    big = 2**31 - 1
+    assert S.spmv_format_recommend(big, big * 8, big * 64) == oracle.format_choice(big, big * 8, big * 64)
+
+
+def test_plan_size_validation():
+    assert S.spmv_csr_plan_size(1000, 5000) > 0
+    with pytest.raises(S.SpmvError) as e:
+        S.spmv_csr_plan_size(10, 10, (32, 16, 8192))
+    assert e.value.status == 1
+    with pytest.raises(S.SpmvError) as e:
+        S.spmv_csr_plan_size(10, 10, (300, 512, 8192))
+    assert e.value.status == 5
+    with pytest.raises(S.SpmvError):
+        S.spmv_csr_plan_size(-1, 10)
+
+
+@pytest.mark.parametrize("s,n_rows,n_cols", [(0.5, 64, 2048), (0.9, 30, 12288), (0.97, 16, 5000),
+                                             (0.0, 4, 300), (0.3, 33, 999)])
+def test_host_encoder_bit_exact_with_oracle(s, n_rows, n_cols):
+    W = gen.pruned_weight(s, n_rows=n_rows, n_cols=n_cols, seed=77)
+    mrp, codes, mv = S.macko_encode(n_rows, n_cols, W.row_ptr, W.col_idx, W.vals_f16)
+    omrp, ocodes, omv = oracle.macko_encode(n_cols, W.row_ptr, W.col_idx, W.vals_f16)
+    assert np.array_equal(mrp, omrp)
+    assert np.array_equal(codes, ocodes)
+    assert np.array_equal(mv, omv)
+    assert S.macko_encode_size(n_rows, n_cols, W.row_ptr, W.col_idx) == oracle.macko_size(n_cols, W.row_ptr, W.col_idx)
+
+
+def test_host_encoder_golden_and_large_gaps():
+    g = json.load(open(os.path.join(GOLD, "macko_examples.json")))
+    for case in [g["page_example"]] + g["cases"]:
+        cols = np.asarray(case["columns"], np.int32)
+        rp = np.array([0, len(cols)], np.int32)
+        v = np.arange(1, len(cols) + 1).astype(np.float16).view(np.uint16)
+        mrp, codes, mv = S.macko_encode(1, 64, rp, cols, v)
+        k = len(case["codes"])
+        nib = [(int(codes[e // 8]) >> (4 * (e % 8))) & 15 for e in range(k)]
+        assert nib == case["codes"]
+    # a single row spanning 200,000 columns with 3 entries
+    cols = np.array([0, 99_999, 199_999], np.int32)
+    rp = np.array([0, 3], np.int32)
+    v = np.ones(3, np.float16).view(np.uint16)
+    a = S.macko_encode(1, 200_000, rp, cols, v)
+    b = oracle.macko_encode(200_000, rp, cols, v)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("cols,status", [([3, 2], 3), ([4, 4], 3), ([-1, 2], 2), ([1, 64], 2)])
+def test_host_encoder_rejects(cols, status):
+    rp = np.array([0, len(cols)], np.int32)
+    v = np.ones(len(cols), np.float16).view(np.uint16)
+    with pytest.raises(S.SpmvError) as e:
+        S.macko_encode(1, 64, rp, np.asarray(cols, np.int32), v)
+    assert e.value.status == status
+    with pytest.raises(S.SpmvError) as e:
+        S.macko_encode_size(1, 64, rp, np.asarray(cols, np.int32))
+    assert e.value.status == status
+
+
+def test_host_validation_before_any_gpu_call():
+    L = S.lib()
+    import ctypes
+    h = ctypes.c_void_p()
+    # negative sizes / NULL pointers are rejected on the host
+    assert L.spmv_csr_create(ctypes.byref(h), -1, 4, 0, None, None, None, 0, None, None, 0, None) == 1
+    assert L.spmv_csr_create(None, 1, 4, 0, None, None, None, 0, None, None, 0, None) == 1
+    assert L.spmv_csr_create(ctypes.byref(h), 4, 4, 4, None, None, None, 0, None, None, 0, None) == 1
+    assert L.spmv_csr_create(ctypes.byref(h), 4, 4, 4, 8, 8, 8, 9, None, None, 0, None) == 1
+    assert b"variant" in L.spmv_last_error()
+    assert L.spmv_csr_apply(None, 1.0, None, 0.0, None, None) == 1
+    assert L.spmv_ell_apply(-1, 1, 1, None, None, 1.0, None, 0.0, None, None) == 1
+    assert L.spmv_ell_apply(1 << 20, 1, 1 << 12, None, None, 1.0, None, 0.0, None, None) == 4
+    assert L.macko_spmv(4, 4, None, None, None, 1.0, None, 0.0, None, None) == 1
+    assert L.macko_spmv(4, 4, 16, 16, 18, 1.0, 16, 0.0, 16, None) == 5      # misaligned values
+    assert L.dense_gemv_f16(-1, 4, None, None, 1.0, 0.0, None, None) == 1
+    assert L.fem_matvec_apply(4, 10, 16, 16, 9, 16, 1.0, 16, 0.0, 16, None) == 1   # penalty > 8
+    assert L.fem_matvec_apply(4, 10, 20, 16, 3, 16, 1.0, 16, 0.0, 16, None) == 5   # edof misaligned
+    assert L.fem_matvec_threestage(4, 10, 16, 16, 3, 16, 1.0, 16, 0.0, 16, None, 0, None) == 1
+    # n_rows == 0 applies are no-ops that succeed without touching the GPU
+    assert L.macko_spmv(0, 4, None, None, None, 1.0, None, 0.0, None, None) == 0
+    assert L.spmv_ell_apply(0, 4, 2, None, None, 1.0, None, 0.0, None, None) == 0
+    assert L.dense_gemv_f16(0, 4, None, None, 1.0, 0.0, None, None) == 0

@@ -1,0 +1,231 @@
+"""GPU parity of the CSR path (planner, scalar / vector / binned apply) against
+the fp64 CPU oracle, through the C ABI.
+
+* grouping plan (bin_offsets, perm): bit-exact with the oracle's counting sort
+  on the tiny, Laplacian and power-law configs, custom thresholds, and a
+  matrix with rows of 8,192 and 100,000 nonzeros (group 3);
+* values: |y - y_ref| <= 1e-5 * scale for every row, every variant, at the
+  configs' full sizes and on edge cases (empty rows, n_rows = 0, nnz = 0,
+  unsorted and duplicate columns, misaligned arrays, rows around the group
+  bounds, alpha / beta);
+* every variant is bit-reproducible run to run;
+* invalid matrices are rejected by the on-GPU validation.
+"""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from helpers import TAU_F32, assert_close, dev, host
+
+torch = pytest.importorskip("torch")
+S = pytest.importorskip("sparse_matrix_vector_amd")
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = {"scalar": S.CSR_SCALAR, "vector": S.CSR_VECTOR, "binned": S.CSR_BINNED}
+
+
+def _mat(A):
+    return dev(A.row_ptr), dev(A.col_idx), dev(A.vals)
+
+
+def _run(A, variant, alpha=1.0, beta=0.0, y_in=None, thresholds=None, tensors=None):
+    rp, ci, v = tensors if tensors is not None else _mat(A)
+    M = S.CSRMatrix(A.n_rows, A.n_cols, rp, ci, v, variant, thresholds)
+    x = dev(A.x)
+    y = dev(y_in) if y_in is not None else torch.full((A.n_rows,), float("nan"), device="cuda")
+    M.apply(x, y, alpha, beta)
+    torch.cuda.synchronize()
+    return M, host(y)
+
+
+_CACHE = {}
+
+
+def _config(name):
+    if name not in _CACHE:
+        _CACHE[name] = {"tiny": gen.tiny_csr, "laplacian": gen.laplacian_2d,
+                        "powerlaw": gen.powerlaw_csr}[name]()
+    return _CACHE[name]
+
+
+@pytest.mark.parametrize("name", ["tiny", "laplacian", "powerlaw"])
+def test_plan_bit_exact(name):
+    A = _config(name)
+    print(f"[plan] {name} n={A.n_rows} nnz={A.nnz}", flush=True)
+    rp, ci, v = _mat(A)
+    M = S.CSRMatrix(A.n_rows, A.n_cols, rp, ci, v, S.CSR_BINNED)
+    perm = torch.empty(A.n_rows, dtype=torch.int32, device="cuda")
+    off = M.plan(perm)
+    ooff, operm = oracle.bins(A.row_ptr)
+    assert off == ooff.tolist()
+    assert np.array_equal(host(perm), operm)
+    if name == "powerlaw":
+        assert off[4] - off[3] == 0 and off[3] - off[2] > 500 and off[2] - off[1] > 10000
+
+
+@pytest.mark.parametrize("name", ["tiny", "laplacian", "powerlaw"])
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_values_full_configs(name, variant):
+    A = _config(name)
+    print(f"[apply] {name} {variant}", flush=True)
+    M, y = _run(A, VARIANTS[variant])
+    yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x)
+    assert_close(y, yr, sc, TAU_F32, f"{name}/{variant}")
+
+
+def _long_rows_matrix():
+    lens = np.array([3, 8192, 0, 100_000, 31, 32, 511, 512, 8191, 1, 9000, 0, 5], dtype=np.int64)
+    return gen.random_csr(len(lens), 120_000, lens, seed=5)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_group_bounds_and_long_rows(variant):
+    A = _long_rows_matrix()
+    M, y = _run(A, VARIANTS[variant], alpha=0.5, beta=-2.0,
+                y_in=np.linspace(-1, 1, A.n_rows).astype(np.float32))
+    yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x, 0.5, -2.0,
+                             np.linspace(-1, 1, A.n_rows).astype(np.float32))
+    assert_close(y, yr, sc, TAU_F32, f"long/{variant}")
+    if variant == "binned":
+        perm = torch.empty(A.n_rows, dtype=torch.int32, device="cuda")
+        off = M.plan(perm)
+        ooff, operm = oracle.bins(A.row_ptr)
+        assert off == ooff.tolist() and np.array_equal(host(perm), operm)
+        assert off[4] - off[3] == 3
+
+
+@pytest.mark.parametrize("thr", [(4, 8, 16), (2, 3, 4), (256, 1000, 5000), (1, 2, 100000)])
+def test_custom_thresholds(thr):
+    rng = np.random.default_rng(11)
+    lens = rng.choice([0, 1, 2, 3, 5, 9, 17, 40, 300], size=3000)
+    A = gen.random_csr(3000, 3000, lens, seed=12)
+    M, y = _run(A, S.CSR_BINNED, thresholds=thr)
+    perm = torch.empty(A.n_rows, dtype=torch.int32, device="cuda")
+    off = M.plan(perm)
+    ooff, operm = oracle.bins(A.row_ptr, thr)
+    assert off == ooff.tolist() and np.array_equal(host(perm), operm)
+    yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x)
+    assert_close(y, yr, sc, TAU_F32, f"thr={thr}")
+
+
+EDGE = {
+    "empty_rows": lambda: gen.random_csr(700, 300, np.where(np.arange(700) % 3 == 0, 0, 7), seed=1),
+    "all_empty": lambda: gen.random_csr(513, 10, np.zeros(513, np.int64), seed=2),
+    "one_row": lambda: gen.random_csr(1, 50, [37], seed=3),
+    "ragged_tail": lambda: gen.random_csr(1001, 1001, np.random.default_rng(4).integers(0, 31, 1001), seed=4),
+    "unsorted": lambda: gen.random_csr(500, 400, np.random.default_rng(5).integers(0, 60, 500), seed=5,
+                                       sorted_cols=False),
+    "many_len1": lambda: gen.random_csr(5000, 5000, np.ones(5000, np.int64), seed=6),
+    "wide": lambda: gen.random_csr(64, 1_000_000, np.full(64, 700), seed=7),
+}
+
+
+@pytest.mark.parametrize("case", list(EDGE))
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_edge_cases(case, variant):
+    A = EDGE[case]()
+    print(f"[edge] {case} {variant}", flush=True)
+    M, y = _run(A, VARIANTS[variant])
+    yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x)
+    assert_close(y, yr, sc, TAU_F32, f"{case}/{variant}")
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_duplicates_summed(variant):
+    A = gen.random_csr(200, 100, np.random.default_rng(9).integers(2, 20, 200), seed=9)
+    ci = A.col_idx.copy()
+    for i in range(A.n_rows):
+        a, b = A.row_ptr[i], A.row_ptr[i + 1]
+        ci[b - 1] = ci[a]
+    A.col_idx = ci
+    M, y = _run(A, VARIANTS[variant])
+    yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x)
+    assert_close(y, yr, sc, TAU_F32, f"dup/{variant}")
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_misaligned_arrays(variant):
+    """Arrays that start 4 bytes past a 16-byte boundary take the 4-byte path."""
+    A = gen.random_csr(900, 900, np.random.default_rng(3).integers(0, 40, 900), seed=13)
+    ci_pad = torch.zeros(A.nnz + 1, dtype=torch.int32, device="cuda")
+    v_pad = torch.zeros(A.nnz + 1, dtype=torch.float32, device="cuda")
+    ci_pad[1:] = dev(A.col_idx)
+    v_pad[1:] = dev(A.vals)
+    M, y = _run(A, VARIANTS[variant], tensors=(dev(A.row_ptr), ci_pad[1:], v_pad[1:]))
+    yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x)
+    assert_close(y, yr, sc, TAU_F32, f"misaligned/{variant}")
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_alpha_beta_and_nan_y(variant):
+    A = gen.random_csr(2000, 1500, np.random.default_rng(2).integers(0, 50, 2000), seed=14)
+    y_in = np.random.default_rng(3).uniform(-1, 1, 2000).astype(np.float32)
+    for alpha, beta in [(2.5, 0.0), (-1.0, 1.0), (0.0, 0.5), (1.0, -3.0)]:
+        M, y = _run(A, VARIANTS[variant], alpha, beta, y_in)
+        yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x, alpha, beta, y_in)
+        assert_close(y, yr, sc, TAU_F32, f"ab/{variant}/{alpha}/{beta}")
+    # beta == 0: y is not read (NaN-filled y gives finite output)
+    M, y = _run(A, VARIANTS[variant], 1.0, 0.0, None)
+    assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_bit_reproducible(variant):
+    A = _config("powerlaw")
+    rp, ci, v = _mat(A)
+    M = S.CSRMatrix(A.n_rows, A.n_cols, rp, ci, v, VARIANTS[variant])
+    x = dev(A.x)
+    ys = []
+    for _ in range(3):
+        y = torch.empty(A.n_rows, device="cuda")
+        M.apply(x, y)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+
+
+def test_zero_rows_and_zero_nnz():
+    rp = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e_i = torch.zeros(0, dtype=torch.int32, device="cuda")
+    e_f = torch.zeros(0, dtype=torch.float32, device="cuda")
+    for var in VARIANTS.values():
+        M = S.CSRMatrix(0, 5, rp, e_i, e_f, var)
+        M.apply(torch.zeros(5, device="cuda"), torch.zeros(0, device="cuda"))
+    rp = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for var in VARIANTS.values():
+        M = S.CSRMatrix(3, 0, rp, e_i, e_f, var)
+        y = torch.tensor([1.0, 2.0, 3.0], device="cuda")
+        M.apply(torch.zeros(0, device="cuda"), y, 1.0, 2.0)
+        assert host(y).tolist() == [2.0, 4.0, 6.0]
+
+
+@pytest.mark.parametrize("bad", ["col_high", "col_neg", "rp_decreasing", "rp_last", "rp_first"])
+def test_invalid_matrix_rejected(bad):
+    A = gen.random_csr(50, 40, np.full(50, 4), seed=1)
+    rp, ci = A.row_ptr.copy(), A.col_idx.copy()
+    if bad == "col_high":
+        ci[17] = 40
+    elif bad == "col_neg":
+        ci[3] = -1
+    elif bad == "rp_decreasing":
+        rp[10] = rp[11] + 1
+    elif bad == "rp_last":
+        rp[-1] -= 1
+    elif bad == "rp_first":
+        rp[0] = 1
+    nnz = len(ci)
+    for var in VARIANTS.values():
+        ws = torch.empty(S.spmv_csr_plan_size(50, nnz), dtype=torch.uint8, device="cuda")
+        with pytest.raises(S.SpmvError) as e:
+            S.spmv_csr_create(50, 40, dev(rp), dev(ci), dev(A.vals), var, None, ws)
+        assert e.value.status == 2
+
+
+def test_row_stats_and_recommendation():
+    for name, want in [("tiny", 0), ("laplacian", 0), ("powerlaw", 2)]:
+        A = _config(name)
+        st = S.spmv_csr_row_stats(dev(A.row_ptr))
+        assert st == oracle.row_stats(A.row_ptr)
+        assert S.spmv_format_recommend(A.n_rows, st[1], st[2]) == want
