@@ -3,11 +3,18 @@
 
 Default run (N = 1): the 2-D 5-point Laplacian on a 1000 x 1000 grid
 (1,000,000 rows, 4,996,000 nonzeros, fp32), CSR path with the row-grouping
-planner (spmv_csr_apply, AUTO variant).  One step = a cache flush (a 1 GiB
-write, larger than the 256 MB Infinity Cache plus the L2s, so the matrix
-comes from HBM) followed by one apply; the apply alone is timed with HIP
-events recorded on the stream it is launched on.  Inputs are resident in HBM
-before the timed region.
+planner (spmv_csr_apply, AUTO variant).  One step = one apply.
+
+Cold-cache protocol ("rotate", the default): the inputs are replicated R
+times in HBM so that R copies span >= 1 GiB (4x the 256 MB Infinity Cache
+plus the L2s); step i applies copy i mod R, so every apply streams a matrix
+that was last touched >= 3/4 GiB of traffic earlier, i.e. from HBM.  K steps
+run back to back on one stream between two HIP events recorded on that
+stream (no host synchronisation inside), so per-launch event overhead does
+not enter the per-step time.  "flush" mode instead writes 1 GiB before
+every apply and brackets each apply with its own event pair.  "warm"
+repeats copy 0 (data cached in the Infinity Cache).  Inputs are resident in
+HBM before the timed region.
 
 Printed: ONE JSON line with the metric (GFLOP/s), effective GB/s over the
 algorithmic bytes, the roofline of the dominant kernel against the 8 TB/s
@@ -34,6 +41,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "SpMV GFLOP/s and effective HBM GB/s (% of MI355X peak) per config, 1 GPU"
 FLUSH_BYTES = 1 << 30
+ROTATE_BYTES = 1 << 30
 
 DEFAULT_PATH = {"tiny": "csr", "laplacian": "csr", "powerlaw": "csr", "pruned50": "macko",
                 "pruned70": "macko", "pruned90": "macko", "fe": "fem"}
@@ -59,9 +67,10 @@ def source_sha(path_name):
 
 
 class Workload:
-    """Inputs on the GPU plus a launch closure for one path."""
+    """Inputs on the GPU (replicated `copies` times) plus one launch closure
+    per copy for one path."""
 
-    def __init__(self, config, path):
+    def __init__(self, config, path, copies=None):
         import numpy as np
         import torch
         import gen
@@ -74,30 +83,38 @@ class Workload:
         if config in ("tiny", "laplacian", "powerlaw"):
             A = {"tiny": gen.tiny_csr, "laplacian": gen.laplacian_2d, "powerlaw": gen.powerlaw_csr}[config]()
             self.A = A
-            self.n_out = A.n_rows
             self.workload = {"tiny": "tiny_csr_4096x4096_8perrow", "laplacian": "laplacian_2d_1000x1000",
                              "powerlaw": "powerlaw_916428_zipf1.9931"}[config]
-            self.rp, self.ci, self.v, self.x = dev(A.row_ptr), dev(A.col_idx), dev(A.vals), dev(A.x)
-            self.y = torch.zeros(A.n_rows, device="cuda")
             self.flops = 2 * A.nnz
             if path.startswith("csr"):
                 var = {"csr": S.CSR_AUTO, "csr-binned": S.CSR_BINNED, "csr-vector": S.CSR_VECTOR,
                        "csr-scalar": S.CSR_SCALAR}[path]
-                self.M = S.CSRMatrix(A.n_rows, A.n_cols, self.rp, self.ci, self.v, var)
                 self.bytes = 8 * A.nnz + 4 * (A.n_rows + 1) + 4 * A.n_cols + 4 * A.n_rows
-                self.launch = lambda: self.M.apply(self.x, self.y, self.alpha, self.beta)
+                base = (dev(A.row_ptr), dev(A.col_idx), dev(A.vals), dev(A.x))
+
+                def make(arrs):
+                    rp, ci, v, x = arrs
+                    M = S.CSRMatrix(A.n_rows, A.n_cols, rp, ci, v, var)
+                    y = torch.zeros(A.n_rows, device="cuda")
+                    return (lambda: M.apply(x, y, self.alpha, self.beta)), y, M
+                self._setup(base, make, copies)
                 self.shape = {"n_rows": A.n_rows, "n_cols": A.n_cols, "nnz": A.nnz,
-                              "plan": self.M.info()}
+                              "plan": self.extra[0].info()}
             elif path == "ell":
                 import oracle
                 W = oracle.row_stats(A.row_ptr)[0]
                 self.W = W
-                self.ec = torch.empty(A.n_rows * W, dtype=torch.int32, device="cuda")
-                self.ev = torch.empty(A.n_rows * W, dtype=torch.float32, device="cuda")
-                S.spmv_ell_from_csr(A.n_rows, A.n_cols, self.rp, self.ci, self.v, W, self.ec, self.ev)
+                ec = torch.empty(A.n_rows * W, dtype=torch.int32, device="cuda")
+                ev = torch.empty(A.n_rows * W, dtype=torch.float32, device="cuda")
+                S.spmv_ell_from_csr(A.n_rows, A.n_cols, dev(A.row_ptr), dev(A.col_idx), dev(A.vals), W, ec, ev)
                 self.bytes = 8 * W * A.n_rows + 4 * A.n_cols + 4 * A.n_rows
-                self.launch = lambda: S.spmv_ell_apply(A.n_rows, A.n_cols, W, self.ec, self.ev, self.alpha,
-                                                       self.x, self.beta, self.y)
+
+                def make(arrs):
+                    ec, ev, x = arrs
+                    y = torch.zeros(A.n_rows, device="cuda")
+                    return (lambda: S.spmv_ell_apply(A.n_rows, A.n_cols, W, ec, ev, self.alpha, x, self.beta,
+                                                     y)), y, None
+                self._setup((ec, ev, dev(A.x)), make, copies)
                 self.shape = {"n_rows": A.n_rows, "nnz": A.nnz, "ell_width": W}
             else:
                 raise SystemExit(f"path {path} does not apply to config {config}")
@@ -105,53 +122,71 @@ class Workload:
             s = int(config[6:]) / 100.0
             P = gen.pruned_weight(s)
             self.P = P
-            self.n_out = P.n_rows
             self.workload = f"pruned_weight_12288x12288_sparsity{int(s * 100)}"
-            self.xh = dev(P.x_f16)
-            self.y = torch.zeros(P.n_rows, device="cuda")
             if path == "macko":
                 mrp, codes, mv = S.macko_encode(P.n_rows, P.n_cols, P.row_ptr, P.col_idx, P.vals_f16)
-                self.enc = (mrp, codes, mv)
-                self.mrp, self.codes, self.mv = dev(mrp), dev(codes), dev(mv)
                 E = int(mrp[-1])
                 self.bytes = 2 * E + E // 2 + 4 * (P.n_rows + 1) + 2 * P.n_cols + 4 * P.n_rows
                 self.flops = 2 * P.nnz
-                self.launch = lambda: S.macko_spmv(P.n_rows, P.n_cols, self.mrp, self.codes, self.mv,
-                                                   self.alpha, self.xh, self.beta, self.y)
+
+                def make(arrs):
+                    mrp_d, codes_d, mv_d, xh = arrs
+                    y = torch.zeros(P.n_rows, device="cuda")
+                    return (lambda: S.macko_spmv(P.n_rows, P.n_cols, mrp_d, codes_d, mv_d, self.alpha, xh,
+                                                 self.beta, y)), y, None
+                self._setup((dev(mrp), dev(codes), dev(mv), dev(P.x_f16)), make, copies)
                 self.shape = {"n_rows": P.n_rows, "n_cols": P.n_cols, "nnz": P.nnz, "entries": E}
             elif path == "dense":
-                self.D = dev(P.dense_f16())
                 self.bytes = 2 * P.n_rows * P.n_cols + 2 * P.n_cols + 4 * P.n_rows
                 self.flops = 2 * P.n_rows * P.n_cols
-                self.launch = lambda: S.dense_gemv_f16(P.n_rows, P.n_cols, self.D, self.xh, self.alpha,
-                                                       self.beta, self.y)
+
+                def make(arrs):
+                    D, xh = arrs
+                    y = torch.zeros(P.n_rows, device="cuda")
+                    return (lambda: S.dense_gemv_f16(P.n_rows, P.n_cols, D, xh, self.alpha, self.beta, y)), y, None
+                self._setup((dev(P.dense_f16()), dev(P.x_f16)), make, copies)
                 self.shape = {"m": P.n_rows, "n": P.n_cols}
             else:
                 raise SystemExit(f"path {path} does not apply to config {config}")
         elif config == "fe":
             M = gen.fe_mesh()
             self.Mesh = M
-            self.n_out = M.n_dof
             self.workload = "fe_hex8_cantilever_120x60x30"
-            self.edof, self.rho, self.Ke = dev(M.edof.reshape(-1)), dev(M.rho), dev(M.Ke.reshape(-1))
-            self.x = dev(M.x)
-            self.y = torch.zeros(M.n_dof, device="cuda")
             self.bytes = 96 * M.n_elem + 4 * M.n_elem + 2304 + 8 * M.n_dof
             self.flops = 1176 * M.n_elem
-            args = lambda: (M.n_elem, M.n_dof, self.edof, self.rho, M.penalty, self.Ke, self.alpha, self.x,
-                            self.beta, self.y)
-            if path == "fem":
-                self.launch = lambda: S.fem_matvec_apply(*args())
-            elif path == "fem-3stage":
-                self.ws = torch.empty(S.fem_threestage_size(M.n_elem), dtype=torch.uint8, device="cuda")
-                self.launch = lambda: S.fem_matvec_threestage(*args(), self.ws)
-            else:
+            if path not in ("fem", "fem-3stage"):
                 raise SystemExit(f"path {path} does not apply to config {config}")
+            ws = None
+            if path == "fem-3stage":
+                ws = torch.empty(S.fem_threestage_size(M.n_elem), dtype=torch.uint8, device="cuda")
+
+            def make(arrs):
+                edof, rho, Ke, x = arrs
+                y = torch.zeros(M.n_dof, device="cuda")
+                a = (M.n_elem, M.n_dof, edof, rho, M.penalty, Ke)
+                if path == "fem":
+                    return (lambda: S.fem_matvec_apply(*a, self.alpha, x, self.beta, y)), y, None
+                return (lambda: S.fem_matvec_threestage(*a, self.alpha, x, self.beta, y, ws)), y, None
+            self._setup((dev(M.edof.reshape(-1)), dev(M.rho), dev(M.Ke.reshape(-1)), dev(M.x)), make, copies)
             self.shape = {"n_elem": M.n_elem, "n_dof": M.n_dof, "atomics": int((M.edof >= 0).sum())}
         else:
             raise SystemExit(f"unknown config {config}")
         torch.cuda.synchronize()
-        log(f"[bench] setup {config}/{path}: {time.time() - t0:.1f}s")
+        log(f"[bench] setup {config}/{path}: {len(self.launches)} copies, {time.time() - t0:.1f}s")
+
+    def _setup(self, base, make, copies):
+        """Replicates the input tensors so that all copies span >= ROTATE_BYTES."""
+        import math
+        n = copies or max(2, math.ceil(ROTATE_BYTES / self.bytes))
+        self.launches, self.outputs, self.extra = [], [], []
+        for i in range(n):
+            arrs = base if i == 0 else tuple(t.clone() for t in base)
+            launch, y, extra = make(arrs)
+            self.launches.append(launch)
+            self.outputs.append(y)
+            self.extra.append(extra)
+        self.launch = self.launches[0]
+        self.y = self.outputs[0]
 
     # -- oracle (the CPU baseline and the parity check) --
     def oracle_call(self):
@@ -218,40 +253,104 @@ def traffic_record(w):
     return int(r["bytes_per_launch"])
 
 
-def timed(w, steps, warmup, flush):
+def timed_rotate(w, steps, warmup, launches, graph=True):
+    """`steps` applies back to back, step i on launches[i % R], between one
+    pair of HIP events on the launch stream, with a device synchronisation
+    on both sides.  With `graph`, one pass over the R launches is captured
+    in a HIP graph and replayed, so host launch cost does not throttle the
+    GPU; the captured kernels are the same launches."""
+    import math
     torch = w.torch
-    buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if flush else None
+    R = len(launches)
+    reps = max(1, math.ceil(steps / R))
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for L in launches:
+                L()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for L in launches:
+                L()
+        run = g.replay
+    else:
+        def run():
+            for L in launches:
+                L()
+    for _ in range(max(1, math.ceil(warmup / R))):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n = reps * R
+    return {"ms_per_apply": a.elapsed_time(b) / n, "wall_ms_per_apply": wall * 1e3 / n, "applies": n,
+            "copies": R, "graph": graph}
+
+
+def timed_flush(w, steps, warmup):
+    """1 GiB write before every apply; each apply between its own event pair."""
+    torch = w.torch
+    buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     for _ in range(warmup):
-        if flush:
-            buf.zero_()
+        buf.zero_()
         w.launch()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0 = time.perf_counter()
     for a, b in ev:
-        if flush:
-            buf.zero_()
+        buf.zero_()
         a.record()
         w.launch()
         b.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ms = sorted(a.elapsed_time(b) for a, b in ev)
-    return {"mean_ms": sum(ms) / len(ms), "median_ms": ms[len(ms) // 2], "p10_ms": ms[len(ms) // 10],
-            "p90_ms": ms[(9 * len(ms)) // 10], "wall_ms_per_step": wall * 1e3 / steps}
+    return {"ms_per_apply": sum(ms) / len(ms), "median_ms": ms[len(ms) // 2]}
+
+
+def copy_reference(nbytes, steps=400):
+    """Bandwidth of torch's device copy (nbytes/2 read + nbytes/2 written)
+    under the same rotation protocol: what a plain streaming kernel reaches
+    at this size on this GPU."""
+    import math
+    import torch
+    half = max(nbytes // 2 // 4, 1)
+    R = max(2, math.ceil(ROTATE_BYTES / (8 * half)))
+    pairs = [(torch.ones(half, dtype=torch.float32, device="cuda"),
+              torch.empty(half, dtype=torch.float32, device="cuda")) for _ in range(R)]
+    launches = [(lambda p=p: p[1].copy_(p[0])) for p in pairs]
+
+    class _W:
+        pass
+    w = _W()
+    w.torch = torch
+    r = timed_rotate(w, steps, 2 * R, launches, graph=True)
+    return {"bytes": 8 * half, "copies": R, "ms": round(r["ms_per_apply"], 6),
+            "gbs": round(8 * half / (r["ms_per_apply"] * 1e-3) / 1e9, 1)}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="laplacian", choices=sorted(DEFAULT_PATH))
     ap.add_argument("--path", default=None, choices=sorted(KERNEL))
-    ap.add_argument("--no-flush", action="store_true", help="time with warm caches only")
+    ap.add_argument("--protocol", default="rotate", choices=["rotate", "flush", "warm"],
+                    help="cold-cache protocol (see the module docstring)")
+    ap.add_argument("--copies", type=int, default=None, help="input copies for the rotate protocol")
+    ap.add_argument("--no-graph", action="store_true", help="launch from Python instead of a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time spent on the oracle baseline (0 = skip)")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-copy-ref", action="store_true", help="skip the plain-copy bandwidth reference")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -265,7 +364,7 @@ def main():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(2)
     path = args.path or DEFAULT_PATH[args.config]
-    w = Workload(args.config, path)
+    w = Workload(args.config, path, args.copies if args.protocol == "rotate" else 1)
 
     par = None
     ref_fn = w.oracle_call() if (not args.no_parity or args.cpu_seconds > 0) else None
@@ -273,9 +372,16 @@ def main():
         par = parity(w, ref_fn)
         log(f"[bench] parity {par}")
 
-    cold = timed(w, args.steps, args.warmup, flush=not args.no_flush)
-    warm = timed(w, args.steps, args.warmup, flush=False) if not args.no_flush else cold
-    ms = cold["mean_ms"]
+    graph = not args.no_graph
+    warm_launches = [w.launches[0]] * min(len(w.launches), 16)
+    if args.protocol == "rotate":
+        meas = timed_rotate(w, args.steps, args.warmup, w.launches, graph)
+    elif args.protocol == "flush":
+        meas = timed_flush(w, args.steps, args.warmup)
+    else:
+        meas = timed_rotate(w, args.steps, args.warmup, warm_launches, graph)
+    warm = timed_rotate(w, args.steps, args.warmup, warm_launches, graph)
+    ms = meas["ms_per_apply"]
     gflops = w.flops / (ms * 1e-3) / 1e9
     gbs = w.bytes / (ms * 1e-3) / 1e9
     traffic = traffic_record(w)
@@ -284,7 +390,7 @@ def main():
         "value": round(gflops, 3),
         "unit": "GFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": meas.get("applies", args.steps),
         "warmup": args.warmup,
         "ms_per_step": round(ms, 6),
         "higher_is_better": True,
@@ -293,17 +399,19 @@ def main():
         "dtype": "f16xf16->f32" if args.config.startswith("pruned") else "f32",
         "data": "synthetic (seeded generators in gen/)",
         "config": {"workload": w.workload, "path": path, **w.shape, "alpha": w.alpha, "beta": w.beta,
-                   "cache": "warm" if args.no_flush else "cold: 1 GiB write before each timed apply",
-                   "timing": "HIP events around each apply on its launch stream",
+                   "protocol": args.protocol, "copies": len(w.launches),
+                   "timing": "HIP events on the launch stream around the timed steps"
+                             + (", replayed from a HIP graph" if graph and args.protocol != "flush" else ""),
                    "algorithmic_bytes": w.bytes, "flops": w.flops},
         "effective_gbs": round(gbs, 2),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": KERNEL[path]},
-        "timing_ms": {k: round(v, 6) for k, v in cold.items()},
+        "timing_ms": {k: round(v, 6) for k, v in meas.items()},
         "warm_timing_ms": {k: round(v, 6) for k, v in warm.items()},
         "parity": par,
+        "copy_reference": copy_reference(w.bytes) if not args.no_copy_ref else None,
     }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, ref_fn, args.cpu_seconds)

@@ -13,7 +13,7 @@
 //
 // gfx950 mapping of the four groups (wave64, 256-thread workgroups):
 //   group 0 (short rows)   runs of consecutive short rows are cut into
-//                          blocks of <= 479 nonzeros / 128 rows; one wave
+//                          blocks of <= 512 staged entries / 128 rows; one wave
 //                          streams a block's values and columns with 16-byte
 //                          loads, multiplies by the gathered x, stages the
 //                          products in LDS and then each lane sums whole
@@ -37,13 +37,18 @@ namespace {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Compile-time shape of the short-row blocks (overridable for tuning sweeps).
+#ifndef SPMV_SHORT_VPL
+#define SPMV_SHORT_VPL 2
+#endif
+
 constexpr int WG = 256;                 // threads per workgroup everywhere here
 constexpr int WAVES = WG / 64;
-constexpr int SHORT_VPL = 2;            // 16-byte vectors per lane in a short block
-constexpr int SHORT_SLOTS = 64 * 4 * SHORT_VPL;   // 512 entries staged per wave
-constexpr int SHORT_RMAX = 128;         // rows per short block (2 per lane)
+constexpr int SHORT_VPL = SPMV_SHORT_VPL;          // 16-byte vectors per lane in a short block
+constexpr int SHORT_SLOTS = 64 * 4 * SHORT_VPL;    // entries staged per wave
+constexpr int SHORT_RMAX = 64 * SHORT_VPL;         // rows per short block (VPL per lane)
 constexpr int LONG_CHUNK = 8192;        // nonzeros per workgroup in group 3
-constexpr int MAX_T0 = 256;             // largest supported bound of group 0
+constexpr int MAX_T0 = SHORT_SLOTS / 2 < 256 ? SHORT_SLOTS / 2 : 256;   // largest bound of group 0
 
 // Error bits raised by the validation kernels.
 constexpr int ERR_RP0 = 1, ERR_RPN = 2, ERR_MONO = 4, ERR_COL = 8;
@@ -51,7 +56,8 @@ constexpr int ERR_RP0 = 1, ERR_RPN = 2, ERR_MONO = 4, ERR_COL = 8;
 // Device-side plan header (int32 words).
 struct Meta {
     int bin_offsets[5];
-    int head_totals[2];   // {0, number of short blocks}
+    int head_totals[2];   // {0, number of runs of short rows}
+    int block_totals[2];  // {0, number of short blocks}
     int err;
 };
 
@@ -226,15 +232,15 @@ __global__ __launch_bounds__(WG) void k_plan_scatter(int n, const int *__restric
     perm[offsets[blockIdx.x * 4 + g] + rank] = i;
 }
 
-// A short block starts at perm position p if p is a multiple of SHORT_RMAX,
-// if row perm[p] does not follow row perm[p-1], or if the two rows start in
-// different windows of `window` nonzeros.  Every block is then a run of
-// consecutive rows with <= SHORT_RMAX rows whose first entries lie in one
-// window, so it spans at most window + t0 + 2 entries from a 16-byte
-// boundary.
+// A run of short rows starts at perm position p if row perm[p] does not
+// follow row perm[p-1], or if the two rows start in different windows of
+// `window` nonzeros.  Every run is then a range of consecutive rows whose
+// first entries lie in one window, so it spans at most window + t0 + 2
+// entries from a 16-byte boundary.  Runs longer than SHORT_RMAX rows are cut
+// into pieces of SHORT_RMAX rows afterwards (k_blocks_write).
 __device__ __forceinline__ bool short_head(int p, const int *__restrict__ perm, const int *__restrict__ rp,
                                            int window) {
-    if (p % SHORT_RMAX == 0) return true;
+    if (p == 0) return true;
     const int r = perm[p];
     if (perm[p - 1] != r - 1) return true;
     return rp[r] / window != rp[r - 1] / window;
@@ -275,25 +281,65 @@ __global__ __launch_bounds__(WG) void k_heads_scatter(const Meta *__restrict__ m
     head_pos[offsets[blockIdx.x] + rank] = p;
 }
 
+// Number of blocks run k becomes: ceil(rows / SHORT_RMAX); 0 past the last run.
+__device__ __forceinline__ int run_blocks(int k, int nh, int n0, const int *__restrict__ head_pos) {
+    if (k >= nh) return 0;
+    const int rows = (k + 1 < nh ? head_pos[k + 1] : n0) - head_pos[k];
+    return (rows + SHORT_RMAX - 1) / SHORT_RMAX;
+}
+
+// Exclusive prefix of v over the workgroup (in thread order) and the total.
+__device__ __forceinline__ int workgroup_exclusive(int v, int *total) {
+    __shared__ int wsum[WAVES];
+    int incl = v;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (__lane_id() >= d) incl += o;
+    }
+    const int w = threadIdx.x / 64;
+    if (__lane_id() == 63) wsum[w] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int k = 0; k < WAVES; ++k) {
+        if (k < w) before += wsum[k];
+        all += wsum[k];
+    }
+    *total = all;
+    return before + incl - v;
+}
+
+__global__ __launch_bounds__(WG) void k_blocks_count(const Meta *__restrict__ meta, const int *__restrict__ head_pos,
+                                                     int *__restrict__ counts) {
+    const int k = blockIdx.x * WG + threadIdx.x;
+    int total;
+    workgroup_exclusive(run_blocks(k, meta->head_totals[1], meta->bin_offsets[1], head_pos), &total);
+    if (threadIdx.x == 0) counts[blockIdx.x] = total;
+}
+
 // Block descriptor: first row, row count, first and one-past-last nonzero.
-__global__ __launch_bounds__(WG) void k_blocks_finalize(const Meta *__restrict__ meta,
-                                                        const int *__restrict__ head_pos,
-                                                        const int *__restrict__ perm,
-                                                        const int *__restrict__ rp, i32x4 *__restrict__ desc) {
-    const int nb = meta->head_totals[1];
+__global__ __launch_bounds__(WG) void k_blocks_write(const Meta *__restrict__ meta,
+                                                     const int *__restrict__ head_pos,
+                                                     const int *__restrict__ offsets,
+                                                     const int *__restrict__ perm, const int *__restrict__ rp,
+                                                     i32x4 *__restrict__ desc) {
+    const int nh = meta->head_totals[1];
     const int n0 = meta->bin_offsets[1];
     const int k = blockIdx.x * WG + threadIdx.x;
-    if (k >= nb) return;
+    int total;
+    int at = offsets[blockIdx.x] + workgroup_exclusive(run_blocks(k, nh, n0, head_pos), &total);
+    if (k >= nh) return;
     const int p = head_pos[k];
-    const int pn = k + 1 < nb ? head_pos[k + 1] : n0;
+    const int rows = (k + 1 < nh ? head_pos[k + 1] : n0) - p;
     const int r0 = perm[p];
-    const int nr = pn - p;
-    i32x4 d;
-    d.x = r0;
-    d.y = nr;
-    d.z = rp[r0];
-    d.w = rp[r0 + nr];
-    desc[k] = d;
+    for (int j = 0; j < rows; j += SHORT_RMAX) {
+        const int nr = min(SHORT_RMAX, rows - j);
+        i32x4 d;
+        d.x = r0 + j;
+        d.y = nr;
+        d.z = rp[r0 + j];
+        d.w = rp[r0 + j + nr];
+        desc[at++] = d;
+    }
 }
 
 // Start and end nonzero of every group-3 row (copied to the host to cut rows
@@ -405,24 +451,16 @@ __global__ __launch_bounds__(WG) void k_csr_binned(BinnedArgs a) {
         // ---- group 0: one short block per wave ----
         const int nw = gridDim.x - a.seg_short;
         const int blk = xcd_contiguous(bid - a.seg_short, nw) * WAVES + wv;
-        const bool has = blk < a.n_blocks;
-        i32x4 d = {0, 0, 0, 0};
-        if (has) d = a.blocks[blk];
+        if (blk >= a.n_blocks) return;
+        const i32x4 d = a.blocks[blk];
         const int r0 = d.x, nr = d.y, s = d.z, e = d.w;
         const int base = s & ~3;
-        // row starts for the second phase, loaded early
-        int rs[SHORT_RMAX / 64 + 1];
-#pragma unroll
-        for (int j = 0; j <= SHORT_RMAX / 64; ++j) {
-            const int i = lane + 64 * j;
-            rs[j] = (has && i <= nr) ? a.rp[r0 + i] : 0;
-        }
         float *st = stage[wv];
 #pragma unroll
         for (int j = 0; j < SHORT_VPL; ++j) {
             const int q = base + 4 * (lane + 64 * j);
             f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (has && q < e) {
+            if (q < e) {
                 i32x4 c;
                 f32x4 f;
                 load4<VEC>(a.ci, a.v, q, a.nnz, c, f);
@@ -434,8 +472,20 @@ __global__ __launch_bounds__(WG) void k_csr_binned(BinnedArgs a) {
             }
             *reinterpret_cast<f32x4 *>(st + 4 * (lane + 64 * j)) = p;
         }
-        __syncthreads();
-        if (!has) return;
+        // row starts for the second phase
+        int rs[SHORT_RMAX / 64 + 1];
+#pragma unroll
+        for (int j = 0; j <= SHORT_RMAX / 64; ++j) {
+            const int i = lane + 64 * j;
+            rs[j] = i <= nr ? a.rp[r0 + i] : 0;
+        }
+        // The staged products are private to this wave: a wave-level barrier
+        // (LDS operations of one wave complete in order) replaces a
+        // workgroup barrier, so the four waves of a workgroup never wait for
+        // each other.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // Each lane sums whole rows from the staged products, in storage
         // order.  Row i's end is row i+1's start: lanes hold starts of rows lane+64j;
         // the start of row lane+64j+1 comes from the next lane (or from the
@@ -682,13 +732,17 @@ spmv_status build_binned_plan(spmv_csr_plan *h, char *ws, const Layout &L, hipSt
     SPMV_LAUNCHED("k_plan_scan(heads)");
     k_heads_scatter<<<nwg, WG, 0, st>>>(meta, perm, h->rp, window, hoffsets, heads);
     SPMV_LAUNCHED("k_heads_scatter");
-    k_blocks_finalize<<<nwg, WG, 0, st>>>(meta, heads, perm, h->rp, blocks);
-    SPMV_LAUNCHED("k_blocks_finalize");
+    k_blocks_count<<<nwg, WG, 0, st>>>(meta, heads, hcounts);
+    SPMV_LAUNCHED("k_blocks_count");
+    k_plan_scan<<<1, 1024, 0, st>>>(nwg, 1, hcounts, hoffsets, meta->block_totals);
+    SPMV_LAUNCHED("k_plan_scan(blocks)");
+    k_blocks_write<<<nwg, WG, 0, st>>>(meta, heads, hoffsets, perm, h->rp, blocks);
+    SPMV_LAUNCHED("k_blocks_write");
     Meta hm{};
     SPMV_HIP(hipMemcpyAsync(&hm, meta, sizeof(Meta), hipMemcpyDeviceToHost, st));
     SPMV_HIP(hipStreamSynchronize(st));
     for (int g = 0; g < 5; ++g) h->bin_off[g] = hm.bin_offsets[g];
-    h->n_blocks = hm.head_totals[1];
+    h->n_blocks = hm.block_totals[1];
     h->perm = perm;
     h->blocks = blocks;
 
