@@ -97,6 +97,40 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Marks loaded values as used at this point.  Without it the compiler may
+// move a load whose result is only consumed under a condition into that
+// conditional block, issuing it after the others and waiting for it there;
+// with it all gathers are issued together and waited for once.
+__device__ __forceinline__ void pin_value(float &v) { asm volatile("" : "+v"(v)); }
+
+template <typename... T>
+__device__ __forceinline__ void issue_together(T &...v) {
+    (pin_value(v), ...);
+}
+
+// Copies n 2-byte elements from global memory into LDS, cooperatively by
+// the whole workgroup.  Each thread issues up to 4 loads (16 bytes each
+// when `src` is 16-byte aligned) before storing any, so the copy costs about
+// one memory round trip per 4 * 8 * blockDim elements instead of one per
+// loop iteration.
+__device__ __forceinline__ void stage_halfs(unsigned short *dst, const unsigned short *__restrict__ src, int n) {
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    const int n8 = (reinterpret_cast<uintptr_t>(src) & 15u) == 0 ? (n & ~7) : 0;
+    const int stride = 8 * blockDim.x;
+    for (int k0 = 8 * threadIdx.x; k0 < n8; k0 += 4 * stride) {
+        u32x4_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int k = min(k0 + u * stride, n8 - 8);
+            v[u] = *reinterpret_cast<const u32x4_t *>(src + k);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (k0 + u * stride < n8) *reinterpret_cast<u32x4_t *>(dst + k0 + u * stride) = v[u];
+    }
+    for (int k = n8 + threadIdx.x; k < n; k += blockDim.x) dst[k] = src[k];
+}
+
 // Non-temporal loads for streamed matrix data: read once, so keep them from
 // evicting the gathered vector from the caches.
 template <typename T>

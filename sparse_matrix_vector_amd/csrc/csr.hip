@@ -357,15 +357,32 @@ __global__ void k_long_rows(int n3, const int *__restrict__ perm3, const int *__
 // Apply kernels
 // ---------------------------------------------------------------------------
 
-// Entries [q, q+4) of the column and value streams, q % 4 == 0.  One 16-byte
-// load per stream when the whole vector lies inside the arrays; entries past
-// nnz read as column 0 / value 0 (the callers mask them).
+// Entries [q, q+4) of the column and value streams, q % 4 == 0.
+//
+// VEC (both arrays 16-byte aligned and nnz >= 4): one 16-byte load per
+// stream at min(q, last_vec), last_vec = (nnz & ~3) - 4, so the load is
+// always inside the arrays and needs no branch; a lane whose vector lies
+// past last_vec (only the array's final partial vector) re-reads its
+// entries one by one.  Entries past nnz read as column 0 / value 0; the
+// callers mask entries outside their row range.  Keeping the common path
+// free of divergent branches matters: a divergent path that writes the
+// same registers would make the compiler wait for the 16-byte loads before
+// the next ones are issued.
 template <bool VEC>
 __device__ __forceinline__ void load4(const int *__restrict__ ci, const float *__restrict__ v, int q, int nnz,
-                                      i32x4 &c, f32x4 &f) {
-    if (VEC && q + 4 <= nnz) {
-        c = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(ci + q));
-        f = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(v + q));
+                                      int last_vec, i32x4 &c, f32x4 &f) {
+    if (VEC) {
+        const int qq = min(q, last_vec);
+        c = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(ci + qq));
+        f = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(v + qq));
+        if (q > last_vec) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bool in = q + t < nnz;
+                c[t] = in ? ci[q + t] : 0;
+                f[t] = in ? v[q + t] : 0.0f;
+            }
+        }
     } else {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -378,22 +395,46 @@ __device__ __forceinline__ void load4(const int *__restrict__ ci, const float *_
 
 // Sum of v[k] * x[ci[k]] over k in [s, e) by the `nthreads` threads of a
 // wave or workgroup, `tid` in [0, nthreads); each thread covers aligned
-// 4-entry vectors strided by 4 * nthreads.
-template <bool VEC>
+// 4-entry vectors strided by 4 * nthreads, U vectors per step with all
+// their loads issued before any is used.  A vector past e is replaced by
+// the thread's first vector of the step (its entries are masked), and the
+// four gathers of each vector are issued unconditionally (entries outside
+// [s, e) hold valid columns of neighbouring rows, or 0 past nnz) and masked
+// afterwards.
+template <bool VEC, int ROW_UNROLL>
 __device__ __forceinline__ float strided_row_sum(const int *__restrict__ ci, const float *__restrict__ v,
-                                                 const float *__restrict__ x, int s, int e, int nnz, int tid,
-                                                 int nthreads) {
+                                                 const float *__restrict__ x, int s, int e, int nnz, int last_vec,
+                                                 int tid, int nthreads) {
     float acc = 0.0f;
     const int base = s & ~3;
-    for (int q = base + 4 * tid; q < e; q += 4 * nthreads) {
-        i32x4 c;
-        f32x4 f;
-        load4<VEC>(ci, v, q, nnz, c, f);
+    const int step = 4 * nthreads;
+    for (int q0 = base + 4 * tid; q0 < e; q0 += step * ROW_UNROLL) {
+        i32x4 c[ROW_UNROLL];
+        f32x4 f[ROW_UNROLL];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int k = q + t;
-            if (k >= s && k < e) acc = fmaf(f[t], x[c[t]], acc);
+        for (int u = 0; u < ROW_UNROLL; ++u) {
+            const int q = q0 + u * step;
+            load4<VEC>(ci, v, q < e ? q : q0, nnz, last_vec, c[u], f[u]);
         }
+        // masked entries gather x[0] (one shared line) instead of a column of
+        // some other row
+        float xv[ROW_UNROLL][4];
+#pragma unroll
+        for (int u = 0; u < ROW_UNROLL; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int k = q0 + u * step + t;
+                xv[u][t] = x[(k >= s && k < e) ? c[u][t] : 0];
+            }
+#pragma unroll
+        for (int u = 0; u < ROW_UNROLL; ++u) issue_together(xv[u][0], xv[u][1], xv[u][2], xv[u][3]);
+#pragma unroll
+        for (int u = 0; u < ROW_UNROLL; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int k = q0 + u * step + t;
+                acc = (k >= s && k < e) ? fmaf(f[u][t], xv[u][t], acc) : acc;
+            }
     }
     return acc;
 }
@@ -406,6 +447,7 @@ struct BinnedArgs {
     float *y;
     float alpha, beta;
     int nnz;
+    int last_vec;          // (nnz & ~3) - 4: start of the last full 16-byte vector
     const int *perm;
     const i32x4 *blocks;   // short-block descriptors
     int n_blocks;
@@ -455,29 +497,47 @@ __global__ __launch_bounds__(WG) void k_csr_binned(BinnedArgs a) {
         const i32x4 d = a.blocks[blk];
         const int r0 = d.x, nr = d.y, s = d.z, e = d.w;
         const int base = s & ~3;
-        float *st = stage[wv];
+        // Row starts for the second phase, issued before the streams so that
+        // waiting for the streams (memory counters drain in issue order)
+        // also covers them.
+        int rs[SHORT_RMAX / 64 + 1];
+#pragma unroll
+        for (int j = 0; j <= SHORT_RMAX / 64; ++j) rs[j] = a.rp[r0 + min(lane + 64 * j, nr)];
+        // Idle lanes (vector past e) re-read the block's first vector, which
+        // keeps every load unconditional and inside the arrays.
+        i32x4 c[SHORT_VPL];
+        f32x4 f[SHORT_VPL];
 #pragma unroll
         for (int j = 0; j < SHORT_VPL; ++j) {
             const int q = base + 4 * (lane + 64 * j);
-            f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (q < e) {
-                i32x4 c;
-                f32x4 f;
-                load4<VEC>(a.ci, a.v, q, a.nnz, c, f);
+            load4<VEC>(a.ci, a.v, q < e ? q : base, a.nnz, a.last_vec, c[j], f[j]);
+        }
+        float *st = stage[wv];
+        if (e > s) {
+            // Gathers for every lane and entry, unconditionally, so all
+            // 4 * VPL gathers are in flight together; an entry outside the
+            // block gathers x[0] and its product is masked after.
+            float xv[SHORT_VPL][4];
+#pragma unroll
+            for (int j = 0; j < SHORT_VPL; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int k = base + 4 * (lane + 64 * j) + t;
+                    xv[j][t] = a.x[(k >= s && k < e) ? c[j][t] : 0];
+                }
+#pragma unroll
+            for (int j = 0; j < SHORT_VPL; ++j) issue_together(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
+#pragma unroll
+            for (int j = 0; j < SHORT_VPL; ++j) {
+                const int q = base + 4 * (lane + 64 * j);
+                f32x4 p;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const int k = q + t;
-                    if (k >= s && k < e) p[t] = f[t] * a.x[c[t]];
+                    p[t] = (k >= s && k < e) ? f[j][t] * xv[j][t] : 0.0f;
                 }
+                *reinterpret_cast<f32x4 *>(st + 4 * (lane + 64 * j)) = p;
             }
-            *reinterpret_cast<f32x4 *>(st + 4 * (lane + 64 * j)) = p;
-        }
-        // row starts for the second phase
-        int rs[SHORT_RMAX / 64 + 1];
-#pragma unroll
-        for (int j = 0; j <= SHORT_RMAX / 64; ++j) {
-            const int i = lane + 64 * j;
-            rs[j] = i <= nr ? a.rp[r0 + i] : 0;
         }
         // The staged products are private to this wave: a wave-level barrier
         // (LDS operations of one wave complete in order) replaces a
@@ -486,19 +546,26 @@ __global__ __launch_bounds__(WG) void k_csr_binned(BinnedArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // Each lane sums whole rows from the staged products, in storage
-        // order.  Row i's end is row i+1's start: lanes hold starts of rows lane+64j;
-        // the start of row lane+64j+1 comes from the next lane (or from the
-        // next j for lane 63).
+        // Each lane sums whole rows from the staged products in storage
+        // order, reading 8 staged entries per step so their LDS latencies
+        // overlap.  Row i's end is row i+1's start: lane l holds the start of
+        // row l + 64 j; the next row's start comes from lane l + 1 (or from
+        // lane 0 of the next j for lane 63).
 #pragma unroll
         for (int j = 0; j < SHORT_RMAX / 64; ++j) {
             const int nxt_same = __shfl_down(rs[j], 1);
             const int nxt_wrap = __shfl(rs[j + 1], 0);
-            const int end = lane < 63 ? nxt_same : nxt_wrap;
+            const int end = (lane < 63 ? nxt_same : nxt_wrap) - base;
             const int i = lane + 64 * j;
             if (i < nr) {
                 float acc = 0.0f;
-                for (int k = rs[j] - base; k < end - base; ++k) acc += st[k];
+                for (int k = rs[j] - base; k < end; k += 8) {
+                    float v[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) v[u] = st[min(k + u, SHORT_SLOTS - 1)];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) acc += k + u < end ? v[u] : 0.0f;
+                }
                 store_y(a.y, r0 + i, acc, a.alpha, a.beta);
             }
         }
@@ -511,7 +578,7 @@ __global__ __launch_bounds__(WG) void k_csr_binned(BinnedArgs a) {
         if (idx >= a.n1) return;
         const int row = a.perm[a.g1_begin + idx];
         const int s = a.rp[row], e = a.rp[row + 1];
-        float acc = strided_row_sum<VEC>(a.ci, a.v, a.x, s, e, a.nnz, lane, 64);
+        float acc = strided_row_sum<VEC, 1>(a.ci, a.v, a.x, s, e, a.nnz, a.last_vec, lane, 64);
         acc = wave_sum(acc);
         if (lane == 0) store_y(a.y, row, acc, a.alpha, a.beta);
         return;
@@ -521,7 +588,7 @@ __global__ __launch_bounds__(WG) void k_csr_binned(BinnedArgs a) {
         // ---- group 2: one workgroup per row ----
         const int row = a.perm[a.g2_begin + (bid - a.seg_g2)];
         const int s = a.rp[row], e = a.rp[row + 1];
-        float acc = strided_row_sum<VEC>(a.ci, a.v, a.x, s, e, a.nnz, threadIdx.x, WG);
+        float acc = strided_row_sum<VEC, 4>(a.ci, a.v, a.x, s, e, a.nnz, a.last_vec, threadIdx.x, WG);
         acc = workgroup_sum(acc, red);
         if (threadIdx.x == 0) store_y(a.y, row, acc, a.alpha, a.beta);
         return;
@@ -529,7 +596,7 @@ __global__ __launch_bounds__(WG) void k_csr_binned(BinnedArgs a) {
 
     // ---- group 3: one workgroup per chunk of a long row ----
     const i32x4 ch = a.chunks[bid];
-    float acc = strided_row_sum<VEC>(a.ci, a.v, a.x, ch.y, ch.z, a.nnz, threadIdx.x, WG);
+    float acc = strided_row_sum<VEC, 4>(a.ci, a.v, a.x, ch.y, ch.z, a.nnz, a.last_vec, threadIdx.x, WG);
     acc = workgroup_sum(acc, red);
     if (threadIdx.x == 0) a.partials[bid] = acc;
 }
@@ -822,7 +889,7 @@ extern "C" spmv_status spmv_csr_create(spmv_csr_t *out, int32_t n_rows, int32_t 
     h->t[0] = t[0];
     h->t[1] = t[1];
     h->t[2] = t[2];
-    h->vec_ok = aligned16(col_idx) && aligned16(vals);
+    h->vec_ok = aligned16(col_idx) && aligned16(vals) && nnz >= 4;
     h->group_lanes = 0;
     if (var == SPMV_CSR_VECTOR) {
         const double mean = n_rows ? double(nnz) / n_rows : 1.0;
@@ -903,6 +970,7 @@ extern "C" spmv_status spmv_csr_apply(spmv_csr_t h, float alpha, const float *x,
     a.alpha = alpha;
     a.beta = beta;
     a.nnz = h->nnz;
+    a.last_vec = (h->nnz & ~3) - 4;
     a.perm = h->perm;
     a.blocks = h->blocks;
     a.n_blocks = h->n_blocks;

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(DW_WG) void k_gemv_f16(int m, int n, const unsigned
                                                     float *__restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) unsigned short xs_dyn[];
     if (X_LDS) {
-        for (int k = threadIdx.x; k < n; k += blockDim.x) xs_dyn[k] = x[k];
+        stage_halfs(xs_dyn, x, n);
         __syncthreads();
     }
     const unsigned short *xv = X_LDS ? xs_dyn : x;

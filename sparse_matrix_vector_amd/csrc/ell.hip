@@ -59,7 +59,12 @@ __device__ __forceinline__ float finish(float acc, float alpha, float beta, floa
     return r;
 }
 
-// Four rows per lane, 16-byte slot loads.
+// Four rows per lane, 16-byte slot loads.  Slots are taken U at a time (U =
+// the whole width when it is at most 8, a compile-time constant): all their
+// column and value loads are issued first, then all their gathers (padding
+// gathers x[0] and is masked after), so one wait covers each batch instead
+// of one per slot.  Slots are summed in slot order.
+template <int U>
 __global__ __launch_bounds__(WG) void k_ell_apply4(int n, int width, const int *__restrict__ ec,
                                                    const float *__restrict__ ev, float alpha,
                                                    const float *__restrict__ x, float beta, float *__restrict__ y) {
@@ -68,13 +73,28 @@ __global__ __launch_bounds__(WG) void k_ell_apply4(int n, int width, const int *
     const int i0 = 4 * quad;
     if (i0 >= n) return;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k = 0; k < width; ++k) {
-        const size_t slot = (size_t)k * (size_t)n + (size_t)i0;
-        const i32x4 c = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(ec + slot));
-        const f32x4 f = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(ev + slot));
+    for (int k0 = 0; k0 < width; k0 += U) {
+        i32x4 c[U];
+        f32x4 f[U];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            if (c[t] >= 0) acc[t] = fmaf(f[t], x[c[t]], acc[t]);
+        for (int u = 0; u < U; ++u) {
+            const int k = min(k0 + u, width - 1);   // only the generic width reaches past the end
+            const size_t slot = (size_t)k * (size_t)n + (size_t)i0;
+            c[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(ec + slot));
+            f[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(ev + slot));
+        }
+        float xv[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xv[u][t] = x[(k0 + u < width) ? max(c[u][t], 0) : 0];
+#pragma unroll
+        for (int u = 0; u < U; ++u) issue_together(xv[u][0], xv[u][1], xv[u][2], xv[u][3]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc[t] = (k0 + u < width && c[u][t] >= 0) ? fmaf(f[u][t], xv[u][t], acc[t]) : acc[t];
     }
     f32x4 yo = {0.0f, 0.0f, 0.0f, 0.0f};
     if (beta != 0.0f) yo = *reinterpret_cast<const f32x4 *>(y + i0);
@@ -95,7 +115,8 @@ __global__ __launch_bounds__(WG) void k_ell_apply1(int n, int width, const int *
     for (int k = 0; k < width; ++k) {
         const size_t slot = (size_t)k * (size_t)n + (size_t)i;
         const int c = ec[slot];
-        if (c >= 0) acc = fmaf(ev[slot], x[c], acc);
+        const float xv = x[max(c, 0)];
+        acc = c >= 0 ? fmaf(ev[slot], xv, acc) : acc;
     }
     y[i] = finish(acc, alpha, beta, beta != 0.0f ? y[i] : 0.0f);
 }
@@ -157,7 +178,7 @@ extern "C" spmv_status spmv_ell_apply(int32_t n_rows, int32_t n_cols, int32_t wi
     if (n_rows == 0) return SPMV_OK;
     if (!y) return fail(SPMV_ERR_INVALID_VALUE, "y is NULL");
     hipStream_t st = as_stream(stream);
-    if (width == 0) {
+    if (width == 0 || n_cols == 0) {   // no slot can hold a column: y = beta * y
         k_scale<<<(int)ceil_div(n_rows, WG), WG, 0, st>>>(n_rows, beta, y);
         SPMV_LAUNCHED("k_scale");
         return SPMV_OK;
@@ -165,7 +186,18 @@ extern "C" spmv_status spmv_ell_apply(int32_t n_rows, int32_t n_cols, int32_t wi
     if (!ell_col || !ell_val || !x) return fail(SPMV_ERR_INVALID_VALUE, "NULL pointer");
     const bool quad = (n_rows % 4 == 0) && aligned16(ell_col) && aligned16(ell_val) && aligned16(y);
     if (quad) {
-        k_ell_apply4<<<(int)ceil_div(n_rows / 4, WG), WG, 0, st>>>(n_rows, width, ell_col, ell_val, alpha, x, beta, y);
+        const int grid = (int)ceil_div(n_rows / 4, WG);
+        switch (width) {
+#define SPMV_ELL_W(W)                                                                                    \
+    case W:                                                                                              \
+        k_ell_apply4<W><<<grid, WG, 0, st>>>(n_rows, width, ell_col, ell_val, alpha, x, beta, y);      \
+        break;
+            SPMV_ELL_W(1) SPMV_ELL_W(2) SPMV_ELL_W(3) SPMV_ELL_W(4) SPMV_ELL_W(5) SPMV_ELL_W(6) SPMV_ELL_W(7)
+            SPMV_ELL_W(8)
+#undef SPMV_ELL_W
+        default:
+            k_ell_apply4<4><<<grid, WG, 0, st>>>(n_rows, width, ell_col, ell_val, alpha, x, beta, y);
+        }
         SPMV_LAUNCHED("k_ell_apply4");
     } else {
         k_ell_apply1<<<(int)ceil_div(n_rows, WG), WG, 0, st>>>(n_rows, width, ell_col, ell_val, alpha, x, beta, y);

@@ -44,6 +44,14 @@ __global__ void k_fe_beta(int n, float beta, float *__restrict__ y) {
     if (i < n) y[i] = beta != 0.0f ? beta * y[i] : 0.0f;
 }
 
+// Ke (576 floats, 16-byte aligned) into LDS: 144 16-byte vectors, all loads
+// issued before the barrier.
+__device__ __forceinline__ void stage_ke(float *ke, const float *__restrict__ Ke) {
+    if (threadIdx.x < NDOF_E * NDOF_E / 4)
+        reinterpret_cast<f32x4 *>(ke)[threadIdx.x] = reinterpret_cast<const f32x4 *>(Ke)[threadIdx.x];
+    __syncthreads();
+}
+
 __device__ __forceinline__ void load_edof(const int *__restrict__ edof, int e, int (&d)[NDOF_E]) {
     const i32x4 *p = reinterpret_cast<const i32x4 *>(edof + (size_t)e * NDOF_E);
 #pragma unroll
@@ -61,15 +69,18 @@ __global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const
                                                     const float *__restrict__ Ke, float alpha,
                                                     const float *__restrict__ x, float *__restrict__ y) {
     __shared__ __attribute__((aligned(16))) float ke[NDOF_E * NDOF_E];
-    for (int k = threadIdx.x; k < NDOF_E * NDOF_E; k += FE_WG) ke[k] = Ke[k];
-    __syncthreads();
+    stage_ke(ke, Ke);
     const int e = blockIdx.x * FE_WG + threadIdx.x;
     if (e >= n_elem) return;
     int d[NDOF_E];
     load_edof(edof, e, d);
+    // 24 gathers issued together (a constrained DOF reads x[0] and is zeroed
+    // after), rather than one masked load at a time
     float u[NDOF_E];
 #pragma unroll
-    for (int b = 0; b < NDOF_E; ++b) u[b] = (unsigned)d[b] < (unsigned)n_dof ? x[d[b]] : 0.0f;
+    for (int b = 0; b < NDOF_E; ++b) u[b] = x[(unsigned)d[b] < (unsigned)n_dof ? d[b] : 0];
+#pragma unroll
+    for (int b = 0; b < NDOF_E; ++b) u[b] = (unsigned)d[b] < (unsigned)n_dof ? u[b] : 0.0f;
     const float s = alpha * simp(rho[e], penalty);
 #pragma unroll
     for (int a = 0; a < NDOF_E; ++a) {
@@ -94,7 +105,8 @@ __global__ void k_fe_gather(int n_elem, int n_dof, const int *__restrict__ edof,
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= (int64_t)n_elem * NDOF_E) return;
     const int d = edof[k];
-    U[k] = (unsigned)d < (unsigned)n_dof ? x[d] : 0.0f;
+    const float xv = x[(unsigned)d < (unsigned)n_dof ? d : 0];
+    U[k] = (unsigned)d < (unsigned)n_dof ? xv : 0.0f;
 }
 
 // F[e] = alpha * rho_e^p * Ke U[e]; one thread per element.
@@ -102,8 +114,7 @@ __global__ __launch_bounds__(FE_WG) void k_fe_elem(int n_elem, const float *__re
                                                    const float *__restrict__ Ke, float alpha,
                                                    const float *__restrict__ U, float *__restrict__ F) {
     __shared__ __attribute__((aligned(16))) float ke[NDOF_E * NDOF_E];
-    for (int k = threadIdx.x; k < NDOF_E * NDOF_E; k += FE_WG) ke[k] = Ke[k];
-    __syncthreads();
+    stage_ke(ke, Ke);
     const int e = blockIdx.x * FE_WG + threadIdx.x;
     if (e >= n_elem) return;
     float u[NDOF_E];

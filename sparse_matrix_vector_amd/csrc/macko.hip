@@ -29,7 +29,7 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int MK_WAVES = 8;           // waves per workgroup
+constexpr int MK_WAVES = 12;          // waves per workgroup (2 workgroups per CU: 24 waves)
 constexpr int MK_WG = 64 * MK_WAVES;
 constexpr int MK_CHUNK = 512;         // entries per wave per step (64 lanes x 8)
 constexpr int MK_UNROLL = 4;          // chunks whose loads are issued together
@@ -47,21 +47,6 @@ __device__ __forceinline__ void nibble_prefix(unsigned int word, int (&p)[8]) {
     }
 }
 
-// Copies x (fp16, n entries) into LDS with 16-byte loads.
-__device__ __forceinline__ void stage_x(unsigned short *xs, const unsigned short *__restrict__ x, int n) {
-    const int n8 = n & ~7;
-    const bool vec = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
-    for (int k = 8 * threadIdx.x; k < n8; k += 8 * blockDim.x) {
-        if (vec) {
-            *reinterpret_cast<u32x4 *>(xs + k) = *reinterpret_cast<const u32x4 *>(x + k);
-        } else {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) xs[k + t] = x[k + t];
-        }
-    }
-    for (int k = n8 + threadIdx.x; k < n; k += blockDim.x) xs[k] = x[k];
-}
-
 template <bool X_LDS>
 __global__ __launch_bounds__(MK_WG) void k_macko_spmv(int n_rows, int n_cols, const int *__restrict__ mrp,
                                                       const unsigned int *__restrict__ codes,
@@ -70,7 +55,7 @@ __global__ __launch_bounds__(MK_WG) void k_macko_spmv(int n_rows, int n_cols, co
                                                       float *__restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) unsigned short xs_dyn[];
     if (X_LDS) {
-        stage_x(xs_dyn, x, n_cols);
+        stage_halfs(xs_dyn, x, n_cols);
         __syncthreads();
     }
     const unsigned short *xv = X_LDS ? xs_dyn : x;
@@ -102,14 +87,16 @@ __global__ __launch_bounds__(MK_WG) void k_macko_spmv(int n_rows, int n_cols, co
                 const int incl = wave_inclusive_scan(tot);
                 const int base = carry + incl - tot;
                 carry += __builtin_amdgcn_readlane(incl, 63);
-                if (valid) {
+                // No branch on `valid`: an idle lane holds zero values and its
+                // clamped columns stay inside x, so all 8 LDS reads of every
+                // lane are issued together.
+                (void)valid;
 #pragma unroll
-                    for (int t = 0; t < 8; t += 2) {
-                        const int ca = min(base + p[t], last_col);
-                        const int cb = min(base + p[t + 1], last_col);
-                        const unsigned int xp = (unsigned int)xv[ca] | ((unsigned int)xv[cb] << 16);
-                        acc = __builtin_amdgcn_fdot2(as_h2(val[u][t >> 1]), as_h2(xp), acc, false);
-                    }
+                for (int t = 0; t < 8; t += 2) {
+                    const int ca = min(base + p[t], last_col);
+                    const int cb = min(base + p[t + 1], last_col);
+                    const unsigned int xp = (unsigned int)xv[ca] | ((unsigned int)xv[cb] << 16);
+                    acc = __builtin_amdgcn_fdot2(as_h2(val[u][t >> 1]), as_h2(xp), acc, false);
                 }
             }
         }
