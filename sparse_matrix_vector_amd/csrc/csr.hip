@@ -6,26 +6,26 @@
 // its row; section 4.1: a warp shares a row and reduces).  The binned variant
 // follows the row grouping of "Sparse matrix multiplication acceleration"
 // (section 2.1.1 table: groups by work per row with bounds 32 / 512 / 8192,
-// one thread-to-row mapping per group; section 2.2.1: the rows of a group
-// are reached through a Map[] array; section 2.3: the largest group falls
-// back to global memory).  For y = A x the work of a row is its nonzero
+// a different thread-to-row mapping per group; section 2.2.1: the rows of a
+// group are reached through a Map[] array; section 2.3: the largest rows
+// fall back to global memory).  For y = A x the work of a row is its nonzero
 // count.
 //
-// gfx950 mapping of the four groups (wave64, 256-thread workgroups):
-//   group 0 (short rows)   runs of consecutive short rows are cut into
-//                          blocks of <= 512 staged entries / 128 rows; one wave
-//                          streams a block's values and columns with 16-byte
-//                          loads, multiplies by the gathered x, stages the
-//                          products in LDS and then each lane sums whole
-//                          rows (a segmented reduction without atomics);
-//   group 1 (32..511)      one wave per row, 16-byte loads, DPP reduction;
-//   group 2 (512..8191)    one workgroup per row, LDS reduction of 4 waves;
-//   group 3 (>= 8192)      a row is split into 8192-nonzero chunks, one
-//                          workgroup per chunk writes a partial sum to the
-//                          workspace, a second kernel adds the partials of a
-//                          row in order (the global-memory fallback).
-// All groups run in one launch; the workgroup id selects the group.  Every
-// path sums in a fixed order, so results are bit-reproducible run to run.
+// gfx950 mapping of the groups.  The planner builds a list of tasks, each
+// covering at most SLOTS = 512 consecutive entries (two 16-byte vectors of
+// columns and of values per lane of a wave64):
+//   group 0 (short rows)   runs of consecutive short rows cut into blocks of
+//                          <= 512 staged entries / 128 rows; the products
+//                          are staged in LDS and each lane sums whole rows
+//                          (a segmented reduction without atomics);
+//   group 1 (32..511)      one task per row (a wave per row, DPP reduction);
+//   groups 2, 3 (>= 512)   one task per 512-entry chunk of the row, so a row
+//                          gets as many waves as it needs; chunk sums go to
+//                          global memory and the wave finishing a row's last
+//                          chunk adds them in order.
+// One launch runs one wave per task (plus a small kernel that adds the
+// chunk sums of split rows).  Every sum has a fixed order, so results are
+// bit-reproducible run to run.
 #include "common.hpp"
 
 #include <algorithm>
@@ -37,18 +37,12 @@ namespace {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Compile-time shape of the short-row blocks (overridable for tuning sweeps).
-#ifndef SPMV_SHORT_VPL
-#define SPMV_SHORT_VPL 2
-#endif
-
 constexpr int WG = 256;                 // threads per workgroup everywhere here
 constexpr int WAVES = WG / 64;
-constexpr int SHORT_VPL = SPMV_SHORT_VPL;          // 16-byte vectors per lane in a short block
-constexpr int SHORT_SLOTS = 64 * 4 * SHORT_VPL;    // entries staged per wave
-constexpr int SHORT_RMAX = 64 * SHORT_VPL;         // rows per short block (VPL per lane)
-constexpr int LONG_CHUNK = 8192;        // nonzeros per workgroup in group 3
-constexpr int MAX_T0 = SHORT_SLOTS / 2 < 256 ? SHORT_SLOTS / 2 : 256;   // largest bound of group 0
+constexpr int TASK_VPL = 2;             // 16-byte vectors per lane and stream in a task
+constexpr int SLOTS = 64 * 4 * TASK_VPL;   // entries a task stages: 512
+constexpr int SHORT_RMAX = 128;         // rows per short block (2 per lane)
+constexpr int MAX_T0 = 256;             // largest supported bound of group 0
 
 // Error bits raised by the validation kernels.
 constexpr int ERR_RP0 = 1, ERR_RPN = 2, ERR_MONO = 4, ERR_COL = 8;
@@ -58,6 +52,7 @@ struct Meta {
     int bin_offsets[5];
     int head_totals[2];   // {0, number of runs of short rows}
     int block_totals[2];  // {0, number of short blocks}
+    int row_task_totals[2];   // {0, number of tasks of rows in groups 1-3}
     int err;
 };
 
@@ -316,17 +311,18 @@ __global__ __launch_bounds__(WG) void k_blocks_count(const Meta *__restrict__ me
     if (threadIdx.x == 0) counts[blockIdx.x] = total;
 }
 
-// Block descriptor: first row, row count, first and one-past-last nonzero.
+// A short block as a task: rows r0 .. r0 + nr - 1, entries [s, e).
 __global__ __launch_bounds__(WG) void k_blocks_write(const Meta *__restrict__ meta,
                                                      const int *__restrict__ head_pos,
                                                      const int *__restrict__ offsets,
                                                      const int *__restrict__ perm, const int *__restrict__ rp,
-                                                     i32x4 *__restrict__ desc) {
+                                                     i32x4 *__restrict__ tasks) {
     const int nh = meta->head_totals[1];
     const int n0 = meta->bin_offsets[1];
     const int k = blockIdx.x * WG + threadIdx.x;
     int total;
-    int at = offsets[blockIdx.x] + workgroup_exclusive(run_blocks(k, nh, n0, head_pos), &total);
+    int at = meta->row_task_totals[1] + offsets[blockIdx.x] +
+             workgroup_exclusive(run_blocks(k, nh, n0, head_pos), &total);
     if (k >= nh) return;
     const int p = head_pos[k];
     const int rows = (k + 1 < nh ? head_pos[k + 1] : n0) - p;
@@ -338,19 +334,53 @@ __global__ __launch_bounds__(WG) void k_blocks_write(const Meta *__restrict__ me
         d.y = nr;
         d.z = rp[r0 + j];
         d.w = rp[r0 + j + nr];
-        desc[at++] = d;
+        tasks[at++] = d;
     }
 }
 
-// Start and end nonzero of every group-3 row (copied to the host to cut rows
-// into chunks).
-__global__ void k_long_rows(int n3, const int *__restrict__ perm3, const int *__restrict__ rp,
-                            int *__restrict__ out) {
-    const int k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= n3) return;
-    const int r = perm3[k];
-    out[2 * k] = rp[r];
-    out[2 * k + 1] = rp[r + 1];
+// Rows of groups 1-3 become one task per SLOTS-entry chunk, counted from
+// the row's 16-byte-aligned start: chunk c covers [max(s, A + c SLOTS),
+// min(e, A + (c + 1) SLOTS)) with A = s & ~3, so every chunk fits the
+// staging area.  A row with one chunk is a task with nr = 1; chunk c of a
+// longer row is a task with nr = -(c + 1).
+__device__ __forceinline__ int row_chunk_count(int s, int e) { return (e - (s & ~3) + SLOTS - 1) / SLOTS; }
+
+__global__ __launch_bounds__(WG) void k_rowtasks_count(const Meta *__restrict__ meta, int n,
+                                                       const int *__restrict__ perm, const int *__restrict__ rp,
+                                                       int *__restrict__ counts) {
+    const int p = meta->bin_offsets[1] + blockIdx.x * WG + threadIdx.x;
+    int c = 0;
+    if (p < n) {
+        const int r = perm[p];
+        c = row_chunk_count(rp[r], rp[r + 1]);
+    }
+    int total;
+    workgroup_exclusive(c, &total);
+    if (threadIdx.x == 0) counts[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(WG) void k_rowtasks_write(const Meta *__restrict__ meta, int n,
+                                                       const int *__restrict__ perm, const int *__restrict__ rp,
+                                                       const int *__restrict__ offsets, i32x4 *__restrict__ tasks) {
+    const int p = meta->bin_offsets[1] + blockIdx.x * WG + threadIdx.x;
+    int r = 0, s = 0, e = 0, nch = 0;
+    if (p < n) {
+        r = perm[p];
+        s = rp[r];
+        e = rp[r + 1];
+        nch = row_chunk_count(s, e);
+    }
+    int total;
+    const int first = offsets[blockIdx.x] + workgroup_exclusive(nch, &total);
+    const int A = s & ~3;
+    for (int c = 0; c < nch; ++c) {
+        i32x4 d;
+        d.x = r;
+        d.y = nch == 1 ? 1 : -(c + 1);
+        d.z = max(s, A + c * SLOTS);
+        d.w = min(e, A + (c + 1) * SLOTS);
+        tasks[first + c] = d;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -364,10 +394,10 @@ __global__ void k_long_rows(int n3, const int *__restrict__ perm3, const int *__
 // always inside the arrays and needs no branch; a lane whose vector lies
 // past last_vec (only the array's final partial vector) re-reads its
 // entries one by one.  Entries past nnz read as column 0 / value 0; the
-// callers mask entries outside their row range.  Keeping the common path
-// free of divergent branches matters: a divergent path that writes the
-// same registers would make the compiler wait for the 16-byte loads before
-// the next ones are issued.
+// callers mask entries outside their range.  Keeping the common path free
+// of divergent branches matters: a divergent path that writes the same
+// registers would make the compiler wait for the 16-byte loads before the
+// next ones are issued.
 template <bool VEC>
 __device__ __forceinline__ void load4(const int *__restrict__ ci, const float *__restrict__ v, int q, int nnz,
                                       int last_vec, i32x4 &c, f32x4 &f) {
@@ -393,87 +423,10 @@ __device__ __forceinline__ void load4(const int *__restrict__ ci, const float *_
     }
 }
 
-// Sum of v[k] * x[ci[k]] over k in [s, e) by the `nthreads` threads of a
-// wave or workgroup, `tid` in [0, nthreads); each thread covers aligned
-// 4-entry vectors strided by 4 * nthreads, U vectors per step with all
-// their loads issued before any is used.  A vector past e is replaced by
-// the thread's first vector of the step (its entries are masked), and the
-// four gathers of each vector are issued unconditionally (entries outside
-// [s, e) hold valid columns of neighbouring rows, or 0 past nnz) and masked
-// afterwards.
-template <bool VEC, int ROW_UNROLL>
-__device__ __forceinline__ float strided_row_sum(const int *__restrict__ ci, const float *__restrict__ v,
-                                                 const float *__restrict__ x, int s, int e, int nnz, int last_vec,
-                                                 int tid, int nthreads) {
-    float acc = 0.0f;
-    const int base = s & ~3;
-    const int step = 4 * nthreads;
-    for (int q0 = base + 4 * tid; q0 < e; q0 += step * ROW_UNROLL) {
-        i32x4 c[ROW_UNROLL];
-        f32x4 f[ROW_UNROLL];
-#pragma unroll
-        for (int u = 0; u < ROW_UNROLL; ++u) {
-            const int q = q0 + u * step;
-            load4<VEC>(ci, v, q < e ? q : q0, nnz, last_vec, c[u], f[u]);
-        }
-        // masked entries gather x[0] (one shared line) instead of a column of
-        // some other row
-        float xv[ROW_UNROLL][4];
-#pragma unroll
-        for (int u = 0; u < ROW_UNROLL; ++u)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int k = q0 + u * step + t;
-                xv[u][t] = x[(k >= s && k < e) ? c[u][t] : 0];
-            }
-#pragma unroll
-        for (int u = 0; u < ROW_UNROLL; ++u) issue_together(xv[u][0], xv[u][1], xv[u][2], xv[u][3]);
-#pragma unroll
-        for (int u = 0; u < ROW_UNROLL; ++u)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int k = q0 + u * step + t;
-                acc = (k >= s && k < e) ? fmaf(f[u][t], xv[u][t], acc) : acc;
-            }
-    }
-    return acc;
-}
-
-struct BinnedArgs {
-    const int *rp;
-    const int *ci;
-    const float *v;
-    const float *x;
-    float *y;
-    float alpha, beta;
-    int nnz;
-    int last_vec;          // (nnz & ~3) - 4: start of the last full 16-byte vector
-    const int *perm;
-    const i32x4 *blocks;   // short-block descriptors
-    int n_blocks;
-    int g1_begin, n1;      // group-1 rows: perm[g1_begin .. g1_begin + n1)
-    int g2_begin, n2;
-    const i32x4 *chunks;   // group-3 chunks: (unused, start, end, unused)
-    int n_chunks;
-    float *partials;
-    int seg_g2, seg_g1, seg_short;   // first workgroup of each segment; chunks come first
-};
-
-// Workgroup-level sum of one value per thread (fixed order).
-__device__ __forceinline__ float workgroup_sum(float acc, float *red) {
-    acc = wave_sum(acc);
-    if (__lane_id() == 0) red[threadIdx.x / 64] = acc;
-    __syncthreads();
-    float r = 0.0f;
-#pragma unroll
-    for (int k = 0; k < WAVES; ++k) r += red[k];
-    return r;
-}
-
-// Maps workgroup w of an nw-workgroup segment so that the workgroups that
-// run on one XCD (dispatch sends workgroup i to XCD i % 8) take one
-// contiguous range of blocks: consecutive rows then share that XCD's L2 when
-// they gather nearby entries of x.
+// Maps workgroup w of an nw-workgroup grid so that the workgroups that run
+// on one XCD (dispatch sends workgroup i to XCD i % 8) take one contiguous
+// range: consecutive rows then share that XCD's L2 when they gather nearby
+// entries of x.
 __device__ __forceinline__ int xcd_contiguous(int w, int nw) {
     constexpr int NX = 8;
     const int q = nw / NX, r = nw % NX;
@@ -481,135 +434,178 @@ __device__ __forceinline__ int xcd_contiguous(int w, int nw) {
     return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(WG) void k_csr_binned(BinnedArgs a) {
-    __shared__ __attribute__((aligned(16))) float stage[WAVES][SHORT_SLOTS];
-    __shared__ float red[WAVES];
-    const int bid = blockIdx.x;
-    const int lane = __lane_id();
-    const int wv = threadIdx.x / 64;
+// Scalars of the task kernel; its arrays are separate __restrict__ kernel
+// parameters, which lets the compiler read task descriptors with scalar
+// loads even after the kernel has stored to y (a struct member pointer
+// could alias y, and the scalar cache does not see vector stores).
+struct TaskArgs {
+    float alpha, beta;
+    int nnz;
+    int last_vec;          // (nnz & ~3) - 4: start of the last full 16-byte vector
+    int n_row_tasks;       // tasks [0, n_row_tasks): rows of groups 1-3; then n_blocks short blocks
+    int n_blocks;
+};
 
-    if (bid >= a.seg_short) {
-        // ---- group 0: one short block per wave ----
-        const int nw = gridDim.x - a.seg_short;
-        const int blk = xcd_contiguous(bid - a.seg_short, nw) * WAVES + wv;
-        if (blk >= a.n_blocks) return;
-        const i32x4 d = a.blocks[blk];
-        const int r0 = d.x, nr = d.y, s = d.z, e = d.w;
-        const int base = s & ~3;
-        // Row starts for the second phase, issued before the streams so that
-        // waiting for the streams (memory counters drain in issue order)
-        // also covers them.
-        int rs[SHORT_RMAX / 64 + 1];
+struct Arrays {
+    const int *__restrict__ rp;
+    const int *__restrict__ ci;
+    const float *__restrict__ v;
+    const float *__restrict__ x;
+};
+
+// Stage-1 data of one task: the streams of its (at most SLOTS) entries and,
+// for a multi-row block, the start of each of its rows.
+struct Staged {
+    i32x4 c[TASK_VPL];
+    f32x4 f[TASK_VPL];
+    int rs[SHORT_RMAX / 64 + 1];
+};
+
+template <bool VEC>
+__device__ __forceinline__ void stage_task(const TaskArgs &a, const Arrays &m, i32x4 d, int lane, Staged &g) {
+    const int base = d.z & ~3;
+    // Idle lanes (vector past e) re-read the task's first vector, which
+    // keeps every load unconditional and inside the arrays.
 #pragma unroll
-        for (int j = 0; j <= SHORT_RMAX / 64; ++j) rs[j] = a.rp[r0 + min(lane + 64 * j, nr)];
-        // Idle lanes (vector past e) re-read the block's first vector, which
-        // keeps every load unconditional and inside the arrays.
-        i32x4 c[SHORT_VPL];
-        f32x4 f[SHORT_VPL];
+    for (int j = 0; j < TASK_VPL; ++j) {
+        const int q = base + 4 * (lane + 64 * j);
+        load4<VEC>(m.ci, m.v, q < d.w ? q : base, a.nnz, a.last_vec, g.c[j], g.f[j]);
+    }
+    // Row starts of a block (rows r0 .. r0 + nr, the last one being the
+    // block's end); other tasks read rp[r0] in every lane.
+    const int nr = max(d.y, 0);
 #pragma unroll
-        for (int j = 0; j < SHORT_VPL; ++j) {
-            const int q = base + 4 * (lane + 64 * j);
-            load4<VEC>(a.ci, a.v, q < e ? q : base, a.nnz, a.last_vec, c[j], f[j]);
+    for (int j = 0; j <= SHORT_RMAX / 64; ++j) g.rs[j] = m.rp[d.x + min(lane + 64 * j, nr)];
+}
+
+// One wave per task.  The grid is [row tasks][short blocks]: row tasks in
+// natural order, blocks through the XCD-contiguous map (neighbouring blocks
+// on one XCD share its L2 for nearby x entries; for the scattered gathers
+// of long rows the plain order measured faster).  The wave loads the
+// task's streams and row starts, issues all gathers at once (entries
+// outside [s, e) gather x[0]), then reduces by task kind:
+//   nr > 1   a block of short rows: products are staged in the wave's LDS
+//            area and each lane sums whole rows in storage order;
+//   nr == 1  one row: lane-local sums, then a DPP wave reduction;
+//   nr < 0   chunk c = -nr - 1 of a long row: the wave sum goes to the
+//            task's partial slot; k_csr_chunks_finish adds a row's partials
+//            in chunk order afterwards.  (Combining here would need
+//            device-scope release/acquire fences, which write back and
+//            invalidate the whole L2 of an XCD on this part.)
+template <bool VEC>
+__global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__restrict__ tasks,
+                                                  const int *__restrict__ rp, const int *__restrict__ ci,
+                                                  const float *__restrict__ v, const float *__restrict__ x,
+                                                  float *__restrict__ y, float *__restrict__ partials) {
+    __shared__ __attribute__((aligned(16))) float stage[WAVES][SLOTS];
+    const Arrays m{rp, ci, v, x};
+    const int lane = __lane_id();
+    // wave-uniform, stated so that task indices and descriptors are scalar
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int seg_rows = (a.n_row_tasks + WAVES - 1) / WAVES;
+    int t;
+    if ((int)blockIdx.x < seg_rows) {
+        t = blockIdx.x * WAVES + wv;
+        if (t >= a.n_row_tasks) return;
+    } else {
+        const int wb = xcd_contiguous(blockIdx.x - seg_rows, gridDim.x - seg_rows) * WAVES + wv;
+        if (wb >= a.n_blocks) return;
+        t = a.n_row_tasks + wb;
+    }
+    float *st = stage[wv];
+    const i32x4 d = tasks[t];
+    Staged cur;
+    stage_task<VEC>(a, m, d, lane, cur);
+    const int s = d.z, e = d.w, base = s & ~3;
+    float xv[TASK_VPL][4];
+#pragma unroll
+    for (int j = 0; j < TASK_VPL; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int k = base + 4 * (lane + 64 * j) + q;
+            xv[j][q] = x[(k >= s && k < e) ? cur.c[j][q] : 0];
         }
-        float *st = stage[wv];
-        if (e > s) {
-            // Gathers for every lane and entry, unconditionally, so all
-            // 4 * VPL gathers are in flight together; an entry outside the
-            // block gathers x[0] and its product is masked after.
-            float xv[SHORT_VPL][4];
 #pragma unroll
-            for (int j = 0; j < SHORT_VPL; ++j)
+    for (int j = 0; j < TASK_VPL; ++j) issue_together(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
+    f32x4 p[TASK_VPL];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int k = base + 4 * (lane + 64 * j) + t;
-                    xv[j][t] = a.x[(k >= s && k < e) ? c[j][t] : 0];
-                }
+    for (int j = 0; j < TASK_VPL; ++j)
 #pragma unroll
-            for (int j = 0; j < SHORT_VPL; ++j) issue_together(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
-#pragma unroll
-            for (int j = 0; j < SHORT_VPL; ++j) {
-                const int q = base + 4 * (lane + 64 * j);
-                f32x4 p;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int k = q + t;
-                    p[t] = (k >= s && k < e) ? f[j][t] * xv[j][t] : 0.0f;
-                }
-                *reinterpret_cast<f32x4 *>(st + 4 * (lane + 64 * j)) = p;
-            }
+        for (int q = 0; q < 4; ++q) {
+            const int k = base + 4 * (lane + 64 * j) + q;
+            p[j][q] = (k >= s && k < e) ? cur.f[j][q] * xv[j][q] : 0.0f;
         }
+
+    if (d.y > 1) {
+        // ---- block of short rows ----
+#pragma unroll
+        for (int j = 0; j < TASK_VPL; ++j) *reinterpret_cast<f32x4 *>(st + 4 * (lane + 64 * j)) = p[j];
         // The staged products are private to this wave: a wave-level barrier
-        // (LDS operations of one wave complete in order) replaces a
-        // workgroup barrier, so the four waves of a workgroup never wait for
-        // each other.
+        // (LDS operations of one wave complete in order) is enough.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // Each lane sums whole rows from the staged products in storage
-        // order, reading 8 staged entries per step so their LDS latencies
-        // overlap.  Row i's end is row i+1's start: lane l holds the start of
-        // row l + 64 j; the next row's start comes from lane l + 1 (or from
-        // lane 0 of the next j for lane 63).
+        const int nr = d.y;
+        // Lane l sums row l + 64 j, reading 8 staged entries per step so
+        // their LDS latencies overlap.  Row i's end is row i+1's start: from
+        // lane l + 1, or from lane 0 of the next j for lane 63.
 #pragma unroll
         for (int j = 0; j < SHORT_RMAX / 64; ++j) {
-            const int nxt_same = __shfl_down(rs[j], 1);
-            const int nxt_wrap = __shfl(rs[j + 1], 0);
+            const int nxt_same = __shfl_down(cur.rs[j], 1);
+            const int nxt_wrap = __shfl(cur.rs[j + 1], 0);
             const int end = (lane < 63 ? nxt_same : nxt_wrap) - base;
-            const int i = lane + 64 * j;
-            if (i < nr) {
+            const int i_row = lane + 64 * j;
+            if (i_row < nr) {
                 float acc = 0.0f;
-                for (int k = rs[j] - base; k < end; k += 8) {
-                    float v[8];
+                for (int k = cur.rs[j] - base; k < end; k += 8) {
+                    float vv[8];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) v[u] = st[min(k + u, SHORT_SLOTS - 1)];
+                    for (int u = 0; u < 8; ++u) vv[u] = st[min(k + u, SLOTS - 1)];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) acc += k + u < end ? v[u] : 0.0f;
+                    for (int u = 0; u < 8; ++u) acc += k + u < end ? vv[u] : 0.0f;
                 }
-                store_y(a.y, r0 + i, acc, a.alpha, a.beta);
+                store_y(y, d.x + i_row, acc, a.alpha, a.beta);
             }
         }
         return;
     }
-
-    if (bid >= a.seg_g1) {
-        // ---- group 1: one wave per row ----
-        const int idx = (bid - a.seg_g1) * WAVES + wv;
-        if (idx >= a.n1) return;
-        const int row = a.perm[a.g1_begin + idx];
-        const int s = a.rp[row], e = a.rp[row + 1];
-        float acc = strided_row_sum<VEC, 1>(a.ci, a.v, a.x, s, e, a.nnz, a.last_vec, lane, 64);
-        acc = wave_sum(acc);
-        if (lane == 0) store_y(a.y, row, acc, a.alpha, a.beta);
-        return;
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < TASK_VPL; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc += p[j][q];
+    acc = wave_sum(acc);
+    if (d.y == 1) {
+        // ---- one whole row ----
+        if (lane == 0) store_y(y, d.x, acc, a.alpha, a.beta);
+    } else {
+        // ---- chunk of a long row: partial sum, added by k_csr_chunks_finish ----
+        if (lane == 0) partials[t] = acc;
     }
-
-    if (bid >= a.seg_g2) {
-        // ---- group 2: one workgroup per row ----
-        const int row = a.perm[a.g2_begin + (bid - a.seg_g2)];
-        const int s = a.rp[row], e = a.rp[row + 1];
-        float acc = strided_row_sum<VEC, 4>(a.ci, a.v, a.x, s, e, a.nnz, a.last_vec, threadIdx.x, WG);
-        acc = workgroup_sum(acc, red);
-        if (threadIdx.x == 0) store_y(a.y, row, acc, a.alpha, a.beta);
-        return;
-    }
-
-    // ---- group 3: one workgroup per chunk of a long row ----
-    const i32x4 ch = a.chunks[bid];
-    float acc = strided_row_sum<VEC, 4>(a.ci, a.v, a.x, ch.y, ch.z, a.nnz, a.last_vec, threadIdx.x, WG);
-    acc = workgroup_sum(acc, red);
-    if (threadIdx.x == 0) a.partials[bid] = acc;
 }
 
-// Adds the chunk partial sums of each group-3 row in chunk order.
-__global__ void k_csr_long_finish(int n3, const int *__restrict__ perm3, const int *__restrict__ row_chunks,
-                                  const float *__restrict__ partials, float alpha, float beta,
-                                  float *__restrict__ y) {
-    const int k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= n3) return;
+// One thread per row task; the thread of a long row's first chunk adds the
+// row's chunk partials in chunk order and writes y.
+__global__ void k_csr_chunks_finish(int n_row_tasks, const i32x4 *__restrict__ tasks, const int *__restrict__ rp,
+                                    const float *__restrict__ partials, float alpha, float beta,
+                                    float *__restrict__ y) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n_row_tasks) return;
+    const i32x4 d = tasks[t];
+    if (d.y != -1) return;
+    const int nch = row_chunk_count(rp[d.x], rp[d.x + 1]);
     float acc = 0.0f;
-    for (int c = row_chunks[k]; c < row_chunks[k + 1]; ++c) acc += partials[c];
-    store_y(y, perm3[k], acc, alpha, beta);
+    for (int c = 0; c < nch; ++c) acc += partials[t + c];
+    store_y(y, d.x, acc, alpha, beta);
+}
+
+// y = beta * y (no read when beta == 0): the whole product when A has no
+// nonzeros.  The task kernel is never launched then, because its masked
+// gathers read x[0], which exists only when n_cols >= 1 (guaranteed by the
+// column validation once nnz > 0).
+__global__ void k_csr_scale(int n, float beta, float *__restrict__ y) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) y[i] = beta != 0.0f ? beta * y[i] : 0.0f;
 }
 
 __global__ __launch_bounds__(WG) void k_csr_scalar(int n, const int *__restrict__ rp, const int *__restrict__ ci,
@@ -644,18 +640,20 @@ __global__ __launch_bounds__(WG) void k_csr_vector(int n, const int *__restrict_
 // Workspace layout of a BINNED plan
 // ---------------------------------------------------------------------------
 struct Layout {
-    size_t meta, perm, counts, offsets, hcounts, hoffsets, heads, blocks, long_rows, chunks, row_chunks,
-        partials, total;
-    int64_t max_long_rows, max_chunks;
+    size_t meta, perm, counts, offsets, hcounts, hoffsets, heads, tasks, partials, total;
+    int64_t max_row_tasks, max_tasks;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-Layout make_layout(int n, int nnz, int t2) {
+// Bounds: a row of groups 1-3 (>= t0 entries) has at most len / SLOTS + 2
+// chunks, and there are at most min(n, nnz / t0) such rows; blocks are at
+// most one per short row.
+Layout make_layout(int n, int nnz, int t0) {
     Layout L{};
     const int64_t nwg = ceil_div(std::max(n, 1), WG);
-    L.max_long_rows = std::min<int64_t>(n, nnz / std::max(t2, 1));
-    L.max_chunks = ceil_div(nnz, LONG_CHUNK) + L.max_long_rows;
+    L.max_row_tasks = (int64_t)nnz / SLOTS + 2 * std::min<int64_t>(n, nnz / std::max(t0, 1)) + 1;
+    L.max_tasks = L.max_row_tasks + n + 1;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -669,11 +667,8 @@ Layout make_layout(int n, int nnz, int t2) {
     L.hcounts = take(sizeof(int) * nwg);
     L.hoffsets = take(sizeof(int) * nwg);
     L.heads = take(sizeof(int) * ((size_t)n + 1));
-    L.blocks = take(sizeof(i32x4) * ((size_t)n + 1));
-    L.long_rows = take(sizeof(int) * 2 * (size_t)(L.max_long_rows + 1));
-    L.chunks = take(sizeof(i32x4) * (size_t)(L.max_chunks + 1));
-    L.row_chunks = take(sizeof(int) * (size_t)(L.max_long_rows + 1));
-    L.partials = take(sizeof(float) * (size_t)(L.max_chunks + 1));
+    L.tasks = take(sizeof(i32x4) * (size_t)L.max_tasks);
+    L.partials = take(sizeof(float) * (size_t)L.max_row_tasks);
     L.total = off;
     return L;
 }
@@ -703,13 +698,13 @@ struct spmv_csr_plan {
     bool vec_ok;
     // BINNED plan (pointers into the caller's workspace)
     int *perm = nullptr;
-    const i32x4 *blocks = nullptr;
-    int n_blocks = 0;
     int bin_off[5] = {0, 0, 0, 0, 0};
-    const i32x4 *chunks = nullptr;
-    const int *row_chunks = nullptr;
+    const i32x4 *tasks = nullptr;
+    int n_row_tasks = 0;
+    int n_blocks = 0;
     float *partials = nullptr;
-    int n_chunks = 0;
+    bool has_chunked_rows = false;   // some row is split into several tasks
+    int grid = 0;          // workgroups of the task kernel
 };
 
 extern "C" spmv_status spmv_csr_row_stats(int32_t n_rows, const int32_t *row_ptr, int32_t *max_len,
@@ -750,7 +745,7 @@ extern "C" spmv_status spmv_csr_plan_size(int32_t n_rows, int32_t nnz, const int
     int t[3];
     spmv_status s = check_thresholds(thresholds, t);
     if (s != SPMV_OK) return s;
-    *bytes = make_layout(n_rows, nnz, t[2]).total;
+    *bytes = make_layout(n_rows, nnz, t[0]).total;
     return SPMV_OK;
 }
 
@@ -783,16 +778,25 @@ spmv_status build_binned_plan(spmv_csr_plan *h, char *ws, const Layout &L, hipSt
     int *hcounts = reinterpret_cast<int *>(ws + L.hcounts);
     int *hoffsets = reinterpret_cast<int *>(ws + L.hoffsets);
     int *heads = reinterpret_cast<int *>(ws + L.heads);
-    i32x4 *blocks = reinterpret_cast<i32x4 *>(ws + L.blocks);
+    i32x4 *tasks = reinterpret_cast<i32x4 *>(ws + L.tasks);
     const int nwg = (int)ceil_div(std::max(n, 1), WG);
-    const int window = SHORT_SLOTS - h->t[0] - 1;
+    const int window = SLOTS - h->t[0] - 1;
 
+    // 1. rows grouped by length: bin_offsets and perm (a stable counting sort)
     k_plan_count<<<nwg, WG, 0, st>>>(n, h->rp, h->t[0], h->t[1], h->t[2], counts);
     SPMV_LAUNCHED("k_plan_count");
     k_plan_scan<<<1, 1024, 0, st>>>(nwg, 4, counts, offsets, meta->bin_offsets);
     SPMV_LAUNCHED("k_plan_scan");
     k_plan_scatter<<<nwg, WG, 0, st>>>(n, h->rp, h->t[0], h->t[1], h->t[2], offsets, perm);
     SPMV_LAUNCHED("k_plan_scatter");
+    // 2. tasks of the rows in groups 1-3 (perm order)
+    k_rowtasks_count<<<nwg, WG, 0, st>>>(meta, n, perm, h->rp, hcounts);
+    SPMV_LAUNCHED("k_rowtasks_count");
+    k_plan_scan<<<1, 1024, 0, st>>>(nwg, 1, hcounts, hoffsets, meta->row_task_totals);
+    SPMV_LAUNCHED("k_plan_scan(row tasks)");
+    k_rowtasks_write<<<nwg, WG, 0, st>>>(meta, n, perm, h->rp, hoffsets, tasks);
+    SPMV_LAUNCHED("k_rowtasks_write");
+    // 3. blocks of short rows, after the row tasks
     k_heads_count<<<nwg, WG, 0, st>>>(meta, perm, h->rp, window, hcounts);
     SPMV_LAUNCHED("k_heads_count");
     k_plan_scan<<<1, 1024, 0, st>>>(nwg, 1, hcounts, hoffsets, meta->head_totals);
@@ -803,52 +807,24 @@ spmv_status build_binned_plan(spmv_csr_plan *h, char *ws, const Layout &L, hipSt
     SPMV_LAUNCHED("k_blocks_count");
     k_plan_scan<<<1, 1024, 0, st>>>(nwg, 1, hcounts, hoffsets, meta->block_totals);
     SPMV_LAUNCHED("k_plan_scan(blocks)");
-    k_blocks_write<<<nwg, WG, 0, st>>>(meta, heads, hoffsets, perm, h->rp, blocks);
+    k_blocks_write<<<nwg, WG, 0, st>>>(meta, heads, hoffsets, perm, h->rp, tasks);
     SPMV_LAUNCHED("k_blocks_write");
     Meta hm{};
     SPMV_HIP(hipMemcpyAsync(&hm, meta, sizeof(Meta), hipMemcpyDeviceToHost, st));
     SPMV_HIP(hipStreamSynchronize(st));
     for (int g = 0; g < 5; ++g) h->bin_off[g] = hm.bin_offsets[g];
+    h->n_row_tasks = hm.row_task_totals[1];
     h->n_blocks = hm.block_totals[1];
+    if (h->n_row_tasks > L.max_row_tasks || (int64_t)h->n_row_tasks + h->n_blocks > L.max_tasks)
+        return fail(SPMV_ERR_INVALID_MATRIX, "task count exceeds its bound");
     h->perm = perm;
-    h->blocks = blocks;
-
-    // group 3: cut rows into chunks on the host
-    const int n3 = h->bin_off[4] - h->bin_off[3];
-    h->n_chunks = 0;
-    if (n3 > 0) {
-        if (n3 > L.max_long_rows) return fail(SPMV_ERR_INVALID_MATRIX, "more long rows than nnz allows");
-        int *long_rows = reinterpret_cast<int *>(ws + L.long_rows);
-        k_long_rows<<<(int)ceil_div(n3, WG), WG, 0, st>>>(n3, perm + h->bin_off[3], h->rp, long_rows);
-        SPMV_LAUNCHED("k_long_rows");
-        std::vector<int> se(2 * (size_t)n3);
-        SPMV_HIP(hipMemcpyAsync(se.data(), long_rows, sizeof(int) * se.size(), hipMemcpyDeviceToHost, st));
-        SPMV_HIP(hipStreamSynchronize(st));
-        std::vector<i32x4> ch;
-        std::vector<int> rc(n3 + 1, 0);
-        for (int k = 0; k < n3; ++k) {
-            rc[k] = (int)ch.size();
-            for (int64_t a = se[2 * k]; a < se[2 * k + 1]; a += LONG_CHUNK) {
-                i32x4 c;
-                c.x = k;
-                c.y = (int)a;
-                c.z = (int)std::min<int64_t>(a + LONG_CHUNK, se[2 * k + 1]);
-                c.w = 0;
-                ch.push_back(c);
-            }
-        }
-        rc[n3] = (int)ch.size();
-        if ((int64_t)ch.size() > L.max_chunks) return fail(SPMV_ERR_INVALID_MATRIX, "chunk count exceeds bound");
-        i32x4 *d_ch = reinterpret_cast<i32x4 *>(ws + L.chunks);
-        int *d_rc = reinterpret_cast<int *>(ws + L.row_chunks);
-        SPMV_HIP(hipMemcpyAsync(d_ch, ch.data(), sizeof(i32x4) * ch.size(), hipMemcpyHostToDevice, st));
-        SPMV_HIP(hipMemcpyAsync(d_rc, rc.data(), sizeof(int) * rc.size(), hipMemcpyHostToDevice, st));
-        SPMV_HIP(hipStreamSynchronize(st));
-        h->chunks = d_ch;
-        h->row_chunks = d_rc;
-        h->partials = reinterpret_cast<float *>(ws + L.partials);
-        h->n_chunks = (int)ch.size();
-    }
+    h->tasks = tasks;
+    h->partials = reinterpret_cast<float *>(ws + L.partials);
+    // rows of groups 1-3 each give one task unless some row was split
+    h->has_chunked_rows = h->n_row_tasks > h->bin_off[4] - h->bin_off[1];
+    // one wave per task: row-task workgroups, then block workgroups
+    h->grid = (int)(ceil_div(h->n_row_tasks, WAVES) + ceil_div(h->n_blocks, WAVES));
+    SPMV_HIP(hipStreamSynchronize(st));
     return SPMV_OK;
 }
 
@@ -869,7 +845,7 @@ extern "C" spmv_status spmv_csr_create(spmv_csr_t *out, int32_t n_rows, int32_t 
     spmv_status s = check_thresholds(thresholds, t);
     if (s != SPMV_OK) return s;
     const int var = variant == SPMV_CSR_AUTO ? SPMV_CSR_BINNED : variant;
-    Layout L = make_layout(n_rows, nnz, t[2]);
+    Layout L = make_layout(n_rows, nnz, t[0]);
     if (var == SPMV_CSR_BINNED) {
         if (!workspace) return fail(SPMV_ERR_INVALID_VALUE, "workspace is NULL");
         if (workspace_bytes < L.total)
@@ -961,42 +937,28 @@ extern "C" spmv_status spmv_csr_apply(spmv_csr_t h, float alpha, const float *x,
     default:
         break;
     }
-    BinnedArgs a{};
-    a.rp = h->rp;
-    a.ci = h->ci;
-    a.v = h->v;
-    a.x = x;
-    a.y = y;
+    if (h->nnz == 0) {
+        k_csr_scale<<<(int)ceil_div(n, WG), WG, 0, st>>>(n, beta, y);
+        SPMV_LAUNCHED("k_csr_scale");
+        return SPMV_OK;
+    }
+    if (h->grid == 0) return SPMV_OK;
+    TaskArgs a{};
     a.alpha = alpha;
     a.beta = beta;
     a.nnz = h->nnz;
     a.last_vec = (h->nnz & ~3) - 4;
-    a.perm = h->perm;
-    a.blocks = h->blocks;
+    a.n_row_tasks = h->n_row_tasks;
     a.n_blocks = h->n_blocks;
-    a.g1_begin = h->bin_off[1];
-    a.n1 = h->bin_off[2] - h->bin_off[1];
-    a.g2_begin = h->bin_off[2];
-    a.n2 = h->bin_off[3] - h->bin_off[2];
-    a.chunks = h->chunks;
-    a.n_chunks = h->n_chunks;
-    a.partials = h->partials;
-    a.seg_g2 = h->n_chunks;
-    a.seg_g1 = a.seg_g2 + a.n2;
-    a.seg_short = a.seg_g1 + (int)ceil_div(a.n1, WAVES);
-    const int grid = a.seg_short + (int)ceil_div(a.n_blocks, WAVES);
-    if (grid > 0) {
-        if (h->vec_ok)
-            k_csr_binned<true><<<grid, WG, 0, st>>>(a);
-        else
-            k_csr_binned<false><<<grid, WG, 0, st>>>(a);
-        SPMV_LAUNCHED("k_csr_binned");
-    }
-    const int n3 = h->bin_off[4] - h->bin_off[3];
-    if (n3 > 0) {
-        k_csr_long_finish<<<(int)ceil_div(n3, WG), WG, 0, st>>>(n3, h->perm + h->bin_off[3], h->row_chunks,
-                                                                h->partials, alpha, beta, y);
-        SPMV_LAUNCHED("k_csr_long_finish");
+    if (h->vec_ok)
+        k_csr_tasks<true><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, h->partials);
+    else
+        k_csr_tasks<false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, h->partials);
+    SPMV_LAUNCHED("k_csr_tasks");
+    if (h->has_chunked_rows) {
+        k_csr_chunks_finish<<<(int)ceil_div(h->n_row_tasks, WG), WG, 0, st>>>(h->n_row_tasks, h->tasks, h->rp,
+                                                                               h->partials, alpha, beta, y);
+        SPMV_LAUNCHED("k_csr_chunks_finish");
     }
     return SPMV_OK;
 }
