@@ -47,7 +47,7 @@ DEFAULT_PATH = {"tiny": "csr", "laplacian": "csr", "powerlaw": "csr", "pruned50"
                 "pruned70": "macko", "pruned90": "macko", "fe": "fem"}
 
 # kernel (as rocprofv3 names it) that dominates each path
-KERNEL = {"csr": "k_csr_binned", "csr-binned": "k_csr_binned", "csr-vector": "k_csr_vector",
+KERNEL = {"csr": "k_csr_tasks", "csr-binned": "k_csr_tasks", "csr-vector": "k_csr_vector",
           "csr-scalar": "k_csr_scalar", "ell": "k_ell_apply", "macko": "k_macko_spmv",
           "dense": "k_gemv_f16", "fem": "k_fe_fused", "fem-3stage": "k_fe_elem"}
 
@@ -336,6 +336,20 @@ def copy_reference(nbytes, steps=400):
             "gbs": round(8 * half / (r["ms_per_apply"] * 1e-3) / 1e9, 1)}
 
 
+def pmc_calibration_copies(nbytes=256 << 20, reps=3):
+    """Plain device copies of a known size (nbytes read + nbytes written),
+    launched outside any graph so that a rocprofv3 counter run records them:
+    the ratio of bytes to the FETCH_SIZE / WRITE_SIZE the copy kernel shows
+    calibrates those counters for the kernels of the same run."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copies: {reps} x {nbytes} bytes read and written")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,6 +361,8 @@ def main():
                     help="cold-cache protocol (see the module docstring)")
     ap.add_argument("--copies", type=int, default=None, help="input copies for the rotate protocol")
     ap.add_argument("--no-graph", action="store_true", help="launch from Python instead of a HIP graph")
+    ap.add_argument("--pmc-calibrate", action="store_true",
+                    help="first run known-size device copies (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time spent on the oracle baseline (0 = skip)")
     ap.add_argument("--no-parity", action="store_true")
@@ -364,6 +380,8 @@ def main():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(2)
     path = args.path or DEFAULT_PATH[args.config]
+    if args.pmc_calibrate:
+        pmc_calibration_copies()
     w = Workload(args.config, path, args.copies if args.protocol == "rotate" else 1)
 
     par = None
