@@ -39,9 +39,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WG = 256;                 // threads per workgroup everywhere here
 constexpr int WAVES = WG / 64;
-constexpr int TASK_VPL = 2;             // 16-byte vectors per lane and stream in a task
+#ifndef SPMV_TASK_VPL
+#define SPMV_TASK_VPL 2
+#endif
+#ifndef SPMV_SHORT_RMAX
+#define SPMV_SHORT_RMAX (64 * SPMV_TASK_VPL)
+#endif
+constexpr int TASK_VPL = SPMV_TASK_VPL;   // 16-byte vectors per lane and stream in a task
 constexpr int SLOTS = 64 * 4 * TASK_VPL;   // entries a task stages: 512
-constexpr int SHORT_RMAX = 128;         // rows per short block (2 per lane)
+constexpr int SHORT_RMAX = SPMV_SHORT_RMAX;   // rows per short block (2 per lane)
 constexpr int MAX_T0 = 256;             // largest supported bound of group 0
 
 // Error bits raised by the validation kernels.
@@ -444,6 +450,7 @@ struct TaskArgs {
     int last_vec;          // (nnz & ~3) - 4: start of the last full 16-byte vector
     int n_row_tasks;       // tasks [0, n_row_tasks): rows of groups 1-3; then n_blocks short blocks
     int n_blocks;
+    int n_rows, n_cols;
 };
 
 struct Arrays {
@@ -453,16 +460,14 @@ struct Arrays {
     const float *__restrict__ x;
 };
 
-// Stage-1 data of one task: the streams of its (at most SLOTS) entries and,
-// for a multi-row block, the start of each of its rows.
+// Stage-1 data of one task: the streams of its (at most SLOTS) entries.
 struct Staged {
     i32x4 c[TASK_VPL];
     f32x4 f[TASK_VPL];
-    int rs[SHORT_RMAX / 64 + 1];
 };
 
 template <bool VEC>
-__device__ __forceinline__ void stage_task(const TaskArgs &a, const Arrays &m, i32x4 d, int lane, Staged &g) {
+__device__ __forceinline__ void stage_streams(const TaskArgs &a, const Arrays &m, i32x4 d, int lane, Staged &g) {
     const int base = d.z & ~3;
     // Idle lanes (vector past e) re-read the task's first vector, which
     // keeps every load unconditional and inside the arrays.
@@ -471,34 +476,66 @@ __device__ __forceinline__ void stage_task(const TaskArgs &a, const Arrays &m, i
         const int q = base + 4 * (lane + 64 * j);
         load4<VEC>(m.ci, m.v, q < d.w ? q : base, a.nnz, a.last_vec, g.c[j], g.f[j]);
     }
-    // Row starts of a block (rows r0 .. r0 + nr, the last one being the
-    // block's end); other tasks read rp[r0] in every lane.
-    const int nr = max(d.y, 0);
-#pragma unroll
-    for (int j = 0; j <= SHORT_RMAX / 64; ++j) g.rs[j] = m.rp[d.x + min(lane + 64 * j, nr)];
 }
+
+// x[c] (and rp[i]) through a buffer resource when the array is below 4 GiB:
+// a 32-bit byte offset per lane instead of 64-bit address arithmetic.
+constexpr int BUF_DWORD3 = 0x00020000;   // gfx9-family buffer resource word 3 (raw 32-bit data)
+
+template <bool BUF>
+struct Gather {
+    const float *__restrict__ p;
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ Gather(const float *ptr, int n) : p(ptr) {
+        if (BUF) r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(ptr), 0, n * 4, BUF_DWORD3);
+    }
+    __device__ __forceinline__ float operator[](int i) const {
+        // the builtin returns the loaded bits as an unsigned integer
+        return BUF ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0)) : p[i];
+    }
+};
+
+template <bool BUF>
+struct GatherI {
+    const int *__restrict__ p;
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ GatherI(const int *ptr, int n) : p(ptr) {
+        if (BUF) r = __builtin_amdgcn_make_buffer_rsrc(const_cast<int *>(ptr), 0, n * 4, BUF_DWORD3);
+    }
+    __device__ __forceinline__ int operator[](int i) const {
+        return BUF ? __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0)) : p[i];
+    }
+};
 
 // One wave per task.  The grid is [row tasks][short blocks]: row tasks in
 // natural order, blocks through the XCD-contiguous map (neighbouring blocks
 // on one XCD share its L2 for nearby x entries; for the scattered gathers
 // of long rows the plain order measured faster).  The wave loads the
-// task's streams and row starts, issues all gathers at once (entries
-// outside [s, e) gather x[0]), then reduces by task kind:
+// task's streams, issues all gathers at once, then reduces by task kind:
 //   nr > 1   a block of short rows: products are staged in the wave's LDS
-//            area and each lane sums whole rows in storage order;
-//   nr == 1  one row: lane-local sums, then a DPP wave reduction;
-//   nr < 0   chunk c = -nr - 1 of a long row: the wave sum goes to the
-//            task's partial slot; k_csr_chunks_finish adds a row's partials
-//            in chunk order afterwards.  (Combining here would need
-//            device-scope release/acquire fences, which write back and
-//            invalidate the whole L2 of an XCD on this part.)
-template <bool VEC>
+//            area and each lane sums whole rows in storage order.  Entries
+//            of the staged vectors outside the block (neighbouring rows,
+//            re-read vectors) are gathered and multiplied too but never
+//            read back, so this path needs no masks: every staged column
+//            is a valid column of A;
+//   nr == 1  one row: masked lane-local sums (entries outside [s, e)
+//            gather x[0]), then a DPP wave reduction;
+//   nr < 0   chunk c = -nr - 1 of a long row: as one row, but the wave sum
+//            goes to the task's partial slot; k_csr_chunks_finish adds a
+//            row's partials in chunk order afterwards.  (Combining here
+//            would need device-scope release/acquire fences, which write
+//            back and invalidate the whole L2 of an XCD on this part.)
+// BUF: x and row_ptr are below 4 GiB and gathered with buffer loads.
+template <bool VEC, bool BUF>
 __global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__restrict__ tasks,
                                                   const int *__restrict__ rp, const int *__restrict__ ci,
                                                   const float *__restrict__ v, const float *__restrict__ x,
                                                   float *__restrict__ y, float *__restrict__ partials) {
-    __shared__ __attribute__((aligned(16))) float stage[WAVES][SLOTS];
+    // 8 slack entries: a row's 8-entry reads never need clamping
+    __shared__ __attribute__((aligned(16))) float stage[WAVES][SLOTS + 8];
     const Arrays m{rp, ci, v, x};
+    const Gather<BUF> xg(x, a.n_cols);
+    const GatherI<BUF> rg(rp, a.n_rows + 1);
     const int lane = __lane_id();
     // wave-uniform, stated so that task indices and descriptors are scalar
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -512,74 +549,89 @@ __global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__res
         if (wb >= a.n_blocks) return;
         t = a.n_row_tasks + wb;
     }
-    float *st = stage[wv];
     const i32x4 d = tasks[t];
-    Staged cur;
-    stage_task<VEC>(a, m, d, lane, cur);
     const int s = d.z, e = d.w, base = s & ~3;
-    float xv[TASK_VPL][4];
-#pragma unroll
-    for (int j = 0; j < TASK_VPL; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int k = base + 4 * (lane + 64 * j) + q;
-            xv[j][q] = x[(k >= s && k < e) ? cur.c[j][q] : 0];
-        }
-#pragma unroll
-    for (int j = 0; j < TASK_VPL; ++j) issue_together(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
-    f32x4 p[TASK_VPL];
-#pragma unroll
-    for (int j = 0; j < TASK_VPL; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int k = base + 4 * (lane + 64 * j) + q;
-            p[j][q] = (k >= s && k < e) ? cur.f[j][q] * xv[j][q] : 0.0f;
-        }
+    Staged cur;
 
     if (d.y > 1) {
-        // ---- block of short rows ----
+        // ---- block of short rows r0 .. r0 + nr - 1 ----
+        const int nr = d.y;
+        // start of each row (lane l: rows l + 64 j; entry nr is the block's
+        // end), loaded together with the streams, ahead of the gathers
+        int rs[SHORT_RMAX / 64 + 1];
 #pragma unroll
-        for (int j = 0; j < TASK_VPL; ++j) *reinterpret_cast<f32x4 *>(st + 4 * (lane + 64 * j)) = p[j];
+        for (int j = 0; j <= SHORT_RMAX / 64; ++j) rs[j] = rg[d.x + min(lane + 64 * j, nr)];
+        stage_streams<VEC>(a, m, d, lane, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        float xv[TASK_VPL][4];
+#pragma unroll
+        for (int j = 0; j < TASK_VPL; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xv[j][q] = xg[cur.c[j][q]];
+#pragma unroll
+        for (int j = 0; j < TASK_VPL; ++j) issue_together(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
+        float *st = stage[wv];
+#pragma unroll
+        for (int j = 0; j < TASK_VPL; ++j) {
+            f32x4 p;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) p[q] = cur.f[j][q] * xv[j][q];
+            *reinterpret_cast<f32x4 *>(st + 4 * (lane + 64 * j)) = p;
+        }
         // The staged products are private to this wave: a wave-level barrier
         // (LDS operations of one wave complete in order) is enough.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int nr = d.y;
         // Lane l sums row l + 64 j, reading 8 staged entries per step so
         // their LDS latencies overlap.  Row i's end is row i+1's start: from
         // lane l + 1, or from lane 0 of the next j for lane 63.
 #pragma unroll
         for (int j = 0; j < SHORT_RMAX / 64; ++j) {
-            const int nxt_same = __shfl_down(cur.rs[j], 1);
-            const int nxt_wrap = __shfl(cur.rs[j + 1], 0);
+            const int nxt_same = __shfl_down(rs[j], 1);
+            const int nxt_wrap = __shfl(rs[j + 1], 0);
             const int end = (lane < 63 ? nxt_same : nxt_wrap) - base;
             const int i_row = lane + 64 * j;
             if (i_row < nr) {
                 float acc = 0.0f;
-                for (int k = cur.rs[j] - base; k < end; k += 8) {
+                for (int k = rs[j] - base; k < end; k += 8) {
                     float vv[8];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) vv[u] = st[min(k + u, SLOTS - 1)];
+                    for (int u = 0; u < 8; ++u) vv[u] = st[k + u];
+                    const int left = end - k;
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) acc += k + u < end ? vv[u] : 0.0f;
+                    for (int u = 0; u < 8; ++u) acc += u < left ? vv[u] : 0.0f;
                 }
                 store_y(y, d.x + i_row, acc, a.alpha, a.beta);
             }
         }
         return;
     }
+
+    // ---- one row, or one chunk of a long row ----
+    stage_streams<VEC>(a, m, d, lane, cur);
+    float xv[TASK_VPL][4];
+#pragma unroll
+    for (int j = 0; j < TASK_VPL; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int k = base + 4 * (lane + 64 * j) + q;
+            xv[j][q] = xg[(k >= s && k < e) ? cur.c[j][q] : 0];
+        }
+#pragma unroll
+    for (int j = 0; j < TASK_VPL; ++j) issue_together(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
     float acc = 0.0f;
 #pragma unroll
     for (int j = 0; j < TASK_VPL; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc += p[j][q];
+        for (int q = 0; q < 4; ++q) {
+            const int k = base + 4 * (lane + 64 * j) + q;
+            acc += (k >= s && k < e) ? cur.f[j][q] * xv[j][q] : 0.0f;
+        }
     acc = wave_sum(acc);
     if (d.y == 1) {
-        // ---- one whole row ----
         if (lane == 0) store_y(y, d.x, acc, a.alpha, a.beta);
     } else {
-        // ---- chunk of a long row: partial sum, added by k_csr_chunks_finish ----
         if (lane == 0) partials[t] = acc;
     }
 }
@@ -950,10 +1002,18 @@ extern "C" spmv_status spmv_csr_apply(spmv_csr_t h, float alpha, const float *x,
     a.last_vec = (h->nnz & ~3) - 4;
     a.n_row_tasks = h->n_row_tasks;
     a.n_blocks = h->n_blocks;
-    if (h->vec_ok)
-        k_csr_tasks<true><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, h->partials);
+    a.n_rows = n;
+    a.n_cols = h->n_cols;
+    // buffer gathers address at most 4 GiB with 32-bit byte offsets
+    const bool buf = h->n_cols < (1 << 30) && n < (1 << 30) - 1;
+    if (h->vec_ok && buf)
+        k_csr_tasks<true, true><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, h->partials);
+    else if (h->vec_ok)
+        k_csr_tasks<true, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, h->partials);
+    else if (buf)
+        k_csr_tasks<false, true><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, h->partials);
     else
-        k_csr_tasks<false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, h->partials);
+        k_csr_tasks<false, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, h->partials);
     SPMV_LAUNCHED("k_csr_tasks");
     if (h->has_chunked_rows) {
         k_csr_chunks_finish<<<(int)ceil_div(h->n_row_tasks, WG), WG, 0, st>>>(h->n_row_tasks, h->tasks, h->rp,
