@@ -77,6 +77,11 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v;
 }
 
+// Sum over the 64 lanes (all lanes active), as a wave-uniform value.
+__device__ __forceinline__ int wave_sum_int(int v) {
+    return __builtin_amdgcn_readlane(wave_inclusive_scan(v), 63);
+}
+
 // One scan step on floats: v += (v of the lane selected by `ctrl`), lanes
 // without a source (or outside `row_mask`) add +0.
 #define SPMV_DPP_FADD(v, ctrl, row_mask)                                              \

@@ -47,65 +47,218 @@ __device__ __forceinline__ void nibble_prefix(unsigned int word, int (&p)[8]) {
     }
 }
 
-template <bool X_LDS>
+// The first MK_UNROLL chunks (up to MK_UNROLL * 512 entries) of [c0, e1):
+// lane l holds entries c0 + 512 u + 8 l .. + 7 of chunk u (its code word and
+// its eight fp16 values).  Entries at or past e1 are not valid; apply_group
+// masks them by position.
+//   UNCOND: every load is issued, at a valid address: lanes past e1 re-read
+//   the row's last 8 entries, and an empty range reads 16 bytes at `dummy`
+//   (which must be readable and 16-byte aligned).  With no branches around
+//   the loads the compiler can keep them in flight across later waits.
+//   Otherwise lanes past e1 load nothing and hold zeros.
+struct Group {
+    unsigned int word[MK_UNROLL];
+    u32x4 val[MK_UNROLL];
+};
+
+template <bool UNCOND>
+__device__ __forceinline__ void load_group(Group &g, const unsigned int *__restrict__ codes,
+                                           const unsigned short *__restrict__ mvals, int c0, int e1, int lane,
+                                           const void *dummy) {
+    if (UNCOND) {
+        const bool any = e1 > c0;   // uniform
+        const unsigned int *wp = any ? codes : static_cast<const unsigned int *>(dummy);
+        const u32x4 *vp = any ? reinterpret_cast<const u32x4 *>(mvals) : static_cast<const u32x4 *>(dummy);
+#pragma unroll
+        for (int u = 0; u < MK_UNROLL; ++u) {
+            const int ent = any ? min(c0 + u * MK_CHUNK + 8 * lane, e1 - 8) : 0;
+            g.word[u] = __builtin_nontemporal_load(wp + (ent >> 3));
+            g.val[u] = __builtin_nontemporal_load(vp + (ent >> 3));
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < MK_UNROLL; ++u) {
+            const int ent = c0 + u * MK_CHUNK + 8 * lane;
+            const bool valid = ent < e1;
+            g.word[u] = valid ? __builtin_nontemporal_load(codes + (ent >> 3)) : 0u;
+            g.val[u] = valid ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(mvals + ent))
+                             : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+// Decodes the columns of a loaded group (continuing from `carry`, the last
+// column decoded so far in the row) and accumulates value * x[column].
+__device__ __forceinline__ void apply_group(const Group &g, int c0, int e1, int lane, int last_col,
+                                            const unsigned short *xv, int &carry, float &acc) {
+#pragma unroll
+    for (int u = 0; u < MK_UNROLL; ++u) {
+        if (c0 + u * MK_CHUNK >= e1) break;   // uniform: rows end on 256-entry units
+        const bool valid = c0 + u * MK_CHUNK + 8 * lane < e1;
+        int p[8];
+        nibble_prefix(g.word[u], p);
+        const int tot = valid ? p[7] : 0;
+        const int incl = wave_inclusive_scan(tot);
+        const int base = carry + incl - tot;
+        carry += __builtin_amdgcn_readlane(incl, 63);
+        // No branch on `valid`: an idle lane's clamped columns stay inside
+        // x (they are >= 0: base >= carry >= -1 and p[t] >= 1), so all 8
+        // reads of every lane are issued together; its values are masked.
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+            const int ca = min(base + p[t], last_col);
+            const int cb = min(base + p[t + 1], last_col);
+            const unsigned int xp = (unsigned int)xv[ca] | ((unsigned int)xv[cb] << 16);
+            const unsigned int vp = valid ? g.val[u][t >> 1] : 0u;
+            acc = __builtin_amdgcn_fdot2(as_h2(vp), as_h2(xp), acc, false);
+        }
+    }
+    // Consume every register of the group, also of chunks past the row's
+    // end, so that no load into them is still outstanding when they are
+    // reloaded (that would make the compiler wait for every younger load,
+    // the prefetched group included).
+#pragma unroll
+    for (int u = 0; u < MK_UNROLL; ++u) asm volatile("" ::"v"(g.word[u]), "v"(g.val[u]));
+}
+
+// Wave w of the grid owns rows w, w + W, w + 2W, ... (W waves in all).  Its
+// row bounds are read up front, one row per lane (64 rows at a time), so
+// the stream loads of a row never wait for a row_ptr load; the first group
+// of the first row is in flight while x is staged into LDS, and the next
+// group (of the same row, or of the wave's next row) is in flight while the
+// current one is decoded and multiplied.
+// XM: 0 = x read from global memory; 1 = x staged into LDS with 16-byte
+// copies (x 16-byte aligned, n_cols >= 8); 2 = x staged element by element.
+template <int XM>
 __global__ __launch_bounds__(MK_WG) void k_macko_spmv(int n_rows, int n_cols, const int *__restrict__ mrp,
                                                       const unsigned int *__restrict__ codes,
                                                       const unsigned short *__restrict__ mvals, float alpha,
                                                       const unsigned short *__restrict__ x, float beta,
                                                       float *__restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) unsigned short xs_dyn[];
-    if (X_LDS) {
-        stage_halfs(xs_dyn, x, n_cols);
-        __syncthreads();
-    }
-    const unsigned short *xv = X_LDS ? xs_dyn : x;
     const int lane = __lane_id();
-    const int wv = threadIdx.x / 64;
+    // wave-uniform, stated so that row indices and bounds are scalar
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int stride = gridDim.x * MK_WAVES;
+    const int first = blockIdx.x * MK_WAVES + wv;
+    const int nk = first < n_rows ? (n_rows - 1 - first) / stride + 1 : 0;   // rows of this wave
+
+    // bounds of the wave's rows 0..63, one per lane
+    int bs = 0, be = 0;
+    if (lane < nk) {
+        const int r = first + lane * stride;
+        bs = mrp[r];
+        be = mrp[r + 1];
+    }
+    // x: the first pass of the LDS copy is loaded now and stored later
+    // (loads at clamped addresses, so they need no branch)
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    constexpr int XU = 4;
+    const int n8 = XM == 1 ? (n_cols & ~7) : 0;
+    const int xstride = 8 * MK_WG;
+    u32x4_t xr[XU];
+    if (XM == 1) {
+#pragma unroll
+        for (int u = 0; u < XU; ++u)
+            xr[u] = *reinterpret_cast<const u32x4_t *>(x + min(8 * (int)threadIdx.x + u * xstride, n8 - 8));
+    }
+    int b0 = __builtin_amdgcn_readlane(bs, 0), b1 = __builtin_amdgcn_readlane(be, 0);
+    Group g;
+    load_group<XM == 1>(g, codes, mvals, b0, nk > 0 ? b1 : 0, lane, x);
+    if (XM != 0) {
+        if (XM == 1) {
+            // clamped like the loads: threads past the end store the last
+            // vector again, with the same data
+#pragma unroll
+            for (int u = 0; u < XU; ++u)
+                *reinterpret_cast<u32x4_t *>(xs_dyn + min(8 * (int)threadIdx.x + u * xstride, n8 - 8)) = xr[u];
+            for (int k = 8 * (int)threadIdx.x + XU * xstride; k < n8; k += xstride)
+                *reinterpret_cast<u32x4_t *>(xs_dyn + k) = *reinterpret_cast<const u32x4_t *>(x + k);
+        }
+        for (int k = n8 + (int)threadIdx.x; k < n_cols; k += MK_WG) xs_dyn[k] = x[k];
+        // an LDS-only barrier: the stream loads issued above stay in flight
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
+    const unsigned short *xv = XM != 0 ? xs_dyn : x;
     const int last_col = n_cols - 1;
-    for (int row = blockIdx.x * MK_WAVES + wv; row < n_rows; row += gridDim.x * MK_WAVES) {
-        const int e0 = mrp[row], e1 = mrp[row + 1];
-        int carry = -1;
-        float acc = 0.0f;
-        for (int c0 = e0; c0 < e1; c0 += MK_CHUNK * MK_UNROLL) {
-            unsigned int word[MK_UNROLL];
-            u32x4 val[MK_UNROLL];
-#pragma unroll
-            for (int u = 0; u < MK_UNROLL; ++u) {
-                const int ent = c0 + u * MK_CHUNK + 8 * lane;
-                const bool valid = ent < e1;
-                word[u] = valid ? __builtin_nontemporal_load(codes + (ent >> 3)) : 0u;
-                val[u] = valid ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(mvals + ent))
-                               : u32x4{0u, 0u, 0u, 0u};
+
+    // Rows are taken in batches of 64 (one per lane for bounds and sums).
+    // Within a batch there is one step per group; two Group buffers take
+    // turns as current and prefetched, so no loaded data is ever copied
+    // between registers (a copy would have to wait for its load), and the
+    // loop has no stores (with a store in the loop the compiler waits for
+    // every outstanding load at the loop head).  Row sums are collected in
+    // `res` (lane l: row l of the batch) and stored after the batch.
+    Group g2;
+    for (int kb = 0; kb < nk; kb += 64) {
+        const int cnt = min(64, nk - kb);
+        if (kb > 0) {
+            // bounds of the batch's rows, then its first group
+            bs = be = 0;
+            if (lane < cnt) {
+                const int r = first + (kb + lane) * stride;
+                bs = mrp[r];
+                be = mrp[r + 1];
             }
-#pragma unroll
-            for (int u = 0; u < MK_UNROLL; ++u) {
-                if (c0 + u * MK_CHUNK >= e1) break;   // uniform: rows end on 256-entry units
-                const bool valid = c0 + u * MK_CHUNK + 8 * lane < e1;
-                int p[8];
-                nibble_prefix(word[u], p);
-                const int tot = valid ? p[7] : 0;
-                const int incl = wave_inclusive_scan(tot);
-                const int base = carry + incl - tot;
-                carry += __builtin_amdgcn_readlane(incl, 63);
-                // No branch on `valid`: an idle lane holds zero values and its
-                // clamped columns stay inside x, so all 8 LDS reads of every
-                // lane are issued together.
-                (void)valid;
-#pragma unroll
-                for (int t = 0; t < 8; t += 2) {
-                    const int ca = min(base + p[t], last_col);
-                    const int cb = min(base + p[t + 1], last_col);
-                    const unsigned int xp = (unsigned int)xv[ca] | ((unsigned int)xv[cb] << 16);
-                    acc = __builtin_amdgcn_fdot2(as_h2(val[u][t >> 1]), as_h2(xp), acc, false);
+            b0 = __builtin_amdgcn_readlane(bs, 0);
+            b1 = __builtin_amdgcn_readlane(be, 0);
+            load_group<XM == 1>(g, codes, mvals, b0, b1, lane, x);
+        }
+        int k = 0;               // row of the batch being reduced
+        int c0 = b0, e1 = b1;    // current group start, current row end
+        int nb0 = 0, nb1 = 0;    // bounds of row k + 1
+        if (cnt > 1) {
+            nb0 = __builtin_amdgcn_readlane(bs, 1);
+            nb1 = __builtin_amdgcn_readlane(be, 1);
+        }
+        int carry = -1;
+        float acc = 0.0f, res = 0.0f;
+        // steps of the batch: one per group of each row, one for an empty row
+        const int len = be - bs;
+        const int nsteps = wave_sum_int(lane < cnt ? max(1, (len + MK_CHUNK * MK_UNROLL - 1) / (MK_CHUNK * MK_UNROLL)) : 0);
+        auto step = [&](const Group &cur, Group &nxt) {
+            const int c1 = c0 + MK_CHUNK * MK_UNROLL;
+            const bool row_done = c1 >= e1;
+            load_group<XM == 1>(nxt, codes, mvals, row_done ? nb0 : c1, row_done ? nb1 : e1, lane, x);
+            apply_group(cur, c0, e1, lane, last_col, xv, carry, acc);
+            if (!row_done) {
+                c0 = c1;
+            } else {
+                const float sum = wave_sum(acc);
+                if (lane == k) res = sum;
+                acc = 0.0f;
+                carry = -1;
+                ++k;
+                c0 = nb0;
+                e1 = nb1;
+                nb0 = nb1 = 0;
+                if (k + 1 < cnt) {
+                    nb0 = __builtin_amdgcn_readlane(bs, k + 1);
+                    nb1 = __builtin_amdgcn_readlane(be, k + 1);
                 }
             }
+        };
+        // no exit inside the loop body: an early exit there would give the
+        // compiler a path on which the prefetched loads reach the loop head
+        // unwaited, and it would then wait for them on every iteration
+        int i = 0;
+        for (; i + 1 < nsteps; i += 2) {
+            step(g, g2);
+            step(g2, g);
         }
-        acc = wave_sum(acc);
-        if (lane == 0) {
-            float r = alpha * acc;
+        if (i < nsteps) step(g, g2);
+        if (lane < cnt) {
+            const int row = first + (kb + lane) * stride;
+            float r = alpha * res;
             if (beta != 0.0f) r = fmaf(beta, y[row], r);
             y[row] = r;
         }
+        // s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at their
+        // maxima): the store is complete before the next batch, so the
+        // compiler sees no outstanding store at the head of the step loop
+        __builtin_amdgcn_s_waitcnt(0x0F70);
     }
 }
 
@@ -160,11 +313,14 @@ extern "C" spmv_status macko_spmv(int32_t n_rows, int32_t n_cols, const int32_t 
         const size_t lds = (size_t)((n_cols + 7) & ~7) * sizeof(uint16_t);
         // as many workgroups per CU as the LDS allows, at most 2
         const int per_cu = lds <= 48 * 1024 ? 2 : 1;
-        k_macko_spmv<true><<<persistent_grid(n_rows, per_cu), MK_WG, lds, st>>>(n_rows, n_cols, mrow_ptr, codes, mvals,
-                                                                                 alpha, x_f16, beta, y);
+        const int grid = persistent_grid(n_rows, per_cu);
+        if (aligned16(x_f16) && n_cols >= 8)
+            k_macko_spmv<1><<<grid, MK_WG, lds, st>>>(n_rows, n_cols, mrow_ptr, codes, mvals, alpha, x_f16, beta, y);
+        else
+            k_macko_spmv<2><<<grid, MK_WG, lds, st>>>(n_rows, n_cols, mrow_ptr, codes, mvals, alpha, x_f16, beta, y);
     } else {
-        k_macko_spmv<false><<<persistent_grid(n_rows, 2), MK_WG, 0, st>>>(n_rows, n_cols, mrow_ptr, codes, mvals,
-                                                                           alpha, x_f16, beta, y);
+        k_macko_spmv<0><<<persistent_grid(n_rows, 2), MK_WG, 0, st>>>(n_rows, n_cols, mrow_ptr, codes, mvals, alpha,
+                                                                       x_f16, beta, y);
     }
     SPMV_LAUNCHED("k_macko_spmv");
     return SPMV_OK;

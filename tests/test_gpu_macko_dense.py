@@ -89,6 +89,50 @@ def test_trailing_pad_beyond_last_column_and_empty_rows():
     assert host(y)[1] == 0.0 and host(y)[3] == 0.0
 
 
+def _random_macko(n_rows, n_cols, lens, seed):
+    A = gen.random_csr(n_rows, n_cols, lens, seed)
+    v16 = A.vals.astype(np.float16)
+    v16[v16 == 0] = np.float16(0.5)          # stored entries are nonzero
+    x16 = A.x.astype(np.float16).view(np.uint16)
+    enc = S.macko_encode(n_rows, n_cols, A.row_ptr, A.col_idx, v16.view(np.uint16))
+    return enc, x16
+
+
+def test_many_rows_per_wave():
+    """More than 64 rows per wave (rows are taken in batches of 64), with
+    empty rows and rows spanning several groups of 2048 entries."""
+    n_rows, n_cols = 450_000, 4096
+    rng = np.random.default_rng(11)
+    lens = rng.integers(0, 5, n_rows)
+    lens[::997] = 3000                     # 3000 entries + pads: 2 groups
+    lens[5::13] = 0
+    (mrp, codes, mv), x16 = _random_macko(n_rows, n_cols, lens, 12)
+    y_in = rng.uniform(-1, 1, n_rows).astype(np.float32)
+    for alpha, beta in [(1.0, 0.0), (0.5, 2.0)]:
+        y = torch.full((n_rows,), float("nan"), device="cuda") if beta == 0 else dev(y_in)
+        print(f"[macko] many rows alpha={alpha} beta={beta}", flush=True)
+        S.macko_spmv(n_rows, n_cols, dev(mrp), dev(codes), dev(mv), alpha, dev(x16), beta, y)
+        torch.cuda.synchronize()
+        yr, sc = oracle.macko_spmv(n_cols, mrp, codes, mv, x16, alpha, beta, y_in)
+        assert_close(host(y), yr, sc, TAU_F16, f"many rows {alpha} {beta}")
+
+
+def test_misaligned_x():
+    """x not 16-byte aligned: staged into LDS element by element."""
+    n_rows, n_cols = 300, 1001
+    lens = np.random.default_rng(5).integers(0, 400, n_rows)
+    (mrp, codes, mv), x16 = _random_macko(n_rows, n_cols, lens, 6)
+    xbuf = torch.zeros(n_cols + 1, dtype=torch.int16, device="cuda")
+    xbuf[1:] = dev(x16.view(np.int16))
+    xv = xbuf[1:]
+    assert xv.data_ptr() % 16 != 0
+    y = torch.full((n_rows,), float("nan"), device="cuda")
+    S.macko_spmv(n_rows, n_cols, dev(mrp), dev(codes), dev(mv), 1.0, xv, 0.0, y)
+    torch.cuda.synchronize()
+    yr, sc = oracle.macko_spmv(n_cols, mrp, codes, mv, x16)
+    assert_close(host(y), yr, sc, TAU_F16, "misaligned x")
+
+
 def test_macko_bit_reproducible():
     W, enc = _pruned(0.7)
     a = _spmv(W, enc)
