@@ -22,8 +22,10 @@ HBM peak, and the CPU oracle timed on the host (serial fp64 C, bounded
 sample).
 
 Other workloads (parity-test configs, also used for profiles):
-  --config tiny | laplacian | powerlaw | pruned50 | pruned70 | pruned90 | fe
-  --path   csr | csr-binned | csr-vector | csr-scalar | ell | macko | dense | fem | fem-3stage
+  --config tiny | laplacian | powerlaw | varlen | pruned50 | pruned70 | pruned90 | fe
+  --path   csr | csr-binned | csr-vector | csr-scalar | ell | hyb | auto | macko | dense | fem | fem-3stage
+  (varlen: 1M rows of 2..10 entries in a +-1000 band, CV 0.43, the HYB range
+  of the CV rule; auto: the format that rule picks)
 """
 from __future__ import annotations
 
@@ -43,18 +45,21 @@ METRIC = "SpMV GFLOP/s and effective HBM GB/s (% of MI355X peak) per config, 1 G
 FLUSH_BYTES = 1 << 30
 ROTATE_BYTES = 1 << 30
 
-DEFAULT_PATH = {"tiny": "csr", "laplacian": "csr", "powerlaw": "csr", "pruned50": "macko",
+DEFAULT_PATH = {"tiny": "csr", "laplacian": "csr", "powerlaw": "csr", "varlen": "auto", "pruned50": "macko",
                 "pruned70": "macko", "pruned90": "macko", "fe": "fem"}
+CSR_CONFIGS = ("tiny", "laplacian", "powerlaw", "varlen")
 
 # kernel (as rocprofv3 names it) that dominates each path
 KERNEL = {"csr": "k_csr_tasks", "csr-binned": "k_csr_tasks", "csr-vector": "k_csr_vector",
           "csr-scalar": "k_csr_scalar", "ell": "k_ell_apply", "macko": "k_macko_spmv",
-          "dense": "k_gemv_f16", "fem": "k_fe_fused", "fem-3stage": "k_fe_elem"}
+          "dense": "k_gemv_f16", "fem": "k_fe_fused", "fem-3stage": "k_fe_elem", "hyb": "k_ell_apply",
+          "auto": None}
 
 # source file of each path's kernels (for the traffic-record freshness check)
-SOURCE = {"csr": "csr.hip", "csr-binned": "csr.hip", "csr-vector": "csr.hip", "csr-scalar": "csr.hip",
-          "ell": "ell.hip", "macko": "macko.hip", "dense": "dense.hip", "fem": "fem.hip",
-          "fem-3stage": "fem.hip"}
+SOURCE = {"csr": ("csr.hip",), "csr-binned": ("csr.hip",), "csr-vector": ("csr.hip",),
+          "csr-scalar": ("csr.hip",), "ell": ("ell.hip",), "macko": ("macko.hip",), "dense": ("dense.hip",),
+          "fem": ("fem.hip",), "fem-3stage": ("fem.hip",), "hyb": ("ell.hip", "hyb.hip"),
+          "auto": ("csr.hip", "ell.hip", "hyb.hip")}
 
 
 def log(*a):
@@ -62,8 +67,10 @@ def log(*a):
 
 
 def source_sha(path_name):
-    p = os.path.join(ROOT, "sparse_matrix_vector_amd", "csrc", SOURCE[path_name])
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in SOURCE[path_name]:
+        h.update(open(os.path.join(ROOT, "sparse_matrix_vector_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 class Workload:
@@ -80,16 +87,23 @@ class Workload:
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
         self.alpha, self.beta = 1.0, 0.0
         t0 = time.time()
-        if config in ("tiny", "laplacian", "powerlaw"):
-            A = {"tiny": gen.tiny_csr, "laplacian": gen.laplacian_2d, "powerlaw": gen.powerlaw_csr}[config]()
+        if config in CSR_CONFIGS:
+            A = {"tiny": gen.tiny_csr, "laplacian": gen.laplacian_2d, "powerlaw": gen.powerlaw_csr,
+                 "varlen": gen.varlen_banded}[config]()
             self.A = A
             self.workload = {"tiny": "tiny_csr_4096x4096_8perrow", "laplacian": "laplacian_2d_1000x1000",
-                             "powerlaw": "powerlaw_916428_zipf1.9931"}[config]
+                             "powerlaw": "powerlaw_916428_zipf1.9931",
+                             "varlen": "varlen_banded_1000000_len2-10_band1000"}[config]
             self.flops = 2 * A.nnz
+            csr_bytes = 8 * A.nnz + 4 * (A.n_rows + 1) + 4 * A.n_cols + 4 * A.n_rows
+            ell_bytes = lambda W: 8 * W * A.n_rows + 4 * A.n_cols + 4 * A.n_rows
+            # HYB: ELL part (padding included), tail arrays, x, y, and y read
+            # and written again for the tail rows
+            hyb_bytes = lambda W, r, t: ell_bytes(W) + 8 * t + 4 * r + 4 * (r + 1) + 8 * r
             if path.startswith("csr"):
                 var = {"csr": S.CSR_AUTO, "csr-binned": S.CSR_BINNED, "csr-vector": S.CSR_VECTOR,
                        "csr-scalar": S.CSR_SCALAR}[path]
-                self.bytes = 8 * A.nnz + 4 * (A.n_rows + 1) + 4 * A.n_cols + 4 * A.n_rows
+                self.bytes = csr_bytes
                 base = (dev(A.row_ptr), dev(A.col_idx), dev(A.vals), dev(A.x))
 
                 def make(arrs):
@@ -107,7 +121,7 @@ class Workload:
                 ec = torch.empty(A.n_rows * W, dtype=torch.int32, device="cuda")
                 ev = torch.empty(A.n_rows * W, dtype=torch.float32, device="cuda")
                 S.spmv_ell_from_csr(A.n_rows, A.n_cols, dev(A.row_ptr), dev(A.col_idx), dev(A.vals), W, ec, ev)
-                self.bytes = 8 * W * A.n_rows + 4 * A.n_cols + 4 * A.n_rows
+                self.bytes = ell_bytes(W)
 
                 def make(arrs):
                     ec, ev, x = arrs
@@ -116,6 +130,39 @@ class Workload:
                                                      y)), y, None
                 self._setup((ec, ev, dev(A.x)), make, copies)
                 self.shape = {"n_rows": A.n_rows, "nnz": A.nnz, "ell_width": W}
+            elif path == "hyb":
+                rp0 = dev(A.row_ptr)
+                W, r, t = S.spmv_hyb_width(A.n_rows, rp0)
+                self.W, self.hyb = W, (W, r, t)
+                self.bytes = hyb_bytes(W, r, t)
+                H = S.HYBMatrix(A.n_rows, A.n_cols, rp0, dev(A.col_idx), dev(A.vals))
+                base = (H.ell_col, H.ell_val, H.tail_rows, H.tail_rp, H.tail_col, H.tail_val, dev(A.x))
+
+                def make(arrs):
+                    ec, ev, tr, trp, tc, tv, x = arrs
+                    y = torch.zeros(A.n_rows, device="cuda")
+                    return (lambda: S.spmv_hyb_apply(A.n_rows, A.n_cols, W, ec, ev, r, t, tr, trp, tc, tv,
+                                                     self.alpha, x, self.beta, y)), y, None
+                self._setup(base, make, copies)
+                self.shape = {"n_rows": A.n_rows, "nnz": A.nnz, "ell_width": W, "tail_rows": r, "tail_nnz": t}
+            elif path == "auto":
+                plan = S.spmv_auto_plan(A.n_rows, A.n_cols, A.nnz, dev(A.row_ptr))
+                fmt = int(plan.format)
+                self.auto_format = ["ell", "hyb", "csr"][fmt]
+                self.kernel = ["k_ell_apply", "k_ell_apply", "k_csr_tasks"][fmt]
+                self.bytes = [ell_bytes(plan.width), hyb_bytes(plan.width, plan.n_tail_rows, plan.tail_nnz),
+                              csr_bytes][fmt]
+                base = (dev(A.row_ptr), dev(A.col_idx), dev(A.vals), dev(A.x))
+
+                def make(arrs):
+                    rp, ci, v, x = arrs
+                    M = S.AutoMatrix(A.n_rows, A.n_cols, rp, ci, v)
+                    y = torch.zeros(A.n_rows, device="cuda")
+                    return (lambda: M.apply(x, y, self.alpha, self.beta)), y, M
+                self._setup(base, make, copies)
+                self.shape = {"n_rows": A.n_rows, "nnz": A.nnz, "format": self.auto_format,
+                              "width": int(plan.width), "tail_rows": int(plan.n_tail_rows),
+                              "tail_nnz": int(plan.tail_nnz)}
             else:
                 raise SystemExit(f"path {path} does not apply to config {config}")
         elif config.startswith("pruned"):
@@ -191,11 +238,14 @@ class Workload:
     # -- oracle (the CPU baseline and the parity check) --
     def oracle_call(self):
         import oracle
-        if self.config in ("tiny", "laplacian", "powerlaw"):
+        if self.config in CSR_CONFIGS:
             A = self.A
             if self.path == "ell":
                 ec, ev = oracle.ell_from_csr(A.row_ptr, A.col_idx, A.vals, self.W)
                 return lambda: oracle.ell_spmv(A.n_rows, self.W, ec, ev, A.x)
+            if self.path == "hyb":
+                parts = oracle.hyb_from_csr(A.row_ptr, A.col_idx, A.vals, self.W)
+                return lambda: oracle.hyb_spmv(A.n_rows, self.W, *parts, A.x)
             return lambda: oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x)
         if self.config.startswith("pruned"):
             P = self.P
@@ -425,7 +475,7 @@ def main():
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": KERNEL[path]},
+                     "kernel": getattr(w, "kernel", None) or KERNEL[path]},
         "timing_ms": {k: round(v, 6) for k, v in meas.items()},
         "warm_timing_ms": {k: round(v, 6) for k, v in warm.items()},
         "parity": par,

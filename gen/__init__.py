@@ -199,6 +199,44 @@ def random_csr(n_rows: int, n_cols: int, lens, seed: int, sorted_cols: bool = Tr
 
 
 # ---------------------------------------------------------------------------
+# Moderate row-length variation (the HYB regime of the CV rule)
+# ---------------------------------------------------------------------------
+def varlen_banded(n: int = 1_000_000, lo: int = 2, hi: int = 10, band: int = 1000, seed: int = 6) -> CSR:
+    """Square matrix whose row lengths are uniform on {lo..hi} (for 2..10:
+    mean 6, CV = sqrt(80/12)/6 = 0.430, inside the HYB range 0.3..0.7), with
+    distinct columns drawn uniformly from the band [i - band, i + band]
+    clipped to [0, n) and sorted: a PDE-like locality with irregular rows.
+    Values U[-1, 1), x U[-1, 1).  Draw order: lengths, columns, values, x."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(lo, hi + 1, size=n).astype(np.int64)
+    start = np.maximum(np.arange(n, dtype=np.int64) - band, 0)
+    stop = np.minimum(np.arange(n, dtype=np.int64) + band + 1, n)
+    width = stop - start
+    lens = np.minimum(lens, width)
+    # distinct offsets within each row's window, redrawn on duplicates
+    nnz = int(lens.sum())
+    row_of = np.repeat(np.arange(n, dtype=np.int64), lens)
+    off = (rng.random(nnz) * width[row_of]).astype(np.int64)
+    while True:
+        key = row_of * (2 * band + 1) + off
+        order = np.argsort(key, kind="stable")
+        ks = key[order]
+        dup = np.zeros(nnz, dtype=bool)
+        dup[1:] = ks[1:] == ks[:-1]
+        if not dup.any():
+            break
+        idx = np.sort(order[dup])
+        off[idx] = (rng.random(len(idx)) * width[row_of[idx]]).astype(np.int64)
+    key = row_of * (2 * band + 1) + off
+    off = off[np.argsort(key, kind="stable")]
+    cols = (start[row_of] + off).astype(np.int32)
+    rp = _rows_from_lengths(lens)
+    vals = rng.uniform(-1.0, 1.0, nnz).astype(np.float32)
+    x = rng.uniform(-1.0, 1.0, n).astype(np.float32)
+    return CSR(n, n, rp, cols, vals, x, {"name": f"varlen_banded_{n}_len{lo}-{hi}_band{band}", "seed": seed})
+
+
+# ---------------------------------------------------------------------------
 # Config 3: pruned fp16 weight matrix (MACKO input)
 # ---------------------------------------------------------------------------
 SPARSITY_INDEX = {0.3: 0, 0.5: 1, 0.7: 2, 0.9: 3}

@@ -130,6 +130,15 @@ spmv_status spmv_csr_get_plan(spmv_csr_t h, int32_t *h_bin_offsets, int32_t *d_p
 spmv_status spmv_csr_info(spmv_csr_t h, int32_t *variant, int32_t *group_lanes,
                           int32_t *n_short_blocks);
 
+/* Scatter form of spmv_csr_apply: for i < n_rows,
+ *   y[row_map[i]] = alpha * (A x)_i + beta * y[row_map[i]],
+ * with the same kernels and sum order.  row_map: device int32[n_rows]; its
+ * entries must be distinct valid indices of y (not checked).  With
+ * beta = 1 it adds A x into selected rows of a longer y (the HYB tail uses
+ * it).  Asynchronous. */
+spmv_status spmv_csr_apply_rows(spmv_csr_t h, float alpha, const float *x, float beta, float *y,
+                                const int32_t *row_map, void *stream);
+
 /* Releases the handle (not the borrowed arrays or the workspace). */
 spmv_status spmv_csr_destroy(spmv_csr_t h);
 
@@ -154,6 +163,86 @@ spmv_status spmv_ell_from_csr(int32_t n_rows, int32_t n_cols, int32_t nnz,
 spmv_status spmv_ell_apply(int32_t n_rows, int32_t n_cols, int32_t width,
                            const int32_t *ell_col, const float *ell_val, float alpha,
                            const float *x, float beta, float *y, void *stream);
+
+/* ======================================================================== */
+/* HYB: ELL part + CSR tail ("Why SpMV needs CUDA optimisation", section    */
+/* 2.1 table: a mixed CSR + ELL format; section 2.2: the format for a       */
+/* row-length CV between 0.3 and 0.7; section 5: a tuned split of 0.7 ELL   */
+/* to 0.3 COO).                                                             */
+/* Layout: the ELL part holds the first min(len_i, W) entries of each row   */
+/* (ELL layout above); the tail holds the rest, for the rows longer than W  */
+/* only: tail_rows[t] (ascending row ids), tail_rp[t] .. tail_rp[t+1]       */
+/* indexing tail_col / tail_val, in each row's storage order.               */
+/* ======================================================================== */
+
+/* Default ELL share of the nonzeros (the page's 0.7 : 0.3 example). */
+#define SPMV_HYB_ELL_NUM 7
+#define SPMV_HYB_ELL_DEN 10
+
+/* Width rule: the smallest W with den * sum_i min(len_i, W) >= num * nnz
+ * (exact integers; needs 0 <= num <= den, den > 0), and the tail sizes for
+ * that W: n_tail_rows = #rows longer than W, tail_nnz = their entries past
+ * W.  row_ptr: device int32[n_rows+1].  Outputs: host.  Synchronises. */
+spmv_status spmv_hyb_width(int32_t n_rows, const int32_t *row_ptr, int32_t num, int32_t den,
+                           int32_t *width, int32_t *n_tail_rows, int64_t *tail_nnz, void *stream);
+
+/* Splits a CSR matrix (device arrays) into HYB of width `width`.  Outputs
+ * (device, caller-allocated): ell_col / ell_val [width * n_rows],
+ * tail_rows [n_tail_rows], tail_rp [n_tail_rows + 1], tail_col / tail_val
+ * [tail_nnz].  n_tail_rows / tail_nnz must be the sizes this width gives
+ * (spmv_hyb_width; SPMV_ERR_INVALID_VALUE otherwise).  Checks the matrix
+ * (SPMV_ERR_INVALID_MATRIX).  Synchronises. */
+spmv_status spmv_hyb_from_csr(int32_t n_rows, int32_t n_cols, int32_t nnz, const int32_t *row_ptr,
+                              const int32_t *col_idx, const float *vals, int32_t width,
+                              int32_t *ell_col, float *ell_val, int32_t n_tail_rows,
+                              int64_t tail_nnz, int32_t *tail_rows, int32_t *tail_rp,
+                              int32_t *tail_col, float *tail_val, void *stream);
+
+/* y = alpha * A * x + beta * y for a HYB matrix: the ELL part writes
+ * alpha * (ELL part) x + beta * y, then each tail row adds alpha * its tail
+ * sum (fp32, fixed order).  All arrays device.  Asynchronous. */
+spmv_status spmv_hyb_apply(int32_t n_rows, int32_t n_cols, int32_t width, const int32_t *ell_col,
+                           const float *ell_val, int32_t n_tail_rows, int64_t tail_nnz,
+                           const int32_t *tail_rows, const int32_t *tail_rp,
+                           const int32_t *tail_col, const float *tail_val, float alpha,
+                           const float *x, float beta, float *y, void *stream);
+
+/* ======================================================================== */
+/* Format chosen by the CV rule (spmv_format_recommend): ELL, HYB or binned */
+/* CSR, built in a caller workspace and applied through one handle.         */
+/* ELL is replaced by HYB when padding to the longest row would more than   */
+/* double the storage of max(nnz, n_rows) entries or overflow int32.        */
+/* ======================================================================== */
+typedef struct {
+    int32_t format;          /* SPMV_FORMAT_ELL / _HYB / _CSR */
+    int32_t width;           /* ELL width (ELL: the longest row; HYB: the width rule) */
+    int32_t n_tail_rows;     /* HYB tail rows (0 otherwise) */
+    int64_t tail_nnz;        /* HYB tail entries (0 otherwise) */
+    size_t workspace_bytes;  /* device workspace spmv_auto_create needs */
+} spmv_auto_plan_t;
+
+typedef struct spmv_auto *spmv_auto_t;
+
+/* Row statistics and the choice (device row_ptr; plan: host).  Synchronises. */
+spmv_status spmv_auto_plan(int32_t n_rows, int32_t n_cols, int32_t nnz, const int32_t *row_ptr,
+                           spmv_auto_plan_t *plan, void *stream);
+
+/* Builds the planned format in `workspace` (device, 256-byte aligned, at
+ * least plan->workspace_bytes).  The handle borrows the CSR arrays when the
+ * format is CSR; ELL and HYB keep their own copy in the workspace (for HYB
+ * also a binned CSR plan of the tail, which spmv_auto_apply runs through
+ * spmv_csr_apply_rows).  Synchronises. */
+spmv_status spmv_auto_create(spmv_auto_t *h, const spmv_auto_plan_t *plan, int32_t n_rows,
+                             int32_t n_cols, int32_t nnz, const int32_t *row_ptr,
+                             const int32_t *col_idx, const float *vals, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* y = alpha * A * x + beta * y with the planned format.  Asynchronous. */
+spmv_status spmv_auto_apply(spmv_auto_t h, float alpha, const float *x, float beta, float *y,
+                            void *stream);
+
+/* Releases the handle (not the workspace or the borrowed arrays). */
+spmv_status spmv_auto_destroy(spmv_auto_t h);
 
 /* ======================================================================== */
 /* MACKO ("MACKO-SpMV: GPU acceleration and storage optimisation at low      */

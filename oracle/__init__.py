@@ -64,6 +64,11 @@ def lib():
             "oracle_format_choice": (c_int, [c_i64, c_i64, c_i64]),
             "oracle_ell_from_csr": (c_int, [c_int, i32p, i32p, f32p, c_int, i32p, f32p]),
             "oracle_ell_spmv": (None, [c_int, c_int, i32p, f32p, f32p, c_double, c_double, vp, f64p, f64p]),
+            "oracle_hyb_width": (c_int, [c_int, i32p, c_int, c_int]),
+            "oracle_hyb_tail_size": (None, [c_int, i32p, c_int, ctypes.POINTER(c_int), ctypes.POINTER(ctypes.c_longlong)]),
+            "oracle_hyb_from_csr": (None, [c_int, i32p, i32p, f32p, c_int, i32p, f32p, i32p, i32p, i32p, f32p]),
+            "oracle_hyb_spmv": (None, [c_int, c_int, i32p, f32p, c_int, i32p, i32p, i32p, f32p, f32p,
+                                       c_double, c_double, vp, f64p, f64p]),
             "oracle_macko_size": (c_i64, [c_int, c_int, i32p, i32p]),
             "oracle_macko_encode": (c_int, [c_int, c_int, i32p, i32p, u16p, i32p, u32p, u16p]),
             "oracle_macko_decode": (None, [c_int, i32p, u32p, i32p]),
@@ -169,6 +174,55 @@ def ell_spmv(n_rows, width, ell_col, ell_val, x, alpha=1.0, beta=0.0, y_in=None)
     y = np.empty(n_rows, np.float64)
     s = np.empty(n_rows, np.float64)
     lib().oracle_ell_spmv(int(n_rows), int(width), _c(ell_col, np.int32), _c(ell_val, np.float32),
+                          _c(x, np.float32), float(alpha), float(beta), yp, y, s)
+    return y, s
+
+
+HYB_FRACTION = (7, 10)   # ELL share of the nonzeros in the HYB split
+
+
+def hyb_width(row_ptr, num=HYB_FRACTION[0], den=HYB_FRACTION[1]) -> int:
+    """Smallest W with den * sum_i min(len_i, W) >= num * nnz."""
+    rp = _c(row_ptr, np.int32)
+    return int(lib().oracle_hyb_width(len(rp) - 1, rp, int(num), int(den)))
+
+
+def hyb_tail_size(row_ptr, width):
+    """(rows with len > width, entries past width)."""
+    rp = _c(row_ptr, np.int32)
+    r, t = ctypes.c_int(), ctypes.c_longlong()
+    lib().oracle_hyb_tail_size(len(rp) - 1, rp, int(width), ctypes.byref(r), ctypes.byref(t))
+    return r.value, t.value
+
+
+def hyb_from_csr(row_ptr, col_idx, vals, width):
+    """(ell_col, ell_val, tail_rows, tail_rp, tail_col, tail_val)."""
+    rp = _c(row_ptr, np.int32)
+    n = len(rp) - 1
+    nt, tn = hyb_tail_size(rp, width)
+    ec = np.empty(max(width * n, 1), np.int32)
+    ev = np.empty(max(width * n, 1), np.float32)
+    tr = np.empty(max(nt, 1), np.int32)
+    trp = np.empty(nt + 1, np.int32)
+    tc = np.empty(max(tn, 1), np.int32)
+    tv = np.empty(max(tn, 1), np.float32)
+    lib().oracle_hyb_from_csr(n, rp, _c(col_idx, np.int32), _c(vals, np.float32), int(width), ec, ev, tr, trp, tc, tv)
+    return ec[:width * n], ev[:width * n], tr[:nt], trp, tc[:tn], tv[:tn]
+
+
+def hyb_spmv(n_rows, width, ell_col, ell_val, tail_rows, tail_rp, tail_col, tail_val, x,
+             alpha=1.0, beta=0.0, y_in=None):
+    keep, yp = _yin(y_in, n_rows, beta)
+    y = np.empty(n_rows, np.float64)
+    s = np.empty(n_rows, np.float64)
+    z32 = np.zeros(1, np.int32)
+    zf = np.zeros(1, np.float32)
+    ec = _c(ell_col, np.int32) if width * n_rows else z32
+    ev = _c(ell_val, np.float32) if width * n_rows else zf
+    tr = _c(tail_rows, np.int32) if len(tail_rows) else z32
+    tc = _c(tail_col, np.int32) if len(tail_col) else z32
+    tv = _c(tail_val, np.float32) if len(tail_val) else zf
+    lib().oracle_hyb_spmv(int(n_rows), int(width), ec, ev, len(tail_rows), tr, _c(tail_rp, np.int32), tc, tv,
                           _c(x, np.float32), float(alpha), float(beta), yp, y, s)
     return y, s
 

@@ -212,6 +212,124 @@ void oracle_ell_spmv(int n_rows, int W, const int32_t *ell_col, const float *ell
 }
 
 /* ------------------------------------------------------------------------ */
+/* HYB ("Why SpMV needs CUDA optimisation", section 2.1 table: a mixed       */
+/* CSR + ELL format; section 2.2: used when the row-length CV is between    */
+/* 0.3 and 0.7; section 5: a tuned example splits the storage 0.7 ELL to    */
+/* 0.3 COO).  Readings taken where the page is silent:                      */
+/*  - the ELL part holds the first min(len_i, W) entries of every row, in    */
+/*    the slot-major ELL layout above (-1 / +0 padding);                     */
+/*  - the remaining entries of each row form the tail, a CSR over only the  */
+/*    rows that have one: tail_rows[t] (ascending row ids), tail_rp[t] ..    */
+/*    tail_rp[t+1] into tail_col / tail_val, in the row's storage order;    */
+/*  - W is the smallest width whose ELL part holds at least the fraction    */
+/*    num/den of the nonzeros: den * sum_i min(len_i, W) >= num * nnz        */
+/*    (exact integers; W = 0 when nnz == 0).                                 */
+/* ------------------------------------------------------------------------ */
+static long long hyb_ell_count(int n_rows, const int32_t *rp, int W)
+{
+    long long c = 0;
+    for (int i = 0; i < n_rows; ++i) {
+        int32_t len = rp[i + 1] - rp[i];
+        c += len < W ? len : W;
+    }
+    return c;
+}
+
+int oracle_hyb_width(int n_rows, const int32_t *rp, int num, int den)
+{
+    long long nnz = n_rows > 0 ? (long long)rp[n_rows] - rp[0] : 0;
+    int W = 0;
+    /* the smallest W that satisfies the rule, by counting upwards */
+    while ((long long)den * hyb_ell_count(n_rows, rp, W) < (long long)num * nnz) ++W;
+    return W;
+}
+
+/* Sizes of the tail for width W: rows with len > W and their entries past W. */
+void oracle_hyb_tail_size(int n_rows, const int32_t *rp, int W, int *n_tail_rows, long long *tail_nnz)
+{
+    int r = 0;
+    long long t = 0;
+    for (int i = 0; i < n_rows; ++i) {
+        int32_t len = rp[i + 1] - rp[i];
+        if (len > W) {
+            ++r;
+            t += len - W;
+        }
+    }
+    *n_tail_rows = r;
+    *tail_nnz = t;
+}
+
+void oracle_hyb_from_csr(int n_rows, const int32_t *rp, const int32_t *ci, const float *v, int W,
+                         int32_t *ell_col, float *ell_val, int32_t *tail_rows, int32_t *tail_rp,
+                         int32_t *tail_col, float *tail_val)
+{
+    for (int k = 0; k < W; ++k) {
+        for (int i = 0; i < n_rows; ++i) {
+            int32_t len = rp[i + 1] - rp[i];
+            size_t slot = (size_t)k * (size_t)n_rows + (size_t)i;
+            if (k < len) {
+                ell_col[slot] = ci[rp[i] + k];
+                ell_val[slot] = v[rp[i] + k];
+            } else {
+                ell_col[slot] = -1;
+                ell_val[slot] = 0.0f;
+            }
+        }
+    }
+    int t = 0;
+    int32_t pos = 0;
+    tail_rp[0] = 0;
+    for (int i = 0; i < n_rows; ++i) {
+        int32_t len = rp[i + 1] - rp[i];
+        if (len <= W) continue;
+        tail_rows[t] = i;
+        for (int32_t k = W; k < len; ++k) {
+            tail_col[pos] = ci[rp[i] + k];
+            tail_val[pos] = v[rp[i] + k];
+            ++pos;
+        }
+        ++t;
+        tail_rp[t] = pos;
+    }
+}
+
+/* Row i's ELL slots in slot order, then its tail entries: the row's storage
+   order, so the sum equals the CSR definition term by term. */
+void oracle_hyb_spmv(int n_rows, int W, const int32_t *ell_col, const float *ell_val,
+                     int n_tail_rows, const int32_t *tail_rows, const int32_t *tail_rp,
+                     const int32_t *tail_col, const float *tail_val, const float *x,
+                     double alpha, double beta, const float *y_in, double *y_out, double *scale)
+{
+    int t = 0;
+    for (int i = 0; i < n_rows; ++i) {
+        double s = 0.0, a = 0.0;
+        for (int k = 0; k < W; ++k) {
+            size_t slot = (size_t)k * (size_t)n_rows + (size_t)i;
+            if (ell_col[slot] < 0) continue;
+            double p = (double)ell_val[slot] * (double)x[ell_col[slot]];
+            s += p;
+            a += fabs(p);
+        }
+        if (t < n_tail_rows && tail_rows[t] == i) {
+            for (int32_t k = tail_rp[t]; k < tail_rp[t + 1]; ++k) {
+                double p = (double)tail_val[k] * (double)x[tail_col[k]];
+                s += p;
+                a += fabs(p);
+            }
+            ++t;
+        }
+        double yi = alpha * s, sc = fabs(alpha) * a;
+        if (beta != 0.0) {
+            yi += beta * (double)y_in[i];
+            sc += fabs(beta * (double)y_in[i]);
+        }
+        y_out[i] = yi;
+        if (scale) scale[i] = sc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* MACKO format ("MACKO-SpMV: GPU acceleration and storage optimisation at  */
 /* low sparsity", section 2.1: delta coding, dynamic zero padding, 4-bit     */
 /* packing 8 per 32-bit word, aligned loads).  Readings taken where the      */

@@ -168,6 +168,12 @@ def spmv_csr_apply(h, alpha, x, beta, y, stream=None):
           _dev(y, _f32_dtype(), "y"), _stream(stream, y))
 
 
+def spmv_csr_apply_rows(h, alpha, x, beta, y, row_map, stream=None):
+    """Scatter form: y[row_map[i]] = alpha * (A x)_i + beta * y[row_map[i]]."""
+    _call("spmv_csr_apply_rows", h, float(alpha), _dev(x, _f32_dtype(), "x"), float(beta),
+          _dev(y, _f32_dtype(), "y"), _dev(row_map, _i32_dtype(), "row_map"), _stream(stream, y))
+
+
 def spmv_csr_get_plan(h, perm_out=None, stream=None):
     """bin_offsets (list of 5 ints); fills perm_out (CUDA int32 [n_rows]) if given."""
     off = (ctypes.c_int32 * 5)()
@@ -205,6 +211,10 @@ class CSRMatrix:
         spmv_csr_apply(self.handle, alpha, x, beta, y, stream)
         return y
 
+    def apply_rows(self, x, y, row_map, alpha=1.0, beta=0.0, stream=None):
+        spmv_csr_apply_rows(self.handle, alpha, x, beta, y, row_map, stream)
+        return y
+
     def plan(self, perm_out=None):
         return spmv_csr_get_plan(self.handle, perm_out)
 
@@ -238,6 +248,136 @@ def spmv_ell_apply(n_rows, n_cols, width, ell_col, ell_val, alpha, x, beta, y, s
           _dev(ell_col, _i32_dtype(), "ell_col"), _dev(ell_val, _f32_dtype(), "ell_val"),
           float(alpha), _dev(x, _f32_dtype(), "x"), float(beta), _dev(y, _f32_dtype(), "y"),
           _stream(stream, y))
+
+
+# ---------------------------------------------------------------------------
+# HYB (ELL part + CSR tail) and the CV-driven format choice
+# ---------------------------------------------------------------------------
+HYB_ELL_NUM, HYB_ELL_DEN = 7, 10
+
+
+def spmv_hyb_width(n_rows, row_ptr, num=HYB_ELL_NUM, den=HYB_ELL_DEN, stream=None):
+    """(width, n_tail_rows, tail_nnz) of the width rule.  Synchronises."""
+    w, r, t = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _call("spmv_hyb_width", int(n_rows), _dev(row_ptr, _i32_dtype(), "row_ptr"), int(num), int(den),
+          ctypes.byref(w), ctypes.byref(r), ctypes.byref(t), _stream(stream, row_ptr))
+    return w.value, r.value, t.value
+
+
+def spmv_hyb_from_csr(n_rows, n_cols, row_ptr, col_idx, vals, width, n_tail_rows, tail_nnz,
+                      ell_col, ell_val, tail_rows, tail_rp, tail_col, tail_val, stream=None):
+    _call("spmv_hyb_from_csr", int(n_rows), int(n_cols), int(col_idx.numel()),
+          _dev(row_ptr, _i32_dtype(), "row_ptr"), _dev(col_idx, _i32_dtype(), "col_idx"),
+          _dev(vals, _f32_dtype(), "vals"), int(width), _dev(ell_col, _i32_dtype(), "ell_col"),
+          _dev(ell_val, _f32_dtype(), "ell_val"), int(n_tail_rows), int(tail_nnz),
+          _dev(tail_rows, _i32_dtype(), "tail_rows"), _dev(tail_rp, _i32_dtype(), "tail_rp"),
+          _dev(tail_col, _i32_dtype(), "tail_col"), _dev(tail_val, _f32_dtype(), "tail_val"),
+          _stream(stream, row_ptr))
+
+
+def spmv_hyb_apply(n_rows, n_cols, width, ell_col, ell_val, n_tail_rows, tail_nnz, tail_rows, tail_rp,
+                   tail_col, tail_val, alpha, x, beta, y, stream=None):
+    _call("spmv_hyb_apply", int(n_rows), int(n_cols), int(width), _dev(ell_col, _i32_dtype(), "ell_col"),
+          _dev(ell_val, _f32_dtype(), "ell_val"), int(n_tail_rows), int(tail_nnz),
+          _dev(tail_rows, _i32_dtype(), "tail_rows"), _dev(tail_rp, _i32_dtype(), "tail_rp"),
+          _dev(tail_col, _i32_dtype(), "tail_col"), _dev(tail_val, _f32_dtype(), "tail_val"),
+          float(alpha), _dev(x, _f32_dtype(), "x"), float(beta), _dev(y, _f32_dtype(), "y"),
+          _stream(stream, y))
+
+
+class HYBMatrix:
+    """A CSR matrix split into HYB (device tensors it owns)."""
+
+    def __init__(self, n_rows, n_cols, row_ptr, col_idx, vals, width=None, num=HYB_ELL_NUM, den=HYB_ELL_DEN,
+                 stream=None):
+        import torch
+        self.n_rows, self.n_cols = int(n_rows), int(n_cols)
+        w, r, t = spmv_hyb_width(n_rows, row_ptr, num, den, stream)
+        if width is not None and int(width) != w:
+            w = int(width)
+            r, t = _tail_size(row_ptr, w)
+        self.width, self.n_tail_rows, self.tail_nnz = w, r, t
+        d = row_ptr.device
+        self.ell_col = torch.empty(w * self.n_rows, dtype=torch.int32, device=d)
+        self.ell_val = torch.empty(w * self.n_rows, dtype=torch.float32, device=d)
+        self.tail_rows = torch.empty(r, dtype=torch.int32, device=d)
+        self.tail_rp = torch.empty(r + 1, dtype=torch.int32, device=d)
+        self.tail_col = torch.empty(t, dtype=torch.int32, device=d)
+        self.tail_val = torch.empty(t, dtype=torch.float32, device=d)
+        spmv_hyb_from_csr(n_rows, n_cols, row_ptr, col_idx, vals, w, r, t, self.ell_col, self.ell_val,
+                          self.tail_rows, self.tail_rp, self.tail_col, self.tail_val, stream)
+
+    def apply(self, x, y, alpha=1.0, beta=0.0, stream=None):
+        spmv_hyb_apply(self.n_rows, self.n_cols, self.width, self.ell_col, self.ell_val, self.n_tail_rows,
+                       self.tail_nnz, self.tail_rows, self.tail_rp, self.tail_col, self.tail_val, alpha, x,
+                       beta, y, stream)
+        return y
+
+
+def _tail_size(row_ptr, width):
+    """Tail sizes for an explicit width (host computation on the row lengths)."""
+    lens = np.diff(row_ptr.cpu().numpy().astype(np.int64))
+    over = lens > width
+    return int(over.sum()), int((lens[over] - width).sum())
+
+
+def spmv_auto_plan(n_rows, n_cols, nnz, row_ptr, stream=None):
+    """The CV rule's choice for this matrix: an AutoPlan (format, width, tail sizes, workspace bytes)."""
+    p = _lib.AutoPlan()
+    _call("spmv_auto_plan", int(n_rows), int(n_cols), int(nnz), _dev(row_ptr, _i32_dtype(), "row_ptr"),
+          ctypes.byref(p), _stream(stream, row_ptr))
+    return p
+
+
+def spmv_auto_create(plan, n_rows, n_cols, row_ptr, col_idx, vals, workspace, stream=None):
+    """Handle (int) of the planned format built in `workspace` (a uint8 CUDA tensor).  Synchronises."""
+    h = ctypes.c_void_p()
+    _call("spmv_auto_create", ctypes.byref(h), ctypes.byref(plan), int(n_rows), int(n_cols),
+          int(col_idx.numel()), _dev(row_ptr, _i32_dtype(), "row_ptr"), _dev(col_idx, _i32_dtype(), "col_idx"),
+          _dev(vals, _f32_dtype(), "vals"), workspace.data_ptr(), int(workspace.numel()),
+          _stream(stream, row_ptr))
+    return h.value
+
+
+def spmv_auto_apply(handle, alpha, x, beta, y, stream=None):
+    _call("spmv_auto_apply", handle, float(alpha), _dev(x, _f32_dtype(), "x"), float(beta),
+          _dev(y, _f32_dtype(), "y"), _stream(stream, y))
+
+
+def spmv_auto_destroy(handle):
+    _call("spmv_auto_destroy", handle)
+
+
+class AutoMatrix:
+    """ELL, HYB or binned CSR, as the CV rule chooses, behind one handle."""
+
+    def __init__(self, n_rows, n_cols, row_ptr, col_idx, vals, stream=None):
+        import torch
+        self.n_rows, self.n_cols = int(n_rows), int(n_cols)
+        self._arrays = (row_ptr, col_idx, vals)          # borrowed when the format is CSR
+        self.plan = spmv_auto_plan(n_rows, n_cols, col_idx.numel(), row_ptr, stream)
+        self.workspace = torch.empty(max(int(self.plan.workspace_bytes), 256), dtype=torch.uint8,
+                                     device=row_ptr.device)
+        self.handle = spmv_auto_create(self.plan, n_rows, n_cols, row_ptr, col_idx, vals, self.workspace, stream)
+
+    @property
+    def format(self):
+        return int(self.plan.format)
+
+    def apply(self, x, y, alpha=1.0, beta=0.0, stream=None):
+        spmv_auto_apply(self.handle, alpha, x, beta, y, stream)
+        return y
+
+    def close(self):
+        if getattr(self, "handle", None):
+            spmv_auto_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ---------------------------------------------------------------------------

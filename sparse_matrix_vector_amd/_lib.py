@@ -18,6 +18,16 @@ P_i64 = ctypes.POINTER(ctypes.c_int64)
 P_sz = ctypes.POINTER(ctypes.c_size_t)
 P_vp = ctypes.POINTER(ctypes.c_void_p)
 
+
+
+class AutoPlan(ctypes.Structure):
+    """spmv_auto_plan_t."""
+    _fields_ = [("format", ctypes.c_int32), ("width", ctypes.c_int32), ("n_tail_rows", ctypes.c_int32),
+                ("tail_nnz", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+
+
+P_plan = ctypes.POINTER(AutoPlan)
+
 # name -> argument types (every function returns spmv_status, an int)
 SIGNATURES = {
     "spmv_csr_row_stats": [c_i32, vp, P_i32, P_i64, P_i64, vp],
@@ -25,11 +35,19 @@ SIGNATURES = {
     "spmv_csr_plan_size": [c_i32, c_i32, vp, P_sz],
     "spmv_csr_create": [P_vp, c_i32, c_i32, c_i32, vp, vp, vp, c_i32, vp, vp, c_sz, vp],
     "spmv_csr_apply": [vp, c_f32, vp, c_f32, vp, vp],
+    "spmv_csr_apply_rows": [vp, c_f32, vp, c_f32, vp, vp, vp],
     "spmv_csr_get_plan": [vp, P_i32, vp, vp],
     "spmv_csr_info": [vp, P_i32, P_i32, P_i32],
     "spmv_csr_destroy": [vp],
     "spmv_ell_from_csr": [c_i32, c_i32, c_i32, vp, vp, vp, c_i32, vp, vp, vp],
     "spmv_ell_apply": [c_i32, c_i32, c_i32, vp, vp, c_f32, vp, c_f32, vp, vp],
+    "spmv_hyb_width": [c_i32, vp, c_i32, c_i32, P_i32, P_i32, P_i64, vp],
+    "spmv_hyb_from_csr": [c_i32, c_i32, c_i32, vp, vp, vp, c_i32, vp, vp, c_i32, c_i64, vp, vp, vp, vp, vp],
+    "spmv_hyb_apply": [c_i32, c_i32, c_i32, vp, vp, c_i32, c_i64, vp, vp, vp, vp, c_f32, vp, c_f32, vp, vp],
+    "spmv_auto_plan": [c_i32, c_i32, c_i32, vp, P_plan, vp],
+    "spmv_auto_create": [P_vp, P_plan, c_i32, c_i32, c_i32, vp, vp, vp, vp, c_sz, vp],
+    "spmv_auto_apply": [vp, c_f32, vp, c_f32, vp, vp],
+    "spmv_auto_destroy": [vp],
     "macko_encode_size": [c_i32, c_i32, vp, vp, P_i64],
     "macko_encode": [c_i32, c_i32, vp, vp, vp, vp, vp, vp],
     "macko_spmv": [c_i32, c_i32, vp, vp, vp, c_f32, vp, c_f32, vp, vp],

@@ -66,7 +66,10 @@ __device__ __forceinline__ int row_group(int len, int t0, int t1, int t2) {
     return len < t0 ? 0 : (len < t1 ? 1 : (len < t2 ? 2 : 3));
 }
 
-__device__ __forceinline__ void store_y(float *y, int row, float acc, float alpha, float beta) {
+// y[row] = alpha * acc + beta * y[row], where y's element for `row` is
+// ymap[row] when an output row map is given (the scatter form), else row.
+__device__ __forceinline__ void store_y(float *y, const int *ymap, int row, float acc, float alpha, float beta) {
+    if (ymap) row = ymap[row];
     float r = alpha * acc;
     if (beta != 0.0f) r = fmaf(beta, y[row], r);
     y[row] = r;
@@ -530,7 +533,8 @@ template <bool VEC, bool BUF>
 __global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__restrict__ tasks,
                                                   const int *__restrict__ rp, const int *__restrict__ ci,
                                                   const float *__restrict__ v, const float *__restrict__ x,
-                                                  float *__restrict__ y, float *__restrict__ partials) {
+                                                  float *__restrict__ y, const int *__restrict__ ymap,
+                                                  float *__restrict__ partials) {
     // 8 slack entries: a row's 8-entry reads never need clamping
     __shared__ __attribute__((aligned(16))) float stage[WAVES][SLOTS + 8];
     const Arrays m{rp, ci, v, x};
@@ -602,7 +606,7 @@ __global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__res
 #pragma unroll
                     for (int u = 0; u < 8; ++u) acc += u < left ? vv[u] : 0.0f;
                 }
-                store_y(y, d.x + i_row, acc, a.alpha, a.beta);
+                store_y(y, ymap, d.x + i_row, acc, a.alpha, a.beta);
             }
         }
         return;
@@ -630,7 +634,7 @@ __global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__res
         }
     acc = wave_sum(acc);
     if (d.y == 1) {
-        if (lane == 0) store_y(y, d.x, acc, a.alpha, a.beta);
+        if (lane == 0) store_y(y, ymap, d.x, acc, a.alpha, a.beta);
     } else {
         if (lane == 0) partials[t] = acc;
     }
@@ -640,7 +644,7 @@ __global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__res
 // row's chunk partials in chunk order and writes y.
 __global__ void k_csr_chunks_finish(int n_row_tasks, const i32x4 *__restrict__ tasks, const int *__restrict__ rp,
                                     const float *__restrict__ partials, float alpha, float beta,
-                                    float *__restrict__ y) {
+                                    float *__restrict__ y, const int *__restrict__ ymap) {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= n_row_tasks) return;
     const i32x4 d = tasks[t];
@@ -648,33 +652,37 @@ __global__ void k_csr_chunks_finish(int n_row_tasks, const i32x4 *__restrict__ t
     const int nch = row_chunk_count(rp[d.x], rp[d.x + 1]);
     float acc = 0.0f;
     for (int c = 0; c < nch; ++c) acc += partials[t + c];
-    store_y(y, d.x, acc, alpha, beta);
+    store_y(y, ymap, d.x, acc, alpha, beta);
 }
 
 // y = beta * y (no read when beta == 0): the whole product when A has no
 // nonzeros.  The task kernel is never launched then, because its masked
 // gathers read x[0], which exists only when n_cols >= 1 (guaranteed by the
 // column validation once nnz > 0).
-__global__ void k_csr_scale(int n, float beta, float *__restrict__ y) {
+__global__ void k_csr_scale(int n, float beta, float *__restrict__ y, const int *__restrict__ ymap) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) y[i] = beta != 0.0f ? beta * y[i] : 0.0f;
+    if (i >= n) return;
+    const int r = ymap ? ymap[i] : i;
+    y[r] = beta != 0.0f ? beta * y[r] : 0.0f;
 }
 
 __global__ __launch_bounds__(WG) void k_csr_scalar(int n, const int *__restrict__ rp, const int *__restrict__ ci,
                                                    const float *__restrict__ v, const float *__restrict__ x,
-                                                   float alpha, float beta, float *__restrict__ y) {
+                                                   float alpha, float beta, float *__restrict__ y,
+                                                   const int *__restrict__ ymap) {
     const int i = blockIdx.x * WG + threadIdx.x;
     if (i >= n) return;
     float acc = 0.0f;
     for (int k = rp[i]; k < rp[i + 1]; ++k) acc = fmaf(v[k], x[ci[k]], acc);
-    store_y(y, i, acc, alpha, beta);
+    store_y(y, ymap, i, acc, alpha, beta);
 }
 
 // G lanes per row, lanes strided by G, butterfly reduction inside the group.
 template <int G>
 __global__ __launch_bounds__(WG) void k_csr_vector(int n, const int *__restrict__ rp, const int *__restrict__ ci,
                                                    const float *__restrict__ v, const float *__restrict__ x,
-                                                   float alpha, float beta, float *__restrict__ y) {
+                                                   float alpha, float beta, float *__restrict__ y,
+                                                   const int *__restrict__ ymap) {
     const int gid = blockIdx.x * WG + threadIdx.x;
     const int row = gid / G;
     const int sub = gid % G;
@@ -685,7 +693,7 @@ __global__ __launch_bounds__(WG) void k_csr_vector(int n, const int *__restrict_
     }
 #pragma unroll
     for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, G);
-    if (row < n && sub == 0) store_y(y, row, acc, alpha, beta);
+    if (row < n && sub == 0) store_y(y, ymap, row, acc, alpha, beta);
 }
 
 // ---------------------------------------------------------------------------
@@ -953,8 +961,10 @@ extern "C" spmv_status spmv_csr_create(spmv_csr_t *out, int32_t n_rows, int32_t 
     return SPMV_OK;
 }
 
-extern "C" spmv_status spmv_csr_apply(spmv_csr_t h, float alpha, const float *x, float beta, float *y,
-                                      void *stream) {
+namespace {
+
+spmv_status csr_apply(spmv_csr_t h, float alpha, const float *x, float beta, float *y, const int *ymap,
+                      void *stream) {
     if (!h) return fail(SPMV_ERR_INVALID_VALUE, "handle is NULL");
     if (h->n_rows == 0) return SPMV_OK;
     if (!y || (h->n_cols > 0 && !x)) return fail(SPMV_ERR_INVALID_VALUE, "x or y is NULL");
@@ -962,7 +972,7 @@ extern "C" spmv_status spmv_csr_apply(spmv_csr_t h, float alpha, const float *x,
     const int n = h->n_rows;
     switch (h->variant) {
     case SPMV_CSR_SCALAR:
-        k_csr_scalar<<<(int)ceil_div(n, WG), WG, 0, st>>>(n, h->rp, h->ci, h->v, x, alpha, beta, y);
+        k_csr_scalar<<<(int)ceil_div(n, WG), WG, 0, st>>>(n, h->rp, h->ci, h->v, x, alpha, beta, y, ymap);
         SPMV_LAUNCHED("k_csr_scalar");
         return SPMV_OK;
     case SPMV_CSR_VECTOR: {
@@ -970,7 +980,7 @@ extern "C" spmv_status spmv_csr_apply(spmv_csr_t h, float alpha, const float *x,
         const int grid = (int)ceil_div((int64_t)n * g, WG);
 #define SPMV_VEC_CASE(G)                                                                   \
     case G:                                                                                \
-        k_csr_vector<G><<<grid, WG, 0, st>>>(n, h->rp, h->ci, h->v, x, alpha, beta, y); \
+        k_csr_vector<G><<<grid, WG, 0, st>>>(n, h->rp, h->ci, h->v, x, alpha, beta, y, ymap); \
         break;
         switch (g) {
             SPMV_VEC_CASE(2)
@@ -990,7 +1000,7 @@ extern "C" spmv_status spmv_csr_apply(spmv_csr_t h, float alpha, const float *x,
         break;
     }
     if (h->nnz == 0) {
-        k_csr_scale<<<(int)ceil_div(n, WG), WG, 0, st>>>(n, beta, y);
+        k_csr_scale<<<(int)ceil_div(n, WG), WG, 0, st>>>(n, beta, y, ymap);
         SPMV_LAUNCHED("k_csr_scale");
         return SPMV_OK;
     }
@@ -1007,20 +1017,33 @@ extern "C" spmv_status spmv_csr_apply(spmv_csr_t h, float alpha, const float *x,
     // buffer gathers address at most 4 GiB with 32-bit byte offsets
     const bool buf = h->n_cols < (1 << 30) && n < (1 << 30) - 1;
     if (h->vec_ok && buf)
-        k_csr_tasks<true, true><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, h->partials);
+        k_csr_tasks<true, true><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap, h->partials);
     else if (h->vec_ok)
-        k_csr_tasks<true, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, h->partials);
+        k_csr_tasks<true, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap, h->partials);
     else if (buf)
-        k_csr_tasks<false, true><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, h->partials);
+        k_csr_tasks<false, true><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap, h->partials);
     else
-        k_csr_tasks<false, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, h->partials);
+        k_csr_tasks<false, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap, h->partials);
     SPMV_LAUNCHED("k_csr_tasks");
     if (h->has_chunked_rows) {
         k_csr_chunks_finish<<<(int)ceil_div(h->n_row_tasks, WG), WG, 0, st>>>(h->n_row_tasks, h->tasks, h->rp,
-                                                                               h->partials, alpha, beta, y);
+                                                                               h->partials, alpha, beta, y, ymap);
         SPMV_LAUNCHED("k_csr_chunks_finish");
     }
     return SPMV_OK;
+}
+
+}  // namespace
+
+extern "C" spmv_status spmv_csr_apply(spmv_csr_t h, float alpha, const float *x, float beta, float *y,
+                                      void *stream) {
+    return csr_apply(h, alpha, x, beta, y, nullptr, stream);
+}
+
+extern "C" spmv_status spmv_csr_apply_rows(spmv_csr_t h, float alpha, const float *x, float beta, float *y,
+                                           const int32_t *row_map, void *stream) {
+    if (h && h->n_rows > 0 && !row_map) return fail(SPMV_ERR_INVALID_VALUE, "row_map is NULL");
+    return csr_apply(h, alpha, x, beta, y, row_map, stream);
 }
 
 extern "C" spmv_status spmv_csr_get_plan(spmv_csr_t h, int32_t *h_bin_offsets, int32_t *d_perm, void *stream) {

@@ -186,6 +186,33 @@ def test_bit_reproducible(variant):
     assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
 
 
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("case", ["short", "long"])
+def test_apply_rows_scatter(variant, case):
+    """y[map[i]] = alpha (A x)_i + beta y[map[i]]; other entries untouched
+    (short rows: blocks; long rows: chunked rows and their finishing pass)."""
+    if case == "short":
+        A = gen.random_csr(5000, 3000, np.random.default_rng(3).integers(0, 20, 5000), seed=3)
+    else:
+        A = _long_rows_matrix()
+    rng = np.random.default_rng(4)
+    n_y = 3 * A.n_rows + 7
+    row_map = rng.permutation(n_y)[:A.n_rows].astype(np.int32)
+    y_in = rng.uniform(-1, 1, n_y).astype(np.float32)
+    rp, ci, v = _mat(A)
+    M = S.CSRMatrix(A.n_rows, A.n_cols, rp, ci, v, VARIANTS[variant])
+    for alpha, beta in [(1.0, 1.0), (-0.5, 0.0)]:
+        y = dev(y_in)
+        print(f"[apply_rows] {case} {variant} {alpha} {beta}", flush=True)
+        M.apply_rows(dev(A.x), y, dev(row_map), alpha, beta)
+        got = host(y)
+        yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x, alpha, beta, y_in[row_map])
+        assert_close(got[row_map], yr, sc, TAU_F32, f"rows/{case}/{variant}")
+        rest = np.ones(n_y, bool)
+        rest[row_map] = False
+        assert np.array_equal(got[rest].view(np.uint32), y_in[rest].view(np.uint32))
+
+
 def test_zero_rows_and_zero_nnz():
     rp = torch.zeros(1, dtype=torch.int32, device="cuda")
     e_i = torch.zeros(0, dtype=torch.int32, device="cuda")
