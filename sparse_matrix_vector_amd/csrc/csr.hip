@@ -29,6 +29,7 @@
 #include "common.hpp"
 
 #include <algorithm>
+#include <climits>
 #include <vector>
 
 namespace spmv {
@@ -49,6 +50,8 @@ constexpr int TASK_VPL = SPMV_TASK_VPL;   // 16-byte vectors per lane and stream
 constexpr int SLOTS = 64 * 4 * TASK_VPL;   // entries a task stages: 512
 constexpr int SHORT_RMAX = SPMV_SHORT_RMAX;   // rows per short block (2 per lane)
 constexpr int MAX_T0 = 256;             // largest supported bound of group 0
+constexpr int X_TILE_MAX = 6144;        // largest x window staged in LDS per block workgroup (floats)
+constexpr int X_TILE_U = X_TILE_MAX / 4 / WG;   // 16-byte loads per thread to stage it
 
 // Error bits raised by the validation kernels.
 constexpr int ERR_RP0 = 1, ERR_RPN = 2, ERR_MONO = 4, ERR_COL = 8;
@@ -60,6 +63,7 @@ struct Meta {
     int block_totals[2];  // {0, number of short blocks}
     int row_task_totals[2];   // {0, number of tasks of rows in groups 1-3}
     int err;
+    int max_window;       // largest column span (from a 16-byte boundary) of a block workgroup
 };
 
 __device__ __forceinline__ int row_group(int len, int t0, int t1, int t2) {
@@ -392,6 +396,45 @@ __global__ __launch_bounds__(WG) void k_rowtasks_write(const Meta *__restrict__ 
     }
 }
 
+// Column window of each block workgroup (blocks 4q .. 4q + 3 of the short-row
+// blocks, the blocks one workgroup of the task kernel applies): the smallest
+// and largest column of their entries.  max_window gets the largest span
+// counted from the 16-byte boundary below the smallest column.
+__global__ __launch_bounds__(WG) void k_block_spans(Meta *__restrict__ meta, const i32x4 *__restrict__ tasks,
+                                                    const int *__restrict__ ci, int2 *__restrict__ spans) {
+    __shared__ int lo[WAVES], hi[WAVES];
+    const int nb = meta->block_totals[1];
+    const int first = meta->row_task_totals[1];
+    const int lane = __lane_id(), wv = threadIdx.x / 64;
+    const int b = blockIdx.x * WAVES + wv;
+    int mn = INT_MAX, mx = -1;
+    if (b < nb) {
+        const i32x4 d = tasks[first + b];
+        for (int k = d.z + lane; k < d.w; k += 64) {
+            const int c = ci[k];
+            mn = min(mn, c);
+            mx = max(mx, c);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        mn = min(mn, __shfl_xor(mn, off));
+        mx = max(mx, __shfl_xor(mx, off));
+    }
+    if (lane == 0) {
+        lo[wv] = mn;
+        hi[wv] = mx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < WAVES; ++w) {
+            mn = min(mn, lo[w]);
+            mx = max(mx, hi[w]);
+        }
+        spans[blockIdx.x] = int2{mn, mx};
+        if (mx >= 0) atomicMax(&meta->max_window, mx + 1 - (mn & ~3));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Apply kernels
 // ---------------------------------------------------------------------------
@@ -510,120 +553,57 @@ struct GatherI {
     }
 };
 
-// One wave per task.  The grid is [row tasks][short blocks]: row tasks in
-// natural order, blocks through the XCD-contiguous map (neighbouring blocks
-// on one XCD share its L2 for nearby x entries; for the scattered gathers
-// of long rows the plain order measured faster).  The wave loads the
-// task's streams, issues all gathers at once, then reduces by task kind:
-//   nr > 1   a block of short rows: products are staged in the wave's LDS
-//            area and each lane sums whole rows in storage order.  Entries
-//            of the staged vectors outside the block (neighbouring rows,
-//            re-read vectors) are gathered and multiplied too but never
-//            read back, so this path needs no masks: every staged column
-//            is a valid column of A;
-//   nr == 1  one row: masked lane-local sums (entries outside [s, e)
-//            gather x[0]), then a DPP wave reduction;
-//   nr < 0   chunk c = -nr - 1 of a long row: as one row, but the wave sum
-//            goes to the task's partial slot; k_csr_chunks_finish adds a
-//            row's partials in chunk order afterwards.  (Combining here
-//            would need device-scope release/acquire fences, which write
-//            back and invalidate the whole L2 of an XCD on this part.)
-// BUF: x and row_ptr are below 4 GiB and gathered with buffer loads.
-template <bool VEC, bool BUF>
-__global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__restrict__ tasks,
-                                                  const int *__restrict__ rp, const int *__restrict__ ci,
-                                                  const float *__restrict__ v, const float *__restrict__ x,
-                                                  float *__restrict__ y, const int *__restrict__ ymap,
-                                                  float *__restrict__ partials) {
-    // 8 slack entries: a row's 8-entry reads never need clamping
-    __shared__ __attribute__((aligned(16))) float stage[WAVES][SLOTS + 8];
-    const Arrays m{rp, ci, v, x};
-    const Gather<BUF> xg(x, a.n_cols);
-    const GatherI<BUF> rg(rp, a.n_rows + 1);
-    const int lane = __lane_id();
-    // wave-uniform, stated so that task indices and descriptors are scalar
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-    const int seg_rows = (a.n_row_tasks + WAVES - 1) / WAVES;
-    int t;
-    if ((int)blockIdx.x < seg_rows) {
-        t = blockIdx.x * WAVES + wv;
-        if (t >= a.n_row_tasks) return;
-    } else {
-        const int wb = xcd_contiguous(blockIdx.x - seg_rows, gridDim.x - seg_rows) * WAVES + wv;
-        if (wb >= a.n_blocks) return;
-        t = a.n_row_tasks + wb;
+// Block of short rows r0 .. r0 + nr - 1 (nr = d.y > 1), given its streams,
+// row starts and gathered x: products are staged in the wave's LDS area and
+// lane l sums rows l + 64 j in storage order.  Entries of the staged vectors
+// outside the block (neighbouring rows, re-read vectors) are multiplied too
+// but never read back.
+__device__ __forceinline__ void finish_block(const TaskArgs &a, i32x4 d, const Staged &cur,
+                                             const int (&rs)[SHORT_RMAX / 64 + 1], const float (&xv)[TASK_VPL][4],
+                                             float *st, int lane, float *__restrict__ y, const int *__restrict__ ymap) {
+    const int nr = d.y, base = d.z & ~3;
+#pragma unroll
+    for (int j = 0; j < TASK_VPL; ++j) {
+        f32x4 p;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p[q] = cur.f[j][q] * xv[j][q];
+        *reinterpret_cast<f32x4 *>(st + 4 * (lane + 64 * j)) = p;
     }
-    const i32x4 d = tasks[t];
-    const int s = d.z, e = d.w, base = s & ~3;
-    Staged cur;
-
-    if (d.y > 1) {
-        // ---- block of short rows r0 .. r0 + nr - 1 ----
-        const int nr = d.y;
-        // start of each row (lane l: rows l + 64 j; entry nr is the block's
-        // end), loaded together with the streams, ahead of the gathers
-        int rs[SHORT_RMAX / 64 + 1];
+    // The staged products are private to this wave: a wave-level barrier
+    // (LDS operations of one wave complete in order) is enough.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Lane l sums row l + 64 j, reading 8 staged entries per step so their
+    // LDS latencies overlap.  Row i's end is row i+1's start: from lane l + 1,
+    // or from lane 0 of the next j for lane 63.
 #pragma unroll
-        for (int j = 0; j <= SHORT_RMAX / 64; ++j) rs[j] = rg[d.x + min(lane + 64 * j, nr)];
-        stage_streams<VEC>(a, m, d, lane, cur);
-        __builtin_amdgcn_sched_barrier(0);
-        float xv[TASK_VPL][4];
+    for (int j = 0; j < SHORT_RMAX / 64; ++j) {
+        const int nxt_same = __shfl_down(rs[j], 1);
+        const int nxt_wrap = __shfl(rs[j + 1], 0);
+        const int end = (lane < 63 ? nxt_same : nxt_wrap) - base;
+        const int i_row = lane + 64 * j;
+        if (i_row < nr) {
+            float acc = 0.0f;
+            for (int k = rs[j] - base; k < end; k += 8) {
+                float vv[8];
 #pragma unroll
-        for (int j = 0; j < TASK_VPL; ++j)
+                for (int u = 0; u < 8; ++u) vv[u] = st[k + u];
+                const int left = end - k;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) xv[j][q] = xg[cur.c[j][q]];
-#pragma unroll
-        for (int j = 0; j < TASK_VPL; ++j) issue_together(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
-        float *st = stage[wv];
-#pragma unroll
-        for (int j = 0; j < TASK_VPL; ++j) {
-            f32x4 p;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) p[q] = cur.f[j][q] * xv[j][q];
-            *reinterpret_cast<f32x4 *>(st + 4 * (lane + 64 * j)) = p;
-        }
-        // The staged products are private to this wave: a wave-level barrier
-        // (LDS operations of one wave complete in order) is enough.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // Lane l sums row l + 64 j, reading 8 staged entries per step so
-        // their LDS latencies overlap.  Row i's end is row i+1's start: from
-        // lane l + 1, or from lane 0 of the next j for lane 63.
-#pragma unroll
-        for (int j = 0; j < SHORT_RMAX / 64; ++j) {
-            const int nxt_same = __shfl_down(rs[j], 1);
-            const int nxt_wrap = __shfl(rs[j + 1], 0);
-            const int end = (lane < 63 ? nxt_same : nxt_wrap) - base;
-            const int i_row = lane + 64 * j;
-            if (i_row < nr) {
-                float acc = 0.0f;
-                for (int k = rs[j] - base; k < end; k += 8) {
-                    float vv[8];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) vv[u] = st[k + u];
-                    const int left = end - k;
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) acc += u < left ? vv[u] : 0.0f;
-                }
-                store_y(y, ymap, d.x + i_row, acc, a.alpha, a.beta);
+                for (int u = 0; u < 8; ++u) acc += u < left ? vv[u] : 0.0f;
             }
+            store_y(y, ymap, d.x + i_row, acc, a.alpha, a.beta);
         }
-        return;
     }
+}
 
-    // ---- one row, or one chunk of a long row ----
-    stage_streams<VEC>(a, m, d, lane, cur);
-    float xv[TASK_VPL][4];
-#pragma unroll
-    for (int j = 0; j < TASK_VPL; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int k = base + 4 * (lane + 64 * j) + q;
-            xv[j][q] = xg[(k >= s && k < e) ? cur.c[j][q] : 0];
-        }
-#pragma unroll
-    for (int j = 0; j < TASK_VPL; ++j) issue_together(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
+// One row (d.y == 1) or one chunk of a long row (d.y < 0): masked lane sums,
+// DPP wave sum, then y or the task's partial slot.
+__device__ __forceinline__ void finish_row(const TaskArgs &a, i32x4 d, int t, const Staged &cur,
+                                           const float (&xv)[TASK_VPL][4], int lane, float *__restrict__ y,
+                                           const int *__restrict__ ymap, float *__restrict__ partials) {
+    const int s = d.z, e = d.w, base = s & ~3;
     float acc = 0.0f;
 #pragma unroll
     for (int j = 0; j < TASK_VPL; ++j)
@@ -637,6 +617,150 @@ __global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__res
         if (lane == 0) store_y(y, ymap, d.x, acc, a.alpha, a.beta);
     } else {
         if (lane == 0) partials[t] = acc;
+    }
+}
+
+// One wave per task.  The grid is [row tasks][short blocks]: row tasks in
+// natural order, blocks through the XCD-contiguous map (neighbouring blocks
+// on one XCD share its L2 for nearby x entries; for the scattered gathers
+// of long rows the plain order measured faster).  The wave loads the task's
+// streams, issues all gathers at once, then reduces by task kind:
+//   nr > 1   a block of short rows (finish_block): every staged entry is
+//            gathered and multiplied without masks, since every staged
+//            column is a valid column of A;
+//   nr == 1  one row: masked lane sums (entries outside [s, e) gather x[0]),
+//            then a DPP wave reduction;
+//   nr < 0   chunk c = -nr - 1 of a long row: as one row, but the wave sum
+//            goes to the task's partial slot; k_csr_chunks_finish adds a
+//            row's partials in chunk order afterwards.  (Combining here
+//            would need device-scope release/acquire fences, which write
+//            back and invalidate the whole L2 of an XCD on this part.)
+// BUF: x and row_ptr are below 4 GiB and gathered with buffer loads.
+// XT: the four blocks of a block workgroup span at most X_TILE_MAX columns
+// (spans[q], from the plan).  The workgroup stages that window of x into
+// LDS with 16-byte loads, issued after each wave's own stream loads, and
+// the gathers read LDS: a 16-byte load moves four x values through the
+// texture addresser where a gather moves one.  The section "x caching in
+// shared memory" of "Why SpMV needs CUDA optimisation" (section 3.1)
+// suggests this; here it is used whenever the plan finds narrow windows.
+template <bool VEC, bool BUF, bool XT>
+__global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__restrict__ tasks,
+                                                  const int *__restrict__ rp, const int *__restrict__ ci,
+                                                  const float *__restrict__ v, const float *__restrict__ x,
+                                                  float *__restrict__ y, const int *__restrict__ ymap,
+                                                  float *__restrict__ partials, const int2 *__restrict__ spans) {
+    // 8 slack entries: a row's 8-entry reads never need clamping
+    __shared__ __attribute__((aligned(16))) float stage[WAVES][SLOTS + 8];
+    extern __shared__ __attribute__((aligned(16))) float xtile[];
+    const Arrays m{rp, ci, v, x};
+    const Gather<BUF> xg(x, a.n_cols);
+    const GatherI<BUF> rg(rp, a.n_rows + 1);
+    const int lane = __lane_id();
+    // wave-uniform, stated so that task indices and descriptors are scalar
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int seg_rows = (a.n_row_tasks + WAVES - 1) / WAVES;
+    float *st = stage[wv];
+    Staged cur;
+    float xv[TASK_VPL][4];
+
+    if ((int)blockIdx.x < seg_rows) {
+        // ---- tasks of rows in groups 1-3 ----
+        const int t = blockIdx.x * WAVES + wv;
+        if (t >= a.n_row_tasks) return;
+        const i32x4 d = tasks[t];
+        stage_streams<VEC>(a, m, d, lane, cur);
+        const int s = d.z, e = d.w, base = s & ~3;
+#pragma unroll
+        for (int j = 0; j < TASK_VPL; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k = base + 4 * (lane + 64 * j) + q;
+                xv[j][q] = xg[(k >= s && k < e) ? cur.c[j][q] : 0];
+            }
+#pragma unroll
+        for (int j = 0; j < TASK_VPL; ++j) issue_together(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
+        finish_row(a, d, t, cur, xv, lane, y, ymap, partials);
+        return;
+    }
+
+    // ---- short-row blocks ----
+    const int qw = xcd_contiguous(blockIdx.x - seg_rows, gridDim.x - seg_rows);
+    const int wb = qw * WAVES + wv;
+    const bool have = wb < a.n_blocks;
+    if (!XT && !have) return;
+    const int t = a.n_row_tasks + wb;
+    // the workgroup's column window (XT), read together with the descriptor
+    const int2 sp = XT ? spans[qw] : int2{0, -1};
+    // a wave without a block (XT only) still helps stage the tile: it loads
+    // a dummy task (the first entries of the arrays)
+    const i32x4 d = have ? tasks[t] : i32x4{0, 0, 0, 0};
+    // start of each row (lane l: rows l + 64 j; entry nr is the block's end),
+    // loaded together with the streams, ahead of the gathers
+    int rs[SHORT_RMAX / 64 + 1];
+    const int nr = max(d.y, 0);
+#pragma unroll
+    for (int j = 0; j <= SHORT_RMAX / 64; ++j) rs[j] = rg[d.x + min(lane + 64 * j, nr)];
+    stage_streams<VEC>(a, m, d, lane, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    if (XT) {
+        // the workgroup's window of x, from the 16-byte boundary below its
+        // smallest column (a workgroup without entries stages x[0..3])
+        const int tb = sp.y >= 0 ? (sp.x & ~3) : 0;
+        const int nvec = sp.y >= 0 ? (sp.y + 4 - tb) >> 2 : 1;
+        f32x4 tv[X_TILE_U];
+#pragma unroll
+        for (int u = 0; u < X_TILE_U; ++u)
+            tv[u] = *reinterpret_cast<const f32x4 *>(x + tb + 4 * min((int)threadIdx.x + u * WG, nvec - 1));
+        // clamped like the loads: extra threads store the last vector again
+#pragma unroll
+        for (int u = 0; u < X_TILE_U; ++u)
+            *reinterpret_cast<f32x4 *>(xtile + 4 * min((int)threadIdx.x + u * WG, nvec - 1)) = tv[u];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        if (!have) return;
+        // entries of this block lie in the window; others (never used) are
+        // clamped into it
+        const int hi = 4 * nvec - 1;
+        if (d.y > 1) {
+#pragma unroll
+            for (int j = 0; j < TASK_VPL; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xv[j][q] = xtile[min(max(cur.c[j][q] - tb, 0), hi)];
+            finish_block(a, d, cur, rs, xv, st, lane, y, ymap);
+        } else {
+            const int s = d.z, e = d.w, base = s & ~3;
+#pragma unroll
+            for (int j = 0; j < TASK_VPL; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int k = base + 4 * (lane + 64 * j) + q;
+                    xv[j][q] = xtile[(k >= s && k < e) ? min(max(cur.c[j][q] - tb, 0), hi) : 0];
+                }
+            finish_row(a, d, t, cur, xv, lane, y, ymap, partials);
+        }
+        return;
+    }
+    if (d.y > 1) {
+#pragma unroll
+        for (int j = 0; j < TASK_VPL; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xv[j][q] = xg[cur.c[j][q]];
+#pragma unroll
+        for (int j = 0; j < TASK_VPL; ++j) issue_together(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
+        finish_block(a, d, cur, rs, xv, st, lane, y, ymap);
+    } else {
+        const int s = d.z, e = d.w, base = s & ~3;
+#pragma unroll
+        for (int j = 0; j < TASK_VPL; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k = base + 4 * (lane + 64 * j) + q;
+                xv[j][q] = xg[(k >= s && k < e) ? cur.c[j][q] : 0];
+            }
+#pragma unroll
+        for (int j = 0; j < TASK_VPL; ++j) issue_together(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
+        finish_row(a, d, t, cur, xv, lane, y, ymap, partials);
     }
 }
 
@@ -700,7 +824,7 @@ __global__ __launch_bounds__(WG) void k_csr_vector(int n, const int *__restrict_
 // Workspace layout of a BINNED plan
 // ---------------------------------------------------------------------------
 struct Layout {
-    size_t meta, perm, counts, offsets, hcounts, hoffsets, heads, tasks, partials, total;
+    size_t meta, perm, counts, offsets, hcounts, hoffsets, heads, tasks, partials, spans, total;
     int64_t max_row_tasks, max_tasks;
 };
 
@@ -729,6 +853,7 @@ Layout make_layout(int n, int nnz, int t0) {
     L.heads = take(sizeof(int) * ((size_t)n + 1));
     L.tasks = take(sizeof(i32x4) * (size_t)L.max_tasks);
     L.partials = take(sizeof(float) * (size_t)L.max_row_tasks);
+    L.spans = take(sizeof(int2) * (size_t)(ceil_div((int64_t)n + 1, WAVES) + 1));
     L.total = off;
     return L;
 }
@@ -765,6 +890,8 @@ struct spmv_csr_plan {
     float *partials = nullptr;
     bool has_chunked_rows = false;   // some row is split into several tasks
     int grid = 0;          // workgroups of the task kernel
+    const int2 *spans = nullptr;     // column window of each block workgroup
+    int x_tile = 0;        // floats of x staged in LDS per block workgroup (0: gathers from memory)
 };
 
 extern "C" spmv_status spmv_csr_row_stats(int32_t n_rows, const int32_t *row_ptr, int32_t *max_len,
@@ -884,6 +1011,19 @@ spmv_status build_binned_plan(spmv_csr_plan *h, char *ws, const Layout &L, hipSt
     h->has_chunked_rows = h->n_row_tasks > h->bin_off[4] - h->bin_off[1];
     // one wave per task: row-task workgroups, then block workgroups
     h->grid = (int)(ceil_div(h->n_row_tasks, WAVES) + ceil_div(h->n_blocks, WAVES));
+    // column windows of the block workgroups: narrow ones let the apply stage
+    // x in LDS
+    if (h->n_blocks > 0) {
+        int2 *spans = reinterpret_cast<int2 *>(ws + L.spans);
+        SPMV_HIP(hipMemsetAsync(&meta->max_window, 0, sizeof(int), st));
+        k_block_spans<<<(int)ceil_div(h->n_blocks, WAVES), WG, 0, st>>>(meta, tasks, h->ci, spans);
+        SPMV_LAUNCHED("k_block_spans");
+        int mw = 0;
+        SPMV_HIP(hipMemcpyAsync(&mw, &meta->max_window, sizeof(int), hipMemcpyDeviceToHost, st));
+        SPMV_HIP(hipStreamSynchronize(st));
+        h->spans = spans;
+        h->x_tile = mw > 0 && mw <= X_TILE_MAX ? 4 * (int)ceil_div(mw, 4) : 0;
+    }
     SPMV_HIP(hipStreamSynchronize(st));
     return SPMV_OK;
 }
@@ -1016,14 +1156,24 @@ spmv_status csr_apply(spmv_csr_t h, float alpha, const float *x, float beta, flo
     a.n_cols = h->n_cols;
     // buffer gathers address at most 4 GiB with 32-bit byte offsets
     const bool buf = h->n_cols < (1 << 30) && n < (1 << 30) - 1;
-    if (h->vec_ok && buf)
-        k_csr_tasks<true, true><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap, h->partials);
+    // x tile in LDS: narrow block windows, aligned arrays, x 16-byte aligned
+    // and a multiple of 4 long (the window's 16-byte loads stay inside x)
+    const bool xt = h->x_tile > 0 && h->vec_ok && buf && aligned16(x) && h->n_cols % 4 == 0;
+    if (xt)
+        k_csr_tasks<true, true, true><<<h->grid, WG, sizeof(float) * (size_t)h->x_tile, st>>>(
+            a, h->tasks, h->rp, h->ci, h->v, x, y, ymap, h->partials, h->spans);
+    else if (h->vec_ok && buf)
+        k_csr_tasks<true, true, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
+                                                               h->partials, h->spans);
     else if (h->vec_ok)
-        k_csr_tasks<true, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap, h->partials);
+        k_csr_tasks<true, false, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
+                                                                h->partials, h->spans);
     else if (buf)
-        k_csr_tasks<false, true><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap, h->partials);
+        k_csr_tasks<false, true, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
+                                                                h->partials, h->spans);
     else
-        k_csr_tasks<false, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap, h->partials);
+        k_csr_tasks<false, false, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
+                                                                 h->partials, h->spans);
     SPMV_LAUNCHED("k_csr_tasks");
     if (h->has_chunked_rows) {
         k_csr_chunks_finish<<<(int)ceil_div(h->n_row_tasks, WG), WG, 0, st>>>(h->n_row_tasks, h->tasks, h->rp,
