@@ -50,8 +50,13 @@ constexpr int TASK_VPL = SPMV_TASK_VPL;   // 16-byte vectors per lane and stream
 constexpr int SLOTS = 64 * 4 * TASK_VPL;   // entries a task stages: 512
 constexpr int SHORT_RMAX = SPMV_SHORT_RMAX;   // rows per short block (2 per lane)
 constexpr int MAX_T0 = 256;             // largest supported bound of group 0
+#ifndef SPMV_TASK_WAVES
+#define SPMV_TASK_WAVES 4
+#endif
+constexpr int TWAVES = SPMV_TASK_WAVES;  // waves per workgroup of the task kernel
+constexpr int TWG = 64 * TWAVES;
 constexpr int X_TILE_MAX = 6144;        // largest x window staged in LDS per block workgroup (floats)
-constexpr int X_TILE_U = X_TILE_MAX / 4 / WG;   // 16-byte loads per thread to stage it
+constexpr int X_TILE_U = (X_TILE_MAX / 4 + TWG - 1) / TWG;   // 16-byte loads per thread to stage it
 
 // Error bits raised by the validation kernels.
 constexpr int ERR_RP0 = 1, ERR_RPN = 2, ERR_MONO = 4, ERR_COL = 8;
@@ -400,13 +405,13 @@ __global__ __launch_bounds__(WG) void k_rowtasks_write(const Meta *__restrict__ 
 // blocks, the blocks one workgroup of the task kernel applies): the smallest
 // and largest column of their entries.  max_window gets the largest span
 // counted from the 16-byte boundary below the smallest column.
-__global__ __launch_bounds__(WG) void k_block_spans(Meta *__restrict__ meta, const i32x4 *__restrict__ tasks,
-                                                    const int *__restrict__ ci, int2 *__restrict__ spans) {
-    __shared__ int lo[WAVES], hi[WAVES];
+__global__ __launch_bounds__(TWG) void k_block_spans(Meta *__restrict__ meta, const i32x4 *__restrict__ tasks,
+                                                     const int *__restrict__ ci, int2 *__restrict__ spans) {
+    __shared__ int lo[TWAVES], hi[TWAVES];
     const int nb = meta->block_totals[1];
     const int first = meta->row_task_totals[1];
     const int lane = __lane_id(), wv = threadIdx.x / 64;
-    const int b = blockIdx.x * WAVES + wv;
+    const int b = blockIdx.x * TWAVES + wv;
     int mn = INT_MAX, mx = -1;
     if (b < nb) {
         const i32x4 d = tasks[first + b];
@@ -426,7 +431,7 @@ __global__ __launch_bounds__(WG) void k_block_spans(Meta *__restrict__ meta, con
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < WAVES; ++w) {
+        for (int w = 1; w < TWAVES; ++w) {
             mn = min(mn, lo[w]);
             mx = max(mx, hi[w]);
         }
@@ -559,7 +564,7 @@ struct GatherI {
 // outside the block (neighbouring rows, re-read vectors) are multiplied too
 // but never read back.
 __device__ __forceinline__ void finish_block(const TaskArgs &a, i32x4 d, const Staged &cur,
-                                             const int (&rs)[SHORT_RMAX / 64 + 1], const float (&xv)[TASK_VPL][4],
+                                             const int (&rs)[SHORT_RMAX / 64], const float (&xv)[TASK_VPL][4],
                                              float *st, int lane, float *__restrict__ y, const int *__restrict__ ymap) {
     const int nr = d.y, base = d.z & ~3;
 #pragma unroll
@@ -576,11 +581,11 @@ __device__ __forceinline__ void finish_block(const TaskArgs &a, i32x4 d, const S
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // Lane l sums row l + 64 j, reading 8 staged entries per step so their
     // LDS latencies overlap.  Row i's end is row i+1's start: from lane l + 1,
-    // or from lane 0 of the next j for lane 63.
+    // or for lane 63 from lane 0 of the next j, or the block's end entry.
 #pragma unroll
     for (int j = 0; j < SHORT_RMAX / 64; ++j) {
         const int nxt_same = __shfl_down(rs[j], 1);
-        const int nxt_wrap = __shfl(rs[j + 1], 0);
+        const int nxt_wrap = j + 1 < SHORT_RMAX / 64 ? __shfl(rs[j + 1 < SHORT_RMAX / 64 ? j + 1 : j], 0) : d.w;
         const int end = (lane < 63 ? nxt_same : nxt_wrap) - base;
         const int i_row = lane + 64 * j;
         if (i_row < nr) {
@@ -644,13 +649,13 @@ __device__ __forceinline__ void finish_row(const TaskArgs &a, i32x4 d, int t, co
 // shared memory" of "Why SpMV needs CUDA optimisation" (section 3.1)
 // suggests this; here it is used whenever the plan finds narrow windows.
 template <bool VEC, bool BUF, bool XT>
-__global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__restrict__ tasks,
+__global__ __launch_bounds__(TWG) void k_csr_tasks(TaskArgs a, const i32x4 *__restrict__ tasks,
                                                   const int *__restrict__ rp, const int *__restrict__ ci,
                                                   const float *__restrict__ v, const float *__restrict__ x,
                                                   float *__restrict__ y, const int *__restrict__ ymap,
                                                   float *__restrict__ partials, const int2 *__restrict__ spans) {
     // 8 slack entries: a row's 8-entry reads never need clamping
-    __shared__ __attribute__((aligned(16))) float stage[WAVES][SLOTS + 8];
+    __shared__ __attribute__((aligned(16))) float stage[TWAVES][SLOTS + 8];
     extern __shared__ __attribute__((aligned(16))) float xtile[];
     const Arrays m{rp, ci, v, x};
     const Gather<BUF> xg(x, a.n_cols);
@@ -658,14 +663,14 @@ __global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__res
     const int lane = __lane_id();
     // wave-uniform, stated so that task indices and descriptors are scalar
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-    const int seg_rows = (a.n_row_tasks + WAVES - 1) / WAVES;
+    const int seg_rows = (a.n_row_tasks + TWAVES - 1) / TWAVES;
     float *st = stage[wv];
     Staged cur;
     float xv[TASK_VPL][4];
 
     if ((int)blockIdx.x < seg_rows) {
         // ---- tasks of rows in groups 1-3 ----
-        const int t = blockIdx.x * WAVES + wv;
+        const int t = blockIdx.x * TWAVES + wv;
         if (t >= a.n_row_tasks) return;
         const i32x4 d = tasks[t];
         stage_streams<VEC>(a, m, d, lane, cur);
@@ -685,7 +690,7 @@ __global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__res
 
     // ---- short-row blocks ----
     const int qw = xcd_contiguous(blockIdx.x - seg_rows, gridDim.x - seg_rows);
-    const int wb = qw * WAVES + wv;
+    const int wb = qw * TWAVES + wv;
     const bool have = wb < a.n_blocks;
     if (!XT && !have) return;
     const int t = a.n_row_tasks + wb;
@@ -696,10 +701,10 @@ __global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__res
     const i32x4 d = have ? tasks[t] : i32x4{0, 0, 0, 0};
     // start of each row (lane l: rows l + 64 j; entry nr is the block's end),
     // loaded together with the streams, ahead of the gathers
-    int rs[SHORT_RMAX / 64 + 1];
+    int rs[SHORT_RMAX / 64];
     const int nr = max(d.y, 0);
 #pragma unroll
-    for (int j = 0; j <= SHORT_RMAX / 64; ++j) rs[j] = rg[d.x + min(lane + 64 * j, nr)];
+    for (int j = 0; j < SHORT_RMAX / 64; ++j) rs[j] = rg[d.x + min(lane + 64 * j, nr)];
     stage_streams<VEC>(a, m, d, lane, cur);
     __builtin_amdgcn_sched_barrier(0);
     if (XT) {
@@ -710,11 +715,11 @@ __global__ __launch_bounds__(WG) void k_csr_tasks(TaskArgs a, const i32x4 *__res
         f32x4 tv[X_TILE_U];
 #pragma unroll
         for (int u = 0; u < X_TILE_U; ++u)
-            tv[u] = *reinterpret_cast<const f32x4 *>(x + tb + 4 * min((int)threadIdx.x + u * WG, nvec - 1));
+            tv[u] = *reinterpret_cast<const f32x4 *>(x + tb + 4 * min((int)threadIdx.x + u * TWG, nvec - 1));
         // clamped like the loads: extra threads store the last vector again
 #pragma unroll
         for (int u = 0; u < X_TILE_U; ++u)
-            *reinterpret_cast<f32x4 *>(xtile + 4 * min((int)threadIdx.x + u * WG, nvec - 1)) = tv[u];
+            *reinterpret_cast<f32x4 *>(xtile + 4 * min((int)threadIdx.x + u * TWG, nvec - 1)) = tv[u];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -853,7 +858,7 @@ Layout make_layout(int n, int nnz, int t0) {
     L.heads = take(sizeof(int) * ((size_t)n + 1));
     L.tasks = take(sizeof(i32x4) * (size_t)L.max_tasks);
     L.partials = take(sizeof(float) * (size_t)L.max_row_tasks);
-    L.spans = take(sizeof(int2) * (size_t)(ceil_div((int64_t)n + 1, WAVES) + 1));
+    L.spans = take(sizeof(int2) * (size_t)(ceil_div((int64_t)n + 1, TWAVES) + 1));
     L.total = off;
     return L;
 }
@@ -1010,13 +1015,13 @@ spmv_status build_binned_plan(spmv_csr_plan *h, char *ws, const Layout &L, hipSt
     // rows of groups 1-3 each give one task unless some row was split
     h->has_chunked_rows = h->n_row_tasks > h->bin_off[4] - h->bin_off[1];
     // one wave per task: row-task workgroups, then block workgroups
-    h->grid = (int)(ceil_div(h->n_row_tasks, WAVES) + ceil_div(h->n_blocks, WAVES));
+    h->grid = (int)(ceil_div(h->n_row_tasks, TWAVES) + ceil_div(h->n_blocks, TWAVES));
     // column windows of the block workgroups: narrow ones let the apply stage
     // x in LDS
     if (h->n_blocks > 0) {
         int2 *spans = reinterpret_cast<int2 *>(ws + L.spans);
         SPMV_HIP(hipMemsetAsync(&meta->max_window, 0, sizeof(int), st));
-        k_block_spans<<<(int)ceil_div(h->n_blocks, WAVES), WG, 0, st>>>(meta, tasks, h->ci, spans);
+        k_block_spans<<<(int)ceil_div(h->n_blocks, TWAVES), TWG, 0, st>>>(meta, tasks, h->ci, spans);
         SPMV_LAUNCHED("k_block_spans");
         int mw = 0;
         SPMV_HIP(hipMemcpyAsync(&mw, &meta->max_window, sizeof(int), hipMemcpyDeviceToHost, st));
@@ -1160,19 +1165,19 @@ spmv_status csr_apply(spmv_csr_t h, float alpha, const float *x, float beta, flo
     // and a multiple of 4 long (the window's 16-byte loads stay inside x)
     const bool xt = h->x_tile > 0 && h->vec_ok && buf && aligned16(x) && h->n_cols % 4 == 0;
     if (xt)
-        k_csr_tasks<true, true, true><<<h->grid, WG, sizeof(float) * (size_t)h->x_tile, st>>>(
+        k_csr_tasks<true, true, true><<<h->grid, TWG, sizeof(float) * (size_t)h->x_tile, st>>>(
             a, h->tasks, h->rp, h->ci, h->v, x, y, ymap, h->partials, h->spans);
     else if (h->vec_ok && buf)
-        k_csr_tasks<true, true, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
+        k_csr_tasks<true, true, false><<<h->grid, TWG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
                                                                h->partials, h->spans);
     else if (h->vec_ok)
-        k_csr_tasks<true, false, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
+        k_csr_tasks<true, false, false><<<h->grid, TWG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
                                                                 h->partials, h->spans);
     else if (buf)
-        k_csr_tasks<false, true, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
+        k_csr_tasks<false, true, false><<<h->grid, TWG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
                                                                 h->partials, h->spans);
     else
-        k_csr_tasks<false, false, false><<<h->grid, WG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
+        k_csr_tasks<false, false, false><<<h->grid, TWG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
                                                                  h->partials, h->spans);
     SPMV_LAUNCHED("k_csr_tasks");
     if (h->has_chunked_rows) {
