@@ -56,7 +56,6 @@ constexpr int MAX_T0 = 256;             // largest supported bound of group 0
 constexpr int TWAVES = SPMV_TASK_WAVES;  // waves per workgroup of the task kernel
 constexpr int TWG = 64 * TWAVES;
 constexpr int X_TILE_MAX = 6144;        // largest x window staged in LDS per block workgroup (floats)
-constexpr int X_TILE_U = (X_TILE_MAX / 4 + TWG - 1) / TWG;   // 16-byte loads per thread to stage it
 
 // Error bits raised by the validation kernels.
 constexpr int ERR_RP0 = 1, ERR_RPN = 2, ERR_MONO = 4, ERR_COL = 8;
@@ -641,19 +640,21 @@ __device__ __forceinline__ void finish_row(const TaskArgs &a, i32x4 d, int t, co
 //            would need device-scope release/acquire fences, which write
 //            back and invalidate the whole L2 of an XCD on this part.)
 // BUF: x and row_ptr are below 4 GiB and gathered with buffer loads.
-// XT: the four blocks of a block workgroup span at most X_TILE_MAX columns
+// XTR > 0: the four blocks of a block workgroup span at most XTR * 4 * TWG
+// columns
 // (spans[q], from the plan).  The workgroup stages that window of x into
 // LDS with 16-byte loads, issued after each wave's own stream loads, and
 // the gathers read LDS: a 16-byte load moves four x values through the
 // texture addresser where a gather moves one.  The section "x caching in
 // shared memory" of "Why SpMV needs CUDA optimisation" (section 3.1)
 // suggests this; here it is used whenever the plan finds narrow windows.
-template <bool VEC, bool BUF, bool XT>
+template <bool VEC, bool BUF, int XTR>
 __global__ __launch_bounds__(TWG) void k_csr_tasks(TaskArgs a, const i32x4 *__restrict__ tasks,
                                                   const int *__restrict__ rp, const int *__restrict__ ci,
                                                   const float *__restrict__ v, const float *__restrict__ x,
                                                   float *__restrict__ y, const int *__restrict__ ymap,
                                                   float *__restrict__ partials, const int2 *__restrict__ spans) {
+    constexpr bool XT = XTR > 0;
     // 8 slack entries: a row's 8-entry reads never need clamping
     __shared__ __attribute__((aligned(16))) float stage[TWAVES][SLOTS + 8];
     extern __shared__ __attribute__((aligned(16))) float xtile[];
@@ -712,13 +713,15 @@ __global__ __launch_bounds__(TWG) void k_csr_tasks(TaskArgs a, const i32x4 *__re
         // smallest column (a workgroup without entries stages x[0..3])
         const int tb = sp.y >= 0 ? (sp.x & ~3) : 0;
         const int nvec = sp.y >= 0 ? (sp.y + 4 - tb) >> 2 : 1;
-        f32x4 tv[X_TILE_U];
+        // XTR rounds of 16-byte loads: enough for the widest window of the
+        // matrix; threads past a window's end load and store its last
+        // vector again
+        f32x4 tv[XTR > 0 ? XTR : 1];
 #pragma unroll
-        for (int u = 0; u < X_TILE_U; ++u)
+        for (int u = 0; u < XTR; ++u)
             tv[u] = *reinterpret_cast<const f32x4 *>(x + tb + 4 * min((int)threadIdx.x + u * TWG, nvec - 1));
-        // clamped like the loads: extra threads store the last vector again
 #pragma unroll
-        for (int u = 0; u < X_TILE_U; ++u)
+        for (int u = 0; u < XTR; ++u)
             *reinterpret_cast<f32x4 *>(xtile + 4 * min((int)threadIdx.x + u * TWG, nvec - 1)) = tv[u];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
@@ -1164,21 +1167,33 @@ spmv_status csr_apply(spmv_csr_t h, float alpha, const float *x, float beta, flo
     // x tile in LDS: narrow block windows, aligned arrays, x 16-byte aligned
     // and a multiple of 4 long (the window's 16-byte loads stay inside x)
     const bool xt = h->x_tile > 0 && h->vec_ok && buf && aligned16(x) && h->n_cols % 4 == 0;
-    if (xt)
-        k_csr_tasks<true, true, true><<<h->grid, TWG, sizeof(float) * (size_t)h->x_tile, st>>>(
-            a, h->tasks, h->rp, h->ci, h->v, x, y, ymap, h->partials, h->spans);
-    else if (h->vec_ok && buf)
-        k_csr_tasks<true, true, false><<<h->grid, TWG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
-                                                               h->partials, h->spans);
+    if (xt) {
+        // rounds of 16-byte loads per thread that the widest window needs
+        const int rounds = (int)ceil_div(h->x_tile / 4, TWG);
+        const size_t lds = sizeof(float) * (size_t)h->x_tile;
+        switch (rounds) {
+#define SPMV_XT_CASE(R)                                                                                  \
+    case R:                                                                                              \
+        k_csr_tasks<true, true, R><<<h->grid, TWG, lds, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap, \
+                                                             h->partials, h->spans);                      \
+        break;
+            SPMV_XT_CASE(1) SPMV_XT_CASE(2) SPMV_XT_CASE(3) SPMV_XT_CASE(4) SPMV_XT_CASE(5) SPMV_XT_CASE(6)
+#undef SPMV_XT_CASE
+        default:
+            return fail(SPMV_ERR_INVALID_VALUE, "x window of %d floats exceeds the tile", h->x_tile);
+        }
+    } else if (h->vec_ok && buf)
+        k_csr_tasks<true, true, 0><<<h->grid, TWG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
+                                                            h->partials, h->spans);
     else if (h->vec_ok)
-        k_csr_tasks<true, false, false><<<h->grid, TWG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
-                                                                h->partials, h->spans);
+        k_csr_tasks<true, false, 0><<<h->grid, TWG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
+                                                             h->partials, h->spans);
     else if (buf)
-        k_csr_tasks<false, true, false><<<h->grid, TWG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
-                                                                h->partials, h->spans);
+        k_csr_tasks<false, true, 0><<<h->grid, TWG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
+                                                             h->partials, h->spans);
     else
-        k_csr_tasks<false, false, false><<<h->grid, TWG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
-                                                                 h->partials, h->spans);
+        k_csr_tasks<false, false, 0><<<h->grid, TWG, 0, st>>>(a, h->tasks, h->rp, h->ci, h->v, x, y, ymap,
+                                                              h->partials, h->spans);
     SPMV_LAUNCHED("k_csr_tasks");
     if (h->has_chunked_rows) {
         k_csr_chunks_finish<<<(int)ceil_div(h->n_row_tasks, WG), WG, 0, st>>>(h->n_row_tasks, h->tasks, h->rp,
