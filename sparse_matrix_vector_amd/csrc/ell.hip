@@ -14,6 +14,7 @@
 #include "common.hpp"
 
 #include <algorithm>
+#include <climits>
 
 namespace spmv {
 namespace {
@@ -104,6 +105,100 @@ __global__ __launch_bounds__(WG) void k_ell_apply4(int n, int width, const int *
     *reinterpret_cast<f32x4 *>(y + i0) = r;
 }
 
+// Four rows per lane with an x tile in LDS (width U <= 8, x 16-byte aligned,
+// n_cols % 4 == 0).  The workgroup's 1024 rows usually gather from a narrow
+// range of columns (a banded matrix): after loading its slots, the
+// workgroup reduces the smallest and largest column it uses, and if that
+// window fits XT_ROUNDS * 4 * WG floats it stages x[window] in LDS with
+// 16-byte loads and gathers from LDS (a 16-byte load moves four x values
+// through the texture addresser, a gather one).  Wider windows gather from
+// memory as in k_ell_apply4.  Every thread takes part in the barriers; rows
+// past n only load the matrix's first slot vector.
+constexpr int XT_ROUNDS = 3;
+
+template <int U>
+__global__ __launch_bounds__(WG) void k_ell_apply4t(int n, const int *__restrict__ ec, const float *__restrict__ ev,
+                                                    float alpha, const float *__restrict__ x, float beta,
+                                                    float *__restrict__ y) {
+    __shared__ __attribute__((aligned(16))) float xt[XT_ROUNDS * 4 * WG];
+    __shared__ int red[2][WG / 64];
+    const int w = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int i0 = 4 * (w * WG + (int)threadIdx.x);
+    const bool live = i0 < n;
+    const int ib = live ? i0 : 0;
+    i32x4 c[U];
+    f32x4 f[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const size_t slot = (size_t)u * (size_t)n + (size_t)ib;
+        c[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(ec + slot));
+        f[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(ev + slot));
+    }
+    // the workgroup's column window (padding, -1, and dead rows excluded)
+    int mn = INT_MAX, mx = -1;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int cc = live ? c[u][t] : -1;
+            mn = cc >= 0 ? min(mn, cc) : mn;
+            mx = max(mx, cc);
+        }
+    for (int off = 32; off > 0; off >>= 1) {
+        mn = min(mn, __shfl_xor(mn, off));
+        mx = max(mx, __shfl_xor(mx, off));
+    }
+    if (__lane_id() == 0) {
+        red[0][threadIdx.x / 64] = mn;
+        red[1][threadIdx.x / 64] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < WG / 64; ++q) {
+        mn = min(mn, red[0][q]);
+        mx = max(mx, red[1][q]);
+    }
+    const int tb = mx >= 0 ? (mn & ~3) : 0;
+    const int nvec = mx >= 0 ? (mx + 4 - tb) >> 2 : 1;
+    float xv[U][4];
+    if (nvec <= XT_ROUNDS * WG) {   // uniform over the workgroup
+        f32x4 tv[XT_ROUNDS];
+#pragma unroll
+        for (int r = 0; r < XT_ROUNDS; ++r)
+            tv[r] = *reinterpret_cast<const f32x4 *>(x + tb + 4 * min((int)threadIdx.x + r * WG, nvec - 1));
+#pragma unroll
+        for (int r = 0; r < XT_ROUNDS; ++r)
+            *reinterpret_cast<f32x4 *>(xt + 4 * min((int)threadIdx.x + r * WG, nvec - 1)) = tv[r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        const int hi = 4 * nvec - 1;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xv[u][t] = xt[min(max(c[u][t] - tb, 0), hi)];
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xv[u][t] = x[max(c[u][t], 0)];
+#pragma unroll
+        for (int u = 0; u < U; ++u) issue_together(xv[u][0], xv[u][1], xv[u][2], xv[u][3]);
+    }
+    if (!live) return;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = c[u][t] >= 0 ? fmaf(f[u][t], xv[u][t], acc[t]) : acc[t];
+    f32x4 yo = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (beta != 0.0f) yo = *reinterpret_cast<const f32x4 *>(y + i0);
+    f32x4 r;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) r[t] = finish(acc[t], alpha, beta, yo[t]);
+    *reinterpret_cast<f32x4 *>(y + i0) = r;
+}
+
 // One row per lane.
 __global__ __launch_bounds__(WG) void k_ell_apply1(int n, int width, const int *__restrict__ ec,
                                                    const float *__restrict__ ev, float alpha,
@@ -185,7 +280,19 @@ extern "C" spmv_status spmv_ell_apply(int32_t n_rows, int32_t n_cols, int32_t wi
     }
     if (!ell_col || !ell_val || !x) return fail(SPMV_ERR_INVALID_VALUE, "NULL pointer");
     const bool quad = (n_rows % 4 == 0) && aligned16(ell_col) && aligned16(ell_val) && aligned16(y);
-    if (quad) {
+    if (quad && width <= 8 && aligned16(x) && n_cols % 4 == 0) {
+        const int grid = (int)ceil_div(n_rows / 4, WG);
+        switch (width) {
+#define SPMV_ELL_T(W)                                                                                   \
+    case W:                                                                                             \
+        k_ell_apply4t<W><<<grid, WG, 0, st>>>(n_rows, ell_col, ell_val, alpha, x, beta, y);           \
+        break;
+            SPMV_ELL_T(1) SPMV_ELL_T(2) SPMV_ELL_T(3) SPMV_ELL_T(4) SPMV_ELL_T(5) SPMV_ELL_T(6) SPMV_ELL_T(7)
+            SPMV_ELL_T(8)
+#undef SPMV_ELL_T
+        }
+        SPMV_LAUNCHED("k_ell_apply4t");
+    } else if (quad) {
         const int grid = (int)ceil_div(n_rows / 4, WG);
         switch (width) {
 #define SPMV_ELL_W(W)                                                                                    \
