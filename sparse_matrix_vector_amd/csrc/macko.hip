@@ -34,6 +34,7 @@ constexpr int MK_WG = 64 * MK_WAVES;
 constexpr int MK_CHUNK = 512;         // entries per wave per step (64 lanes x 8)
 constexpr int MK_UNROLL = 4;          // chunks whose loads are issued together
 constexpr int MK_LDS_MAX_COLS = 32768;   // x in LDS up to 64 KB
+constexpr int MK_XPAD = 512;          // zero halfs after x in LDS (> 255 + 128)
 
 __device__ __forceinline__ f16x2 as_h2(unsigned int w) { return __builtin_bit_cast(f16x2, w); }
 
@@ -87,31 +88,48 @@ __device__ __forceinline__ void load_group(Group &g, const unsigned int *__restr
     }
 }
 
+// One chunk of 512 entries: lane-local prefix of (code + 1), wave scan of
+// the lane totals plus the running carry, then 8 reads of x and 4
+// v_dot2_f32_f16.  MASKED: some lanes lie past the row's end (the row's last
+// chunk); their totals count 0 and their values are masked.  CLAMP: x is
+// read from memory, so columns are clamped to the last column; with x in
+// LDS they are not, because the LDS copy is followed by MK_XPAD zeros and
+// no decoded column goes further (see k_macko_spmv).
+template <bool MASKED, bool CLAMP>
+__device__ __forceinline__ void apply_chunk(unsigned int word, u32x4 val, bool valid, int last_col,
+                                            const unsigned short *xv, int &carry, float &acc) {
+    int p[8];
+    nibble_prefix(word, p);
+    const int tot = (!MASKED || valid) ? p[7] : 0;
+    const int incl = wave_inclusive_scan(tot);
+    const int base = carry + incl - tot;
+    carry += __builtin_amdgcn_readlane(incl, 63);
+    // No branch on `valid`: an idle lane's columns stay inside x or its
+    // padding (they are >= 0: base >= carry >= -1 and p[t] >= 1), so all 8
+    // reads of every lane are issued together; its values are masked.
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+        const int ca = CLAMP ? min(base + p[t], last_col) : base + p[t];
+        const int cb = CLAMP ? min(base + p[t + 1], last_col) : base + p[t + 1];
+        const unsigned int xp = (unsigned int)xv[ca] | ((unsigned int)xv[cb] << 16);
+        const unsigned int vp = (!MASKED || valid) ? val[t >> 1] : 0u;
+        acc = __builtin_amdgcn_fdot2(as_h2(vp), as_h2(xp), acc, false);
+    }
+}
+
 // Decodes the columns of a loaded group (continuing from `carry`, the last
 // column decoded so far in the row) and accumulates value * x[column].
+template <bool CLAMP>
 __device__ __forceinline__ void apply_group(const Group &g, int c0, int e1, int lane, int last_col,
                                             const unsigned short *xv, int &carry, float &acc) {
 #pragma unroll
     for (int u = 0; u < MK_UNROLL; ++u) {
-        if (c0 + u * MK_CHUNK >= e1) break;   // uniform: rows end on 256-entry units
-        const bool valid = c0 + u * MK_CHUNK + 8 * lane < e1;
-        int p[8];
-        nibble_prefix(g.word[u], p);
-        const int tot = valid ? p[7] : 0;
-        const int incl = wave_inclusive_scan(tot);
-        const int base = carry + incl - tot;
-        carry += __builtin_amdgcn_readlane(incl, 63);
-        // No branch on `valid`: an idle lane's clamped columns stay inside
-        // x (they are >= 0: base >= carry >= -1 and p[t] >= 1), so all 8
-        // reads of every lane are issued together; its values are masked.
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-            const int ca = min(base + p[t], last_col);
-            const int cb = min(base + p[t + 1], last_col);
-            const unsigned int xp = (unsigned int)xv[ca] | ((unsigned int)xv[cb] << 16);
-            const unsigned int vp = valid ? g.val[u][t >> 1] : 0u;
-            acc = __builtin_amdgcn_fdot2(as_h2(vp), as_h2(xp), acc, false);
-        }
+        const int cs = c0 + u * MK_CHUNK;
+        if (cs >= e1) break;   // uniform: rows end on 256-entry units
+        if (cs + MK_CHUNK <= e1)   // uniform: the whole chunk is inside the row
+            apply_chunk<false, CLAMP>(g.word[u], g.val[u], true, last_col, xv, carry, acc);
+        else
+            apply_chunk<true, CLAMP>(g.word[u], g.val[u], cs + 8 * lane < e1, last_col, xv, carry, acc);
     }
     // Consume every register of the group, also of chunks past the row's
     // end, so that no load into them is still outstanding when they are
@@ -176,6 +194,10 @@ __global__ __launch_bounds__(MK_WG) void k_macko_spmv(int n_rows, int n_cols, co
                 *reinterpret_cast<u32x4_t *>(xs_dyn + k) = *reinterpret_cast<const u32x4_t *>(x + k);
         }
         for (int k = n8 + (int)threadIdx.x; k < n_cols; k += MK_WG) xs_dyn[k] = x[k];
+        // MK_XPAD zeros after x: decoded columns of trailing alignment
+        // entries (at most 255 past the last real column) and of idle lanes
+        // (at most 128 further) read zeros instead of being clamped
+        for (int k = n_cols + (int)threadIdx.x; k < n_cols + MK_XPAD; k += MK_WG) xs_dyn[k] = 0;
         // an LDS-only barrier: the stream loads issued above stay in flight
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
@@ -222,7 +244,7 @@ __global__ __launch_bounds__(MK_WG) void k_macko_spmv(int n_rows, int n_cols, co
             const int c1 = c0 + MK_CHUNK * MK_UNROLL;
             const bool row_done = c1 >= e1;
             load_group<XM == 1>(nxt, codes, mvals, row_done ? nb0 : c1, row_done ? nb1 : e1, lane, x);
-            apply_group(cur, c0, e1, lane, last_col, xv, carry, acc);
+            apply_group<XM == 0>(cur, c0, e1, lane, last_col, xv, carry, acc);
             if (!row_done) {
                 c0 = c1;
             } else {
@@ -310,7 +332,7 @@ extern "C" spmv_status macko_spmv(int32_t n_rows, int32_t n_cols, const int32_t 
         return fail(SPMV_ERR_UNSUPPORTED, "mvals must be 16-byte aligned and codes 4-byte aligned");
     hipStream_t st = as_stream(stream);
     if (n_cols <= MK_LDS_MAX_COLS) {
-        const size_t lds = (size_t)((n_cols + 7) & ~7) * sizeof(uint16_t);
+        const size_t lds = (size_t)((n_cols + MK_XPAD + 7) & ~7) * sizeof(uint16_t);
         // as many workgroups per CU as the LDS allows, at most 2
         const int per_cu = lds <= 48 * 1024 ? 2 : 1;
         const int grid = persistent_grid(n_rows, per_cu);
