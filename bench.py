@@ -48,10 +48,13 @@ ROTATE_BYTES = 1 << 30
 DEFAULT_PATH = {"tiny": "csr", "laplacian": "csr", "powerlaw": "csr", "varlen": "auto", "pruned50": "macko",
                 "pruned70": "macko", "pruned90": "macko", "fe": "fem"}
 CSR_CONFIGS = ("tiny", "laplacian", "powerlaw", "varlen")
+# further paths the config itself names, measured beside the default one when
+# no --path is given (the Laplacian config names a CSR and an ELL path)
+OTHER_PATHS = {"laplacian": ("ell",)}
 
 # kernel (as rocprofv3 names it) that dominates each path
 KERNEL = {"csr": "k_csr_tasks", "csr-binned": "k_csr_tasks", "csr-vector": "k_csr_vector",
-          "csr-scalar": "k_csr_scalar", "ell": "k_ell_apply", "macko": "k_macko_spmv",
+          "csr-scalar": "k_csr_scalar", "ell": "k_ell_apply4t", "macko": "k_macko_spmv",
           "dense": "k_gemv_f16", "fem": "k_fe_fused", "fem-3stage": "k_fe_elem", "hyb": "k_ell_apply",
           "auto": None}
 
@@ -483,6 +486,21 @@ def main():
     }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, ref_fn, args.cpu_seconds)
+    if args.path is None and args.config in OTHER_PATHS:
+        others = {}
+        del w
+        torch.cuda.empty_cache()
+        for op in OTHER_PATHS[args.config]:
+            w2 = Workload(args.config, op, args.copies)
+            p2 = None if args.no_parity else parity(w2, w2.oracle_call())
+            m2 = timed_rotate(w2, args.steps, args.warmup, w2.launches, graph)
+            g2 = w2.bytes / (m2["ms_per_apply"] * 1e-3) / 1e9
+            others[op] = {"ms_per_apply": round(m2["ms_per_apply"], 6), "algorithmic_bytes": w2.bytes,
+                          "effective_gbs": round(g2, 2), "pct_hbm_peak": round(100 * g2 / HBM_PEAK_GBS, 2),
+                          "kernel": KERNEL[op], "traffic": traffic_record(w2), "parity": p2, "shape": w2.shape}
+            del w2
+            torch.cuda.empty_cache()
+        line["other_paths"] = others
     print(json.dumps(line), flush=True)
 
 
