@@ -27,6 +27,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 u32p = np.ctypeslib.ndpointer(dtype=np.uint32, flags="C_CONTIGUOUS")
 u16p = np.ctypeslib.ndpointer(dtype=np.uint16, flags="C_CONTIGUOUS")
+i8p = np.ctypeslib.ndpointer(dtype=np.int8, flags="C_CONTIGUOUS")
 f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
 f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
@@ -69,10 +70,14 @@ def lib():
             "oracle_hyb_from_csr": (None, [c_int, i32p, i32p, f32p, c_int, i32p, f32p, i32p, i32p, i32p, f32p]),
             "oracle_hyb_spmv": (None, [c_int, c_int, i32p, f32p, c_int, i32p, i32p, i32p, f32p, f32p,
                                        c_double, c_double, vp, f64p, f64p]),
-            "oracle_macko_size": (c_i64, [c_int, c_int, i32p, i32p]),
-            "oracle_macko_encode": (c_int, [c_int, c_int, i32p, i32p, u16p, i32p, u32p, u16p]),
-            "oracle_macko_decode": (None, [c_int, i32p, u32p, i32p]),
-            "oracle_macko_spmv": (None, [c_int, c_int, i32p, u32p, u16p, u16p, c_double, c_double, vp, f64p, f64p]),
+            "oracle_macko_size": (c_i64, [c_int, c_int, c_int, i32p, i32p]),
+            "oracle_macko_encode": (c_int, [c_int, c_int, c_int, i32p, i32p, u16p, i32p, u32p, u16p]),
+            "oracle_macko_decode": (None, [c_int, c_int, i32p, u32p, i32p]),
+            "oracle_macko_spmv": (None, [c_int, c_int, c_int, i32p, u32p, u16p, u16p, c_double, c_double, vp,
+                                         f64p, f64p]),
+            "oracle_macko_quantize_i8": (None, [c_int, i32p, u16p, i8p, f32p]),
+            "oracle_macko_spmv_i8": (None, [c_int, c_int, c_int, i32p, u32p, i8p, f32p, u16p, c_double, c_double,
+                                            vp, f64p, f64p]),
             "oracle_gemv_f16": (None, [c_int, c_int, u16p, u16p, c_double, c_double, vp, f64p, f64p]),
             "oracle_fe_matvec": (None, [c_int, c_int, i32p, f32p, c_int, f32p, f32p, c_double, c_double, vp, f64p, f64p]),
             "oracle_fe_assemble": (c_i64, [c_int, c_int, i32p, f32p, c_int, f32p, vp, vp, vp]),
@@ -227,43 +232,75 @@ def hyb_spmv(n_rows, width, ell_col, ell_val, tail_rows, tail_rp, tail_col, tail
     return y, s
 
 
-def macko_size(n_cols, row_ptr, col_idx) -> int:
+MACKO_BITS = (1, 2, 4, 8)
+
+
+def macko_align(bdelta=4) -> int:
+    """Row alignment in entries: 1024 / b (one 128-byte block of codes)."""
+    return 1024 // bdelta
+
+
+def macko_size(n_cols, row_ptr, col_idx, bdelta=4) -> int:
     rp = _c(row_ptr, np.int32)
-    return int(lib().oracle_macko_size(len(rp) - 1, int(n_cols), rp, _c(col_idx, np.int32)))
+    return int(lib().oracle_macko_size(len(rp) - 1, int(n_cols), int(bdelta), rp, _c(col_idx, np.int32)))
 
 
-def macko_encode(n_cols, row_ptr, col_idx, vals_f16):
-    """(mrow_ptr int32[R+1], codes uint32[E/8], mvals uint16[E])."""
+def macko_encode(n_cols, row_ptr, col_idx, vals_f16, bdelta=4):
+    """(mrow_ptr int32[R+1], codes uint32[E*b/32], mvals uint16[E])."""
     rp = _c(row_ptr, np.int32)
     n = len(rp) - 1
     ci = _c(col_idx, np.int32)
-    E = macko_size(n_cols, rp, ci)
+    E = macko_size(n_cols, rp, ci, bdelta)
+    if E == -2:
+        raise ValueError("code width must be 1, 2, 4 or 8")
     if E < 0:
         raise ValueError("columns must be strictly increasing per row and in range")
     mrp = np.empty(n + 1, np.int32)
-    codes = np.zeros(E // 8, np.uint32)
+    codes = np.zeros(E * bdelta // 32, np.uint32)
     mv = np.zeros(E, np.uint16)
-    rc = lib().oracle_macko_encode(n, int(n_cols), rp, ci, _c(vals_f16, np.uint16), mrp, codes, mv)
+    rc = lib().oracle_macko_encode(n, int(n_cols), int(bdelta), rp, ci, _c(vals_f16, np.uint16), mrp, codes, mv)
     if rc != 0:
         raise ValueError("MACKO encode failed")
     return mrp, codes, mv
 
 
-def macko_decode(mrow_ptr, codes):
+def macko_decode(mrow_ptr, codes, bdelta=4):
     mrp = _c(mrow_ptr, np.int32)
     cols = np.empty(int(mrp[-1]), np.int32)
-    lib().oracle_macko_decode(len(mrp) - 1, mrp, _c(codes, np.uint32), cols)
+    lib().oracle_macko_decode(len(mrp) - 1, int(bdelta), mrp, _c(codes, np.uint32), cols)
     return cols
 
 
-def macko_spmv(n_cols, mrow_ptr, codes, mvals, x_f16, alpha=1.0, beta=0.0, y_in=None):
+def macko_spmv(n_cols, mrow_ptr, codes, mvals, x_f16, alpha=1.0, beta=0.0, y_in=None, bdelta=4):
     mrp = _c(mrow_ptr, np.int32)
     n = len(mrp) - 1
     keep, yp = _yin(y_in, n, beta)
     y = np.empty(n, np.float64)
     s = np.empty(n, np.float64)
-    lib().oracle_macko_spmv(n, int(n_cols), mrp, _c(codes, np.uint32), _c(mvals, np.uint16),
+    lib().oracle_macko_spmv(n, int(n_cols), int(bdelta), mrp, _c(codes, np.uint32), _c(mvals, np.uint16),
                             _c(x_f16, np.uint16), float(alpha), float(beta), yp, y, s)
+    return y, s
+
+
+def macko_quantize_i8(mrow_ptr, mvals):
+    """(q int8[E], row_scale float32[R]) of the 8-bit value mode."""
+    mrp = _c(mrow_ptr, np.int32)
+    n = len(mrp) - 1
+    q = np.empty(int(mrp[-1]), np.int8)
+    sc = np.empty(n, np.float32)
+    lib().oracle_macko_quantize_i8(n, mrp, _c(mvals, np.uint16), q, sc)
+    return q, sc
+
+
+def macko_spmv_i8(n_cols, mrow_ptr, codes, q, row_scale, x_f16, alpha=1.0, beta=0.0, y_in=None, bdelta=4):
+    mrp = _c(mrow_ptr, np.int32)
+    n = len(mrp) - 1
+    keep, yp = _yin(y_in, n, beta)
+    y = np.empty(n, np.float64)
+    s = np.empty(n, np.float64)
+    lib().oracle_macko_spmv_i8(n, int(n_cols), int(bdelta), mrp, _c(codes, np.uint32), _c(q, np.int8),
+                               _c(row_scale, np.float32), _c(x_f16, np.uint16), float(alpha), float(beta), yp,
+                               y, s)
     return y, s
 
 

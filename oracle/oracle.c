@@ -331,73 +331,87 @@ void oracle_hyb_spmv(int n_rows, int W, const int32_t *ell_col, const float *ell
 
 /* ------------------------------------------------------------------------ */
 /* MACKO format ("MACKO-SpMV: GPU acceleration and storage optimisation at  */
-/* low sparsity", section 2.1: delta coding, dynamic zero padding, 4-bit     */
-/* packing 8 per 32-bit word, aligned loads).  Readings taken where the      */
-/* page is silent or self-contradictory:                                     */
+/* low sparsity", section 2.1: delta coding, dynamic zero padding, packing   */
+/* of the codes into 32-bit words, aligned loads; section 3.3: the code      */
+/* width b (the page's b-delta) is one of 1, 2, 4, 8, default 4).  Readings  */
+/* taken where the page is silent or self-contradictory:                     */
 /*  - a row starts at previous column -1, every stored entry has a column    */
-/*    gap g = col - prev in 1..16 and code g-1 in 0..15 (the page: a 4-bit   */
-/*    delta spans at most 16);                                               */
-/*  - a gap larger than 16 is bridged by zero-valued padding entries placed  */
-/*    16 columns after the previous entry (code 15, value +0);               */
+/*    gap g = col - prev in 1..2^b and code g-1 in 0..2^b-1 (the page: a     */
+/*    4-bit delta spans at most 16);                                         */
+/*  - a gap larger than 2^b is bridged by zero-valued padding entries placed */
+/*    2^b columns after the previous entry (code 2^b-1, value +0);           */
 /*  - each row is then padded with (code 0, value +0) entries to a multiple  */
-/*    of 256 entries, so 128 B of codes and 512 B of values are aligned per  */
-/*    256 entries;                                                           */
-/*  - entry e's code is nibble (e % 8) of word e / 8, least significant      */
-/*    nibble first.                                                          */
+/*    of 1024/b entries, i.e. whole 128-byte blocks of codes (256 entries at */
+/*    b = 4, where 128 B of codes go with 512 B of fp16 values);             */
+/*  - entry e's code is field (e % (32/b)) of word e / (32/b), fields of b   */
+/*    bits, least significant field first.                                   */
 /* Columns must be strictly increasing in each row and lie in [0, n_cols).  */
 /* ------------------------------------------------------------------------ */
-#define ORACLE_MACKO_SPAN 16
-#define ORACLE_MACKO_ALIGN 256
-
-static int64_t oracle_macko_row_entries(const int32_t *cols, int32_t len)
+static int oracle_macko_bits_ok(int b)
 {
+    return b == 1 || b == 2 || b == 4 || b == 8;
+}
+
+static int64_t oracle_macko_row_entries(const int32_t *cols, int32_t len, int b)
+{
+    const int64_t span = (int64_t)1 << b, align = 1024 / b;
     int64_t count = 0;
     int64_t prev = -1;
     for (int32_t k = 0; k < len; ++k) {
         int64_t g = (int64_t)cols[k] - prev;
-        while (g > ORACLE_MACKO_SPAN) {       /* one padding entry per 16 columns */
+        while (g > span) {                    /* one padding entry per span */
             count++;
-            prev += ORACLE_MACKO_SPAN;
-            g -= ORACLE_MACKO_SPAN;
+            prev += span;
+            g -= span;
         }
         count++;
         prev = cols[k];
     }
-    int64_t rem = count % ORACLE_MACKO_ALIGN;
-    if (rem) count += ORACLE_MACKO_ALIGN - rem;
+    int64_t rem = count % align;
+    if (rem) count += align - rem;
     return count;
 }
 
-/* Total encoded entries, or -1 for unsorted/duplicate/out-of-range columns. */
-int64_t oracle_macko_size(int n_rows, int n_cols, const int32_t *rp, const int32_t *ci)
+/* Total encoded entries, -1 for unsorted/duplicate/out-of-range columns, -2
+ * for a code width other than 1, 2, 4, 8. */
+int64_t oracle_macko_size(int n_rows, int n_cols, int b, const int32_t *rp, const int32_t *ci)
 {
+    if (!oracle_macko_bits_ok(b)) return -2;
     int64_t total = 0;
     for (int i = 0; i < n_rows; ++i) {
         for (int32_t k = rp[i]; k < rp[i + 1]; ++k) {
             if (ci[k] < 0 || ci[k] >= n_cols) return -1;
             if (k > rp[i] && ci[k] <= ci[k - 1]) return -1;
         }
-        total += oracle_macko_row_entries(ci + rp[i], rp[i + 1] - rp[i]);
+        total += oracle_macko_row_entries(ci + rp[i], rp[i + 1] - rp[i], b);
     }
     return total;
 }
 
-static void oracle_macko_put(uint32_t *codes, uint16_t *mvals, int64_t e,
+static uint32_t oracle_macko_code(const uint32_t *codes, int64_t e, int b)
+{
+    const int per_word = 32 / b;
+    return (codes[e / per_word] >> (b * (e % per_word))) & (((uint32_t)1 << b) - 1u);
+}
+
+static void oracle_macko_put(uint32_t *codes, uint16_t *mvals, int64_t e, int b,
                              uint32_t code, uint16_t val)
 {
-    codes[e / 8] |= (code & 0xfu) << (4 * (e % 8));
+    const int per_word = 32 / b;
+    codes[e / per_word] |= code << (b * (e % per_word));
     mvals[e] = val;
 }
 
-/* Fills mrow_ptr[n_rows+1] (entry offsets), codes[E/8] and mvals[E] (fp16
- * bits).  Returns 0, or -1 on invalid columns. */
-int oracle_macko_encode(int n_rows, int n_cols, const int32_t *rp, const int32_t *ci,
+/* Fills mrow_ptr[n_rows+1] (entry offsets), codes[E*b/32] and mvals[E]
+ * (fp16 bits).  Returns 0, or -1 on invalid columns or code width. */
+int oracle_macko_encode(int n_rows, int n_cols, int b, const int32_t *rp, const int32_t *ci,
                         const uint16_t *vals, int32_t *mrow_ptr, uint32_t *codes,
                         uint16_t *mvals)
 {
-    int64_t total = oracle_macko_size(n_rows, n_cols, rp, ci);
+    int64_t total = oracle_macko_size(n_rows, n_cols, b, rp, ci);
     if (total < 0 || total > INT32_MAX) return -1;
-    memset(codes, 0, (size_t)(total / 8) * sizeof(uint32_t));
+    const int64_t span = (int64_t)1 << b, align = 1024 / b;
+    memset(codes, 0, (size_t)(total * b / 32) * sizeof(uint32_t));
     int64_t e = 0;
     for (int i = 0; i < n_rows; ++i) {
         mrow_ptr[i] = (int32_t)e;
@@ -405,30 +419,29 @@ int oracle_macko_encode(int n_rows, int n_cols, const int32_t *rp, const int32_t
         int64_t prev = -1;
         for (int32_t k = rp[i]; k < rp[i + 1]; ++k) {
             int64_t g = (int64_t)ci[k] - prev;
-            while (g > ORACLE_MACKO_SPAN) {
-                oracle_macko_put(codes, mvals, e++, ORACLE_MACKO_SPAN - 1, 0);
-                prev += ORACLE_MACKO_SPAN;
-                g -= ORACLE_MACKO_SPAN;
+            while (g > span) {
+                oracle_macko_put(codes, mvals, e++, b, (uint32_t)(span - 1), 0);
+                prev += span;
+                g -= span;
             }
-            oracle_macko_put(codes, mvals, e++, (uint32_t)(g - 1), vals[k]);
+            oracle_macko_put(codes, mvals, e++, b, (uint32_t)(g - 1), vals[k]);
             prev = ci[k];
         }
-        while ((e - row_begin) % ORACLE_MACKO_ALIGN)
-            oracle_macko_put(codes, mvals, e++, 0, 0);
+        while ((e - row_begin) % align)
+            oracle_macko_put(codes, mvals, e++, b, 0, 0);
     }
     mrow_ptr[n_rows] = (int32_t)e;
     return 0;
 }
 
 /* Column of every stored entry: restart at -1 per row, col = prev + code + 1. */
-void oracle_macko_decode(int n_rows, const int32_t *mrow_ptr, const uint32_t *codes,
+void oracle_macko_decode(int n_rows, int b, const int32_t *mrow_ptr, const uint32_t *codes,
                          int32_t *cols)
 {
     for (int i = 0; i < n_rows; ++i) {
         int64_t prev = -1;
         for (int64_t e = mrow_ptr[i]; e < mrow_ptr[i + 1]; ++e) {
-            uint32_t code = (codes[e / 8] >> (4 * (e % 8))) & 0xfu;
-            prev = prev + (int64_t)code + 1;
+            prev = prev + (int64_t)oracle_macko_code(codes, e, b) + 1;
             cols[e] = (int32_t)prev;
         }
     }
@@ -438,7 +451,7 @@ void oracle_macko_decode(int n_rows, const int32_t *mrow_ptr, const uint32_t *co
  * of value * x[col] + beta * y_i, with fp16 values and fp16 x taken exactly
  * into fp64.  Trailing alignment entries may decode to a column >= n_cols;
  * they hold +0 and are skipped. */
-void oracle_macko_spmv(int n_rows, int n_cols, const int32_t *mrow_ptr,
+void oracle_macko_spmv(int n_rows, int n_cols, int b, const int32_t *mrow_ptr,
                        const uint32_t *codes, const uint16_t *mvals,
                        const uint16_t *x, double alpha, double beta,
                        const float *y_in, double *y_out, double *scale)
@@ -447,10 +460,68 @@ void oracle_macko_spmv(int n_rows, int n_cols, const int32_t *mrow_ptr,
         double s = 0.0, a = 0.0;
         int64_t prev = -1;
         for (int64_t e = mrow_ptr[i]; e < mrow_ptr[i + 1]; ++e) {
-            uint32_t code = (codes[e / 8] >> (4 * (e % 8))) & 0xfu;
-            prev = prev + (int64_t)code + 1;
+            prev = prev + (int64_t)oracle_macko_code(codes, e, b) + 1;
             if (prev >= n_cols) continue;
             double p = oracle_half_to_double(mvals[e]) * oracle_half_to_double(x[prev]);
+            s += p;
+            a += fabs(p);
+        }
+        double yi = alpha * s, sc = fabs(alpha) * a;
+        if (beta != 0.0) {
+            yi += beta * (double)y_in[i];
+            sc += fabs(beta * (double)y_in[i]);
+        }
+        y_out[i] = yi;
+        if (scale) scale[i] = sc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* MACKO 8-bit value mode (the MACKO-SpMV page, section 3.3 names int8      */
+/* values for some layers; section 5 lists an 8-bit mode).  The page does   */
+/* not say how the int8 values are scaled.  Reading: symmetric per-row      */
+/* scaling, the plainest form of int8 weight quantisation:                   */
+/*   m_i     = max |v| over the row's stored fp16 values (exact);            */
+/*   s_i     = m_i / 127 as a correctly rounded fp32 division (1 if m_i = 0);*/
+/*   q_e     = v_e / s_i in fp64, rounded to the nearest integer with ties   */
+/*             to even, clamped to [-127, 127];                              */
+/* the value of entry e is then s_i * q_e.  Pads stay 0.                     */
+/* ------------------------------------------------------------------------ */
+void oracle_macko_quantize_i8(int n_rows, const int32_t *mrow_ptr, const uint16_t *mvals,
+                              int8_t *q, float *row_scale)
+{
+    for (int i = 0; i < n_rows; ++i) {
+        double m = 0.0;
+        for (int64_t e = mrow_ptr[i]; e < mrow_ptr[i + 1]; ++e) {
+            double v = fabs(oracle_half_to_double(mvals[e]));
+            if (v > m) m = v;
+        }
+        /* (float)m is exact: m is an fp16 value */
+        float s = m > 0.0 ? (float)m / 127.0f : 1.0f;
+        row_scale[i] = s;
+        for (int64_t e = mrow_ptr[i]; e < mrow_ptr[i + 1]; ++e) {
+            double r = nearbyint(oracle_half_to_double(mvals[e]) / (double)s);
+            if (r > 127.0) r = 127.0;
+            if (r < -127.0) r = -127.0;
+            q[e] = (int8_t)r;
+        }
+    }
+}
+
+/* y_i = alpha * sum over stored entries of (s_i * q_e) * x[col] + beta * y_i,
+ * everything exact in fp64 up to the sum's rounding. */
+void oracle_macko_spmv_i8(int n_rows, int n_cols, int b, const int32_t *mrow_ptr,
+                          const uint32_t *codes, const int8_t *q, const float *row_scale,
+                          const uint16_t *x, double alpha, double beta,
+                          const float *y_in, double *y_out, double *scale)
+{
+    for (int i = 0; i < n_rows; ++i) {
+        double s = 0.0, a = 0.0;
+        int64_t prev = -1;
+        for (int64_t e = mrow_ptr[i]; e < mrow_ptr[i + 1]; ++e) {
+            prev = prev + (int64_t)oracle_macko_code(codes, e, b) + 1;
+            if (prev >= n_cols) continue;
+            double p = (double)row_scale[i] * (double)q[e] * oracle_half_to_double(x[prev]);
             s += p;
             a += fabs(p);
         }
