@@ -24,6 +24,8 @@ sample).
 Other workloads (parity-test configs, also used for profiles):
   --config tiny | laplacian | powerlaw | varlen | pruned50 | pruned70 | pruned90 | fe
   --path   csr | csr-binned | csr-vector | csr-scalar | ell | hyb | auto | macko | dense | fem | fem-3stage
+           (MACKO variants: macko-b1 | macko-b2 | macko-b8 for 1-, 2- or 8-bit
+           codes instead of 4, macko-i8 and macko-i8-bN for int8 values)
   (varlen: 1M rows of 2..10 entries in a +-1000 band, CV 0.43, the HYB range
   of the CV rule; auto: the format that rule picks)
 """
@@ -63,6 +65,9 @@ SOURCE = {"csr": ("csr.hip",), "csr-binned": ("csr.hip",), "csr-vector": ("csr.h
           "csr-scalar": ("csr.hip",), "ell": ("ell.hip",), "macko": ("macko.hip",), "dense": ("dense.hip",),
           "fem": ("fem.hip",), "fem-3stage": ("fem.hip",), "hyb": ("ell.hip", "hyb.hip"),
           "auto": ("csr.hip", "ell.hip", "hyb.hip")}
+for _v in ("b1", "b2", "b8", "i8", "i8-b1", "i8-b2", "i8-b8"):
+    KERNEL["macko-" + _v] = "k_macko_spmv"
+    SOURCE["macko-" + _v] = ("macko.hip",)
 
 
 def log(*a):
@@ -173,19 +178,33 @@ class Workload:
             P = gen.pruned_weight(s)
             self.P = P
             self.workload = f"pruned_weight_12288x12288_sparsity{int(s * 100)}"
-            if path == "macko":
-                mrp, codes, mv = S.macko_encode(P.n_rows, P.n_cols, P.row_ptr, P.col_idx, P.vals_f16)
+            if path.startswith("macko"):
+                i8, bd = macko_variant(path)
+                mrp, codes, mv = S.macko_encode(P.n_rows, P.n_cols, P.row_ptr, P.col_idx, P.vals_f16, bdelta=bd)
                 E = int(mrp[-1])
-                self.bytes = 2 * E + E // 2 + 4 * (P.n_rows + 1) + 2 * P.n_cols + 4 * P.n_rows
+                # codes + values (+ row scales) + row pointers + x + y
+                self.bytes = (E * bd // 8 + (E + 4 * P.n_rows if i8 else 2 * E) + 4 * (P.n_rows + 1)
+                              + 2 * P.n_cols + 4 * P.n_rows)
                 self.flops = 2 * P.nnz
+                if i8:
+                    q, rsc = S.macko_quantize_i8(P.n_rows, mrp, mv)
+                    vals = (dev(q), dev(rsc))
+                else:
+                    vals = (dev(mv),)
 
                 def make(arrs):
-                    mrp_d, codes_d, mv_d, xh = arrs
+                    mrp_d, codes_d, xh = arrs[0], arrs[1], arrs[-1]
                     y = torch.zeros(P.n_rows, device="cuda")
+                    if i8:
+                        q_d, s_d = arrs[2], arrs[3]
+                        return (lambda: S.macko_spmv_i8(P.n_rows, P.n_cols, mrp_d, codes_d, q_d, s_d, self.alpha,
+                                                        xh, self.beta, y, bdelta=bd)), y, None
+                    mv_d = arrs[2]
                     return (lambda: S.macko_spmv(P.n_rows, P.n_cols, mrp_d, codes_d, mv_d, self.alpha, xh,
-                                                 self.beta, y)), y, None
-                self._setup((dev(mrp), dev(codes), dev(mv), dev(P.x_f16)), make, copies)
-                self.shape = {"n_rows": P.n_rows, "n_cols": P.n_cols, "nnz": P.nnz, "entries": E}
+                                                 self.beta, y, bdelta=bd)), y, None
+                self._setup((dev(mrp), dev(codes)) + vals + (dev(P.x_f16),), make, copies)
+                self.shape = {"n_rows": P.n_rows, "n_cols": P.n_cols, "nnz": P.nnz, "entries": E,
+                              "bdelta": bd, "values": "int8" if i8 else "fp16"}
             elif path == "dense":
                 self.bytes = 2 * P.n_rows * P.n_cols + 2 * P.n_cols + 4 * P.n_rows
                 self.flops = 2 * P.n_rows * P.n_cols
@@ -252,13 +271,30 @@ class Workload:
             return lambda: oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x)
         if self.config.startswith("pruned"):
             P = self.P
-            if self.path == "macko":
-                mrp, codes, mv = oracle.macko_encode(P.n_cols, P.row_ptr, P.col_idx, P.vals_f16)
-                return lambda: oracle.macko_spmv(P.n_cols, mrp, codes, mv, P.x_f16)
+            if self.path.startswith("macko"):
+                i8, bd = macko_variant(self.path)
+                mrp, codes, mv = oracle.macko_encode(P.n_cols, P.row_ptr, P.col_idx, P.vals_f16, bdelta=bd)
+                if i8:
+                    q, rsc = oracle.macko_quantize_i8(mrp, mv)
+                    return lambda: oracle.macko_spmv_i8(P.n_cols, mrp, codes, q, rsc, P.x_f16, bdelta=bd)
+                return lambda: oracle.macko_spmv(P.n_cols, mrp, codes, mv, P.x_f16, bdelta=bd)
             D = P.dense_f16()
             return lambda: oracle.gemv_f16(D, P.x_f16)
         M = self.Mesh
         return lambda: oracle.fe_matvec(M.edof, M.rho, M.Ke, M.x, M.n_dof)
+
+
+def macko_variant(path):
+    """(int8 values?, code width) of a MACKO path name such as macko-i8-b2."""
+    parts = path.split("-")[1:]
+    i8 = "i8" in parts
+    bd = 4
+    for p in parts:
+        if p.startswith("b") and p[1:] in ("1", "2", "4", "8"):
+            bd = int(p[1:])
+        elif p != "i8":
+            raise SystemExit(f"unknown MACKO variant {path}")
+    return i8, bd
 
 
 def parity(w, ref_fn):

@@ -246,41 +246,65 @@ spmv_status spmv_auto_destroy(spmv_auto_t h);
 
 /* ======================================================================== */
 /* MACKO ("MACKO-SpMV: GPU acceleration and storage optimisation at low      */
-/* sparsity", section 2)                                                    */
-/* Format: per row, entries in column order; each entry has a 4-bit code c  */
-/* meaning "column = previous column + c + 1" (the previous column starts   */
-/* at -1 in each row) and an fp16 value.  A gap larger than 16 is bridged by */
-/* padding entries (code 15, value +0) placed 16 columns after the previous */
-/* entry; each row is padded with (code 0, value +0) to a multiple of 256   */
-/* entries.  codes: entry e in bits [4(e%8), 4(e%8)+3] of word e/8.         */
-/* mrow_ptr[i] is the first entry of row i; mrow_ptr[n_rows] = total.       */
+/* sparsity", section 2; code widths and int8 values: section 3.3)          */
+/* Format for code width b in {1, 2, 4, 8} (the page's b-delta, 4 by        */
+/* default): per row, entries in column order; each entry has a b-bit code  */
+/* c meaning "column = previous column + c + 1" (the previous column starts */
+/* at -1 in each row) and a value.  A gap larger than 2^b is bridged by     */
+/* padding entries (code 2^b - 1, value +0) placed 2^b columns after the    */
+/* previous entry; each row is padded with (code 0, value +0) to a multiple */
+/* of 1024 / b entries (one 128-byte block of codes).  codes: entry e in    */
+/* bits [b (e % (32/b)), b (e % (32/b)) + b - 1] of word e / (32/b); the    */
+/* array holds n_entries * b / 32 words.  mrow_ptr[i] is the first entry of */
+/* row i; mrow_ptr[n_rows] = total.  The device entry points expect         */
+/* mrow_ptr, codes and values exactly as the encoder wrote them.             */
+/* A code width other than 1, 2, 4, 8 gives SPMV_ERR_INVALID_VALUE.         */
 /* ======================================================================== */
 
 /* Number of encoded entries (host inputs).  SPMV_ERR_UNSORTED if a row's
  * columns are not strictly increasing, SPMV_ERR_INVALID_MATRIX for a column
  * outside [0, n_cols) or a bad row_ptr, SPMV_ERR_OVERFLOW past int32. */
-spmv_status macko_encode_size(int32_t n_rows, int32_t n_cols, const int32_t *h_row_ptr,
+spmv_status macko_encode_size(int32_t n_rows, int32_t n_cols, int32_t bdelta, const int32_t *h_row_ptr,
                               const int32_t *h_col, int64_t *n_entries);
 
 /* Encodes on the host into caller buffers: h_mrow_ptr int32[n_rows+1],
- * h_codes uint32[n_entries/8], h_mvals uint16[n_entries] (fp16 bits).  Same
- * errors as macko_encode_size. */
-spmv_status macko_encode(int32_t n_rows, int32_t n_cols, const int32_t *h_row_ptr,
+ * h_codes uint32[n_entries*bdelta/32], h_mvals uint16[n_entries] (fp16
+ * bits).  Same errors as macko_encode_size. */
+spmv_status macko_encode(int32_t n_rows, int32_t n_cols, int32_t bdelta, const int32_t *h_row_ptr,
                          const int32_t *h_col, const uint16_t *h_vals_f16,
                          int32_t *h_mrow_ptr, uint32_t *h_codes, uint16_t *h_mvals);
 
+/* The 8-bit value mode (section 3.3 names int8 values; the scaling is this
+ * library's reading): for each row, s = max |v| / 127 over its stored fp16
+ * values as an fp32 division (1 for a row of zeros), and every value becomes
+ * q = v / s computed in double, rounded to nearest with ties to even and
+ * clamped to [-127, 127]; the entry's value is then s * q.  Host inputs
+ * h_mrow_ptr int32[n_rows+1] and h_mvals uint16[total] as written by
+ * macko_encode (values must be finite); outputs h_q int8[total] and
+ * h_row_scale fp32[n_rows].  SPMV_ERR_INVALID_MATRIX for a decreasing
+ * mrow_ptr. */
+spmv_status macko_quantize_i8(int32_t n_rows, const int32_t *h_mrow_ptr, const uint16_t *h_mvals,
+                              int8_t *h_q, float *h_row_scale);
+
 /* y = alpha * A * x + beta * y: fp16 values times fp16 x, fp32 accumulate,
  * fp32 y.  Columns are rebuilt on the GPU from the codes by a wave-wide
- * prefix sum (section 2.2.2).  All pointers are device; mvals and codes must
- * be 16-byte and 4-byte aligned (SPMV_ERR_UNSUPPORTED otherwise).
- * Asynchronous. */
-spmv_status macko_spmv(int32_t n_rows, int32_t n_cols, const int32_t *mrow_ptr,
+ * prefix sum (section 2.2.2).  All pointers are device; mvals must be
+ * 16-byte aligned and codes 4-byte aligned (8-byte for bdelta 8), else
+ * SPMV_ERR_UNSUPPORTED.  Asynchronous. */
+spmv_status macko_spmv(int32_t n_rows, int32_t n_cols, int32_t bdelta, const int32_t *mrow_ptr,
                        const uint32_t *codes, const uint16_t *mvals, float alpha,
                        const uint16_t *x_f16, float beta, float *y, void *stream);
 
+/* The same product with int8 values: y_i = alpha * s_i * sum q * x + beta * y_i
+ * (q int8[total] 8-byte aligned, row_scale fp32[n_rows], both device; the
+ * products q * x are exact in fp32, the sum is fp32).  Asynchronous. */
+spmv_status macko_spmv_i8(int32_t n_rows, int32_t n_cols, int32_t bdelta, const int32_t *mrow_ptr,
+                          const uint32_t *codes, const int8_t *q, const float *row_scale, float alpha,
+                          const uint16_t *x_f16, float beta, float *y, void *stream);
+
 /* Test hook: the column of every stored entry (device int32[total entries]),
  * rebuilt by the same on-GPU decoder.  Asynchronous. */
-spmv_status macko_decode_columns(int32_t n_rows, const int32_t *mrow_ptr,
+spmv_status macko_decode_columns(int32_t n_rows, int32_t bdelta, const int32_t *mrow_ptr,
                                  const uint32_t *codes, int32_t *cols_out, void *stream);
 
 /* ======================================================================== */

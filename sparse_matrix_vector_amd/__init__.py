@@ -25,7 +25,7 @@ __all__ = [
     "spmv_csr_row_stats", "spmv_format_recommend", "spmv_csr_plan_size", "spmv_csr_create",
     "spmv_csr_apply", "spmv_csr_get_plan", "spmv_csr_info", "spmv_csr_destroy",
     "spmv_ell_from_csr", "spmv_ell_apply", "macko_encode_size", "macko_encode", "macko_spmv",
-    "macko_decode_columns", "dense_gemv_f16", "fem_matvec_apply", "fem_threestage_size",
+    "macko_quantize_i8", "macko_spmv_i8", "macko_decode_columns", "dense_gemv_f16", "fem_matvec_apply", "fem_threestage_size",
     "fem_matvec_threestage", "CSRMatrix",
 ]
 
@@ -383,36 +383,57 @@ class AutoMatrix:
 # ---------------------------------------------------------------------------
 # MACKO (encoder on the host, kernels on the device)
 # ---------------------------------------------------------------------------
-def macko_encode_size(n_rows, n_cols, row_ptr, col_idx) -> int:
+def macko_encode_size(n_rows, n_cols, row_ptr, col_idx, bdelta=4) -> int:
     rp = _host(row_ptr, np.int32, "row_ptr")
     ci = _host(col_idx, np.int32, "col_idx")
     out = ctypes.c_int64()
-    _call("macko_encode_size", int(n_rows), int(n_cols), rp.ctypes.data, ci.ctypes.data, ctypes.byref(out))
+    _call("macko_encode_size", int(n_rows), int(n_cols), int(bdelta), rp.ctypes.data, ci.ctypes.data,
+          ctypes.byref(out))
     return out.value
 
 
-def macko_encode(n_rows, n_cols, row_ptr, col_idx, vals_f16):
-    """Host encode: returns (mrow_ptr int32[R+1], codes uint32[E/8], mvals uint16[E])."""
+def macko_encode(n_rows, n_cols, row_ptr, col_idx, vals_f16, bdelta=4):
+    """Host encode with b-bit codes: (mrow_ptr int32[R+1], codes uint32[E*b/32], mvals uint16[E])."""
     rp = _host(row_ptr, np.int32, "row_ptr")
     ci = _host(col_idx, np.int32, "col_idx")
     vv = _host(vals_f16, np.uint16, "vals_f16")
-    E = macko_encode_size(n_rows, n_cols, rp, ci)
+    E = macko_encode_size(n_rows, n_cols, rp, ci, bdelta)
+    nw = E * int(bdelta) // 32
     mrp = np.empty(n_rows + 1, np.int32)
-    codes = np.empty(max(E // 8, 1), np.uint32)[:E // 8]
+    codes = np.empty(max(nw, 1), np.uint32)[:nw]
     mv = np.empty(max(E, 1), np.uint16)[:E]
-    _call("macko_encode", int(n_rows), int(n_cols), rp.ctypes.data, ci.ctypes.data, vv.ctypes.data,
+    _call("macko_encode", int(n_rows), int(n_cols), int(bdelta), rp.ctypes.data, ci.ctypes.data, vv.ctypes.data,
           mrp.ctypes.data, codes.ctypes.data, mv.ctypes.data)
     return mrp, codes, mv
 
 
-def macko_spmv(n_rows, n_cols, mrow_ptr, codes, mvals, alpha, x_f16, beta, y, stream=None):
-    _call("macko_spmv", int(n_rows), int(n_cols), _dev(mrow_ptr, _i32_dtype(), "mrow_ptr"),
+def macko_quantize_i8(n_rows, mrow_ptr, mvals):
+    """Host int8 values of an encoded matrix: (q int8[E], row_scale float32[R])."""
+    mrp = _host(mrow_ptr, np.int32, "mrow_ptr")
+    mv = _host(mvals, np.uint16, "mvals")
+    E = int(mrp[n_rows]) if n_rows > 0 else 0
+    q = np.empty(max(E, 1), np.int8)[:E]
+    sc = np.empty(max(n_rows, 1), np.float32)[:n_rows]
+    _call("macko_quantize_i8", int(n_rows), mrp.ctypes.data, mv.ctypes.data, q.ctypes.data, sc.ctypes.data)
+    return q, sc
+
+
+def macko_spmv(n_rows, n_cols, mrow_ptr, codes, mvals, alpha, x_f16, beta, y, stream=None, bdelta=4):
+    _call("macko_spmv", int(n_rows), int(n_cols), int(bdelta), _dev(mrow_ptr, _i32_dtype(), "mrow_ptr"),
           _dev(codes, _u32_dtype(), "codes"), _dev(mvals, _u16_dtype(), "mvals"), float(alpha),
           _dev(x_f16, _u16_dtype(), "x_f16"), float(beta), _dev(y, _f32_dtype(), "y"), _stream(stream, y))
 
 
-def macko_decode_columns(n_rows, mrow_ptr, codes, cols_out, stream=None):
-    _call("macko_decode_columns", int(n_rows), _dev(mrow_ptr, _i32_dtype(), "mrow_ptr"),
+def macko_spmv_i8(n_rows, n_cols, mrow_ptr, codes, q, row_scale, alpha, x_f16, beta, y, stream=None, bdelta=4):
+    import torch
+    _call("macko_spmv_i8", int(n_rows), int(n_cols), int(bdelta), _dev(mrow_ptr, _i32_dtype(), "mrow_ptr"),
+          _dev(codes, _u32_dtype(), "codes"), _dev(q, (torch.int8, torch.uint8), "q"),
+          _dev(row_scale, _f32_dtype(), "row_scale"), float(alpha), _dev(x_f16, _u16_dtype(), "x_f16"),
+          float(beta), _dev(y, _f32_dtype(), "y"), _stream(stream, y))
+
+
+def macko_decode_columns(n_rows, mrow_ptr, codes, cols_out, stream=None, bdelta=4):
+    _call("macko_decode_columns", int(n_rows), int(bdelta), _dev(mrow_ptr, _i32_dtype(), "mrow_ptr"),
           _dev(codes, _u32_dtype(), "codes"), _dev(cols_out, _i32_dtype(), "cols_out"),
           _stream(stream, cols_out))
 

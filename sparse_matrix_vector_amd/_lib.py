@@ -48,10 +48,12 @@ SIGNATURES = {
     "spmv_auto_create": [P_vp, P_plan, c_i32, c_i32, c_i32, vp, vp, vp, vp, c_sz, vp],
     "spmv_auto_apply": [vp, c_f32, vp, c_f32, vp, vp],
     "spmv_auto_destroy": [vp],
-    "macko_encode_size": [c_i32, c_i32, vp, vp, P_i64],
-    "macko_encode": [c_i32, c_i32, vp, vp, vp, vp, vp, vp],
-    "macko_spmv": [c_i32, c_i32, vp, vp, vp, c_f32, vp, c_f32, vp, vp],
-    "macko_decode_columns": [c_i32, vp, vp, vp, vp],
+    "macko_encode_size": [c_i32, c_i32, c_i32, vp, vp, P_i64],
+    "macko_encode": [c_i32, c_i32, c_i32, vp, vp, vp, vp, vp, vp],
+    "macko_quantize_i8": [c_i32, vp, vp, vp, vp],
+    "macko_spmv": [c_i32, c_i32, c_i32, vp, vp, vp, c_f32, vp, c_f32, vp, vp],
+    "macko_spmv_i8": [c_i32, c_i32, c_i32, vp, vp, vp, vp, c_f32, vp, c_f32, vp, vp],
+    "macko_decode_columns": [c_i32, c_i32, vp, vp, vp, vp],
     "dense_gemv_f16": [c_i32, c_i32, vp, vp, c_f32, c_f32, vp, vp],
     "fem_matvec_apply": [c_i32, c_i32, vp, vp, c_i32, vp, c_f32, vp, c_f32, vp, vp],
     "fem_threestage_size": [c_i32, P_sz],

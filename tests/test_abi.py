@@ -81,6 +81,49 @@ def test_host_encoder_bit_exact_with_oracle(s, n_rows, n_cols):
     assert S.macko_encode_size(n_rows, n_cols, W.row_ptr, W.col_idx) == oracle.macko_size(n_cols, W.row_ptr, W.col_idx)
 
 
+@pytest.mark.parametrize("b", [1, 2, 8])
+@pytest.mark.parametrize("s,n_rows,n_cols", [(0.5, 40, 2048), (0.9, 20, 12288), (0.0, 4, 300)])
+def test_host_encoder_all_widths_bit_exact_with_oracle(b, s, n_rows, n_cols):
+    W = gen.pruned_weight(s, n_rows=n_rows, n_cols=n_cols, seed=78)
+    got = S.macko_encode(n_rows, n_cols, W.row_ptr, W.col_idx, W.vals_f16, bdelta=b)
+    ref = oracle.macko_encode(n_cols, W.row_ptr, W.col_idx, W.vals_f16, bdelta=b)
+    assert all(np.array_equal(x, y) for x, y in zip(got, ref))
+    assert S.macko_encode_size(n_rows, n_cols, W.row_ptr, W.col_idx, b) == len(ref[2])
+
+
+def test_host_encoder_width_golden_cases():
+    g = json.load(open(os.path.join(GOLD, "macko_widths.json")))
+    for case in g["cases"]:
+        cols = np.asarray(case["columns"], np.int32)
+        rp = np.array([0, len(cols)], np.int32)
+        v = np.arange(1, len(cols) + 1).astype(np.float16).view(np.uint16)
+        mrp, codes, mv = S.macko_encode(1, 1024, rp, cols, v, bdelta=case["b"])
+        assert mrp.tolist() == [0, case["align"]] and int(codes[0]) == case["word0"], case
+
+
+@pytest.mark.parametrize("b", [0, 3, 16])
+def test_host_encoder_rejects_width(b):
+    with pytest.raises(S.SpmvError) as e:
+        S.macko_encode_size(1, 64, np.array([0, 1], np.int32), np.array([3], np.int32), b)
+    assert e.value.status == 1
+
+
+def test_host_quantizer_bit_exact_with_oracle():
+    g = json.load(open(os.path.join(GOLD, "macko_int8.json")))
+    rows = g["rows"]
+    mrp = np.concatenate([[0], np.cumsum([len(r["values"]) for r in rows])]).astype(np.int32)
+    mv = np.concatenate([np.array(r["values"], np.float16) for r in rows]).view(np.uint16)
+    q, sc = S.macko_quantize_i8(len(rows), mrp, mv)
+    for i, r in enumerate(rows):
+        assert float(sc[i]) == r["scale"] and q[mrp[i]:mrp[i + 1]].tolist() == r["q"], r
+    for s_, b in [(0.5, 4), (0.7, 2), (0.9, 8)]:
+        W = gen.pruned_weight(s_, n_rows=50, n_cols=4000, seed=79)
+        mrp, codes, mv = S.macko_encode(50, 4000, W.row_ptr, W.col_idx, W.vals_f16, bdelta=b)
+        q, sc = S.macko_quantize_i8(50, mrp, mv)
+        oq, osc = oracle.macko_quantize_i8(mrp, mv)
+        assert np.array_equal(q, oq) and np.array_equal(sc.view(np.uint32), osc.view(np.uint32))
+
+
 def test_host_encoder_golden_and_large_gaps():
     g = json.load(open(os.path.join(GOLD, "macko_examples.json")))
     for case in [g["page_example"]] + g["cases"]:
@@ -125,13 +168,19 @@ def test_host_validation_before_any_gpu_call():
     assert L.spmv_csr_apply(None, 1.0, None, 0.0, None, None) == 1
     assert L.spmv_ell_apply(-1, 1, 1, None, None, 1.0, None, 0.0, None, None) == 1
     assert L.spmv_ell_apply(1 << 20, 1, 1 << 12, None, None, 1.0, None, 0.0, None, None) == 4
-    assert L.macko_spmv(4, 4, None, None, None, 1.0, None, 0.0, None, None) == 1
-    assert L.macko_spmv(4, 4, 16, 16, 18, 1.0, 16, 0.0, 16, None) == 5      # misaligned values
+    assert L.macko_spmv(4, 4, 4, None, None, None, 1.0, None, 0.0, None, None) == 1
+    assert L.macko_spmv(4, 4, 4, 16, 16, 18, 1.0, 16, 0.0, 16, None) == 5      # misaligned values
+    assert L.macko_spmv(4, 4, 8, 16, 20, 16, 1.0, 16, 0.0, 16, None) == 5      # codes not 8-byte aligned
+    assert L.macko_spmv(4, 4, 3, 16, 16, 16, 1.0, 16, 0.0, 16, None) == 1      # code width
+    assert L.macko_spmv_i8(4, 4, 2, 16, 16, 20, 16, 1.0, 16, 0.0, 16, None) == 5   # q not 8-byte aligned
+    assert L.macko_spmv_i8(4, 4, 2, 16, 16, 16, None, 1.0, 16, 0.0, 16, None) == 1  # no scales
+    assert L.macko_decode_columns(4, 16, 16, 16, 16, None) == 1
     assert L.dense_gemv_f16(-1, 4, None, None, 1.0, 0.0, None, None) == 1
     assert L.fem_matvec_apply(4, 10, 16, 16, 9, 16, 1.0, 16, 0.0, 16, None) == 1   # penalty > 8
     assert L.fem_matvec_apply(4, 10, 20, 16, 3, 16, 1.0, 16, 0.0, 16, None) == 5   # edof misaligned
     assert L.fem_matvec_threestage(4, 10, 16, 16, 3, 16, 1.0, 16, 0.0, 16, None, 0, None) == 1
     # n_rows == 0 applies are no-ops that succeed without touching the GPU
-    assert L.macko_spmv(0, 4, None, None, None, 1.0, None, 0.0, None, None) == 0
+    assert L.macko_spmv(0, 4, 4, None, None, None, 1.0, None, 0.0, None, None) == 0
+    assert L.macko_spmv_i8(0, 4, 1, None, None, None, None, 1.0, None, 0.0, None, None) == 0
     assert L.spmv_ell_apply(0, 4, 2, None, None, 1.0, None, 0.0, None, None) == 0
     assert L.dense_gemv_f16(0, 4, None, None, 1.0, 0.0, None, None) == 0
