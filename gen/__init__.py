@@ -23,6 +23,10 @@ workloads the source pages measure:
 * ``fe_mesh``        a structured hex8 cantilever mesh with a shared seeded SPD
                      24x24 element matrix and SIMP densities (fused FE matvec
                      page, sections 2 and 3.2; 120x60x30 is its 216k case).
+* ``fe_cantilever``  the same mesh with the linear-elasticity element matrix
+                     of a unit hex8 (``hex8_elasticity_ke``), uniform density
+                     and an end load: the system the page's Jacobi-PCG solves
+                     and whose condition number it reports (sections 4.1, 6.1).
 """
 from __future__ import annotations
 
@@ -32,7 +36,7 @@ import numpy as np
 __all__ = [
     "CSR", "tiny_csr", "laplacian_2d", "powerlaw_csr", "powerlaw_pmf",
     "random_csr", "PrunedWeight", "pruned_weight", "FEMesh", "fe_mesh",
-    "fe_ke_translation_free", "sine_mode", "SPARSITY_INDEX",
+    "fe_ke_translation_free", "hex8_elasticity_ke", "fe_cantilever", "sine_mode", "SPARSITY_INDEX",
     "POWERLAW_ALPHA", "POWERLAW_KMAX",
 ]
 
@@ -314,6 +318,7 @@ class FEMesh:
     Ke: np.ndarray               # float32[24, 24], symmetric positive definite
     x: np.ndarray                # float32[n_dof]
     penalty: int = 3
+    f: np.ndarray | None = None  # float32[n_dof] load (fe_cantilever only)
 
 
 def _fe_structure(nx, ny, nz, clamp_x0):
@@ -378,3 +383,61 @@ def fe_ke_translation_free(seed: int = 5) -> np.ndarray:
     Q = np.eye(24) - T @ T.T
     K = Q @ (G @ G.T) @ Q
     return 0.5 * (K + K.T)
+
+
+def hex8_elasticity_ke(E: float = 1.0, nu: float = 0.3) -> np.ndarray:
+    """fp64 24x24 stiffness matrix of a unit-cube trilinear hex8 element in
+    isotropic linear elasticity (Young's modulus E, Poisson ratio nu):
+    Ke = sum over the 2 x 2 x 2 Gauss points (weight 1/8) of B^T D B, which
+    is exact for this element.  Local DOF 3a + comp with the node order of
+    ``HEX8_LOCAL_NODES``; strains in Voigt order (xx, yy, zz, xy, yz, zx) with
+    engineering shears.  Symmetric, positive semidefinite with the six rigid
+    motions as its null space."""
+    lam = E * nu / ((1 + nu) * (1 - 2 * nu))
+    mu = E / (2 * (1 + nu))
+    D = np.zeros((6, 6))
+    D[:3, :3] = lam
+    D[np.arange(3), np.arange(3)] = lam + 2 * mu
+    D[np.arange(3, 6), np.arange(3, 6)] = mu
+    g = (0.5 - 0.5 / np.sqrt(3.0), 0.5 + 0.5 / np.sqrt(3.0))
+    Ke = np.zeros((24, 24))
+    for px in g:
+        for py in g:
+            for pz in g:
+                B = np.zeros((6, 24))
+                for a, (ax, ay, az) in enumerate(HEX8_LOCAL_NODES):
+                    fx = px if ax else 1 - px
+                    fy = py if ay else 1 - py
+                    fz = pz if az else 1 - pz
+                    sx, sy, sz = (1 if ax else -1), (1 if ay else -1), (1 if az else -1)
+                    dx, dy, dz = sx * fy * fz, fx * sy * fz, fx * fy * sz
+                    c = 3 * a
+                    B[0, c] = dx
+                    B[1, c + 1] = dy
+                    B[2, c + 2] = dz
+                    B[3, c], B[3, c + 1] = dy, dx
+                    B[4, c + 1], B[4, c + 2] = dz, dy
+                    B[5, c], B[5, c + 2] = dz, dx
+                Ke += 0.125 * (B.T @ D @ B)
+    return 0.5 * (Ke + Ke.T)
+
+
+def fe_cantilever(nx: int = 120, ny: int = 60, nz: int = 30, rho: float = 0.5, E: float = 1.0,
+                  nu: float = 0.3, penalty: int = 3) -> FEMesh:
+    """The cantilever the fused-FE page solves: the hex8 mesh of ``fe_mesh``
+    with the ix = 0 face clamped, the elasticity element matrix (fp32), the
+    same density rho in every element, and a load of total -1 in z spread
+    evenly over the nodes of the free end face ix = nx (``f``; ``x`` holds
+    the same vector).  No random draws."""
+    edof, n_dof = _fe_structure(nx, ny, nz, True)
+    n_elem = nx * ny * nz
+    nnx, nny, nnz_ = nx + 1, ny + 1, nz + 1
+    node = np.arange(nnx * nny * nnz_)
+    free = np.repeat(node % nnx != 0, 3)
+    newid = np.full(3 * len(node), -1, dtype=np.int64)
+    newid[free] = np.arange(int(free.sum()))
+    end = node[node % nnx == nx]
+    f = np.zeros(n_dof, np.float32)
+    f[newid[3 * end + 2]] = np.float32(-1.0 / len(end))
+    Ke = hex8_elasticity_ke(E, nu).astype(np.float32)
+    return FEMesh(nx, ny, nz, n_elem, n_dof, edof, np.full(n_elem, rho, np.float32), Ke, f.copy(), penalty, f)

@@ -341,3 +341,6 @@ def fe_assemble(edof, rho, Ke, n_dof, penalty=3):
     lib().oracle_fe_assemble(n_elem, int(n_dof), ed, r, int(penalty), K,
                              rp.ctypes.data, ci.ctypes.data, v.ctypes.data)
     return rp, ci, v
+
+
+from .solver import fe_diagonal, pcg_jacobi, power_lambda_max, inverse_lambda_min  # noqa: E402
