@@ -22,12 +22,16 @@ HBM peak, and the CPU oracle timed on the host (serial fp64 C, bounded
 sample).
 
 Other workloads (parity-test configs, also used for profiles):
-  --config tiny | laplacian | powerlaw | varlen | pruned50 | pruned70 | pruned90 | fe
+  --config tiny | laplacian | powerlaw | varlen | pruned50 | pruned70 | pruned90 | fe | cantilever
   --path   csr | csr-binned | csr-vector | csr-scalar | ell | hyb | auto | macko | dense | fem | fem-3stage
            (MACKO variants: macko-b1 | macko-b2 | macko-b8 for 1-, 2- or 8-bit
            codes instead of 4, macko-i8 and macko-i8-bN for int8 values)
   (varlen: 1M rows of 2..10 entries in a +-1000 band, CV 0.43, the HYB range
   of the CV rule; auto: the format that rule picks)
+  cantilever / fem-pcg: Jacobi-PCG on the 216k-element elasticity cantilever
+  (rho = 0.5); one step = one PCG iteration (fixed count, rtol = 0), timed
+  warm, as a solver runs it; the line also carries a solve to rtol 1e-6 and
+  the condition-number estimate.
 """
 from __future__ import annotations
 
@@ -48,7 +52,7 @@ FLUSH_BYTES = 1 << 30
 ROTATE_BYTES = 1 << 30
 
 DEFAULT_PATH = {"tiny": "csr", "laplacian": "csr", "powerlaw": "csr", "varlen": "auto", "pruned50": "macko",
-                "pruned70": "macko", "pruned90": "macko", "fe": "fem"}
+                "pruned70": "macko", "pruned90": "macko", "fe": "fem", "cantilever": "fem-pcg"}
 CSR_CONFIGS = ("tiny", "laplacian", "powerlaw", "varlen")
 # further paths the config itself names, measured beside the default one when
 # no --path is given (the Laplacian config names a CSR and an ELL path)
@@ -58,13 +62,13 @@ OTHER_PATHS = {"laplacian": ("ell",)}
 KERNEL = {"csr": "k_csr_tasks", "csr-binned": "k_csr_tasks", "csr-vector": "k_csr_vector",
           "csr-scalar": "k_csr_scalar", "ell": "k_ell_apply4t", "macko": "k_macko_spmv",
           "dense": "k_gemv_f16", "fem": "k_fe_fused", "fem-3stage": "k_fe_elem", "hyb": "k_ell_apply",
-          "auto": None}
+          "auto": None, "fem-pcg": "k_fe_matvec64 + k_pcg_alpha + k_pcg_update + k_pcg_direction"}
 
 # source file of each path's kernels (for the traffic-record freshness check)
 SOURCE = {"csr": ("csr.hip",), "csr-binned": ("csr.hip",), "csr-vector": ("csr.hip",),
           "csr-scalar": ("csr.hip",), "ell": ("ell.hip",), "macko": ("macko.hip",), "dense": ("dense.hip",),
           "fem": ("fem.hip",), "fem-3stage": ("fem.hip",), "hyb": ("ell.hip", "hyb.hip"),
-          "auto": ("csr.hip", "ell.hip", "hyb.hip")}
+          "auto": ("csr.hip", "ell.hip", "hyb.hip"), "fem-pcg": ("fem_solver.hip",)}
 for _v in ("b1", "b2", "b8", "i8", "i8-b1", "i8-b2", "i8-b8"):
     KERNEL["macko-" + _v] = "k_macko_spmv"
     SOURCE["macko-" + _v] = ("macko.hip",)
@@ -439,6 +443,92 @@ def pmc_calibration_copies(nbytes=256 << 20, reps=3):
     log(f"[bench] calibration copies: {reps} x {nbytes} bytes read and written")
 
 
+def bench_pcg(args):
+    """One JSON line for Jacobi-PCG on the cantilever (see the module docstring)."""
+    import numpy as np
+    import torch
+    import gen
+    import sparse_matrix_vector_amd as S
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    dims = (120, 60, 30)
+    m = gen.fe_cantilever(*dims)
+    E, n = m.n_elem, m.n_dof
+    op = (E, n, dev(m.edof.reshape(-1)), dev(m.rho), m.penalty, dev(m.Ke.reshape(-1)))
+    f = dev(m.f)
+    ws = torch.empty(S.fem_solver_workspace_size(n, 400), dtype=torch.uint8, device="cuda")
+    u = torch.zeros(n, device="cuda")
+    stream = torch.cuda.current_stream()
+    # per iteration: matvec (edof 96 B + rho 4 B per element; p 4 B, fp64 accumulator read+write 16 B per
+    # DOF), alpha (p, acc in; q, cleared acc out: 24 B), update (p q dinv u r in, u r z out: 32 B),
+    # direction (z p in, p out: 12 B)
+    nbytes = 100 * E + 88 * n
+    flops = 2 * 576 * E + 13 * n
+    S.fem_pcg_solve(*op, f, u, 0.0, max(args.warmup, 1), workspace=ws)
+    u.zero_()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    it, _ = S.fem_pcg_solve(*op, f, u, 0.0, args.steps, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(it, 1)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    # a solve to rtol 1e-6 and the condition number, as the page reports them
+    u.zero_()
+    torch.cuda.synchronize()
+    t0 = time.time()
+    it6, rr6 = S.fem_pcg_solve(*op, f, u, 1e-6, 20000, workspace=ws)
+    t_solve = time.time() - t0
+    comp = float(m.f.astype(np.float64) @ u.cpu().numpy().astype(np.float64))
+    v0 = dev(np.random.default_rng(5).standard_normal(n).astype(np.float32))
+    t0 = time.time()
+    lam = S.fem_lambda_max(*op, v0, 400, workspace=ws)
+    mu, inner = S.fem_lambda_min(*op, v0, 4, 1e-6, 20000, workspace=ws)
+    t_kappa = time.time() - t0
+    par = None
+    gpath = os.path.join(ROOT, "tests", "golden", "fe_cantilever.json")
+    if not args.no_parity and os.path.exists(gpath):
+        g = json.load(open(gpath))["cases"]["120x60x30"]
+        par = {"ok": bool(abs(comp - g["compliance"]) <= 1e-4 * abs(g["compliance"])
+                          and abs(it6 - g["pcg_iterations_rtol_1e-6"]) <= 0.35 * g["pcg_iterations_rtol_1e-6"]),
+               "compliance": comp, "compliance_fp64_oracle": g["compliance"],
+               "iterations": it6, "iterations_fp64_oracle": g["pcg_iterations_rtol_1e-6"],
+               "source": "tests/golden/fe_cantilever.json (written by the fp64 oracle)"}
+    line = {
+        "metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e9, 3), "unit": "GFLOP/s", "n_gpus": 1,
+        "steps": it, "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 (fp64 sums)", "data": "synthetic (gen.fe_cantilever)",
+        "config": {"workload": "fe_elasticity_cantilever_120x60x30_rho0.5", "path": "fem-pcg", "n_elem": E,
+                   "n_dof": n, "step": "one Jacobi-PCG iteration", "protocol": "warm (the solver's own vectors)",
+                   "timing": "HIP events on the launch stream around a fixed-count solve",
+                   "algorithmic_bytes": nbytes, "flops": flops},
+        "effective_gbs": round(gbs, 2), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": KERNEL["fem-pcg"]},
+        "solve": {"rtol": 1e-6, "iterations": it6, "rel_residual": rr6, "seconds": round(t_solve, 4),
+                  "compliance": comp},
+        "kappa": {"lambda_max": lam[-1], "lambda_min": float(mu[-1]), "kappa": lam[-1] / mu[-1],
+                  "page_kappa_216k": 1.3e6, "power_steps": 400, "inverse_steps": 4,
+                  "inner_pcg_iterations": inner.tolist(), "seconds": round(t_kappa, 3)},
+        "parity": par,
+    }
+    if args.cpu_seconds > 0:
+        import scipy.sparse as sp
+        import oracle
+        rp, ci, v = oracle.fe_assemble(m.edof, m.rho, m.Ke, n, m.penalty)
+        K = sp.csr_matrix((v, ci, rp), shape=(n, n))
+        d = oracle.fe_diagonal(m.edof, m.rho, m.Ke, n, m.penalty)
+        k, t0 = 0, time.time()
+        while time.time() - t0 < args.cpu_seconds:
+            oracle.pcg_jacobi(lambda x: K @ x, d, m.f.astype(np.float64), rtol=0.0, max_iter=10)
+            k += 10
+        el = time.time() - t0
+        line["cpu_baseline"] = {"value": round(flops * k / el / 1e9, 3), "unit": "GFLOP/s", "cores": 1,
+                                "kind": "oracle", "ms_per_step": round(1e3 * el / k, 3),
+                                "sample": f"{k} fp64 PCG iterations on the assembled CSR (SciPy), same mesh"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -469,6 +559,11 @@ def main():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(2)
     path = args.path or DEFAULT_PATH[args.config]
+    if args.config == "cantilever" or path == "fem-pcg":
+        if args.config != "cantilever" or path != "fem-pcg":
+            raise SystemExit("the fem-pcg path runs on the cantilever config only")
+        bench_pcg(args)
+        return
     if args.pmc_calibrate:
         pmc_calibration_copies()
     w = Workload(args.config, path, args.copies if args.protocol == "rotate" else 1)

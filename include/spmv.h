@@ -346,6 +346,56 @@ spmv_status fem_matvec_threestage(int32_t n_elem, int32_t n_dof, const int32_t *
                                   float alpha, const float *x, float beta, float *y,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
+/* ======================================================================== */
+/* FE solver ("Fused GPU SpMV kernel optimisation", section 6.1: Jacobi-     */
+/* preconditioned CG around the fused matvec, with an iteration cap;        */
+/* section 4.1: the condition number of K by power iteration).  The        */
+/* operator arguments (n_elem, n_dof, edof, rho, penalty, Ke) are those of  */
+/* fem_matvec_apply, with the same validation.  Vectors are fp32 device     */
+/* arrays of n_dof entries; inner products are accumulated in fp64.  The    */
+/* workspace is device memory, 256-byte aligned, of at least the size       */
+/* fem_solver_workspace_size returns; it is not freed by these calls.       */
+/* ======================================================================== */
+
+/* diag[d] = sum of rho_e^penalty * Ke[a][a] over the elements e and local
+ * DOFs a with edof[e][a] = d: the Jacobi preconditioner.  Asynchronous. */
+spmv_status fem_jacobi_diagonal(int32_t n_elem, int32_t n_dof, const int32_t *edof, const float *rho,
+                                int32_t penalty, const float *Ke, float *diag, void *stream);
+
+/* Workspace bytes for the calls below; max_history >= the `iterations` of
+ * fem_lambda_max / fem_lambda_min (0 for fem_pcg_solve alone). */
+spmv_status fem_solver_workspace_size(int32_t n_dof, int32_t max_history, size_t *bytes);
+
+/* Solves K u = f by Jacobi-PCG from the initial guess in u (device, fp32,
+ * overwritten with the solution).  Stops when the recursively updated
+ * residual satisfies ||r|| <= rtol * ||f|| or after max_iter iterations.
+ * *iterations (host, optional) receives the iterations done and
+ * *rel_residual (host, optional) ||r|| / ||f|| (||r|| if f = 0).
+ * SPMV_ERR_INVALID_MATRIX if a diagonal entry is not positive or p.Kp <= 0
+ * (the operator is not SPD).  Synchronises the stream. */
+spmv_status fem_pcg_solve(int32_t n_elem, int32_t n_dof, const int32_t *edof, const float *rho,
+                          int32_t penalty, const float *Ke, const float *f, float *u, float rtol,
+                          int32_t max_iter, void *workspace, size_t workspace_bytes, int32_t *iterations,
+                          double *rel_residual, void *stream);
+
+/* Largest eigenvalue of K by power iteration from v0 (device, nonzero):
+ * v <- K v / ||K v||; h_lambda (host, `iterations` entries) receives the
+ * Rayleigh quotient v.Kv of every normalised iterate; the last one is the
+ * estimate.  Synchronises the stream. */
+spmv_status fem_lambda_max(int32_t n_elem, int32_t n_dof, const int32_t *edof, const float *rho,
+                           int32_t penalty, const float *Ke, const float *v0, int32_t iterations,
+                           void *workspace, size_t workspace_bytes, double *h_lambda, void *stream);
+
+/* Smallest eigenvalue of K by the same iteration on K^-1: each step solves
+ * K w = v by Jacobi-PCG from zero (inner_rtol, inner_max_iter), then
+ * v <- w / ||w||; h_lambda (host) receives the Rayleigh quotients v.Kv,
+ * h_inner_iterations (host, optional) the PCG iterations of each step.
+ * kappa(K) = lambda_max / lambda_min.  Synchronises the stream. */
+spmv_status fem_lambda_min(int32_t n_elem, int32_t n_dof, const int32_t *edof, const float *rho,
+                           int32_t penalty, const float *Ke, const float *v0, int32_t iterations,
+                           float inner_rtol, int32_t inner_max_iter, void *workspace, size_t workspace_bytes,
+                           double *h_lambda, int32_t *h_inner_iterations, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,8 @@ __all__ = [
     "spmv_csr_apply", "spmv_csr_get_plan", "spmv_csr_info", "spmv_csr_destroy",
     "spmv_ell_from_csr", "spmv_ell_apply", "macko_encode_size", "macko_encode", "macko_spmv",
     "macko_quantize_i8", "macko_spmv_i8", "macko_decode_columns", "dense_gemv_f16", "fem_matvec_apply", "fem_threestage_size",
-    "fem_matvec_threestage", "CSRMatrix",
+    "fem_matvec_threestage", "fem_jacobi_diagonal", "fem_solver_workspace_size", "fem_pcg_solve",
+    "fem_lambda_max", "fem_lambda_min", "CSRMatrix",
 ]
 
 STATUS = {0: "SPMV_OK", 1: "SPMV_ERR_INVALID_VALUE", 2: "SPMV_ERR_INVALID_MATRIX",
@@ -459,6 +460,61 @@ def fem_threestage_size(n_elem) -> int:
     out = ctypes.c_size_t()
     _call("fem_threestage_size", int(n_elem), ctypes.byref(out))
     return out.value
+
+
+def fem_jacobi_diagonal(n_elem, n_dof, edof, rho, penalty, Ke, diag, stream=None):
+    _call("fem_jacobi_diagonal", int(n_elem), int(n_dof), _dev(edof, _i32_dtype(), "edof"),
+          _dev(rho, _f32_dtype(), "rho"), int(penalty), _dev(Ke, _f32_dtype(), "Ke"),
+          _dev(diag, _f32_dtype(), "diag"), _stream(stream, diag))
+
+
+def fem_solver_workspace_size(n_dof, max_history=0) -> int:
+    out = ctypes.c_size_t()
+    _call("fem_solver_workspace_size", int(n_dof), int(max_history), ctypes.byref(out))
+    return out.value
+
+
+def _workspace(nbytes, like):
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
+
+
+def fem_pcg_solve(n_elem, n_dof, edof, rho, penalty, Ke, f, u, rtol=1e-6, max_iter=1000, workspace=None,
+                  stream=None):
+    """Jacobi-PCG for K u = f (u: initial guess in, solution out).  Returns
+    (iterations, ||r|| / ||f||).  Synchronises."""
+    ws = workspace if workspace is not None else _workspace(fem_solver_workspace_size(n_dof), u)
+    it = ctypes.c_int32()
+    rr = ctypes.c_double()
+    _call("fem_pcg_solve", int(n_elem), int(n_dof), _dev(edof, _i32_dtype(), "edof"),
+          _dev(rho, _f32_dtype(), "rho"), int(penalty), _dev(Ke, _f32_dtype(), "Ke"), _dev(f, _f32_dtype(), "f"),
+          _dev(u, _f32_dtype(), "u"), float(rtol), int(max_iter), ws.data_ptr(),
+          ws.numel() * ws.element_size(), ctypes.byref(it), ctypes.byref(rr), _stream(stream, u))
+    return it.value, rr.value
+
+
+def fem_lambda_max(n_elem, n_dof, edof, rho, penalty, Ke, v0, iterations, workspace=None, stream=None):
+    """Power iteration: the Rayleigh quotient of every iterate (float64[iterations])."""
+    ws = workspace if workspace is not None else _workspace(fem_solver_workspace_size(n_dof, iterations), v0)
+    lam = np.zeros(int(iterations), np.float64)
+    _call("fem_lambda_max", int(n_elem), int(n_dof), _dev(edof, _i32_dtype(), "edof"),
+          _dev(rho, _f32_dtype(), "rho"), int(penalty), _dev(Ke, _f32_dtype(), "Ke"), _dev(v0, _f32_dtype(), "v0"),
+          int(iterations), ws.data_ptr(), ws.numel() * ws.element_size(), lam.ctypes.data, _stream(stream, v0))
+    return lam
+
+
+def fem_lambda_min(n_elem, n_dof, edof, rho, penalty, Ke, v0, iterations, inner_rtol=1e-6, inner_max_iter=5000,
+                   workspace=None, stream=None):
+    """Inverse iteration with Jacobi-PCG solves: (Rayleigh quotients
+    float64[iterations], PCG iterations int32[iterations])."""
+    ws = workspace if workspace is not None else _workspace(fem_solver_workspace_size(n_dof, iterations), v0)
+    lam = np.zeros(int(iterations), np.float64)
+    inner = np.zeros(int(iterations), np.int32)
+    _call("fem_lambda_min", int(n_elem), int(n_dof), _dev(edof, _i32_dtype(), "edof"),
+          _dev(rho, _f32_dtype(), "rho"), int(penalty), _dev(Ke, _f32_dtype(), "Ke"), _dev(v0, _f32_dtype(), "v0"),
+          int(iterations), float(inner_rtol), int(inner_max_iter), ws.data_ptr(), ws.numel() * ws.element_size(),
+          lam.ctypes.data, inner.ctypes.data, _stream(stream, v0))
+    return lam, inner
 
 
 def fem_matvec_threestage(n_elem, n_dof, edof, rho, penalty, Ke, alpha, x, beta, y, workspace,

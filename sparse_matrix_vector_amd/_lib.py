@@ -16,6 +16,7 @@ c_i32, c_i64, c_f32, c_sz, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, 
 P_i32 = ctypes.POINTER(ctypes.c_int32)
 P_i64 = ctypes.POINTER(ctypes.c_int64)
 P_sz = ctypes.POINTER(ctypes.c_size_t)
+P_f64 = ctypes.POINTER(ctypes.c_double)
 P_vp = ctypes.POINTER(ctypes.c_void_p)
 
 
@@ -58,6 +59,11 @@ SIGNATURES = {
     "fem_matvec_apply": [c_i32, c_i32, vp, vp, c_i32, vp, c_f32, vp, c_f32, vp, vp],
     "fem_threestage_size": [c_i32, P_sz],
     "fem_matvec_threestage": [c_i32, c_i32, vp, vp, c_i32, vp, c_f32, vp, c_f32, vp, vp, c_sz, vp],
+    "fem_jacobi_diagonal": [c_i32, c_i32, vp, vp, c_i32, vp, vp, vp],
+    "fem_solver_workspace_size": [c_i32, c_i32, P_sz],
+    "fem_pcg_solve": [c_i32, c_i32, vp, vp, c_i32, vp, vp, vp, c_f32, c_i32, vp, c_sz, P_i32, P_f64, vp],
+    "fem_lambda_max": [c_i32, c_i32, vp, vp, c_i32, vp, vp, c_i32, vp, c_sz, vp, vp],
+    "fem_lambda_min": [c_i32, c_i32, vp, vp, c_i32, vp, vp, c_i32, c_f32, c_i32, vp, c_sz, vp, vp, vp],
 }
 
 _lib = None

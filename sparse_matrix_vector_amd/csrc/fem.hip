@@ -17,9 +17,13 @@
 // gfx950 shape of the fused kernel: one lane per element, Ke staged in LDS
 // once per workgroup and read with broadcast (same-address) LDS reads, the
 // element's 24 DOF indices read with six 16-byte loads, 24 gathers of x,
-// 576 FMAs, and 24 fp32 atomic adds (hardware global_atomic_add_f32).  The
-// beta pass runs first as a separate small kernel, because atomics only add.
+// 576 FMAs, then the contributions to the face shared with the next lane's
+// element are added in registers (wave shifts), and the rest go out as fp32
+// atomic adds (hardware global_atomic_add_f32): 12 instead of 24 per
+// element when elements are numbered x-fastest.  The beta pass runs first
+// as a separate small kernel, because atomics only add.
 #include "common.hpp"
+#include "fem_common.hpp"
 
 #include <algorithm>
 
@@ -70,10 +74,15 @@ __global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const
                                                     const float *__restrict__ x, float *__restrict__ y) {
     __shared__ __attribute__((aligned(16))) float ke[NDOF_E * NDOF_E];
     stage_ke(ke, Ke);
+    // lanes past the last element stay (the wave exchange below needs all
+    // 64) with every DOF index -1
     const int e = blockIdx.x * FE_WG + threadIdx.x;
-    if (e >= n_elem) return;
+    const bool live = e < n_elem;
+    const int ec = live ? e : n_elem - 1;
     int d[NDOF_E];
-    load_edof(edof, e, d);
+    load_edof(edof, ec, d);
+#pragma unroll
+    for (int b = 0; b < NDOF_E; ++b) d[b] = live ? d[b] : -1;
     // 24 gathers issued together (a constrained DOF reads x[0] and is zeroed
     // after), rather than one masked load at a time
     float u[NDOF_E];
@@ -81,7 +90,8 @@ __global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const
     for (int b = 0; b < NDOF_E; ++b) u[b] = x[(unsigned)d[b] < (unsigned)n_dof ? d[b] : 0];
 #pragma unroll
     for (int b = 0; b < NDOF_E; ++b) u[b] = (unsigned)d[b] < (unsigned)n_dof ? u[b] : 0.0f;
-    const float s = alpha * simp(rho[e], penalty);
+    const float s = alpha * simp(rho[ec], penalty);
+    float fa[NDOF_E];
 #pragma unroll
     for (int a = 0; a < NDOF_E; ++a) {
         float f = 0.0f;
@@ -93,8 +103,12 @@ __global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const
             f = fmaf(k4.z, u[b + 2], f);
             f = fmaf(k4.w, u[b + 3], f);
         }
-        if ((unsigned)d[a] < (unsigned)n_dof) atomicAdd(y + d[a], s * f);
+        fa[a] = s * f;
     }
+    fe_combine_x_neighbours(d, fa, n_dof);
+#pragma unroll
+    for (int a = 0; a < NDOF_E; ++a)
+        if ((unsigned)d[a] < (unsigned)n_dof) atomicAdd(y + d[a], fa[a]);
 }
 
 // ---- three-stage comparator ----

@@ -1,0 +1,166 @@
+"""GPU parity of the FE solver step (Jacobi diagonal, Jacobi-PCG, power and
+inverse iteration) against the oracle, through the C ABI.
+
+* the Jacobi diagonal within 1e-5 (relative; every term is positive) of the
+  oracle's fp64 diagonal, on the random-Ke benchmark mesh and a cantilever;
+* PCG on elasticity cantilevers: the reported residual is below rtol; the
+  true residual ||f - K u|| / ||f||, recomputed by the oracle in fp64, is
+  below 10 (rtol + floor), floor being the true residual of the exact
+  solution rounded to fp32 (what fp32 storage of u alone leaves); the compliance f.u is within 1e-4 of the fp64 solution's
+  (the page reports fp32 within 0.2% of fp64 for its solver); iteration
+  counts within 20% of the fp64 oracle's; the cap, a converged initial
+  guess, f = 0, a non-positive diagonal, and two solves agreeing;
+* largest / smallest eigenvalue of small cantilevers against LAPACK, and the
+  power-iteration sequence against the fp64 oracle's from the same start.
+"""
+import numpy as np
+import pytest
+import scipy.sparse as sp
+
+import gen
+import oracle
+from helpers import dev, host
+
+torch = pytest.importorskip("torch")
+S = pytest.importorskip("sparse_matrix_vector_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+def _op(m):
+    return (m.n_elem, m.n_dof, dev(m.edof.reshape(-1)), dev(m.rho), m.penalty, dev(m.Ke.reshape(-1)))
+
+
+def _K(m):
+    rp, ci, v = oracle.fe_assemble(m.edof, m.rho, m.Ke, m.n_dof, m.penalty)
+    return sp.csr_matrix((v, ci, rp), shape=(m.n_dof, m.n_dof))
+
+
+@pytest.mark.parametrize("which", ["bench_mesh", "cantilever"])
+def test_jacobi_diagonal(which):
+    m = gen.fe_mesh(40, 20, 10) if which == "bench_mesh" else gen.fe_cantilever(30, 10, 6)
+    d = torch.full((m.n_dof,), float("nan"), device="cuda")
+    S.fem_jacobi_diagonal(*_op(m), d)
+    torch.cuda.synchronize()
+    ref = oracle.fe_diagonal(m.edof, m.rho, m.Ke, m.n_dof, m.penalty)
+    assert np.all(np.abs(host(d) - ref) <= 1e-5 * ref)
+
+
+def _solve(m, rtol, max_iter=20000, u0=None, f=None):
+    u = dev(np.zeros(m.n_dof, np.float32) if u0 is None else u0)
+    it, rr = S.fem_pcg_solve(*_op(m), dev(m.f if f is None else f), u, rtol, max_iter)
+    return host(u), it, rr
+
+
+@pytest.mark.parametrize("dims", [(4, 2, 2), (12, 6, 3), (24, 12, 6), (40, 20, 10)])
+def test_pcg_cantilever(dims):
+    m = gen.fe_cantilever(*dims)
+    K = _K(m)
+    d = oracle.fe_diagonal(m.edof, m.rho, m.Ke, m.n_dof, m.penalty)
+    f64 = m.f.astype(np.float64)
+    rtol = 1e-6
+    u, it, rr = _solve(m, rtol)
+    ur, itr, rrr = oracle.pcg_jacobi(lambda x: K @ x, d, f64, rtol=rtol, max_iter=20000)
+    uex, _, _ = oracle.pcg_jacobi(lambda x: K @ x, d, f64, rtol=1e-12, max_iter=50000)
+    true_res = np.linalg.norm(f64 - K @ u.astype(np.float64)) / np.linalg.norm(f64)
+    # what storing the exact solution in fp32 alone leaves: the floor of any fp32 u
+    floor = np.linalg.norm(f64 - K @ uex.astype(np.float32).astype(np.float64)) / np.linalg.norm(f64)
+    c, cex = f64 @ u, f64 @ uex
+    print(f"[pcg] {dims} n_dof={m.n_dof} it={it} (fp64 {itr}) reported={rr:.3g} true={true_res:.3g} "
+          f"fp32 floor={floor:.3g} compliance rel err={abs(c - cex) / abs(cex):.3g}", flush=True)
+    assert rr <= rtol
+    assert true_res <= 10 * (rtol + floor)
+    assert abs(c - cex) <= 1e-4 * abs(cex)
+    assert abs(it - itr) <= max(3, 0.2 * itr)
+
+
+def test_pcg_cap_initial_guess_zero_rhs_and_reproducible():
+    m = gen.fe_cantilever(12, 6, 3)
+    u, it, rr = _solve(m, 0.0, max_iter=5)
+    assert it == 5 and rr > 0
+    # the matvec's atomic adds land in any order, so two solves agree to
+    # rounding, not bit for bit
+    a, ita, _ = _solve(m, 1e-6)
+    b, itb, _ = _solve(m, 1e-6)
+    f64 = m.f.astype(np.float64)
+    assert abs(ita - itb) <= 1 and abs(f64 @ a - f64 @ b) <= 1e-6 * abs(f64 @ a)
+    # a solution as the initial guess: converged before the first iteration
+    u2, it2, rr2 = _solve(m, 1e-3, u0=a)
+    assert it2 == 0 and rr2 <= 1e-3 and np.array_equal(u2, a)
+    # f = 0 from u = 0: nothing to do
+    u3, it3, rr3 = _solve(m, 1e-6, f=np.zeros(m.n_dof, np.float32))
+    assert it3 == 0 and rr3 == 0.0 and not u3.any()
+
+
+def test_pcg_rejects_non_positive_diagonal():
+    m = gen.fe_cantilever(6, 3, 2)
+    rho = m.rho.copy()
+    rho[0] = -0.5                         # rho^3 < 0 for one element: that element's DOFs lose positivity
+    m2 = gen.FEMesh(m.nx, m.ny, m.nz, m.n_elem, m.n_dof, m.edof, rho, m.Ke * 40, m.x, m.penalty, m.f)
+    d = oracle.fe_diagonal(m2.edof, m2.rho, m2.Ke, m2.n_dof, m2.penalty)
+    assert (d <= 0).any()
+    with pytest.raises(S.SpmvError) as e:
+        _solve(m2, 1e-6)
+    assert e.value.status == 2
+
+
+@pytest.mark.parametrize("dims", [(4, 2, 2), (12, 6, 3)])
+def test_extreme_eigenvalues_small(dims):
+    m = gen.fe_cantilever(*dims)
+    K = _K(m)
+    w = np.linalg.eigvalsh(K.toarray())
+    v0 = np.random.default_rng(5).standard_normal(m.n_dof).astype(np.float32)
+    lam = S.fem_lambda_max(*_op(m), dev(v0), 3000)
+    ref = oracle.power_lambda_max(lambda x: K @ x, v0.astype(np.float64), 3000)
+    print(f"[eig] {dims} lmax gpu={lam[-1]:.9g} oracle={ref[-1]:.9g} lapack={w[-1]:.9g}", flush=True)
+    assert abs(lam[-1] - w[-1]) <= 2e-3 * w[-1]
+    assert np.all(np.abs(lam[:50] - ref[:50]) <= 1e-5 * ref[:50])
+    mu, inner = S.fem_lambda_min(*_op(m), dev(v0), 8, 1e-7, 20000)
+    print(f"[eig] {dims} lmin gpu={mu[-1]:.9g} lapack={w[0]:.9g} inner={inner.tolist()}", flush=True)
+    assert abs(mu[-1] - w[0]) <= 1e-4 * w[0]
+    assert np.all(inner > 0)
+
+
+def _golden():
+    import json
+    import os
+    p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fe_cantilever.json")
+    return json.load(open(p))["cases"]
+
+
+# The fused-FE page's section 4.1: kappa(K) at rho = 0.5 by power iteration.
+PAGE_KAPPA = {"80x40x20": 6.1e5, "120x60x30": 1.3e6, "160x80x40": 2.3e6}
+
+
+@pytest.mark.parametrize("dims", [(80, 40, 20), (120, 60, 30)])
+def test_full_size_pcg_and_kappa(dims):
+    """The 64k- and 216k-element cantilevers: PCG iterations within 35% of
+    the fp64 oracle's (with fp32 vectors at kappa ~ 1e6 the iteration loses
+    orthogonality and needs 15-30% more steps than in fp64, by an amount that
+    varies with the order of the matvec's atomic adds), compliance within
+    1e-4 of the oracle's tight solve; the extreme eigenvalues within 1e-4 of
+    the oracle's from the same start vector; and kappa within 10% of the
+    page's value."""
+    key = "x".join(map(str, dims))
+    g = _golden()[key]
+    m = gen.fe_cantilever(*dims)
+    op = _op(m)
+    ws = torch.empty(S.fem_solver_workspace_size(m.n_dof, 400), dtype=torch.uint8, device="cuda")
+    u = torch.zeros(m.n_dof, device="cuda")
+    it, rr = S.fem_pcg_solve(*op, dev(m.f), u, 1e-6, 20000, workspace=ws)
+    c = float(m.f.astype(np.float64) @ host(u).astype(np.float64))
+    v0 = np.random.default_rng(5).standard_normal(m.n_dof).astype(np.float32)
+    lam = S.fem_lambda_max(*op, dev(v0), 400, workspace=ws)
+    mu, inner = S.fem_lambda_min(*op, dev(v0), 4, 1e-6, 20000, workspace=ws)
+    kappa = lam[-1] / mu[-1]
+    print(f"[pcg] {key} it={it} (fp64 {g['pcg_iterations_rtol_1e-6']}) compliance={c:.9g} "
+          f"(fp64 {g['compliance']:.9g}) lmax={lam[-1]:.9g} ({g['lambda_max_power_400']:.9g}) "
+          f"lmin={mu[-1]:.9g} ({g['lambda_min_inverse'][-1]:.9g}) kappa={kappa:.4g} page={PAGE_KAPPA[key]:.2g}",
+          flush=True)
+    assert rr <= 1e-6
+    assert abs(it - g["pcg_iterations_rtol_1e-6"]) <= 0.35 * g["pcg_iterations_rtol_1e-6"]
+    assert abs(c - g["compliance"]) <= 1e-4 * abs(g["compliance"])
+    assert abs(lam[99] - g["lambda_max_power_100"]) <= 1e-4 * g["lambda_max_power_100"]
+    assert abs(lam[-1] - g["lambda_max_power_400"]) <= 1e-4 * g["lambda_max_power_400"]
+    assert abs(mu[-1] - g["lambda_min_inverse"][-1]) <= 1e-4 * g["lambda_min_inverse"][-1]
+    assert abs(kappa - PAGE_KAPPA[key]) <= 0.1 * PAGE_KAPPA[key]
