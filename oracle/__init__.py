@@ -76,6 +76,10 @@ def lib():
             "oracle_macko_spmv": (None, [c_int, c_int, c_int, i32p, u32p, u16p, u16p, c_double, c_double, vp,
                                          f64p, f64p]),
             "oracle_macko_quantize_i8": (None, [c_int, i32p, u16p, i8p, f32p]),
+            "oracle_spgemm_ip": (None, [c_int, i32p, i32p, i32p, i64p]),
+            "oracle_spgemm_rows": (c_i64, [c_int, c_int, i32p, i32p, i32p, i32p, i64p]),
+            "oracle_spgemm_fill": (c_int, [c_int, c_int, i32p, i32p, f32p, i32p, i32p, f32p, i64p, i32p, f64p,
+                                           f64p]),
             "oracle_macko_spmv_i8": (None, [c_int, c_int, c_int, i32p, u32p, i8p, f32p, u16p, c_double, c_double,
                                             vp, f64p, f64p]),
             "oracle_gemv_f16": (None, [c_int, c_int, u16p, u16p, c_double, c_double, vp, f64p, f64p]),
@@ -341,6 +345,32 @@ def fe_assemble(edof, rho, Ke, n_dof, penalty=3):
     lib().oracle_fe_assemble(n_elem, int(n_dof), ed, r, int(penalty), K,
                              rp.ctypes.data, ci.ctypes.data, v.ctypes.data)
     return rp, ci, v
+
+
+def spgemm_ip(rp_a, ci_a, rp_b):
+    """Intermediate products per row of A*B (int64[m])."""
+    rpa = _c(rp_a, np.int32)
+    ip = np.empty(len(rpa) - 1, np.int64)
+    lib().oracle_spgemm_ip(len(rpa) - 1, rpa, _c(ci_a, np.int32), _c(rp_b, np.int32), ip)
+    return ip
+
+
+def spgemm(n_cols_b, rp_a, ci_a, v_a, rp_b, ci_b, v_b):
+    """C = A*B: (rp_c int64[m+1], ci_c int32[nnz], v_c float64[nnz], scale float64[nnz]),
+    columns increasing in each row."""
+    rpa, cia, rpb, cib = (_c(x, np.int32) for x in (rp_a, ci_a, rp_b, ci_b))
+    m = len(rpa) - 1
+    rpc = np.empty(m + 1, np.int64)
+    nnz = lib().oracle_spgemm_rows(m, int(n_cols_b), rpa, cia, rpb, cib, rpc)
+    if nnz < 0:
+        raise MemoryError("oracle_spgemm_rows")
+    cic = np.empty(max(nnz, 1), np.int32)
+    vc = np.empty(max(nnz, 1), np.float64)
+    sc = np.empty(max(nnz, 1), np.float64)
+    if lib().oracle_spgemm_fill(m, int(n_cols_b), rpa, cia, _c(v_a, np.float32), rpb, cib, _c(v_b, np.float32),
+                                rpc, cic, vc, sc) != 0:
+        raise MemoryError("oracle_spgemm_fill")
+    return rpc, cic[:nnz], vc[:nnz], sc[:nnz]
 
 
 from .solver import fe_diagonal, pcg_jacobi, power_lambda_max, inverse_lambda_min  # noqa: E402

@@ -671,3 +671,98 @@ int64_t oracle_fe_assemble(int n_elem, int n_dof, const int32_t *edof, const flo
     free(coo);
     return nnz;
 }
+
+/* ------------------------------------------------------------------------ */
+/* SpGEMM C = A * B ("Sparse matrix multiplication acceleration techniques", */
+/* the hash-based multi-phase SpGEMM page, sections 1.1 and 2.1).           */
+/* The product's definition: C_ij = sum_k A_ik B_kj.  Row i of C needs, for */
+/* each stored A_ik, row k of B: its intermediate products (IP) number      */
+/* sum over k in row i of A of nnz(B row k) (section 2.1.1 bins rows by     */
+/* this count).  The oracle is Gustavson's row-by-row form with a dense    */
+/* fp64 accumulator over the columns of B and a marker per column; each    */
+/* row of C lists its distinct columns in increasing order (the method     */
+/* leaves the order open; sorted is the canonical CSR).  Entries that sum  */
+/* to zero are kept: the pattern is the set of columns reached.            */
+/* ------------------------------------------------------------------------ */
+void oracle_spgemm_ip(int m, const int32_t *rpa, const int32_t *cia, const int32_t *rpb, int64_t *ip)
+{
+    for (int i = 0; i < m; ++i) {
+        int64_t s = 0;
+        for (int32_t j = rpa[i]; j < rpa[i + 1]; ++j) s += rpb[cia[j] + 1] - rpb[cia[j]];
+        ip[i] = s;
+    }
+}
+
+static int oracle_cmp_i32(const void *a, const void *b)
+{
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* Row counts of C into rpc (rpc[0] = 0, rpc[i+1] = rpc[i] + distinct columns
+ * of row i); returns nnz(C), or -1 if n < 1 with a nonempty product. */
+int64_t oracle_spgemm_rows(int m, int n, const int32_t *rpa, const int32_t *cia,
+                           const int32_t *rpb, const int32_t *cib, int64_t *rpc)
+{
+    int32_t *mark = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    if (!mark) return -1;
+    for (int c = 0; c < n; ++c) mark[c] = -1;
+    rpc[0] = 0;
+    for (int i = 0; i < m; ++i) {
+        int64_t cnt = 0;
+        for (int32_t j = rpa[i]; j < rpa[i + 1]; ++j) {
+            int32_t k = cia[j];
+            for (int32_t t = rpb[k]; t < rpb[k + 1]; ++t)
+                if (mark[cib[t]] != i) {
+                    mark[cib[t]] = i;
+                    cnt++;
+                }
+        }
+        rpc[i + 1] = rpc[i] + cnt;
+    }
+    free(mark);
+    return rpc[m];
+}
+
+/* Fills cic[nnz(C)] (sorted per row) and vc[nnz(C)] = sum_k A_ik B_kj in fp64,
+ * and scale[nnz(C)] = sum_k |A_ik B_kj| (the error scale of each entry);
+ * rpc from oracle_spgemm_rows.  Returns 0, or -1 on allocation failure. */
+int oracle_spgemm_fill(int m, int n, const int32_t *rpa, const int32_t *cia, const float *va,
+                       const int32_t *rpb, const int32_t *cib, const float *vb,
+                       const int64_t *rpc, int32_t *cic, double *vc, double *scale)
+{
+    double *acc = (double *)calloc((size_t)(n > 0 ? n : 1), sizeof(double));
+    double *mag = (double *)calloc((size_t)(n > 0 ? n : 1), sizeof(double));
+    int32_t *mark = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    if (!acc || !mag || !mark) {
+        free(acc); free(mag); free(mark);
+        return -1;
+    }
+    for (int c = 0; c < n; ++c) mark[c] = -1;
+    for (int i = 0; i < m; ++i) {
+        int64_t at = rpc[i];
+        for (int32_t j = rpa[i]; j < rpa[i + 1]; ++j) {
+            int32_t k = cia[j];
+            double a = va[j];
+            for (int32_t t = rpb[k]; t < rpb[k + 1]; ++t) {
+                int32_t c = cib[t];
+                if (mark[c] != i) {
+                    mark[c] = i;
+                    cic[at++] = c;
+                    acc[c] = 0.0;
+                    mag[c] = 0.0;
+                }
+                double p = a * (double)vb[t];
+                acc[c] += p;
+                mag[c] += fabs(p);
+            }
+        }
+        qsort(cic + rpc[i], (size_t)(rpc[i + 1] - rpc[i]), sizeof(int32_t), oracle_cmp_i32);
+        for (int64_t e = rpc[i]; e < rpc[i + 1]; ++e) {
+            vc[e] = acc[cic[e]];
+            if (scale) scale[e] = mag[cic[e]];
+        }
+    }
+    free(acc); free(mag); free(mark);
+    return 0;
+}
