@@ -28,6 +28,10 @@ Other workloads (parity-test configs, also used for profiles):
            codes instead of 4, macko-i8 and macko-i8-bN for int8 values)
   (varlen: 1M rows of 2..10 entries in a +-1000 band, CV 0.43, the HYB range
   of the CV rule; auto: the format that rule picks)
+  powerlaw | laplacian / spgemm: C = A * A by the hash-based multi-phase
+  SpGEMM; one step = one whole product (row grouping, allocation phase,
+  accumulation phase into fresh output), host-synchronous, as a caller runs
+  it; the accumulation phase alone is also timed with HIP events.
   cantilever / fem-pcg: Jacobi-PCG on the 216k-element elasticity cantilever
   (rho = 0.5); one step = one PCG iteration (fixed count, rtol = 0), timed
   warm, as a solver runs it; the line also carries a solve to rtol 1e-6 and
@@ -62,13 +66,14 @@ OTHER_PATHS = {"laplacian": ("ell",)}
 KERNEL = {"csr": "k_csr_tasks", "csr-binned": "k_csr_tasks", "csr-vector": "k_csr_vector",
           "csr-scalar": "k_csr_scalar", "ell": "k_ell_apply4t", "macko": "k_macko_spmv",
           "dense": "k_gemv_f16", "fem": "k_fe_fused", "fem-3stage": "k_fe_elem", "hyb": "k_ell_apply",
-          "auto": None, "fem-pcg": "k_fe_matvec64 + k_pcg_alpha + k_pcg_update + k_pcg_direction"}
+          "auto": None, "fem-pcg": "k_fe_matvec64 + k_pcg_pq + k_pcg_update + k_pcg_direction",
+          "spgemm": "k_sg_* (grouping, allocation, accumulation)"}
 
 # source file of each path's kernels (for the traffic-record freshness check)
 SOURCE = {"csr": ("csr.hip",), "csr-binned": ("csr.hip",), "csr-vector": ("csr.hip",),
           "csr-scalar": ("csr.hip",), "ell": ("ell.hip",), "macko": ("macko.hip",), "dense": ("dense.hip",),
           "fem": ("fem.hip",), "fem-3stage": ("fem.hip",), "hyb": ("ell.hip", "hyb.hip"),
-          "auto": ("csr.hip", "ell.hip", "hyb.hip"), "fem-pcg": ("fem_solver.hip",)}
+          "auto": ("csr.hip", "ell.hip", "hyb.hip"), "fem-pcg": ("fem_solver.hip",), "spgemm": ("spgemm.hip",)}
 for _v in ("b1", "b2", "b8", "i8", "i8-b1", "i8-b2", "i8-b8"):
     KERNEL["macko-" + _v] = "k_macko_spmv"
     SOURCE["macko-" + _v] = ("macko.hip",)
@@ -529,6 +534,113 @@ def bench_pcg(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_spgemm(args):
+    """One JSON line for C = A * A (see the module docstring)."""
+    import numpy as np
+    import torch
+    import gen
+    import sparse_matrix_vector_amd as S
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    A = gen.powerlaw_csr() if args.config == "powerlaw" else gen.laplacian_2d(1000, with_x=False)
+    workload = {"powerlaw": "powerlaw_916428_zipf1.9931", "laplacian": "laplacian_2d_1000x1000"}[args.config]
+    arrs = [dev(A.row_ptr), dev(A.col_idx), dev(A.vals)]
+    m = A.n_rows
+    steps = max(1, min(args.steps, 20))
+
+    def full():
+        G = S.SpGEMM(m, A.n_cols, A.n_cols, *arrs, *arrs)
+        out = G.compute()
+        torch.cuda.synchronize()
+        return G, out
+    for _ in range(max(1, min(args.warmup, 3))):
+        G, out = full()
+        G.close()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        G, out = full()
+        G.close()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    G, out = full()
+    nnz_c, ip, groups = G.nnz, G.intermediate_products, G.group_rows
+    # the accumulation phase alone, HIP events on the stream
+    stream = torch.cuda.current_stream()
+    k = max(10, min(args.steps, 100))
+    G.compute(out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(k):
+        G.compute(out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_acc = e0.elapsed_time(e1) / k
+    # bytes the accumulation phase must move: A (row pointers, columns, values), the reached rows of B (their
+    # row-pointer pairs, and columns and values once per intermediate product), and C written once
+    nnz = A.nnz
+    nbytes = 4 * (m + 1) + 8 * nnz + 8 * nnz + 8 * ip + 4 * (m + 1) + 8 * nnz_c
+    flops = 2 * ip
+    gbs_acc = nbytes / (ms_acc * 1e-3) / 1e9
+    par = None
+    if not args.no_parity:
+        import oracle
+        rp, ci, v = (t.cpu().numpy() for t in out)
+        ipr = oracle.spgemm_ip(A.row_ptr, A.col_idx, A.row_ptr)
+        g = np.digitize(ipr, [32, 512, 8192])
+        rng = np.random.default_rng(11)
+        rows = np.sort(np.concatenate([np.flatnonzero(g == q) if (g == q).sum() <= 300 else
+                                       rng.choice(np.flatnonzero(g == q), 300, replace=False) for q in range(4)]))
+        sub_rp = np.concatenate([[0], np.cumsum(A.row_ptr[rows + 1] - A.row_ptr[rows])]).astype(np.int32)
+        sub_ci = np.concatenate([A.col_idx[A.row_ptr[r]:A.row_ptr[r + 1]] for r in rows])
+        sub_v = np.concatenate([A.vals[A.row_ptr[r]:A.row_ptr[r + 1]] for r in rows])
+        orp, oci, ov, osc = oracle.spgemm(A.n_cols, sub_rp, sub_ci, sub_v, A.row_ptr, A.col_idx, A.vals)
+        ok, worst = True, 0.0
+        for q, r in enumerate(rows):
+            a, b = rp[r], rp[r + 1]
+            oa, ob = orp[q], orp[q + 1]
+            ok = ok and (b - a == ob - oa) and np.array_equal(ci[a:b], oci[oa:ob])
+            if ok and ob > oa:
+                e = np.abs(v[a:b].astype(np.float64) - ov[oa:ob])
+                ok = ok and bool(np.all(e <= 1e-5 * osc[oa:ob]))
+                worst = max(worst, float(np.max(e / np.maximum(osc[oa:ob], 1e-300))))
+        par = {"ok": bool(ok and rp[-1] == nnz_c), "rows_checked": int(len(rows)), "tau": 1e-5,
+               "max_err_over_scale": worst}
+    G.close()
+    line = {
+        "metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e9, 3), "unit": "GFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": max(1, min(args.warmup, 3)), "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded generators in gen/)",
+        "config": {"workload": workload, "path": "spgemm", "product": "C = A * A", "n_rows": m, "nnz_a": nnz,
+                   "intermediate_products": ip, "nnz_c": nnz_c, "ip_groups": groups,
+                   "step": "one whole product (grouping, allocation, accumulation), host-synchronous",
+                   "timing": "host clock around synchronous products; accumulation phase: HIP events",
+                   "algorithmic_bytes_accumulation": nbytes, "flops": flops},
+        "accumulation_phase": {"ms": round(ms_acc, 6), "gflops": round(flops / (ms_acc * 1e-3) / 1e9, 3),
+                               "effective_gbs": round(gbs_acc, 2)},
+        "effective_gbs": round(gbs_acc, 2), "pct_hbm_peak": round(100 * gbs_acc / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs_acc, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs_acc / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "accumulation phase (k_sg_g0_fill, k_sg_tb_fill, k_sg_g3_fill)"},
+        "parity": par,
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+        n_sample, t0 = 0, time.time()
+        while time.time() - t0 < args.cpu_seconds and n_sample < m:
+            r0, r1 = n_sample, min(m, n_sample + 50000)
+            base = A.row_ptr[r0]
+            sub_rp = (A.row_ptr[r0:r1 + 1] - base).astype(np.int32)
+            oracle.spgemm(A.n_cols, sub_rp, A.col_idx[base:A.row_ptr[r1]], A.vals[base:A.row_ptr[r1]],
+                          A.row_ptr, A.col_idx, A.vals)
+            n_sample = r1
+        el = time.time() - t0
+        ip_s = int(oracle.spgemm_ip(A.row_ptr[:n_sample + 1], A.col_idx, A.row_ptr).sum())
+        line["cpu_baseline"] = {"value": round(2 * ip_s / el / 1e9, 4), "unit": "GFLOP/s", "cores": 1,
+                                "kind": "oracle", "sample": f"rows 0..{n_sample} of the same product "
+                                f"({ip_s} intermediate products, {el:.1f} s)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -559,6 +671,11 @@ def main():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(2)
     path = args.path or DEFAULT_PATH[args.config]
+    if path == "spgemm":
+        if args.config not in ("powerlaw", "laplacian"):
+            raise SystemExit("the spgemm path runs on the powerlaw and laplacian configs")
+        bench_spgemm(args)
+        return
     if args.config == "cantilever" or path == "fem-pcg":
         if args.config != "cantilever" or path != "fem-pcg":
             raise SystemExit("the fem-pcg path runs on the cantilever config only")

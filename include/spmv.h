@@ -396,6 +396,51 @@ spmv_status fem_lambda_min(int32_t n_elem, int32_t n_dof, const int32_t *edof, c
                            float inner_rtol, int32_t inner_max_iter, void *workspace, size_t workspace_bytes,
                            double *h_lambda, int32_t *h_inner_iterations, void *stream);
 
+/* ======================================================================== */
+/* SpGEMM C = A * B ("Sparse matrix multiplication acceleration techniques", */
+/* the hash-based multi-phase SpGEMM page, section 2): rows grouped by their */
+/* intermediate products (IP = the total length of the rows of B that a row */
+/* of A reaches; groups 0-31, 32-511, 512-8191, >= 8192, section 2.1.1), an */
+/* allocation phase that counts each row's distinct columns with hash       */
+/* tables (section 2.2), and an accumulation phase that adds the products   */
+/* (section 2.3).  A is m x k, B is k x n, both CSR with int32 indices and  */
+/* fp32 values on the device; columns in a row may come in any order and   */
+/* repeat.  C is CSR with each row's distinct columns in increasing order;  */
+/* a column that is reached is stored even when its products cancel to 0.   */
+/* ======================================================================== */
+typedef struct spgemm *spgemm_t;
+
+/* Workspace bytes for spgemm_create on these A and B (device arrays).
+ * Validates both (SPMV_ERR_INVALID_MATRIX for a row_ptr that is not
+ * monotone from 0 to nnz or a column out of range).  Synchronises. */
+spmv_status spgemm_workspace_size(int32_t m, int32_t k, int32_t n, int32_t nnz_a, const int32_t *rp_a,
+                                  const int32_t *ci_a, int32_t nnz_b, const int32_t *rp_b,
+                                  const int32_t *ci_b, size_t *bytes, void *stream);
+
+/* Grouping and allocation phase: validates, counts the distinct columns of
+ * every row of C and their offsets.  The handle borrows A, B and the
+ * workspace (device, 256-byte aligned, at least spgemm_workspace_size
+ * bytes) until spgemm_destroy.  SPMV_ERR_OVERFLOW if nnz(C) exceeds int32.
+ * Synchronises. */
+spmv_status spgemm_create(spgemm_t *h, int32_t m, int32_t k, int32_t n, int32_t nnz_a, const int32_t *rp_a,
+                          const int32_t *ci_a, const float *v_a, int32_t nnz_b, const int32_t *rp_b,
+                          const int32_t *ci_b, const float *v_b, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* nnz(C), the total intermediate products, and the rows per IP group
+ * (group_rows: int32[4]); any output may be NULL.  Host only. */
+spmv_status spgemm_info(spgemm_t h, int64_t *nnz_c, int64_t *intermediate_products, int32_t *group_rows);
+
+/* Accumulation phase: rp_c int32[m+1], ci_c int32[nnz(C)], v_c fp32[nnz(C)]
+ * (device, caller-owned).  Uses the current values of A and B, so it may be
+ * repeated after they change with the same patterns.  fp32 products summed
+ * by atomic adds: values agree with the exact sum to rounding, in an order
+ * that varies.  Asynchronous; allocates nothing. */
+spmv_status spgemm_compute(spgemm_t h, int32_t *rp_c, int32_t *ci_c, float *v_c, void *stream);
+
+/* Releases the handle (not the workspace or the borrowed arrays). */
+spmv_status spgemm_destroy(spgemm_t h);
+
 #ifdef __cplusplus
 }
 #endif

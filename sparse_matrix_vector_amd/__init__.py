@@ -27,7 +27,8 @@ __all__ = [
     "spmv_ell_from_csr", "spmv_ell_apply", "macko_encode_size", "macko_encode", "macko_spmv",
     "macko_quantize_i8", "macko_spmv_i8", "macko_decode_columns", "dense_gemv_f16", "fem_matvec_apply", "fem_threestage_size",
     "fem_matvec_threestage", "fem_jacobi_diagonal", "fem_solver_workspace_size", "fem_pcg_solve",
-    "fem_lambda_max", "fem_lambda_min", "CSRMatrix",
+    "fem_lambda_max", "fem_lambda_min", "spgemm_workspace_size", "spgemm_create", "spgemm_info",
+    "spgemm_compute", "spgemm_destroy", "SpGEMM", "CSRMatrix",
 ]
 
 STATUS = {0: "SPMV_OK", 1: "SPMV_ERR_INVALID_VALUE", 2: "SPMV_ERR_INVALID_MATRIX",
@@ -372,6 +373,82 @@ class AutoMatrix:
     def close(self):
         if getattr(self, "handle", None):
             spmv_auto_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------------------------------
+# SpGEMM C = A * B (hash-based, multi-phase)
+# ---------------------------------------------------------------------------
+def spgemm_workspace_size(m, k, n, rp_a, ci_a, rp_b, ci_b, stream=None) -> int:
+    out = ctypes.c_size_t()
+    _call("spgemm_workspace_size", int(m), int(k), int(n), int(ci_a.numel()), _dev(rp_a, _i32_dtype(), "rp_a"),
+          _dev(ci_a, _i32_dtype(), "ci_a"), int(ci_b.numel()), _dev(rp_b, _i32_dtype(), "rp_b"),
+          _dev(ci_b, _i32_dtype(), "ci_b"), ctypes.byref(out), _stream(stream, rp_a))
+    return out.value
+
+
+def spgemm_create(m, k, n, rp_a, ci_a, v_a, rp_b, ci_b, v_b, workspace, stream=None):
+    """Handle (int) after the grouping and allocation phases.  Synchronises."""
+    h = ctypes.c_void_p()
+    _call("spgemm_create", ctypes.byref(h), int(m), int(k), int(n), int(ci_a.numel()),
+          _dev(rp_a, _i32_dtype(), "rp_a"), _dev(ci_a, _i32_dtype(), "ci_a"), _dev(v_a, _f32_dtype(), "v_a"),
+          int(ci_b.numel()), _dev(rp_b, _i32_dtype(), "rp_b"), _dev(ci_b, _i32_dtype(), "ci_b"),
+          _dev(v_b, _f32_dtype(), "v_b"), workspace.data_ptr(), int(workspace.numel()), _stream(stream, rp_a))
+    return h.value
+
+
+def spgemm_info(handle):
+    """(nnz_c, intermediate products, rows per IP group [4])."""
+    nnz, ip = ctypes.c_int64(), ctypes.c_int64()
+    g = (ctypes.c_int32 * 4)()
+    _call("spgemm_info", handle, ctypes.byref(nnz), ctypes.byref(ip), g)
+    return nnz.value, ip.value, list(g)
+
+
+def spgemm_compute(handle, rp_c, ci_c, v_c, stream=None):
+    _call("spgemm_compute", handle, _dev(rp_c, _i32_dtype(), "rp_c"),
+          _dev(ci_c, _i32_dtype(), "ci_c", allow_none=True) if ci_c is not None and ci_c.numel() else None,
+          _dev(v_c, _f32_dtype(), "v_c", allow_none=True) if v_c is not None and v_c.numel() else None,
+          _stream(stream, rp_c))
+
+
+def spgemm_destroy(handle):
+    _call("spgemm_destroy", handle)
+
+
+class SpGEMM:
+    """C = A * B for device CSR matrices (A m x k, B k x n): the grouping and
+    allocation phases run at construction; compute() runs the accumulation
+    phase into new (or given) output tensors."""
+
+    def __init__(self, m, k, n, rp_a, ci_a, v_a, rp_b, ci_b, v_b, stream=None):
+        import torch
+        self.m, self.k, self.n = int(m), int(k), int(n)
+        self._arrays = (rp_a, ci_a, v_a, rp_b, ci_b, v_b)      # borrowed by the handle
+        nbytes = spgemm_workspace_size(m, k, n, rp_a, ci_a, rp_b, ci_b, stream)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=rp_a.device)
+        self.handle = spgemm_create(m, k, n, rp_a, ci_a, v_a, rp_b, ci_b, v_b, self.workspace, stream)
+        self.nnz, self.intermediate_products, self.group_rows = spgemm_info(self.handle)
+
+    def compute(self, out=None, stream=None):
+        import torch
+        dev = self._arrays[0].device
+        if out is None:
+            out = (torch.empty(self.m + 1, dtype=torch.int32, device=dev),
+                   torch.empty(self.nnz, dtype=torch.int32, device=dev),
+                   torch.empty(self.nnz, dtype=torch.float32, device=dev))
+        spgemm_compute(self.handle, *out, stream)
+        return out
+
+    def close(self):
+        if getattr(self, "handle", None):
+            spgemm_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

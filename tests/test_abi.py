@@ -179,6 +179,14 @@ def test_host_validation_before_any_gpu_call():
     assert L.fem_matvec_apply(4, 10, 16, 16, 9, 16, 1.0, 16, 0.0, 16, None) == 1   # penalty > 8
     assert L.fem_matvec_apply(4, 10, 20, 16, 3, 16, 1.0, 16, 0.0, 16, None) == 5   # edof misaligned
     assert L.fem_matvec_threestage(4, 10, 16, 16, 3, 16, 1.0, 16, 0.0, 16, None, 0, None) == 1
+    h = ctypes.c_void_p()
+    assert L.spgemm_create(None, 1, 1, 1, 0, 16, None, None, 0, 16, None, None, 16, 1 << 20, None) == 1
+    assert L.spgemm_create(ctypes.byref(h), -1, 1, 1, 0, 16, None, None, 0, 16, None, None, 16, 1 << 20, None) == 1
+    assert L.spgemm_create(ctypes.byref(h), 2, 2, 2, 3, 16, None, 16, 0, 16, None, None, 16, 1 << 20, None) == 1
+    assert L.spgemm_info(None, None, None, None) == 1
+    assert L.spgemm_compute(None, None, None, None, None) == 1
+    assert L.spgemm_workspace_size(1, 1, 1, 0, None, None, 0, 16, None, ctypes.byref(ctypes.c_size_t()), None) == 1
+    assert L.spgemm_destroy(None) == 0
     # n_rows == 0 applies are no-ops that succeed without touching the GPU
     assert L.macko_spmv(0, 4, 4, None, None, None, 1.0, None, 0.0, None, None) == 0
     assert L.macko_spmv_i8(0, 4, 1, None, None, None, None, 1.0, None, 0.0, None, None) == 0
