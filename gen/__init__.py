@@ -205,6 +205,22 @@ def random_csr(n_rows: int, n_cols: int, lens, seed: int, sorted_cols: bool = Tr
 # ---------------------------------------------------------------------------
 # Moderate row-length variation (the HYB regime of the CV rule)
 # ---------------------------------------------------------------------------
+def stencil_csr(n: int, offsets, seed: int) -> CSR:
+    """Row i holds columns i + d for each offset d (those inside [0, n)),
+    ascending; values and x uniform in [-1, 1].  A banded matrix whose
+    entries fall in a few narrow bands far apart (edge-case tests)."""
+    rng = np.random.default_rng(seed)
+    offs = np.unique(np.asarray(offsets, dtype=np.int64))
+    cand = np.arange(n, dtype=np.int64)[:, None] + offs[None, :]
+    mask = (cand >= 0) & (cand < n)
+    lens = mask.sum(axis=1)
+    cols = cand[mask].astype(np.int32)
+    rp = _rows_from_lengths(lens)
+    vals = rng.uniform(-1.0, 1.0, len(cols)).astype(np.float32)
+    x = rng.uniform(-1.0, 1.0, n).astype(np.float32)
+    return CSR(n, n, rp, cols, vals, x, {"name": f"stencil{n}", "offsets": offs.tolist(), "seed": seed})
+
+
 def varlen_banded(n: int = 1_000_000, lo: int = 2, hi: int = 10, band: int = 1000, seed: int = 6) -> CSR:
     """Square matrix whose row lengths are uniform on {lo..hi} (for 2..10:
     mean 6, CV = sqrt(80/12)/6 = 0.430, inside the HYB range 0.3..0.7), with

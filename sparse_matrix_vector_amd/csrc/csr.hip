@@ -56,6 +56,18 @@ constexpr int MAX_T0 = 256;             // largest supported bound of group 0
 constexpr int TWAVES = SPMV_TASK_WAVES;  // waves per workgroup of the task kernel
 constexpr int TWG = 64 * TWAVES;
 constexpr int X_TILE_MAX = 6144;        // largest x window staged in LDS per block workgroup (floats)
+constexpr int X_SEG = 32;               // floats per segment of an x window (one 128-byte line)
+constexpr int X_SEG_WORDS = X_TILE_MAX / X_SEG / 32;
+static_assert(X_TILE_MAX % (32 * X_SEG) == 0, "whole mask words");
+
+// Column window of one block workgroup: the smallest and largest column of
+// its entries and, over the window from the X_SEG-float boundary below the
+// smallest column, one bit per X_SEG-float segment holding a column of its
+// entries (all ones when the window is wider than X_TILE_MAX).
+struct __attribute__((aligned(16))) XWindow {
+    int lo, hi;
+    unsigned seg[X_SEG_WORDS];
+};
 
 // Error bits raised by the validation kernels.
 constexpr int ERR_RP0 = 1, ERR_RPN = 2, ERR_MONO = 4, ERR_COL = 8;
@@ -400,25 +412,25 @@ __global__ __launch_bounds__(WG) void k_rowtasks_write(const Meta *__restrict__ 
     }
 }
 
-// Column window of each block workgroup (blocks 4q .. 4q + 3 of the short-row
-// blocks, the blocks one workgroup of the task kernel applies): the smallest
-// and largest column of their entries.  max_window gets the largest span
-// counted from the 16-byte boundary below the smallest column.
+// Column window of each block workgroup (blocks TWAVES q .. TWAVES q + TWAVES - 1
+// of the short-row blocks, the blocks one workgroup of the task kernel
+// applies): its smallest and largest column, and which X_SEG-float segments
+// of the window its entries touch.  max_window gets the largest span counted
+// from the X_SEG-float boundary below the smallest column.
 __global__ __launch_bounds__(TWG) void k_block_spans(Meta *__restrict__ meta, const i32x4 *__restrict__ tasks,
-                                                     const int *__restrict__ ci, int2 *__restrict__ spans) {
+                                                     const int *__restrict__ ci, XWindow *__restrict__ spans) {
     __shared__ int lo[TWAVES], hi[TWAVES];
+    __shared__ unsigned segs[X_SEG_WORDS];
     const int nb = meta->block_totals[1];
     const int first = meta->row_task_totals[1];
     const int lane = __lane_id(), wv = threadIdx.x / 64;
     const int b = blockIdx.x * TWAVES + wv;
+    const i32x4 d = b < nb ? tasks[first + b] : i32x4{0, 0, 0, 0};
     int mn = INT_MAX, mx = -1;
-    if (b < nb) {
-        const i32x4 d = tasks[first + b];
-        for (int k = d.z + lane; k < d.w; k += 64) {
-            const int c = ci[k];
-            mn = min(mn, c);
-            mx = max(mx, c);
-        }
+    for (int k = d.z + lane; k < d.w; k += 64) {
+        const int c = ci[k];
+        mn = min(mn, c);
+        mx = max(mx, c);
     }
     for (int off = 32; off > 0; off >>= 1) {
         mn = min(mn, __shfl_xor(mn, off));
@@ -428,14 +440,27 @@ __global__ __launch_bounds__(TWG) void k_block_spans(Meta *__restrict__ meta, co
         lo[wv] = mn;
         hi[wv] = mx;
     }
+    if ((int)threadIdx.x < X_SEG_WORDS) segs[threadIdx.x] = 0u;
+    __syncthreads();
+    for (int w = 0; w < TWAVES; ++w) {
+        mn = min(mn, lo[w]);
+        mx = max(mx, hi[w]);
+    }
+    const int tb = mn & ~(X_SEG - 1);
+    const bool fits = mx >= 0 && mx + 1 - tb <= X_TILE_MAX;
+    if (fits)
+        for (int k = d.z + lane; k < d.w; k += 64) {
+            const int sg = (ci[k] - tb) / X_SEG;
+            atomicOr(&segs[sg >> 5], 1u << (sg & 31));
+        }
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < TWAVES; ++w) {
-            mn = min(mn, lo[w]);
-            mx = max(mx, hi[w]);
-        }
-        spans[blockIdx.x] = int2{mn, mx};
-        if (mx >= 0) atomicMax(&meta->max_window, mx + 1 - (mn & ~3));
+        XWindow w;
+        w.lo = mn;
+        w.hi = mx;
+        for (int i = 0; i < X_SEG_WORDS; ++i) w.seg[i] = fits ? segs[i] : ~0u;
+        spans[blockIdx.x] = w;
+        if (mx >= 0) atomicMax(&meta->max_window, mx + 1 - tb);
     }
 }
 
@@ -531,13 +556,16 @@ __device__ __forceinline__ void stage_streams(const TaskArgs &a, const Arrays &m
 // x[c] (and rp[i]) through a buffer resource when the array is below 4 GiB:
 // a 32-bit byte offset per lane instead of 64-bit address arithmetic.
 constexpr int BUF_DWORD3 = 0x00020000;   // gfx9-family buffer resource word 3 (raw 32-bit data)
+// A buffer offset that is out of range for every x below 2 GiB (a load there
+// returns zeros and touches no memory) and inside any larger x.
+constexpr int X_OOB = 0x7FFFFFF0;
 
 template <bool BUF>
 struct Gather {
     const float *__restrict__ p;
     __amdgpu_buffer_rsrc_t r;
     __device__ __forceinline__ Gather(const float *ptr, int n) : p(ptr) {
-        if (BUF) r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(ptr), 0, n * 4, BUF_DWORD3);
+        if (BUF) r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(ptr), 0, (int)(4u * (unsigned)n), BUF_DWORD3);
     }
     __device__ __forceinline__ float operator[](int i) const {
         // the builtin returns the loaded bits as an unsigned integer
@@ -545,15 +573,20 @@ struct Gather {
     }
 };
 
+// Cache-policy operand of a buffer load: non-temporal, for data a pass reads
+// once (the row starts of short blocks, like the column and value streams).
+constexpr int CPOL_NT = 2;
+
 template <bool BUF>
 struct GatherI {
     const int *__restrict__ p;
     __amdgpu_buffer_rsrc_t r;
     __device__ __forceinline__ GatherI(const int *ptr, int n) : p(ptr) {
-        if (BUF) r = __builtin_amdgcn_make_buffer_rsrc(const_cast<int *>(ptr), 0, n * 4, BUF_DWORD3);
+        if (BUF) r = __builtin_amdgcn_make_buffer_rsrc(const_cast<int *>(ptr), 0, (int)(4u * (unsigned)n), BUF_DWORD3);
     }
     __device__ __forceinline__ int operator[](int i) const {
-        return BUF ? __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0)) : p[i];
+        return BUF ? __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, CPOL_NT))
+                   : __builtin_nontemporal_load(p + i);
     }
 };
 
@@ -640,20 +673,20 @@ __device__ __forceinline__ void finish_row(const TaskArgs &a, i32x4 d, int t, co
 //            would need device-scope release/acquire fences, which write
 //            back and invalidate the whole L2 of an XCD on this part.)
 // BUF: x and row_ptr are below 4 GiB and gathered with buffer loads.
-// XTR > 0: the four blocks of a block workgroup span at most XTR * 4 * TWG
-// columns
-// (spans[q], from the plan).  The workgroup stages that window of x into
-// LDS with 16-byte loads, issued after each wave's own stream loads, and
-// the gathers read LDS: a 16-byte load moves four x values through the
-// texture addresser where a gather moves one.  The section "x caching in
-// shared memory" of "Why SpMV needs CUDA optimisation" (section 3.1)
-// suggests this; here it is used whenever the plan finds narrow windows.
+// XTR > 0: the TWAVES blocks of a block workgroup span at most
+// XTR * 4 * TWG columns (spans[q], from the plan).  The workgroup stages the
+// segments of that window of x that its entries touch into LDS with 16-byte
+// loads, issued after each wave's own stream loads, and the gathers read
+// LDS: a 16-byte load moves four x values through the texture addresser
+// where a gather moves one.  The section "x caching in shared memory" of
+// "Why SpMV needs CUDA optimisation" (section 3.1) suggests this; here it
+// is used whenever the plan finds narrow windows.
 template <bool VEC, bool BUF, int XTR>
 __global__ __launch_bounds__(TWG) void k_csr_tasks(TaskArgs a, const i32x4 *__restrict__ tasks,
                                                   const int *__restrict__ rp, const int *__restrict__ ci,
                                                   const float *__restrict__ v, const float *__restrict__ x,
                                                   float *__restrict__ y, const int *__restrict__ ymap,
-                                                  float *__restrict__ partials, const int2 *__restrict__ spans) {
+                                                  float *__restrict__ partials, const XWindow *__restrict__ spans) {
     constexpr bool XT = XTR > 0;
     // 8 slack entries: a row's 8-entry reads never need clamping
     __shared__ __attribute__((aligned(16))) float stage[TWAVES][SLOTS + 8];
@@ -696,7 +729,7 @@ __global__ __launch_bounds__(TWG) void k_csr_tasks(TaskArgs a, const i32x4 *__re
     if (!XT && !have) return;
     const int t = a.n_row_tasks + wb;
     // the workgroup's column window (XT), read together with the descriptor
-    const int2 sp = XT ? spans[qw] : int2{0, -1};
+    const XWindow sp = XT ? spans[qw] : XWindow{0, -1, {}};
     // a wave without a block (XT only) still helps stage the tile: it loads
     // a dummy task (the first entries of the arrays)
     const i32x4 d = have ? tasks[t] : i32x4{0, 0, 0, 0};
@@ -709,17 +742,34 @@ __global__ __launch_bounds__(TWG) void k_csr_tasks(TaskArgs a, const i32x4 *__re
     stage_streams<VEC>(a, m, d, lane, cur);
     __builtin_amdgcn_sched_barrier(0);
     if (XT) {
-        // the workgroup's window of x, from the 16-byte boundary below its
-        // smallest column (a workgroup without entries stages x[0..3])
-        const int tb = sp.y >= 0 ? (sp.x & ~3) : 0;
-        const int nvec = sp.y >= 0 ? (sp.y + 4 - tb) >> 2 : 1;
+        // the workgroup's window of x, from the X_SEG-float boundary below
+        // its smallest column (a workgroup without entries stages x[0..3])
+        const int tb = sp.hi >= 0 ? (sp.lo & ~(X_SEG - 1)) : 0;
+        const int nvec = sp.hi >= 0 ? (sp.hi + 4 - tb) >> 2 : 1;
         // XTR rounds of 16-byte loads: enough for the widest window of the
         // matrix; threads past a window's end load and store its last
-        // vector again
+        // vector again.  Only segments holding a column of the workgroup's
+        // entries are read (a banded matrix touches a few bands of its
+        // window): the other lanes get a buffer offset past the end of x,
+        // which the hardware answers with zeros and no memory access, so
+        // the loads need no branch.
+        // Round u of wave wv covers vectors 64 wv + u TWG .. + 63, i.e. the
+        // 8 segments from 8 wv + 32 u TWAVES / 4: one mask word for the
+        // wave, picked without per-lane selects, and one bit per 8 lanes.
+        // Threads past the window's end re-load its last vector, which holds
+        // the largest column and must be read.
+        static_assert(X_SEG == 32 && TWAVES % 4 == 0, "segment word layout");
+        __builtin_assume(wv >= 0 && wv < TWAVES);
         f32x4 tv[XTR > 0 ? XTR : 1];
 #pragma unroll
-        for (int u = 0; u < XTR; ++u)
-            tv[u] = *reinterpret_cast<const f32x4 *>(x + tb + 4 * min((int)threadIdx.x + u * TWG, nvec - 1));
+        for (int u = 0; u < XTR; ++u) {
+            const int iu = (int)threadIdx.x + u * TWG;
+            const int i = min(iu, nvec - 1);
+            const unsigned word = sp.seg[u * (TWAVES / 4) + (wv >> 2)];
+            const bool need = iu >= nvec || ((word >> ((8 * wv + lane / 8) & 31)) & 1u);
+            const int off = need ? (int)(4u * (unsigned)(tb + 4 * i)) : X_OOB;
+            tv[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xg.r, off, 0, 0));
+        }
 #pragma unroll
         for (int u = 0; u < XTR; ++u)
             *reinterpret_cast<f32x4 *>(xtile + 4 * min((int)threadIdx.x + u * TWG, nvec - 1)) = tv[u];
@@ -861,7 +911,7 @@ Layout make_layout(int n, int nnz, int t0) {
     L.heads = take(sizeof(int) * ((size_t)n + 1));
     L.tasks = take(sizeof(i32x4) * (size_t)L.max_tasks);
     L.partials = take(sizeof(float) * (size_t)L.max_row_tasks);
-    L.spans = take(sizeof(int2) * (size_t)(ceil_div((int64_t)n + 1, TWAVES) + 1));
+    L.spans = take(sizeof(XWindow) * (size_t)(ceil_div((int64_t)n + 1, TWAVES) + 1));
     L.total = off;
     return L;
 }
@@ -898,7 +948,7 @@ struct spmv_csr_plan {
     float *partials = nullptr;
     bool has_chunked_rows = false;   // some row is split into several tasks
     int grid = 0;          // workgroups of the task kernel
-    const int2 *spans = nullptr;     // column window of each block workgroup
+    const XWindow *spans = nullptr;  // column window of each block workgroup
     int x_tile = 0;        // floats of x staged in LDS per block workgroup (0: gathers from memory)
 };
 
@@ -1022,7 +1072,7 @@ spmv_status build_binned_plan(spmv_csr_plan *h, char *ws, const Layout &L, hipSt
     // column windows of the block workgroups: narrow ones let the apply stage
     // x in LDS
     if (h->n_blocks > 0) {
-        int2 *spans = reinterpret_cast<int2 *>(ws + L.spans);
+        XWindow *spans = reinterpret_cast<XWindow *>(ws + L.spans);
         SPMV_HIP(hipMemsetAsync(&meta->max_window, 0, sizeof(int), st));
         k_block_spans<<<(int)ceil_div(h->n_blocks, TWAVES), TWG, 0, st>>>(meta, tasks, h->ci, spans);
         SPMV_LAUNCHED("k_block_spans");

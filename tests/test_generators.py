@@ -58,3 +58,14 @@ def test_fe_mesh_structure():
         assert len(set(d[:, 0].tolist())) == 8
     assert np.allclose(M.Ke, M.Ke.T)
     assert np.linalg.eigvalsh(M.Ke.astype(np.float64)).min() >= 1.0 - 1e-5
+
+
+def test_stencil_structure():
+    offs = (-5, 0, 3)
+    A = gen.stencil_csr(20, offs, seed=1)
+    rows = [A.col_idx[A.row_ptr[i]:A.row_ptr[i + 1]].tolist() for i in range(20)]
+    for i, r in enumerate(rows):
+        assert r == [i + d for d in sorted(offs) if 0 <= i + d < 20]
+    assert A.vals.dtype == np.float32 and len(A.vals) == A.nnz
+    B = gen.stencil_csr(20, offs, seed=1)
+    assert np.array_equal(A.vals, B.vals) and np.array_equal(A.x, B.x)

@@ -132,6 +132,20 @@ def test_edge_cases(case, variant):
     assert_close(y, yr, sc, TAU_F32, f"{case}/{variant}")
 
 
+@pytest.mark.parametrize("offsets", [(-2700, -1300, -1, 0, 1, 900, 2650),
+                                     (-2900, -2100, -777, -64, -3, 0, 5, 31, 400, 1999, 2500, 2900)])
+def test_x_window_sparse_bands(offsets):
+    """Rows whose entries fall in a few bands far apart: every block
+    workgroup's column window fits in LDS, but most of its segments hold no
+    column (the apply stages only the touched ones), with beta != 0."""
+    A = gen.stencil_csr(300_000, offsets, seed=21)
+    y0 = np.random.default_rng(22).uniform(-1, 1, A.n_rows).astype(np.float32)
+    print(f"[window] offsets {offsets}", flush=True)
+    M, y = _run(A, S.CSR_BINNED, alpha=0.75, beta=-0.5, y_in=y0)
+    yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x, alpha=0.75, beta=-0.5, y_in=y0)
+    assert_close(y, yr, sc, TAU_F32, f"bands {offsets}")
+
+
 @pytest.mark.parametrize("variant", list(VARIANTS))
 def test_duplicates_summed(variant):
     A = gen.random_csr(200, 100, np.random.default_rng(9).integers(2, 20, 200), seed=9)
