@@ -38,12 +38,19 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 #ifndef SPMV_MK_WAVES
-#define SPMV_MK_WAVES 12
+#define SPMV_MK_WAVES 8
 #endif
-constexpr int MK_WAVES = SPMV_MK_WAVES;   // waves per workgroup (2 workgroups per CU: 24 waves)
+constexpr int MK_WAVES = SPMV_MK_WAVES;   // waves per workgroup (2 workgroups per CU: 16 waves)
 constexpr int MK_WG = 64 * MK_WAVES;
+#ifndef SPMV_MK_PER_CU
+#define SPMV_MK_PER_CU 2
+#endif
+constexpr int MK_PER_CU = SPMV_MK_PER_CU;   // workgroups per CU when x fits in 48 KB of LDS
 constexpr int MK_CHUNK = 512;         // entries per wave per step (64 lanes x 8)
-constexpr int MK_UNROLL = 4;          // chunks whose loads are issued together
+#ifndef SPMV_MK_UNROLL
+#define SPMV_MK_UNROLL 3
+#endif
+constexpr int MK_UNROLL = SPMV_MK_UNROLL;   // chunks whose loads are issued together
 constexpr int MK_LDS_MAX_HALFS = 32768;  // x and its zero padding in LDS: up to 64 KB
 
 // Code layout of width BD bits.
@@ -448,7 +455,7 @@ void launch_spmv(int32_t n_rows, int32_t n_cols, const int32_t *mrow_ptr, const 
     if (halfs <= MK_LDS_MAX_HALFS) {
         const size_t lds = (size_t)halfs * sizeof(uint16_t);
         // as many workgroups per CU as the LDS allows, at most 2
-        const int per_cu = lds <= 48 * 1024 ? 2 : 1;
+        const int per_cu = lds <= 48 * 1024 ? MK_PER_CU : 1;
         const int grid = persistent_grid(n_rows, per_cu);
         if (aligned16(x) && n_cols >= 8)
             k_macko_spmv<1, BD, I8><<<grid, MK_WG, lds, st>>>(n_rows, n_cols, mrow_ptr, codes, vals, row_scale,
