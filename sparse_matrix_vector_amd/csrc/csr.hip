@@ -77,7 +77,8 @@ struct Meta {
     int bin_offsets[5];
     int head_totals[2];   // {0, number of runs of short rows}
     int block_totals[2];  // {0, number of short blocks}
-    int row_task_totals[2];   // {0, number of tasks of rows in groups 1-3}
+    int row_task_totals[2];   // {0, number of one-wave tasks of rows in groups 1-3}
+    int wgrow_totals[2];      // {0, number of rows in groups 1-3 applied by one workgroup each}
     int err;
     int max_window;       // largest column span (from a 16-byte boundary) of a block workgroup
 };
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(WG) void k_blocks_write(const Meta *__restrict__ me
     const int n0 = meta->bin_offsets[1];
     const int k = blockIdx.x * WG + threadIdx.x;
     int total;
-    int at = meta->row_task_totals[1] + offsets[blockIdx.x] +
+    int at = meta->wgrow_totals[1] + meta->row_task_totals[1] + offsets[blockIdx.x] +
              workgroup_exclusive(run_blocks(k, nh, n0, head_pos), &total);
     if (k >= nh) return;
     const int p = head_pos[k];
@@ -367,30 +368,46 @@ __global__ __launch_bounds__(WG) void k_blocks_write(const Meta *__restrict__ me
     }
 }
 
-// Rows of groups 1-3 become one task per SLOTS-entry chunk, counted from
-// the row's 16-byte-aligned start: chunk c covers [max(s, A + c SLOTS),
+// Rows of groups 1-3 are cut into SLOTS-entry chunks, counted from the row's
+// 16-byte-aligned start: chunk c covers [max(s, A + c SLOTS),
 // min(e, A + (c + 1) SLOTS)) with A = s & ~3, so every chunk fits the
-// staging area.  A row with one chunk is a task with nr = 1; chunk c of a
-// longer row is a task with nr = -(c + 1).
+// staging area.  A row with one chunk is a one-wave task with nr = 1.  A row
+// of 2 .. WG_ROW_MAX_CHUNKS chunks is one workgroup task {row, chunks, s, e}
+// (its waves take every TWAVES-th chunk and add their sums in LDS, so no
+// second kernel is needed).  Chunk c of a longer row is a one-wave task with
+// nr = -(c + 1) whose sum goes to a partial slot.
 __device__ __forceinline__ int row_chunk_count(int s, int e) { return (e - (s & ~3) + SLOTS - 1) / SLOTS; }
+
+constexpr int WG_ROW_MAX_CHUNKS = 4 * TWAVES;   // at most 4 chunks per wave
+
+__device__ __forceinline__ bool is_wg_row(int nch) { return nch >= 2 && nch <= WG_ROW_MAX_CHUNKS; }
 
 __global__ __launch_bounds__(WG) void k_rowtasks_count(const Meta *__restrict__ meta, int n,
                                                        const int *__restrict__ perm, const int *__restrict__ rp,
-                                                       int *__restrict__ counts) {
+                                                       int *__restrict__ counts, int *__restrict__ wcounts) {
     const int p = meta->bin_offsets[1] + blockIdx.x * WG + threadIdx.x;
-    int c = 0;
+    int nch = 0;
     if (p < n) {
         const int r = perm[p];
-        c = row_chunk_count(rp[r], rp[r + 1]);
+        nch = row_chunk_count(rp[r], rp[r + 1]);
     }
-    int total;
-    workgroup_exclusive(c, &total);
-    if (threadIdx.x == 0) counts[blockIdx.x] = total;
+    const bool wgr = is_wg_row(nch);
+    int total, wtotal;
+    workgroup_exclusive(wgr ? 0 : nch, &total);
+    __syncthreads();   // the scan's LDS is reused
+    workgroup_exclusive(wgr ? 1 : 0, &wtotal);
+    if (threadIdx.x == 0) {
+        counts[blockIdx.x] = total;
+        wcounts[blockIdx.x] = wtotal;
+    }
 }
 
+// Task order: the workgroup rows, then the one-wave tasks of rows in groups
+// 1-3 (both in perm order), then the short-row blocks.
 __global__ __launch_bounds__(WG) void k_rowtasks_write(const Meta *__restrict__ meta, int n,
                                                        const int *__restrict__ perm, const int *__restrict__ rp,
-                                                       const int *__restrict__ offsets, i32x4 *__restrict__ tasks) {
+                                                       const int *__restrict__ offsets,
+                                                       const int *__restrict__ woffsets, i32x4 *__restrict__ tasks) {
     const int p = meta->bin_offsets[1] + blockIdx.x * WG + threadIdx.x;
     int r = 0, s = 0, e = 0, nch = 0;
     if (p < n) {
@@ -399,8 +416,15 @@ __global__ __launch_bounds__(WG) void k_rowtasks_write(const Meta *__restrict__ 
         e = rp[r + 1];
         nch = row_chunk_count(s, e);
     }
-    int total;
-    const int first = offsets[blockIdx.x] + workgroup_exclusive(nch, &total);
+    const bool wgr = is_wg_row(nch);
+    int total, wtotal;
+    const int first = meta->wgrow_totals[1] + offsets[blockIdx.x] + workgroup_exclusive(wgr ? 0 : nch, &total);
+    __syncthreads();   // the scan's LDS is reused
+    const int wfirst = woffsets[blockIdx.x] + workgroup_exclusive(wgr ? 1 : 0, &wtotal);
+    if (wgr) {
+        tasks[wfirst] = i32x4{r, nch, s, e};
+        nch = 0;
+    }
     const int A = s & ~3;
     for (int c = 0; c < nch; ++c) {
         i32x4 d;
@@ -422,7 +446,7 @@ __global__ __launch_bounds__(TWG) void k_block_spans(Meta *__restrict__ meta, co
     __shared__ int lo[TWAVES], hi[TWAVES];
     __shared__ unsigned segs[X_SEG_WORDS];
     const int nb = meta->block_totals[1];
-    const int first = meta->row_task_totals[1];
+    const int first = meta->wgrow_totals[1] + meta->row_task_totals[1];
     const int lane = __lane_id(), wv = threadIdx.x / 64;
     const int b = blockIdx.x * TWAVES + wv;
     const i32x4 d = b < nb ? tasks[first + b] : i32x4{0, 0, 0, 0};
@@ -524,6 +548,7 @@ struct TaskArgs {
     int nnz;
     int last_vec;          // (nnz & ~3) - 4: start of the last full 16-byte vector
     int n_row_tasks;       // tasks [0, n_row_tasks): rows of groups 1-3; then n_blocks short blocks
+    int n_wg_rows;         // the first n_wg_rows of them: one workgroup each
     int n_blocks;
     int n_rows, n_cols;
 };
@@ -657,11 +682,15 @@ __device__ __forceinline__ void finish_row(const TaskArgs &a, i32x4 d, int t, co
     }
 }
 
-// One wave per task.  The grid is [row tasks][short blocks]: row tasks in
-// natural order, blocks through the XCD-contiguous map (neighbouring blocks
-// on one XCD share its L2 for nearby x entries; for the scattered gathers
-// of long rows the plain order measured faster).  The wave loads the task's
-// streams, issues all gathers at once, then reduces by task kind:
+// The grid is [workgroup rows][row tasks][short blocks].  A workgroup row
+// (a row of 2 .. WG_ROW_MAX_CHUNKS chunks) takes a whole workgroup: its
+// waves walk every TWAVES-th chunk and their sums meet in LDS, so such rows
+// need no second kernel and start first.  Otherwise one wave per task: row
+// tasks in natural order, blocks through the XCD-contiguous map
+// (neighbouring blocks on one XCD share its L2 for nearby x entries; for the
+// scattered gathers of long rows the plain order measured faster).  The
+// wave loads the task's streams, issues all gathers at once, then reduces by
+// task kind:
 //   nr > 1   a block of short rows (finish_block): every staged entry is
 //            gathered and multiplied without masks, since every staged
 //            column is a valid column of A;
@@ -697,14 +726,55 @@ __global__ __launch_bounds__(TWG) void k_csr_tasks(TaskArgs a, const i32x4 *__re
     const int lane = __lane_id();
     // wave-uniform, stated so that task indices and descriptors are scalar
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-    const int seg_rows = (a.n_row_tasks + TWAVES - 1) / TWAVES;
+    const int nwgr = a.n_wg_rows;
+    const int seg_rows = (a.n_row_tasks - nwgr + TWAVES - 1) / TWAVES;
     float *st = stage[wv];
     Staged cur;
     float xv[TASK_VPL][4];
 
-    if ((int)blockIdx.x < seg_rows) {
-        // ---- tasks of rows in groups 1-3 ----
-        const int t = blockIdx.x * TWAVES + wv;
+    if ((int)blockIdx.x < nwgr) {
+        // ---- a row of 2 .. WG_ROW_MAX_CHUNKS chunks: wave wv takes chunks
+        // wv, wv + TWAVES, ... in order; the wave sums are added in wave
+        // order ----
+        const i32x4 d = tasks[blockIdx.x];
+        const int s = d.z, e = d.w, A = s & ~3;
+        float acc = 0.0f;
+        for (int c = wv; c < d.y; c += TWAVES) {
+            const int cs = max(s, A + c * SLOTS), ce = min(e, A + (c + 1) * SLOTS), cb = cs & ~3;
+            stage_streams<VEC>(a, m, i32x4{d.x, 1, cs, ce}, lane, cur);
+#pragma unroll
+            for (int j = 0; j < TASK_VPL; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int k = cb + 4 * (lane + 64 * j) + q;
+                    xv[j][q] = xg[(k >= cs && k < ce) ? cur.c[j][q] : 0];
+                }
+#pragma unroll
+            for (int j = 0; j < TASK_VPL; ++j) issue_together(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
+#pragma unroll
+            for (int j = 0; j < TASK_VPL; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int k = cb + 4 * (lane + 64 * j) + q;
+                    acc += (k >= cs && k < ce) ? cur.f[j][q] * xv[j][q] : 0.0f;
+                }
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) st[0] = acc;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        if (wv == 0 && lane == 0) {
+            float sum = stage[0][0];
+            for (int w = 1; w < TWAVES; ++w) sum += stage[w][0];
+            store_y(y, ymap, d.x, sum, a.alpha, a.beta);
+        }
+        return;
+    }
+    const int bx = (int)blockIdx.x - nwgr;
+    if (bx < seg_rows) {
+        // ---- one-wave tasks of rows in groups 1-3 ----
+        const int t = nwgr + bx * TWAVES + wv;
         if (t >= a.n_row_tasks) return;
         const i32x4 d = tasks[t];
         stage_streams<VEC>(a, m, d, lane, cur);
@@ -723,7 +793,7 @@ __global__ __launch_bounds__(TWG) void k_csr_tasks(TaskArgs a, const i32x4 *__re
     }
 
     // ---- short-row blocks ----
-    const int qw = xcd_contiguous(blockIdx.x - seg_rows, gridDim.x - seg_rows);
+    const int qw = xcd_contiguous(bx - seg_rows, (int)gridDim.x - nwgr - seg_rows);
     const int wb = qw * TWAVES + wv;
     const bool have = wb < a.n_blocks;
     if (!XT && !have) return;
@@ -943,7 +1013,8 @@ struct spmv_csr_plan {
     int *perm = nullptr;
     int bin_off[5] = {0, 0, 0, 0, 0};
     const i32x4 *tasks = nullptr;
-    int n_row_tasks = 0;
+    int n_row_tasks = 0;   // tasks of rows in groups 1-3 (workgroup rows included)
+    int n_wg_rows = 0;     // rows applied by one workgroup each (the first tasks)
     int n_blocks = 0;
     float *partials = nullptr;
     bool has_chunked_rows = false;   // some row is split into several tasks
@@ -1035,11 +1106,14 @@ spmv_status build_binned_plan(spmv_csr_plan *h, char *ws, const Layout &L, hipSt
     k_plan_scatter<<<nwg, WG, 0, st>>>(n, h->rp, h->t[0], h->t[1], h->t[2], offsets, perm);
     SPMV_LAUNCHED("k_plan_scatter");
     // 2. tasks of the rows in groups 1-3 (perm order)
-    k_rowtasks_count<<<nwg, WG, 0, st>>>(meta, n, perm, h->rp, hcounts);
+    //    (counts / offsets of step 1 are free again and hold the workgroup rows)
+    k_rowtasks_count<<<nwg, WG, 0, st>>>(meta, n, perm, h->rp, hcounts, counts);
     SPMV_LAUNCHED("k_rowtasks_count");
     k_plan_scan<<<1, 1024, 0, st>>>(nwg, 1, hcounts, hoffsets, meta->row_task_totals);
     SPMV_LAUNCHED("k_plan_scan(row tasks)");
-    k_rowtasks_write<<<nwg, WG, 0, st>>>(meta, n, perm, h->rp, hoffsets, tasks);
+    k_plan_scan<<<1, 1024, 0, st>>>(nwg, 1, counts, offsets, meta->wgrow_totals);
+    SPMV_LAUNCHED("k_plan_scan(workgroup rows)");
+    k_rowtasks_write<<<nwg, WG, 0, st>>>(meta, n, perm, h->rp, hoffsets, offsets, tasks);
     SPMV_LAUNCHED("k_rowtasks_write");
     // 3. blocks of short rows, after the row tasks
     k_heads_count<<<nwg, WG, 0, st>>>(meta, perm, h->rp, window, hcounts);
@@ -1058,17 +1132,20 @@ spmv_status build_binned_plan(spmv_csr_plan *h, char *ws, const Layout &L, hipSt
     SPMV_HIP(hipMemcpyAsync(&hm, meta, sizeof(Meta), hipMemcpyDeviceToHost, st));
     SPMV_HIP(hipStreamSynchronize(st));
     for (int g = 0; g < 5; ++g) h->bin_off[g] = hm.bin_offsets[g];
-    h->n_row_tasks = hm.row_task_totals[1];
+    h->n_wg_rows = hm.wgrow_totals[1];
+    h->n_row_tasks = hm.wgrow_totals[1] + hm.row_task_totals[1];
     h->n_blocks = hm.block_totals[1];
     if (h->n_row_tasks > L.max_row_tasks || (int64_t)h->n_row_tasks + h->n_blocks > L.max_tasks)
         return fail(SPMV_ERR_INVALID_MATRIX, "task count exceeds its bound");
     h->perm = perm;
     h->tasks = tasks;
     h->partials = reinterpret_cast<float *>(ws + L.partials);
-    // rows of groups 1-3 each give one task unless some row was split
+    // rows of groups 1-3 each give one task unless some row was split into
+    // chunk tasks
     h->has_chunked_rows = h->n_row_tasks > h->bin_off[4] - h->bin_off[1];
-    // one wave per task: row-task workgroups, then block workgroups
-    h->grid = (int)(ceil_div(h->n_row_tasks, TWAVES) + ceil_div(h->n_blocks, TWAVES));
+    // a workgroup per workgroup row, then one wave per task: row-task
+    // workgroups, then block workgroups
+    h->grid = (int)(h->n_wg_rows + ceil_div(h->n_row_tasks - h->n_wg_rows, TWAVES) + ceil_div(h->n_blocks, TWAVES));
     // column windows of the block workgroups: narrow ones let the apply stage
     // x in LDS
     if (h->n_blocks > 0) {
@@ -1209,6 +1286,7 @@ spmv_status csr_apply(spmv_csr_t h, float alpha, const float *x, float beta, flo
     a.nnz = h->nnz;
     a.last_vec = (h->nnz & ~3) - 4;
     a.n_row_tasks = h->n_row_tasks;
+    a.n_wg_rows = h->n_wg_rows;
     a.n_blocks = h->n_blocks;
     a.n_rows = n;
     a.n_cols = h->n_cols;

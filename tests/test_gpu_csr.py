@@ -96,6 +96,26 @@ def test_group_bounds_and_long_rows(variant):
         assert off[4] - off[3] == 3
 
 
+def test_workgroup_rows_and_chunked_rows():
+    """Rows of 2-16 chunks (one workgroup each, no second kernel) next to
+    rows of 1 chunk and of more than 16 chunks (chunk partials), from
+    unaligned starts, among short rows; alpha, beta and run-to-run bits."""
+    rng = np.random.default_rng(31)
+    longs = [600, 1021, 1024, 1500, 2049, 4334, 8188, 8200, 20000, 509, 510, 513]
+    lens = np.concatenate([rng.integers(0, 12, 3000), longs, rng.integers(0, 40, 500), longs[::-1]])
+    A = gen.random_csr(len(lens), 50_000, lens, seed=32)
+    y0 = rng.uniform(-1, 1, A.n_rows).astype(np.float32)
+    print(f"[wgrows] n={A.n_rows} nnz={A.nnz}", flush=True)
+    M, y = _run(A, S.CSR_BINNED, alpha=1.5, beta=0.25, y_in=y0)
+    yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x, alpha=1.5, beta=0.25, y_in=y0)
+    assert_close(y, yr, sc, TAU_F32, "workgroup rows")
+    x = dev(A.x)
+    y2 = dev(y0)
+    M.apply(x, y2, 1.5, 0.25)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y2).view(np.uint32), y.view(np.uint32))
+
+
 @pytest.mark.parametrize("thr", [(4, 8, 16), (2, 3, 4), (256, 1000, 5000), (1, 2, 100000)])
 def test_custom_thresholds(thr):
     rng = np.random.default_rng(11)
