@@ -435,7 +435,9 @@ spmv_status spgemm_info(spgemm_t h, int64_t *nnz_c, int64_t *intermediate_produc
  * (device, caller-owned).  Uses the current values of A and B, so it may be
  * repeated after they change with the same patterns.  fp32 products summed
  * by atomic adds: values agree with the exact sum to rounding, in an order
- * that varies.  Asynchronous; allocates nothing. */
+ * that varies.  Asynchronous; allocates nothing.  The row groups run
+ * concurrently on the handle's own streams, forked from and joined back into
+ * `stream`; calls on one handle must not overlap. */
 spmv_status spgemm_compute(spgemm_t h, int32_t *rp_c, int32_t *ci_c, float *v_c, void *stream);
 
 /* Releases the handle (not the workspace or the borrowed arrays). */

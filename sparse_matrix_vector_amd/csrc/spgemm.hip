@@ -45,7 +45,10 @@
 #include "common.hpp"
 
 #include <algorithm>
+#include <array>
 #include <climits>
+#include <map>
+#include <mutex>
 #include <vector>
 
 namespace spmv {
@@ -662,12 +665,43 @@ struct spgemm {
     unsigned *tkeys;
     float *tvals;
     spmv::IpTotals *tot;
+    // Side streams (the device's shared pool, default priority) and this
+    // handle's events: the bins of a phase run concurrently, forked from and
+    // joined back into the caller's stream.
+    hipStream_t side[3] = {};
+    hipEvent_t fork = nullptr, join[3] = {};
+    ~spgemm() {
+        for (hipEvent_t e : join)
+            if (e) (void)hipEventDestroy(e);
+        if (fork) (void)hipEventDestroy(fork);
+    }
 };
 
 namespace spmv {
 namespace {
 
 size_t r256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Three non-blocking streams per device, created on first use and kept for
+// the life of the process (creating streams per handle costs more than a
+// small product).  Handles on one device share them, which only orders
+// their bins, never their results.
+bool side_streams(hipStream_t (&out)[3]) {
+    static std::mutex mu;
+    static std::map<int, std::array<hipStream_t, 3>> pool;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = pool.find(dev);
+    if (it == pool.end()) {
+        std::array<hipStream_t, 3> q{};
+        for (auto &x : q)
+            if (hipStreamCreateWithFlags(&x, hipStreamNonBlocking) != hipSuccess) return false;
+        it = pool.emplace(dev, q).first;
+    }
+    for (int i = 0; i < 3; ++i) out[i] = it->second[i];
+    return true;
+}
 
 struct SgLayout {
     size_t ip, map, cnt, rp, sums, bcnt, dbase, g3off, tot, err, tkeys, tvals, total;
@@ -746,11 +780,44 @@ spmv_status sg_ip(int32_t m, const int32_t *rpa, const int32_t *cia, const int32
 }
 
 // Allocation (SYM) or accumulation phase over every bin.
+// The bins are independent, so they run concurrently: the global-table rows
+// (the longest-running, with the fewest workgroups) start first on one side
+// stream, bins 5 and 4 on a second, bins 3 and 2 on a third, and bins 1 and
+// 0 on the caller's stream, which then waits for the side streams.
 template <bool SYM>
 spmv_status sg_phase(const spgemm *h, int *ci_c, float *v_c, hipStream_t st) {
     const int *mp = h->map;
     const int *b = h->base;
     const int *c = h->counts;
+    // without rows in bins 2-6 everything runs on the caller's stream
+    const bool fork = c[2] + c[3] + c[4] + c[5] + c[6] > 0;
+    if (fork) {
+        SPMV_HIP(hipEventRecord(h->fork, st));
+        for (hipStream_t q : h->side) SPMV_HIP(hipStreamWaitEvent(q, h->fork, 0));
+    }
+    if (c[6] > 0) {
+        if (SYM)
+            k_sg_g3_count<<<c[6], G3_WG, 0, h->side[0]>>>(mp + b[6], h->g3off, h->tkeys, h->rpa, h->cia, h->rpb,
+                                                          h->cib, h->cnt, h->err);
+        else
+            k_sg_g3_fill<<<c[6], G3_WG, 0, h->side[0]>>>(mp + b[6], h->g3off, h->tkeys, h->tvals, h->rpa, h->cia,
+                                                         h->va, h->rpb, h->cib, h->vb, h->rp, ci_c, v_c, h->err);
+    }
+#define SG_TB(BIN, WG, TMAX, Q)                                                                                     \
+    if (c[BIN] > 0) {                                                                                              \
+        if (SYM)                                                                                                   \
+            k_sg_tb_count<WG, TMAX><<<c[BIN], WG, 0, Q>>>(mp + b[BIN], h->ip, h->rpa, h->cia, h->rpb, h->cib,        \
+                                                          h->cnt, h->err);                                        \
+        else                                                                                                       \
+            k_sg_tb_fill<WG, TMAX><<<c[BIN], WG, 0, Q>>>(mp + b[BIN], h->ip, h->rpa, h->cia, h->va, h->rpb, h->cib,  \
+                                                         h->vb, h->rp, ci_c, v_c, h->err);                        \
+    }
+    SG_TB(5, 1024, 16384, h->side[1])
+    SG_TB(4, 1024, 8192, h->side[1])
+    SG_TB(3, 512, 4096, h->side[2])
+    SG_TB(2, 256, 2048, h->side[2])
+    SG_TB(1, 256, 1024, st)
+#undef SG_TB
     if (c[0] > 0) {
         const int g = (int)ceil_div(c[0], G0_ROWS);
         if (SYM)
@@ -759,30 +826,11 @@ spmv_status sg_phase(const spgemm *h, int *ci_c, float *v_c, hipStream_t st) {
             k_sg_g0_fill<<<g, G0_WG, 0, st>>>(c[0], mp + b[0], h->rpa, h->cia, h->va, h->rpb, h->cib, h->vb, h->rp,
                                               ci_c, v_c, h->err);
     }
-#define SG_TB(BIN, WG, TMAX)                                                                                         \
-    if (c[BIN] > 0) {                                                                                                \
-        if (SYM)                                                                                                     \
-            k_sg_tb_count<WG, TMAX><<<c[BIN], WG, 0, st>>>(mp + b[BIN], h->ip, h->rpa, h->cia, h->rpb, h->cib,       \
-                                                           h->cnt, h->err);                                         \
-        else                                                                                                         \
-            k_sg_tb_fill<WG, TMAX><<<c[BIN], WG, 0, st>>>(mp + b[BIN], h->ip, h->rpa, h->cia, h->va, h->rpb, h->cib, \
-                                                          h->vb, h->rp, ci_c, v_c, h->err);                         \
-    }
-    SG_TB(1, 256, 1024)
-    SG_TB(2, 256, 2048)
-    SG_TB(3, 512, 4096)
-    SG_TB(4, 1024, 8192)
-    SG_TB(5, 1024, 16384)
-#undef SG_TB
-    if (c[6] > 0) {
-        if (SYM)
-            k_sg_g3_count<<<c[6], G3_WG, 0, st>>>(mp + b[6], h->g3off, h->tkeys, h->rpa, h->cia, h->rpb, h->cib,
-                                                  h->cnt, h->err);
-        else
-            k_sg_g3_fill<<<c[6], G3_WG, 0, st>>>(mp + b[6], h->g3off, h->tkeys, h->tvals, h->rpa, h->cia, h->va,
-                                                 h->rpb, h->cib, h->vb, h->rp, ci_c, v_c, h->err);
-    }
     SPMV_LAUNCHED(SYM ? "the allocation phase" : "the accumulation phase");
+    for (int i = 0; fork && i < 3; ++i) {
+        SPMV_HIP(hipEventRecord(h->join[i], h->side[i]));
+        SPMV_HIP(hipStreamWaitEvent(st, h->join[i], 0));
+    }
     return SPMV_OK;
 }
 
@@ -863,6 +911,12 @@ extern "C" spmv_status spgemm_create(spgemm_t *handle, int32_t m, int32_t k, int
         delete H;
         return e;
     };
+    if (!side_streams(H->side)) return cleanup(fail(SPMV_ERR_HIP, "creating the side streams failed"));
+    for (int i = 0; i < 3; ++i)
+        if (hipEventCreateWithFlags(&H->join[i], hipEventDisableTiming) != hipSuccess)
+            return cleanup(fail(SPMV_ERR_HIP, "creating an event failed"));
+    if (hipEventCreateWithFlags(&H->fork, hipEventDisableTiming) != hipSuccess)
+        return cleanup(fail(SPMV_ERR_HIP, "creating an event failed"));
     // Map[]: rows binned, in row order inside each bin
     if (hipMemcpyAsync(H->dbase, H->base, sizeof(int) * SG_NBIN, hipMemcpyHostToDevice, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
