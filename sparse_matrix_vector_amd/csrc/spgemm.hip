@@ -322,77 +322,35 @@ __device__ void sg_bitonic(KeyPtr keys, ValPtr vals, unsigned T) {
     }
 }
 
-// Bitonic sort of T (a power of two) pairs held in global memory, with the
-// same network as sg_bitonic: every stage whose partner distance is below
-// CH runs on one CH-slot chunk at a time staged in LDS (lk, lv), so only the
-// log2(T / CH) * (log2(T / CH) + 1) / 2 stages with longer distances touch
-// global memory.  The direction of a compare-exchange follows the global
-// index, as in the plain network.
-template <int WG, int CH>
-__device__ void sg_bitonic_staged(unsigned *keys, float *vals, unsigned T, unsigned *lk, float *lv) {
-    auto load = [&](unsigned c0, unsigned len) {
-        for (unsigned i = threadIdx.x; i < len; i += WG) {
-            lk[i] = keys[c0 + i];
-            lv[i] = vals[c0 + i];
-        }
-        __syncthreads();
-    };
-    auto store = [&](unsigned c0, unsigned len) {
-        for (unsigned i = threadIdx.x; i < len; i += WG) {
-            keys[c0 + i] = lk[i];
-            vals[c0 + i] = lv[i];
-        }
-        __syncthreads();
-    };
-    // stages k, j with j < CH on the chunk at c0 (global index c0 + i)
-    auto local_stages = [&](unsigned c0, unsigned len, unsigned k, unsigned jtop) {
-        for (unsigned j = jtop; j > 0; j >>= 1) {
-            for (unsigned i = threadIdx.x; i < len; i += WG) {
-                const unsigned l = i ^ j;
-                if (l > i) {
-                    const unsigned a = lk[i], b = lk[l];
-                    const bool up = ((c0 + i) & k) == 0;
-                    if ((a > b) == up) {
-                        lk[i] = b;
-                        lk[l] = a;
-                        const float va = lv[i];
-                        lv[i] = lv[l];
-                        lv[l] = va;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    };
-    const unsigned len = T < CH ? T : CH;
-    // every chunk sorted by the stages k <= CH
-    for (unsigned c0 = 0; c0 < T; c0 += len) {
-        load(c0, len);
-        for (unsigned k = 2; k <= len; k <<= 1) local_stages(c0, len, k, k >> 1);
-        store(c0, len);
+// Merges the sorted runs a[0, la) and b[0, lb) (distinct keys) into
+// out[0, la + lb) with the whole workgroup: thread t writes the outputs
+// t * per .. (t + 1) * per - 1, starting where the merge path crosses that
+// diagonal (found by binary search), so no thread waits for another.
+template <int WG>
+__device__ void sg_merge(const unsigned *ak, const float *av, int la, const unsigned *bk, const float *bv, int lb,
+                         unsigned *ok, float *ov) {
+    const int n = la + lb;
+    const int per = (n + WG - 1) / WG;
+    const int d0 = min(n, (int)threadIdx.x * per), d1 = min(n, d0 + per);
+    if (d0 >= d1) return;
+    // i = how many of the first d0 outputs come from a
+    int lo = max(0, d0 - lb), hi = min(d0, la);
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (ak[mid] < bk[d0 - 1 - mid]) lo = mid + 1;
+        else hi = mid;
     }
-    for (unsigned k = 2 * CH; k <= T; k <<= 1) {
-        for (unsigned j = k >> 1; j >= CH; j >>= 1) {
-            for (unsigned i = threadIdx.x; i < T; i += WG) {
-                const unsigned l = i ^ j;
-                if (l > i) {
-                    const unsigned a = keys[i], b = keys[l];
-                    const bool up = (i & k) == 0;
-                    if ((a > b) == up) {
-                        keys[i] = b;
-                        keys[l] = a;
-                        const float va = vals[i];
-                        vals[i] = vals[l];
-                        vals[l] = va;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-        for (unsigned c0 = 0; c0 < T; c0 += CH) {
-            load(c0, CH);
-            local_stages(c0, CH, k, CH >> 1);
-            store(c0, CH);
+    int i = lo, j = d0 - lo;
+    for (int d = d0; d < d1; ++d) {
+        const bool from_a = j >= lb || (i < la && ak[i] < bk[j]);
+        if (from_a) {
+            ok[d] = ak[i];
+            ov[d] = av[i];
+            ++i;
+        } else {
+            ok[d] = bk[j];
+            ov[d] = bv[j];
+            ++j;
         }
     }
 }
@@ -579,13 +537,68 @@ __global__ __launch_bounds__(G3_WG) void k_sg_g3_fill(const int *__restrict__ li
             ok = ok && sg_insert_add(keys, vals, T - 1, cib[t], a * vb[t]);
     }
     if (!ok) atomicOr(err, SG_ERR_PROBE);
+    // Compact the table's len entries into C's row (in any order): the table
+    // is at least half empty, so sorting it whole would sort mostly padding.
+    __shared__ int fill;
+    if (threadIdx.x == 0) fill = 0;
     __syncthreads();
-    sg_bitonic_staged<G3_WG, G3_CH>(keys, vals, T, lk, lv);
     const int base = rpc[row], len = rpc[row + 1] - base;
-    for (int s = threadIdx.x; s < len && (unsigned)s < T; s += G3_WG) {
-        cic[base + s] = (int)keys[s];
-        vc[base + s] = vals[s];
+    unsigned *ck = reinterpret_cast<unsigned *>(cic + base);
+    float *cv = vc + base;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (unsigned s0 = 0; s0 < T; s0 += G3_WG) {
+        const unsigned s = s0 + threadIdx.x;
+        const unsigned key = s < T ? keys[s] : SG_EMPTY;
+        const bool has = key != SG_EMPTY;
+        const unsigned long long bal = __ballot(has);
+        int at = 0;
+        if (lane == 0 && bal) at = atomicAdd(&fill, __popcll(bal));
+        at = __shfl(at, 0) + __popcll(bal & below);
+        if (has && at < len) {
+            ck[at] = key;
+            cv[at] = vals[s];
+        }
     }
+    __syncthreads();
+    // Sort: runs of up to G3_CH entries in LDS, then pairwise merges between
+    // C's row and the (now free) table, which holds at least 2 * len slots.
+    for (int c0 = 0; c0 < len; c0 += G3_CH) {
+        const int cl = min(G3_CH, len - c0);
+        unsigned P = 64;
+        while ((int)P < cl) P <<= 1;
+        for (unsigned i = threadIdx.x; i < P; i += G3_WG) {
+            const bool in = (int)i < cl;
+            lk[i] = in ? ck[c0 + i] : SG_EMPTY;
+            lv[i] = in ? cv[c0 + i] : 0.0f;
+        }
+        __syncthreads();
+        sg_bitonic<G3_WG>(lk, lv, P);
+        for (int i = threadIdx.x; i < cl; i += G3_WG) {
+            ck[c0 + i] = lk[i];
+            cv[c0 + i] = lv[i];
+        }
+        __syncthreads();
+    }
+    unsigned *sk = ck, *dk = keys;
+    float *sv = cv, *dv = vals;
+    for (int run = G3_CH; run < len; run *= 2) {
+        for (int a0 = 0; a0 < len; a0 += 2 * run) {
+            const int la = min(run, len - a0), lb = min(run, max(0, len - a0 - run));
+            sg_merge<G3_WG>(sk + a0, sv + a0, la, sk + a0 + la, sv + a0 + la, lb, dk + a0, dv + a0);
+        }
+        __syncthreads();
+        unsigned *tk = sk;
+        sk = dk;
+        dk = tk;
+        float *tv = sv;
+        sv = dv;
+        dv = tv;
+    }
+    if (sk != ck)
+        for (int i = threadIdx.x; i < len; i += G3_WG) {
+            ck[i] = sk[i];
+            cv[i] = sv[i];
+        }
 }
 
 // ---- row pointers of C: exclusive scan of the counts ----

@@ -102,6 +102,27 @@ def test_mixed_groups(seed):
     _check(n, A, B, got)
 
 
+def test_global_rows_many_sorted_runs():
+    """Global-table rows whose C row has more than 16,384 entries (sorted in
+    LDS runs, then merged): one of 47,455 entries (three runs, two merge
+    passes, an uneven last run), one of 19,806 (two runs) and one of 16,592
+    (a 208-entry second run), next to small rows."""
+    rng = np.random.default_rng(41)
+    k, n = 6000, 400_000
+    B = gen.random_csr(k, n, rng.integers(8, 17, k), seed=42)
+    alens = np.array([4200, 0, 3, 1700, 1, 1400, 7], dtype=np.int64)
+    rows = np.repeat(np.arange(len(alens)), alens)
+    cols = np.concatenate([np.sort(rng.choice(k, L, replace=False)) for L in alens]).astype(np.int32)
+    rp = np.concatenate([[0], np.cumsum(alens)]).astype(np.int32)
+    A = (rp, cols, rng.uniform(-1, 1, len(rows)).astype(np.float32))
+    Bt = (B.row_ptr, B.col_idx, B.vals)
+    got = _run(len(alens), k, n, A, Bt)
+    lens = np.diff(got[0])
+    print(f"[spgemm] long rows nnz per row={lens.tolist()} groups={got[3][2]}", flush=True)
+    assert lens[0] > 2 * 16384 and 16384 < lens[3] <= 2 * 16384 and lens[5] > 16384 and got[3][2][3] == 3
+    _check(n, A, Bt, got)
+
+
 @pytest.mark.parametrize("shape", [(30, 40, 20), (1, 1, 1), (200, 50, 300)])
 def test_small_random(shape):
     m, k, n = shape
