@@ -322,6 +322,48 @@ __device__ void sg_bitonic(KeyPtr keys, ValPtr vals, unsigned T) {
     }
 }
 
+// Moves the non-empty slots of an LDS hash table of T <= PER * WG slots to
+// its front (in any order), pads them with empty slots up to P, the
+// smallest power of two >= their count (at least 64), and returns P: the
+// sort then works on P slots instead of the whole, at most half-full, table.
+template <int WG, int PER>
+__device__ unsigned sg_compact(unsigned *keys, float *vals, unsigned T, int *counter) {
+    const int lane = __lane_id();
+    const unsigned long long below = (1ull << lane) - 1ull;
+    unsigned k[PER];
+    float v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const unsigned s = threadIdx.x + i * WG;
+        k[i] = s < T ? keys[s] : SG_EMPTY;
+        v[i] = s < T ? vals[s] : 0.0f;
+    }
+    if (threadIdx.x == 0) *counter = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const bool has = k[i] != SG_EMPTY;
+        const unsigned long long bal = __ballot(has);
+        int at = 0;
+        if (lane == 0 && bal) at = atomicAdd(counter, __popcll(bal));
+        at = __shfl(at, 0) + __popcll(bal & below);
+        if (has) {
+            keys[at] = k[i];
+            vals[at] = v[i];
+        }
+    }
+    __syncthreads();
+    const unsigned n = (unsigned)*counter;
+    unsigned P = 64;
+    while (P < n) P <<= 1;
+    for (unsigned s = n + threadIdx.x; s < P; s += WG) {
+        keys[s] = SG_EMPTY;
+        vals[s] = 0.0f;
+    }
+    __syncthreads();
+    return P;
+}
+
 // Merges the sorted runs a[0, la) and b[0, lb) (distinct keys) into
 // out[0, la + lb) with the whole workgroup: thread t writes the outputs
 // t * per .. (t + 1) * per - 1, starting where the merge path crosses that
@@ -459,6 +501,7 @@ __global__ __launch_bounds__(WG) void k_sg_tb_fill(const int *__restrict__ list,
                                                    float *__restrict__ vc, int *err) {
     __shared__ unsigned keys[TMAX];
     __shared__ float vals[TMAX];
+    __shared__ int used;
     const int row = list[blockIdx.x];
     const unsigned T = (unsigned)min((long long)TMAX, (long long)g3_table(ip[row]));
     for (unsigned s = threadIdx.x; s < T; s += WG) {
@@ -476,7 +519,9 @@ __global__ __launch_bounds__(WG) void k_sg_tb_fill(const int *__restrict__ list,
     }
     if (!ok) atomicOr(err, SG_ERR_PROBE);
     __syncthreads();
-    sg_bitonic<WG>(keys, vals, T);
+    static_assert(TMAX % WG == 0, "whole slots per thread");
+    const unsigned P = sg_compact<WG, TMAX / WG>(keys, vals, T, &used);
+    sg_bitonic<WG>(keys, vals, P);
     const int base = rpc[row], len = rpc[row + 1] - base;
     for (int s = threadIdx.x; s < len && (unsigned)s < T; s += WG) {
         cic[base + s] = (int)keys[s];
