@@ -115,6 +115,37 @@ def test_auto_choice_and_apply(case, expect):
         assert_close(host(y), yr, sc, TAU_F32, f"auto {case}")
 
 
+@pytest.mark.parametrize("n,misaligned_y", [(8192, False), (8190, False), (8192, True), (4 * 1024 * 3 + 4, False)])
+def test_auto_hyb_shapes(n, misaligned_y):
+    """Moderate-CV matrices (HYB) through the auto handle: the 4-row ELL
+    kernel (n % 4 == 0, aligned) or the 1-row one (n % 4 != 0, misaligned y),
+    then the binned tail. Rows up to 40 entries, tail rows at ELL-workgroup
+    edges, a partial last workgroup; alpha / beta; repeated applies are
+    bit-equal."""
+    rng = np.random.default_rng(n)
+    lens = rng.integers(1, 13, n)
+    lens[rng.choice(n, n // 200, replace=False)] = rng.integers(20, 41, n // 200)
+    lens[[0, 1023, 1024, 4095, 4096, n - 1]] = 17
+    A = gen.random_csr(n, 3000, lens, seed=n + 1)
+    s1, s2 = int(lens.sum()), int((lens.astype(np.int64) ** 2).sum())
+    assert oracle.format_choice(n, s1, s2) == 1
+    M = S.AutoMatrix(A.n_rows, A.n_cols, dev(A.row_ptr), dev(A.col_idx), dev(A.vals))
+    assert M.format == 1
+    y_in = rng.uniform(-1, 1, n).astype(np.float32)
+    buf = torch.zeros(n + 1, device="cuda")
+    y = buf[1:] if misaligned_y else buf[:n]
+    outs = []
+    for _ in range(2):
+        y.copy_(dev(y_in))
+        M.apply(dev(A.x), y, 0.5, 2.0)
+        torch.cuda.synchronize()
+        outs.append(host(y).copy())
+    print(f"[auto hyb] n={n} misaligned_y={misaligned_y}", flush=True)
+    yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x, 0.5, 2.0, y_in)
+    assert_close(outs[0], yr, sc, TAU_F32, f"auto hyb n={n}")
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
 def test_auto_ell_padding_guard():
     """CV < 0.3 but one long row: padding every row to it would more than
     double the storage, so HYB is used instead of ELL."""
