@@ -322,6 +322,44 @@ __device__ void sg_bitonic(KeyPtr keys, ValPtr vals, unsigned T) {
     }
 }
 
+// Calls f(j, t) for every intermediate product a_j * b_t of row `row` of A
+// (j: entry of A's row, t: entry of the row of B it reaches), by a whole
+// workgroup of WG threads.  Each thread first takes whole entries of A's row
+// and walks their B rows itself when they are short (at most SG_SHORT_B
+// entries), so a row of many short B rows costs one round of dependent
+// loads instead of one per entry; entries with longer B rows go to an LDS
+// list (`defer`, SG_DEFER slots, `ndefer` zeroed by the caller before a
+// barrier) and are then walked by whole waves, lanes over the B row.  An
+// entry that finds the list full is walked by its thread.
+constexpr int SG_SHORT_B = 16;
+constexpr int SG_DEFER = 1024;
+
+template <int WG, typename F>
+__device__ __forceinline__ void sg_walk(int row, const int *__restrict__ rpa, const int *__restrict__ cia,
+                                        const int *__restrict__ rpb, int *defer, int *ndefer, F &&f) {
+    const int a0 = rpa[row], a1 = rpa[row + 1];
+    for (int j = a0 + (int)threadIdx.x; j < a1; j += WG) {
+        const int k = cia[j];
+        const int t0 = rpb[k], t1 = rpb[k + 1];
+        if (t1 - t0 > SG_SHORT_B) {
+            const int at = atomicAdd(ndefer, 1);
+            if (at < SG_DEFER) {
+                defer[at] = j;
+                continue;
+            }
+        }
+        for (int t = t0; t < t1; ++t) f(j, t);
+    }
+    __syncthreads();
+    const int nd = min(*ndefer, SG_DEFER);
+    const int wv = threadIdx.x / 64, lane = threadIdx.x % 64;
+    for (int q = wv; q < nd; q += WG / 64) {
+        const int j = defer[q];
+        const int k = cia[j];
+        for (int t = rpb[k] + lane; t < rpb[k + 1]; t += 64) f(j, t);
+    }
+}
+
 // Moves the non-empty slots of an LDS hash table of T <= PER * WG slots to
 // its front (in any order), pads them with empty slots up to P, the
 // smallest power of two >= their count (at least 64), and returns P: the
@@ -475,18 +513,16 @@ __global__ __launch_bounds__(WG) void k_sg_tb_count(const int *__restrict__ list
                                                     const int *__restrict__ rpb, const int *__restrict__ cib,
                                                     int *__restrict__ cnt, int *err) {
     __shared__ unsigned keys[TMAX];
-    __shared__ int count;
+    __shared__ int count, ndefer;
+    __shared__ int defer[SG_DEFER];
     const int row = list[blockIdx.x];
     const unsigned T = (unsigned)min((long long)TMAX, (long long)g3_table(ip[row]));
     for (unsigned s = threadIdx.x; s < T; s += WG) keys[s] = SG_EMPTY;
-    if (threadIdx.x == 0) count = 0;
+    if (threadIdx.x == 0) count = ndefer = 0;
     __syncthreads();
-    const int wv = threadIdx.x / 64, lane = threadIdx.x % 64;
     bool ok = true;
-    for (int j = rpa[row] + wv; j < rpa[row + 1]; j += WG / 64) {
-        const int k = cia[j];
-        for (int t = rpb[k] + lane; t < rpb[k + 1]; t += 64) ok = ok && sg_insert_key(keys, T - 1, cib[t], &count);
-    }
+    sg_walk<WG>(row, rpa, cia, rpb, defer, &ndefer,
+                [&](int, int t) { ok = ok && sg_insert_key(keys, T - 1, cib[t], &count); });
     if (!ok) atomicOr(err, SG_ERR_PROBE);
     __syncthreads();
     if (threadIdx.x == 0) cnt[row] = count;
@@ -501,22 +537,19 @@ __global__ __launch_bounds__(WG) void k_sg_tb_fill(const int *__restrict__ list,
                                                    float *__restrict__ vc, int *err) {
     __shared__ unsigned keys[TMAX];
     __shared__ float vals[TMAX];
-    __shared__ int used;
+    __shared__ int used, ndefer;
+    __shared__ int defer[SG_DEFER];
     const int row = list[blockIdx.x];
     const unsigned T = (unsigned)min((long long)TMAX, (long long)g3_table(ip[row]));
     for (unsigned s = threadIdx.x; s < T; s += WG) {
         keys[s] = SG_EMPTY;
         vals[s] = 0.0f;
     }
+    if (threadIdx.x == 0) ndefer = 0;
     __syncthreads();
-    const int wv = threadIdx.x / 64, lane = threadIdx.x % 64;
     bool ok = true;
-    for (int j = rpa[row] + wv; j < rpa[row + 1]; j += WG / 64) {
-        const int k = cia[j];
-        const float a = va[j];
-        for (int t = rpb[k] + lane; t < rpb[k + 1]; t += 64)
-            ok = ok && sg_insert_add(keys, vals, T - 1, cib[t], a * vb[t]);
-    }
+    sg_walk<WG>(row, rpa, cia, rpb, defer, &ndefer,
+                [&](int j, int t) { ok = ok && sg_insert_add(keys, vals, T - 1, cib[t], va[j] * vb[t]); });
     if (!ok) atomicOr(err, SG_ERR_PROBE);
     __syncthreads();
     static_assert(TMAX % WG == 0, "whole slots per thread");
@@ -535,20 +568,18 @@ __global__ __launch_bounds__(G3_WG) void k_sg_g3_count(const int *__restrict__ l
                                                        unsigned *__restrict__ tkeys, const int *__restrict__ rpa,
                                                        const int *__restrict__ cia, const int *__restrict__ rpb,
                                                        const int *__restrict__ cib, int *__restrict__ cnt, int *err) {
-    __shared__ int count;
+    __shared__ int count, ndefer;
+    __shared__ int defer[SG_DEFER];
     const int r = blockIdx.x;
     const int row = list[r];
     const unsigned T = (unsigned)(off[r + 1] - off[r]);
     unsigned *keys = tkeys + off[r];
     for (unsigned s = threadIdx.x; s < T; s += G3_WG) keys[s] = SG_EMPTY;
-    if (threadIdx.x == 0) count = 0;
+    if (threadIdx.x == 0) count = ndefer = 0;
     __syncthreads();
-    const int wv = threadIdx.x / 64, lane = threadIdx.x % 64;
     bool ok = true;
-    for (int j = rpa[row] + wv; j < rpa[row + 1]; j += G3_WG / 64) {
-        const int k = cia[j];
-        for (int t = rpb[k] + lane; t < rpb[k + 1]; t += 64) ok = ok && sg_insert_key(keys, T - 1, cib[t], &count);
-    }
+    sg_walk<G3_WG>(row, rpa, cia, rpb, defer, &ndefer,
+                   [&](int, int t) { ok = ok && sg_insert_key(keys, T - 1, cib[t], &count); });
     if (!ok) atomicOr(err, SG_ERR_PROBE);
     __syncthreads();
     if (threadIdx.x == 0) cnt[row] = count;
@@ -563,6 +594,8 @@ __global__ __launch_bounds__(G3_WG) void k_sg_g3_fill(const int *__restrict__ li
                                                       float *__restrict__ vc, int *err) {
     __shared__ unsigned lk[G3_CH];
     __shared__ float lv[G3_CH];
+    __shared__ int ndefer;
+    __shared__ int defer[SG_DEFER];
     const int r = blockIdx.x;
     const int row = list[r];
     const unsigned T = (unsigned)(off[r + 1] - off[r]);
@@ -572,15 +605,12 @@ __global__ __launch_bounds__(G3_WG) void k_sg_g3_fill(const int *__restrict__ li
         keys[s] = SG_EMPTY;
         vals[s] = 0.0f;
     }
+    if (threadIdx.x == 0) ndefer = 0;
     __syncthreads();
-    const int wv = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int lane = threadIdx.x % 64;
     bool ok = true;
-    for (int j = rpa[row] + wv; j < rpa[row + 1]; j += G3_WG / 64) {
-        const int k = cia[j];
-        const float a = va[j];
-        for (int t = rpb[k] + lane; t < rpb[k + 1]; t += 64)
-            ok = ok && sg_insert_add(keys, vals, T - 1, cib[t], a * vb[t]);
-    }
+    sg_walk<G3_WG>(row, rpa, cia, rpb, defer, &ndefer,
+                   [&](int j, int t) { ok = ok && sg_insert_add(keys, vals, T - 1, cib[t], va[j] * vb[t]); });
     if (!ok) atomicOr(err, SG_ERR_PROBE);
     // Compact the table's len entries into C's row (in any order): the table
     // is at least half empty, so sorting it whole would sort mostly padding.
@@ -855,11 +885,12 @@ spmv_status sg_phase(const spgemm *h, int *ci_c, float *v_c, hipStream_t st) {
     }
     if (c[6] > 0) {
         if (SYM)
-            k_sg_g3_count<<<c[6], G3_WG, 0, h->side[0]>>>(mp + b[6], h->g3off, h->tkeys, h->rpa, h->cia, h->rpb,
-                                                          h->cib, h->cnt, h->err);
+            k_sg_g3_count<<<c[6], G3_WG, 0, h->side[0]>>>(mp + b[6], h->g3off, h->tkeys, h->rpa, h->cia,
+                                                          h->rpb, h->cib, h->cnt, h->err);
         else
-            k_sg_g3_fill<<<c[6], G3_WG, 0, h->side[0]>>>(mp + b[6], h->g3off, h->tkeys, h->tvals, h->rpa, h->cia,
-                                                         h->va, h->rpb, h->cib, h->vb, h->rp, ci_c, v_c, h->err);
+            k_sg_g3_fill<<<c[6], G3_WG, 0, h->side[0]>>>(mp + b[6], h->g3off, h->tkeys, h->tvals, h->rpa,
+                                                         h->cia, h->va, h->rpb, h->cib, h->vb, h->rp, ci_c, v_c,
+                                                         h->err);
     }
 #define SG_TB(BIN, WG, TMAX, Q)                                                                                     \
     if (c[BIN] > 0) {                                                                                              \
