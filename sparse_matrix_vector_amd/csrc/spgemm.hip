@@ -331,7 +331,7 @@ __device__ void sg_bitonic(KeyPtr keys, ValPtr vals, unsigned T) {
 // list (`defer`, SG_DEFER slots, `ndefer` zeroed by the caller before a
 // barrier) and are then walked by whole waves, lanes over the B row.  An
 // entry that finds the list full is walked by its thread.
-constexpr int SG_SHORT_B = 16;
+constexpr int SG_SHORT_B = 4;
 constexpr int SG_DEFER = 1024;
 
 template <int WG, typename F>
