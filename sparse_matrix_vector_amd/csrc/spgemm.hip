@@ -32,16 +32,18 @@
 // (measured: 10 ms of the 18 ms accumulation phase on the power-law square),
 // so group 2 gets 16384 slots at most.  Sizing each table to its row also
 // keeps the clearing and the sort proportional to the row.
-// In the workgroup mappings each wave walks entries of A's row and its
-// lanes walk the reached row of B.  Tables are powers of two, the hash of
-// column c is (c * 2654435761) mod size, and no table can fill (distinct
-// columns <= IP < size), so every probe sequence ends; each is still bounded
-// by the table size.  The accumulation phase then writes the row in
-// increasing column order: group 0 ranks each key against its table, the
-// others sort the table (bitonic, empty slots last; for the global tables
-// with the short-distance stages run chunk by chunk in LDS) and copy the
-// first entries.  Values add up in fp32 through atomics, so their low bits vary
-// from run to run; the pattern does not.
+// In the workgroup mappings each thread walks the B rows of short reach (at
+// most SG_SHORT_B entries) of its entries of A's row, and whole waves walk
+// the longer ones, lanes over the B row.  Tables are powers of two, the
+// hash of column c is (c * 2654435761) mod size, and no table can fill
+// (distinct columns <= IP < size), so every probe sequence ends; each is
+// still bounded by the table size.  The accumulation phase then writes the
+// row in increasing column order: group 0 ranks each key against its table;
+// the LDS-table bins move the table's entries to its front and sort those
+// (bitonic); a global-table row compacts its table into C's row, sorts runs
+// of G3_CH entries in LDS and merges them along merge paths.  The bins of a
+// phase run concurrently on side streams.  Values add up in fp32 through
+// atomics, so their low bits vary from run to run; the pattern does not.
 #include "common.hpp"
 
 #include <algorithm>
