@@ -19,13 +19,14 @@
 //                          are staged in LDS and each lane sums whole rows
 //                          (a segmented reduction without atomics);
 //   group 1 (32..511)      one task per row (a wave per row, DPP reduction);
-//   groups 2, 3 (>= 512)   one task per 512-entry chunk of the row, so a row
-//                          gets as many waves as it needs; chunk sums go to
-//                          global memory and the wave finishing a row's last
-//                          chunk adds them in order.
-// One launch runs one wave per task (plus a small kernel that adds the
-// chunk sums of split rows).  Every sum has a fixed order, so results are
-// bit-reproducible run to run.
+//   rows of 2..16 chunks   one workgroup per row: its waves take every
+//                          fourth 512-entry chunk and add their sums in LDS;
+//   longer rows            one task per 512-entry chunk, so such a row gets
+//                          as many waves as it needs; chunk sums go to a
+//                          partial slot and a small second kernel adds them
+//                          in chunk order.
+// One launch runs the workgroup rows, then one wave per task.  Every sum has
+// a fixed order, so results are bit-reproducible run to run.
 #include "common.hpp"
 
 #include <algorithm>
