@@ -92,8 +92,10 @@ typedef enum {
 typedef struct spmv_csr_plan *spmv_csr_t;
 
 /* Bytes of device workspace spmv_csr_create needs for a matrix of this size.
- * thresholds: host int32[3] or NULL for the page's {32, 512, 8192}; valid
- * thresholds satisfy 1 <= t0 < t1 < t2 and t0 <= 256. */
+ * thresholds: host int32[3] or NULL for {128, 512, 8192} (the grouping
+ * page's table starts at 32; a wave task stages 512 entries, so rows up to
+ * 127 entries still share a wave here); valid thresholds satisfy
+ * 1 <= t0 < t1 < t2 and t0 <= 256. */
 spmv_status spmv_csr_plan_size(int32_t n_rows, int32_t nnz, const int32_t *thresholds,
                                size_t *bytes);
 

@@ -82,6 +82,7 @@ struct Meta {
     int wgrow_totals[2];      // {0, number of rows in groups 1-3 applied by one workgroup each}
     int err;
     int max_window;       // largest column span (from a 16-byte boundary) of a block workgroup
+    int max_short;        // longest row of group 0
 };
 
 __device__ __forceinline__ int row_group(int len, int t0, int t1, int t2) {
@@ -174,11 +175,15 @@ __global__ void k_row_stats(int n, const int *__restrict__ rp, int *__restrict__
 
 // Per-workgroup count of rows in each group.
 __global__ __launch_bounds__(WG) void k_plan_count(int n, const int *__restrict__ rp, int t0, int t1,
-                                                   int t2, int *__restrict__ counts) {
+                                                   int t2, int *__restrict__ counts, int *__restrict__ max_short) {
     __shared__ int wc[WAVES][4];
     const int i = blockIdx.x * WG + threadIdx.x;
-    const int g = i < n ? row_group(rp[i + 1] - rp[i], t0, t1, t2) : -1;
+    const int len = i < n ? rp[i + 1] - rp[i] : 0;
+    const int g = i < n ? row_group(len, t0, t1, t2) : -1;
     const int w = threadIdx.x / 64;
+    int ms = g == 0 ? len : 0;
+    for (int off = 32; off > 0; off >>= 1) ms = max(ms, __shfl_xor(ms, off));
+    if (__lane_id() == 0 && ms > 0) atomicMax(max_short, ms);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         const unsigned long long m = __ballot(g == b);
@@ -261,9 +266,14 @@ __global__ __launch_bounds__(WG) void k_plan_scatter(int n, const int *__restric
 // A run of short rows starts at perm position p if row perm[p] does not
 // follow row perm[p-1], or if the two rows start in different windows of
 // `window` nonzeros.  Every run is then a range of consecutive rows whose
-// first entries lie in one window, so it spans at most window + t0 + 2
-// entries from a 16-byte boundary.  Runs longer than SHORT_RMAX rows are cut
+// first entries lie in one window, so it spans at most window + L + 2
+// entries from a 16-byte boundary, L the longest short row; the window is
+// SLOTS - L - 2 (run_window), so a run always fits one task.  Sizing it by
+// the matrix's L rather than the group bound keeps runs long when short rows
+// are much shorter than the bound.  Runs longer than SHORT_RMAX rows are cut
 // into pieces of SHORT_RMAX rows afterwards (k_blocks_write).
+__device__ __forceinline__ int run_window(const Meta *__restrict__ meta) { return SLOTS - meta->max_short - 2; }
+
 __device__ __forceinline__ bool short_head(int p, const int *__restrict__ perm, const int *__restrict__ rp,
                                            int window) {
     if (p == 0) return true;
@@ -273,10 +283,10 @@ __device__ __forceinline__ bool short_head(int p, const int *__restrict__ perm, 
 }
 
 __global__ __launch_bounds__(WG) void k_heads_count(const Meta *__restrict__ meta, const int *__restrict__ perm,
-                                                    const int *__restrict__ rp, int window,
-                                                    int *__restrict__ counts) {
+                                                    const int *__restrict__ rp, int *__restrict__ counts) {
     __shared__ int wc[WAVES];
     const int n0 = meta->bin_offsets[1];
+    const int window = run_window(meta);
     const int p = blockIdx.x * WG + threadIdx.x;
     const bool h = p < n0 && short_head(p, perm, rp, window);
     const unsigned long long m = __ballot(h);
@@ -290,11 +300,11 @@ __global__ __launch_bounds__(WG) void k_heads_count(const Meta *__restrict__ met
 }
 
 __global__ __launch_bounds__(WG) void k_heads_scatter(const Meta *__restrict__ meta, const int *__restrict__ perm,
-                                                      const int *__restrict__ rp, int window,
-                                                      const int *__restrict__ offsets,
+                                                      const int *__restrict__ rp, const int *__restrict__ offsets,
                                                       int *__restrict__ head_pos) {
     __shared__ int wc[WAVES];
     const int n0 = meta->bin_offsets[1];
+    const int window = run_window(meta);
     const int p = blockIdx.x * WG + threadIdx.x;
     const bool h = p < n0 && short_head(p, perm, rp, window);
     const unsigned long long m = __ballot(h);
@@ -988,7 +998,11 @@ Layout make_layout(int n, int nnz, int t0) {
 }
 
 spmv_status check_thresholds(const int32_t *thr, int t[3]) {
-    const int def[3] = {32, 512, 8192};
+    // The first bound is 128, not the page's 32: a task stages 512 entries,
+    // so rows up to 127 entries still pack several to a wave, and a wave per
+    // 32..127-entry row left most of its lanes idle (power-law: 38.4 ->
+    // 36.3 us).  The other bounds are the page's.
+    const int def[3] = {128, 512, 8192};
     for (int k = 0; k < 3; ++k) t[k] = thr ? thr[k] : def[k];
     if (!(t[0] >= 1 && t[0] < t[1] && t[1] < t[2]))
         return fail(SPMV_ERR_INVALID_VALUE, "thresholds must satisfy 1 <= t0 < t1 < t2 (got %d %d %d)", t[0],
@@ -1097,10 +1111,10 @@ spmv_status build_binned_plan(spmv_csr_plan *h, char *ws, const Layout &L, hipSt
     int *heads = reinterpret_cast<int *>(ws + L.heads);
     i32x4 *tasks = reinterpret_cast<i32x4 *>(ws + L.tasks);
     const int nwg = (int)ceil_div(std::max(n, 1), WG);
-    const int window = SLOTS - h->t[0] - 1;
 
     // 1. rows grouped by length: bin_offsets and perm (a stable counting sort)
-    k_plan_count<<<nwg, WG, 0, st>>>(n, h->rp, h->t[0], h->t[1], h->t[2], counts);
+    SPMV_HIP(hipMemsetAsync(&meta->max_short, 0, sizeof(int), st));
+    k_plan_count<<<nwg, WG, 0, st>>>(n, h->rp, h->t[0], h->t[1], h->t[2], counts, &meta->max_short);
     SPMV_LAUNCHED("k_plan_count");
     k_plan_scan<<<1, 1024, 0, st>>>(nwg, 4, counts, offsets, meta->bin_offsets);
     SPMV_LAUNCHED("k_plan_scan");
@@ -1117,11 +1131,11 @@ spmv_status build_binned_plan(spmv_csr_plan *h, char *ws, const Layout &L, hipSt
     k_rowtasks_write<<<nwg, WG, 0, st>>>(meta, n, perm, h->rp, hoffsets, offsets, tasks);
     SPMV_LAUNCHED("k_rowtasks_write");
     // 3. blocks of short rows, after the row tasks
-    k_heads_count<<<nwg, WG, 0, st>>>(meta, perm, h->rp, window, hcounts);
+    k_heads_count<<<nwg, WG, 0, st>>>(meta, perm, h->rp, hcounts);
     SPMV_LAUNCHED("k_heads_count");
     k_plan_scan<<<1, 1024, 0, st>>>(nwg, 1, hcounts, hoffsets, meta->head_totals);
     SPMV_LAUNCHED("k_plan_scan(heads)");
-    k_heads_scatter<<<nwg, WG, 0, st>>>(meta, perm, h->rp, window, hoffsets, heads);
+    k_heads_scatter<<<nwg, WG, 0, st>>>(meta, perm, h->rp, hoffsets, heads);
     SPMV_LAUNCHED("k_heads_scatter");
     k_blocks_count<<<nwg, WG, 0, st>>>(meta, heads, hcounts);
     SPMV_LAUNCHED("k_blocks_count");

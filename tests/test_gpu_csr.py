@@ -24,6 +24,8 @@ S = pytest.importorskip("sparse_matrix_vector_amd")
 pytestmark = pytest.mark.gpu
 
 VARIANTS = {"scalar": S.CSR_SCALAR, "vector": S.CSR_VECTOR, "binned": S.CSR_BINNED}
+PAGE_BOUNDS = (32, 512, 8192)          # the grouping page's table
+DEFAULT_BOUNDS = (128, 512, 8192)      # the library's default (first bound raised for wave64 tasks)
 
 
 def _mat(A):
@@ -55,14 +57,20 @@ def test_plan_bit_exact(name):
     A = _config(name)
     print(f"[plan] {name} n={A.n_rows} nnz={A.nnz}", flush=True)
     rp, ci, v = _mat(A)
-    M = S.CSRMatrix(A.n_rows, A.n_cols, rp, ci, v, S.CSR_BINNED)
-    perm = torch.empty(A.n_rows, dtype=torch.int32, device="cuda")
-    off = M.plan(perm)
-    ooff, operm = oracle.bins(A.row_ptr)
-    assert off == ooff.tolist()
-    assert np.array_equal(host(perm), operm)
-    if name == "powerlaw":
-        assert off[4] - off[3] == 0 and off[3] - off[2] > 500 and off[2] - off[1] > 10000
+    for bounds, given in [(PAGE_BOUNDS, PAGE_BOUNDS), (DEFAULT_BOUNDS, None)]:
+        M = S.CSRMatrix(A.n_rows, A.n_cols, rp, ci, v, S.CSR_BINNED, given)
+        perm = torch.empty(A.n_rows, dtype=torch.int32, device="cuda")
+        off = M.plan(perm)
+        ooff, operm = oracle.bins(A.row_ptr, bounds)
+        assert off == ooff.tolist()
+        assert np.array_equal(host(perm), operm)
+        if name == "powerlaw" and bounds == PAGE_BOUNDS:
+            assert off[4] - off[3] == 0 and off[3] - off[2] > 500 and off[2] - off[1] > 10000
+        x = dev(A.x)
+        y = torch.empty(A.n_rows, device="cuda")
+        M.apply(x, y)
+        yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x)
+        assert_close(host(y), yr, sc, TAU_F32, f"{name} bounds {bounds}")
 
 
 @pytest.mark.parametrize("name", ["tiny", "laplacian", "powerlaw"])
@@ -91,7 +99,7 @@ def test_group_bounds_and_long_rows(variant):
     if variant == "binned":
         perm = torch.empty(A.n_rows, dtype=torch.int32, device="cuda")
         off = M.plan(perm)
-        ooff, operm = oracle.bins(A.row_ptr)
+        ooff, operm = oracle.bins(A.row_ptr, DEFAULT_BOUNDS)
         assert off == ooff.tolist() and np.array_equal(host(perm), operm)
         assert off[4] - off[3] == 3
 
