@@ -104,6 +104,24 @@ def test_group_bounds_and_long_rows(variant):
         assert off[4] - off[3] == 3
 
 
+@pytest.mark.parametrize("lo,hi", [(100, 128), (120, 128), (1, 128)])
+def test_short_rows_near_the_bound(lo, hi):
+    """Short rows up to 127 entries (the default first bound is 128): runs are
+    cut at windows of 512 - L - 2 nonzeros, L the longest short row, so every
+    block still fits one 512-entry task; empty rows mixed in."""
+    rng = np.random.default_rng(lo)
+    lens = rng.integers(lo, hi, 6000)
+    lens[::97] = 0
+    A = gen.random_csr(len(lens), 20_000, lens, seed=lo + 1)
+    print(f"[near bound] {lo}..{hi - 1}", flush=True)
+    M, y = _run(A, S.CSR_BINNED, alpha=-1.0, beta=0.5, y_in=np.ones(A.n_rows, np.float32))
+    yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x, -1.0, 0.5, np.ones(A.n_rows, np.float32))
+    assert_close(y, yr, sc, TAU_F32, f"near bound {lo}")
+    perm = torch.empty(A.n_rows, dtype=torch.int32, device="cuda")
+    off = M.plan(perm)
+    assert off[1] == A.n_rows                     # every row is short under the default bounds
+
+
 def test_workgroup_rows_and_chunked_rows():
     """Rows of 2-16 chunks (one workgroup each, no second kernel) next to
     rows of 1 chunk and of more than 16 chunks (chunk partials), from
