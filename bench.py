@@ -419,6 +419,26 @@ def timed_flush(w, steps, warmup):
     return {"ms_per_apply": sum(ms) / len(ms), "median_ms": ms[len(ms) // 2]}
 
 
+def launch_spread(w, launches, n=200):
+    """Spread of single applies: n launches (rotating over the copies, so each
+    finds its inputs out of cache), each between its own HIP event pair on
+    the launch stream; p10 / median / p90 in microseconds.  A single launch
+    also holds its own ramp and drain, which back-to-back launches overlap."""
+    torch = w.torch
+    for L in launches[: min(len(launches), 8)]:
+        L()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        launches[i % len(launches)]()
+        b.record()
+    torch.cuda.synchronize()
+    us = sorted(1e3 * a.elapsed_time(b) for a, b in ev)
+    q = lambda f: round(us[min(n - 1, int(f * n))], 3)  # noqa: E731
+    return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "launches": n}
+
+
 def copy_reference(nbytes, steps=400):
     """Bandwidth of torch's device copy (nbytes/2 read + nbytes/2 written)
     under the same rotation protocol: what a plain streaming kernel reaches
@@ -706,6 +726,7 @@ def main():
     else:
         meas = timed_rotate(w, args.steps, args.warmup, warm_launches, graph)
     warm = timed_rotate(w, args.steps, args.warmup, warm_launches, graph)
+    spread = launch_spread(w, w.launches)
     ms = meas["ms_per_apply"]
     gflops = w.flops / (ms * 1e-3) / 1e9
     gbs = w.bytes / (ms * 1e-3) / 1e9
@@ -735,6 +756,7 @@ def main():
                      "kernel": getattr(w, "kernel", None) or KERNEL[path]},
         "timing_ms": {k: round(v, 6) for k, v in meas.items()},
         "warm_timing_ms": {k: round(v, 6) for k, v in warm.items()},
+        "single_launch_us": spread,
         "parity": par,
         "copy_reference": copy_reference(w.bytes) if not args.no_copy_ref else None,
     }
