@@ -165,3 +165,49 @@ def test_spgemm_compute_replay():
         print(f"[graph] spgemm replay {i}", flush=True)
         check(None, av)
     G.close()
+
+
+def test_two_streams_at_once():
+    """Applies of different handles on two streams at the same time (CSR
+    plans are read-only during an apply; two SpGEMM handles share the
+    device's side streams) give the results each gives alone."""
+    rng = np.random.default_rng(21)
+    mats = [gen.random_csr(30_000, 30_000, rng.integers(0, 30, 30_000), seed=s) for s in (22, 23)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs, Ms = [], []
+    for A in mats:
+        M = S.CSRMatrix(A.n_rows, A.n_cols, dev(A.row_ptr), dev(A.col_idx), dev(A.vals), S.CSR_BINNED)
+        Ms.append((M, dev(A.x), torch.zeros(A.n_rows, device="cuda")))
+    torch.cuda.synchronize()
+    for (M, x, y), st in zip(Ms, streams):
+        with torch.cuda.stream(st):
+            for _ in range(20):
+                M.apply(x, y)
+    torch.cuda.synchronize()
+    for A, (M, x, y) in zip(mats, Ms):
+        yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x)
+        assert_close(host(y), yr, sc, TAU_F32, "two streams csr")
+    # two SpGEMM products at once
+    Gs, pairs = [], []
+    for s in (24, 25):
+        k, n, m = 1500, 2000, 600
+        blens = np.where(rng.random(k) < 0.03, rng.integers(300, 1200, k), rng.integers(0, 10, k))
+        B = gen.random_csr(k, n, blens, seed=s)
+        alens = np.where(rng.random(m) < 0.1, rng.integers(10, 40, m), rng.integers(0, 5, m))
+        A = gen.random_csr(m, k, alens, seed=s + 10)
+        arrs = [dev(a) for a in (A.row_ptr, A.col_idx, A.vals, B.row_ptr, B.col_idx, B.vals)]
+        Gs.append((S.SpGEMM(m, k, n, *arrs), arrs))
+        pairs.append((n, A, B))
+    torch.cuda.synchronize()
+    results = []
+    for (G, _), st in zip(Gs, streams):
+        with torch.cuda.stream(st):
+            results.append(G.compute(stream=st))
+    torch.cuda.synchronize()
+    print("[streams] csr and spgemm on two streams", flush=True)
+    for (n, A, B), out in zip(pairs, results):
+        orp, oci, ov, osc = oracle.spgemm(n, A.row_ptr, A.col_idx, A.vals, B.row_ptr, B.col_idx, B.vals)
+        assert np.array_equal(host(out[0]), orp) and np.array_equal(host(out[1]), oci)
+        assert np.all(np.abs(host(out[2]).astype(np.float64) - ov) <= TAU_F32 * osc)
+    for G, _ in Gs:
+        G.close()
