@@ -26,6 +26,10 @@ Other workloads (parity-test configs, also used for profiles):
   --path   csr | csr-binned | csr-vector | csr-scalar | ell | hyb | auto | macko | dense | fem | fem-3stage
            (MACKO variants: macko-b1 | macko-b2 | macko-b8 for 1-, 2- or 8-bit
            codes instead of 4, macko-i8 and macko-i8-bN for int8 values)
+  --path rocsparse (CSR configs): torch.sparse's CSR matvec, which runs
+  rocSPARSE's adaptive CSR kernel; a reference, not this library: its
+  event time includes rocSPARSE's per-call set-up, rocprofv3 gives the
+  kernel's own time
   (varlen: 1M rows of 2..10 entries in a +-1000 band, CV 0.43, the HYB range
   of the CV rule; auto: the format that rule picks)
   powerlaw | laplacian / spgemm: C = A * A by the hash-based multi-phase
@@ -67,13 +71,15 @@ KERNEL = {"csr": "k_csr_tasks", "csr-binned": "k_csr_tasks", "csr-vector": "k_cs
           "csr-scalar": "k_csr_scalar", "ell": "k_ell_apply4t", "macko": "k_macko_spmv",
           "dense": "k_gemv_f16", "fem": "k_fe_fused", "fem-3stage": "k_fe_elem", "hyb": "k_ell_apply",
           "auto": None, "fem-pcg": "k_fe_matvec64 + k_pcg_pq + k_pcg_update + k_pcg_direction",
-          "spgemm": "k_sg_* (grouping, allocation, accumulation)"}
+          "spgemm": "k_sg_* (grouping, allocation, accumulation)",
+          "rocsparse": "rocsparse::csrmvn_adaptive_kernel"}
 
 # source file of each path's kernels (for the traffic-record freshness check)
 SOURCE = {"csr": ("csr.hip",), "csr-binned": ("csr.hip",), "csr-vector": ("csr.hip",),
           "csr-scalar": ("csr.hip",), "ell": ("ell.hip",), "macko": ("macko.hip",), "dense": ("dense.hip",),
           "fem": ("fem.hip",), "fem-3stage": ("fem.hip",), "hyb": ("ell.hip", "hyb.hip"),
-          "auto": ("csr.hip", "ell.hip", "hyb.hip"), "fem-pcg": ("fem_solver.hip",), "spgemm": ("spgemm.hip",)}
+          "auto": ("csr.hip", "ell.hip", "hyb.hip"), "fem-pcg": ("fem_solver.hip",), "spgemm": ("spgemm.hip",),
+          "rocsparse": ()}
 for _v in ("b1", "b2", "b8", "i8", "i8-b1", "i8-b2", "i8-b8"):
     KERNEL["macko-" + _v] = "k_macko_spmv"
     SOURCE["macko-" + _v] = ("macko.hip",)
@@ -123,7 +129,23 @@ class Workload:
             # HYB: ELL part (padding included), tail arrays, x, y, and y read
             # and written again for the tail rows
             hyb_bytes = lambda W, r, t: ell_bytes(W) + 8 * t + 4 * r + 4 * (r + 1) + 8 * r
-            if path.startswith("csr"):
+            if path == "rocsparse":
+                # Reference only, not this library: torch.sparse's CSR matvec,
+                # which runs rocSPARSE's adaptive CSR kernel.  Each call also
+                # runs rocSPARSE's per-call set-up, so the event time per apply
+                # is not its kernel time; rocprofv3 gives that.
+                self.bytes = csr_bytes
+                base = (dev(A.row_ptr), dev(A.col_idx), dev(A.vals), dev(A.x))
+
+                def make(arrs):
+                    rp, ci, v, x = arrs
+                    M = torch.sparse_csr_tensor(rp, ci, v, size=(A.n_rows, A.n_cols))
+                    y = torch.zeros(A.n_rows, device="cuda")
+                    return (lambda: y.copy_(torch.mv(M, x))), y, M
+                self._setup(base, make, copies)
+                self.shape = {"n_rows": A.n_rows, "n_cols": A.n_cols, "nnz": A.nnz,
+                              "library": "torch.sparse_csr_tensor @ x (rocSPARSE)"}
+            elif path.startswith("csr"):
                 var = {"csr": S.CSR_AUTO, "csr-binned": S.CSR_BINNED, "csr-vector": S.CSR_VECTOR,
                        "csr-scalar": S.CSR_SCALAR}[path]
                 self.bytes = csr_bytes
@@ -717,7 +739,8 @@ def main():
         par = parity(w, ref_fn)
         log(f"[bench] parity {par}")
 
-    graph = not args.no_graph
+    # torch.sparse's matvec sets up rocSPARSE on every call, so it is launched eagerly
+    graph = not args.no_graph and path != "rocsparse"
     warm_launches = [w.launches[0]] * min(len(w.launches), 16)
     if args.protocol == "rotate":
         meas = timed_rotate(w, args.steps, args.warmup, w.launches, graph)
