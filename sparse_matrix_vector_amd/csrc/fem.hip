@@ -14,9 +14,11 @@
 // rho_e^p.  An edof entry outside [0, n_dof) (the mesh uses -1 for a
 // clamped DOF) contributes no gather and no scatter.
 //
-// gfx950 shape of the fused kernel: one lane per element, Ke staged in LDS
-// once per workgroup and read with broadcast (same-address) LDS reads, the
-// element's 24 DOF indices read with six 16-byte loads, 24 gathers of x,
+// gfx950 shape of the fused kernel: one lane per element; Ke is the same
+// for every lane, so the product reads it with scalar loads (the constant
+// cache is the on-chip home of section 5.2 here) and uses it as scalar
+// operands of the FMAs, with no LDS staging and no barrier; the element's
+// 24 DOF indices are read with six 16-byte loads, 24 gathers of x,
 // 576 FMAs, then the contributions to the face shared with the next lane's
 // element are added in registers (wave shifts), and the rest go out as fp32
 // atomic adds (hardware global_atomic_add_f32): 12 instead of 24 per
@@ -72,8 +74,6 @@ __global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const
                                                     const float *__restrict__ rho, int penalty,
                                                     const float *__restrict__ Ke, float alpha,
                                                     const float *__restrict__ x, float *__restrict__ y) {
-    __shared__ __attribute__((aligned(16))) float ke[NDOF_E * NDOF_E];
-    stage_ke(ke, Ke);
     // lanes past the last element stay (the wave exchange below needs all
     // 64) with every DOF index -1
     const int e = blockIdx.x * FE_WG + threadIdx.x;
@@ -96,13 +96,7 @@ __global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const
     for (int a = 0; a < NDOF_E; ++a) {
         float f = 0.0f;
 #pragma unroll
-        for (int b = 0; b < NDOF_E; b += 4) {
-            const f32x4 k4 = *reinterpret_cast<const f32x4 *>(ke + a * NDOF_E + b);
-            f = fmaf(k4.x, u[b], f);
-            f = fmaf(k4.y, u[b + 1], f);
-            f = fmaf(k4.z, u[b + 2], f);
-            f = fmaf(k4.w, u[b + 3], f);
-        }
+        for (int b = 0; b < NDOF_E; ++b) f = fmaf(Ke[a * NDOF_E + b], u[b], f);
         fa[a] = s * f;
     }
     fe_combine_x_neighbours(d, fa, n_dof);

@@ -167,7 +167,8 @@ __global__ void k_sv_zero64(int n, double *__restrict__ y) {
 
 // acc += sum_e rho_e^p P_e^T Ke P_e x, with the element product and the
 // scatter in fp64 (products of fp32 values are exact in fp64).  The fused
-// shape of fem_matvec_apply: one lane per element, Ke in LDS, 24 gathers,
+// shape of fem_matvec_apply: one lane per element, Ke through the scalar
+// cache, 24 gathers,
 // the shared-face contributions of x-neighbours combined in registers, and
 // the remaining atomic adds.  Does nothing when `st` says the iteration is
 // done.
@@ -176,12 +177,7 @@ __global__ __launch_bounds__(SV_WG) void k_fe_matvec64(int n_elem, int n_dof, co
                                                        const float *__restrict__ Ke, const float *__restrict__ x,
                                                        double *__restrict__ acc, const SolverState *st) {
     typedef int i32x4 __attribute__((ext_vector_type(4)));
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
     if (st && st->done) return;   // uniform
-    __shared__ __attribute__((aligned(16))) float ke[NDOF_E * NDOF_E];
-    if (threadIdx.x < NDOF_E * NDOF_E / 4)
-        reinterpret_cast<f32x4 *>(ke)[threadIdx.x] = reinterpret_cast<const f32x4 *>(Ke)[threadIdx.x];
-    __syncthreads();
     // lanes past the last element stay for the wave exchange, with index -1
     const int e = blockIdx.x * SV_WG + threadIdx.x;
     const bool live = e < n_elem;
@@ -210,13 +206,7 @@ __global__ __launch_bounds__(SV_WG) void k_fe_matvec64(int n_elem, int n_dof, co
     for (int a = 0; a < NDOF_E; ++a) {
         double f = 0.0;
 #pragma unroll
-        for (int b = 0; b < NDOF_E; b += 4) {
-            const f32x4 k4 = *reinterpret_cast<const f32x4 *>(ke + a * NDOF_E + b);
-            f = fma((double)k4.x, (double)u[b], f);
-            f = fma((double)k4.y, (double)u[b + 1], f);
-            f = fma((double)k4.z, (double)u[b + 2], f);
-            f = fma((double)k4.w, (double)u[b + 3], f);
-        }
+        for (int b = 0; b < NDOF_E; ++b) f = fma((double)Ke[a * NDOF_E + b], (double)u[b], f);
         fa[a] = s * f;
     }
     fe_combine_x_neighbours(d, fa, n_dof);
