@@ -77,8 +77,8 @@ KERNEL = {"csr": "k_csr_tasks", "csr-binned": "k_csr_tasks", "csr-vector": "k_cs
 # source file of each path's kernels (for the traffic-record freshness check)
 SOURCE = {"csr": ("csr.hip",), "csr-binned": ("csr.hip",), "csr-vector": ("csr.hip",),
           "csr-scalar": ("csr.hip",), "ell": ("ell.hip",), "macko": ("macko.hip",), "dense": ("dense.hip",),
-          "fem": ("fem.hip",), "fem-3stage": ("fem.hip",), "hyb": ("ell.hip", "hyb.hip"),
-          "auto": ("csr.hip", "ell.hip", "hyb.hip"), "fem-pcg": ("fem_solver.hip",), "spgemm": ("spgemm.hip",),
+          "fem": ("fem.hip", "fem_common.hpp"), "fem-3stage": ("fem.hip",), "hyb": ("ell.hip", "hyb.hip"),
+          "auto": ("csr.hip", "ell.hip", "hyb.hip"), "fem-pcg": ("fem_solver.hip", "fem_common.hpp"), "spgemm": ("spgemm.hip",),
           "rocsparse": ()}
 for _v in ("b1", "b2", "b8", "i8", "i8-b1", "i8-b2", "i8-b8"):
     KERNEL["macko-" + _v] = "k_macko_spmv"

@@ -19,11 +19,13 @@
 // cache is the on-chip home of section 5.2 here) and uses it as scalar
 // operands of the FMAs, with no LDS staging and no barrier; the element's
 // 24 DOF indices are read with six 16-byte loads, 24 gathers of x,
-// 576 FMAs, then the contributions to the face shared with the next lane's
-// element are added in registers (wave shifts), and the rest go out as fp32
-// atomic adds (hardware global_atomic_add_f32): 12 instead of 24 per
-// element when elements are numbered x-fastest.  The beta pass runs first
-// as a separate small kernel, because atomics only add.
+// 576 FMAs, then the wave's contributions are merged along x-lines of
+// nodes in LDS (the face shared with the next lane's element is summed
+// there) and go out as fp32 atomic adds (hardware global_atomic_add_f32)
+// with consecutive lanes on consecutive DOFs: 12 instead of 24 adds per
+// element when elements are numbered x-fastest, ~16 lanes per memory-side
+// request.  The beta pass runs first as a separate small kernel, because
+// atomics only add.
 #include "common.hpp"
 #include "fem_common.hpp"
 
@@ -74,6 +76,8 @@ __global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const
                                                     const float *__restrict__ rho, int penalty,
                                                     const float *__restrict__ Ke, float alpha,
                                                     const float *__restrict__ x, float *__restrict__ y) {
+    __shared__ int line_dof[FE_WG / 64][3 * 65];
+    __shared__ float line_val[FE_WG / 64][3 * 65];
     // lanes past the last element stay (the wave exchange below needs all
     // 64) with every DOF index -1
     const int e = blockIdx.x * FE_WG + threadIdx.x;
@@ -99,10 +103,7 @@ __global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const
         for (int b = 0; b < NDOF_E; ++b) f = fmaf(Ke[a * NDOF_E + b], u[b], f);
         fa[a] = s * f;
     }
-    fe_combine_x_neighbours(d, fa, n_dof);
-#pragma unroll
-    for (int a = 0; a < NDOF_E; ++a)
-        if ((unsigned)d[a] < (unsigned)n_dof) atomicAdd(y + d[a], fa[a]);
+    fe_scatter_lines(d, fa, n_dof, y, line_dof[threadIdx.x >> 6], line_val[threadIdx.x >> 6]);
 }
 
 // ---- three-stage comparator ----

@@ -168,16 +168,17 @@ __global__ void k_sv_zero64(int n, double *__restrict__ y) {
 // acc += sum_e rho_e^p P_e^T Ke P_e x, with the element product and the
 // scatter in fp64 (products of fp32 values are exact in fp64).  The fused
 // shape of fem_matvec_apply: one lane per element, Ke through the scalar
-// cache, 24 gathers,
-// the shared-face contributions of x-neighbours combined in registers, and
-// the remaining atomic adds.  Does nothing when `st` says the iteration is
-// done.
+// cache, 24 gathers, and the contributions merged along x-lines of nodes in
+// LDS before the fp64 atomic adds.  Does nothing when `st` says the
+// iteration is done.
 __global__ __launch_bounds__(SV_WG) void k_fe_matvec64(int n_elem, int n_dof, const int *__restrict__ edof,
                                                        const float *__restrict__ rho, int penalty,
                                                        const float *__restrict__ Ke, const float *__restrict__ x,
                                                        double *__restrict__ acc, const SolverState *st) {
     typedef int i32x4 __attribute__((ext_vector_type(4)));
     if (st && st->done) return;   // uniform
+    __shared__ int line_dof[SV_WG / 64][3 * 65];
+    __shared__ double line_val[SV_WG / 64][3 * 65];
     // lanes past the last element stay for the wave exchange, with index -1
     const int e = blockIdx.x * SV_WG + threadIdx.x;
     const bool live = e < n_elem;
@@ -209,10 +210,7 @@ __global__ __launch_bounds__(SV_WG) void k_fe_matvec64(int n_elem, int n_dof, co
         for (int b = 0; b < NDOF_E; ++b) f = fma((double)Ke[a * NDOF_E + b], (double)u[b], f);
         fa[a] = s * f;
     }
-    fe_combine_x_neighbours(d, fa, n_dof);
-#pragma unroll
-    for (int a = 0; a < NDOF_E; ++a)
-        if ((unsigned)d[a] < (unsigned)n_dof) atomicAdd(acc + d[a], fa[a]);
+    fe_scatter_lines(d, fa, n_dof, acc, line_dof[threadIdx.x >> 6], line_val[threadIdx.x >> 6]);
 }
 
 // diag[edof[e][a]] += rho_e^p Ke[a][a] over the element's free DOFs.
