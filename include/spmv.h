@@ -20,7 +20,9 @@
  *     SPMV_ERR_OVERFLOW.
  *   - "device" pointers point to GPU memory (hipMalloc / torch CUDA tensors),
  *     "host" pointers to CPU memory.  All memory is owned by the caller; the
- *     library never frees what it is given.  A CSR handle *borrows* the
+ *     library never allocates device memory and never frees what it is
+ *     given.  Device scratch and plan storage come in as workspace or
+ *     scratch arguments sized by the *_size queries.  A CSR handle *borrows* the
  *     matrix arrays: they must stay allocated and structurally unchanged until
  *     spmv_csr_destroy (values may be rewritten in place between applies).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
@@ -55,16 +57,32 @@ typedef enum {
 /* Message of the last failing call on this thread ("" if none). */
 const char *spmv_last_error(void);
 
+/* Device scratch of the synchronous statistics, planning and conversion
+ * calls: spmv_csr_row_stats, spmv_hyb_width, spmv_hyb_tail_size,
+ * spmv_ell_from_csr, spmv_hyb_from_csr, spmv_auto_plan and
+ * spgemm_workspace_size.  They keep reduction counters and per-workgroup
+ * counts there, so that the library itself allocates no device memory.
+ * *bytes receives the size for a matrix of n_rows rows (for SpGEMM: the rows
+ * of A): 256 bytes plus 8 bytes per 256 rows, rounded up to 256.  The caller
+ * allocates it (device memory, 256-byte aligned) and keeps ownership; its
+ * contents on entry do not matter and on return are unspecified.  Those
+ * calls synchronise, so one scratch buffer may serve call after call on one
+ * stream.  Host only.  SPMV_ERR_INVALID_VALUE for n_rows < 0. */
+spmv_status spmv_scratch_size(int32_t n_rows, size_t *bytes);
+
 /* ======================================================================== */
 /* Row statistics and format choice                                         */
 /* ======================================================================== */
 
-/* Longest row, sum and sum of squares of the row lengths of a CSR row_ptr.
- * row_ptr: device int32[n_rows+1].  Outputs: host.  Synchronises `stream`.
+/* Longest row, sum and sum of squares of the row lengths of a CSR row_ptr
+ * (the statistics of the CV rule below).
+ * row_ptr: device int32[n_rows+1].  Outputs: host.  scratch: device, at
+ * least spmv_scratch_size(n_rows) bytes.  Synchronises `stream`.
  * SPMV_ERR_INVALID_MATRIX if some row has negative length. */
 spmv_status spmv_csr_row_stats(int32_t n_rows, const int32_t *row_ptr,
                                int32_t *max_len, int64_t *sum_len,
-                               int64_t *sum_len_sq, void *stream);
+                               int64_t *sum_len_sq, void *scratch,
+                               size_t scratch_bytes, void *stream);
 
 /* Format recommendation by the coefficient of variation (CV) of the row
  * lengths ("Why SpMV needs CUDA optimisation", section 2.2): CV < 0.3 -> ELL,
@@ -101,8 +119,10 @@ spmv_status spmv_csr_plan_size(int32_t n_rows, int32_t nnz, const int32_t *thres
 
 /* Validates the matrix on the GPU (row_ptr[0] == 0, row_ptr[n_rows] == nnz,
  * non-decreasing row_ptr, 0 <= col < n_cols) and, for BINNED/AUTO, builds
- * the row-grouping plan in `workspace` (device, >= spmv_csr_plan_size bytes,
- * owned by the caller, kept until destroy).  The grouping: group g holds rows
+ * the row-grouping plan in `workspace` (device, 256-byte aligned, >=
+ * spmv_csr_plan_size bytes, owned by the caller, kept until destroy).
+ * SCALAR and VECTOR need only 256 bytes of workspace, used for the
+ * validation flags during this call and free again afterwards.  The grouping: group g holds rows
  * with t[g-1] <= length < t[g]; `perm` lists rows group by group in
  * ascending row order.  row_ptr, col_idx: device int32; vals: device fp32.
  * Column order inside a row is free (duplicates are summed).  Synchronises
@@ -153,11 +173,13 @@ spmv_status spmv_csr_destroy(spmv_csr_t h);
 /* Converts CSR (device arrays) to ELL of the given width (device outputs
  * int32 / fp32 [width * n_rows]).  width must be >= the longest row
  * (SPMV_ERR_INVALID_VALUE otherwise).  Row order of entries is kept.
+ * scratch: device, >= spmv_scratch_size(n_rows) bytes.
  * Synchronises `stream` (it checks the width and the matrix first). */
 spmv_status spmv_ell_from_csr(int32_t n_rows, int32_t n_cols, int32_t nnz,
                               const int32_t *row_ptr, const int32_t *col_idx,
                               const float *vals, int32_t width, int32_t *ell_col,
-                              float *ell_val, void *stream);
+                              float *ell_val, void *scratch, size_t scratch_bytes,
+                              void *stream);
 
 /* y = alpha * A * x + beta * y for an ELL matrix; slots are summed in slot
  * order in fp32.  ell_col entries must be -1 or in [0, n_cols) (as written
@@ -184,21 +206,35 @@ spmv_status spmv_ell_apply(int32_t n_rows, int32_t n_cols, int32_t width,
 /* Width rule: the smallest W with den * sum_i min(len_i, W) >= num * nnz
  * (exact integers; needs 0 <= num <= den, den > 0), and the tail sizes for
  * that W: n_tail_rows = #rows longer than W, tail_nnz = their entries past
- * W.  row_ptr: device int32[n_rows+1].  Outputs: host.  Synchronises. */
+ * W.  row_ptr: device int32[n_rows+1].  Outputs: host.  scratch: device,
+ * >= spmv_scratch_size(n_rows) bytes.  Synchronises. */
 spmv_status spmv_hyb_width(int32_t n_rows, const int32_t *row_ptr, int32_t num, int32_t den,
-                           int32_t *width, int32_t *n_tail_rows, int64_t *tail_nnz, void *stream);
+                           int32_t *width, int32_t *n_tail_rows, int64_t *tail_nnz, void *scratch,
+                           size_t scratch_bytes, void *stream);
+
+/* Tail sizes of the HYB split at an explicit width W >= 0 (the sizes the
+ * tail arrays of spmv_hyb_from_csr need): n_tail_rows = #rows longer than
+ * W, tail_nnz = the sum of (len_i - W) over those rows.  row_ptr: device
+ * int32[n_rows+1]; outputs: host; scratch as above.  SPMV_ERR_INVALID_MATRIX
+ * if some row has negative length.  Synchronises. */
+spmv_status spmv_hyb_tail_size(int32_t n_rows, const int32_t *row_ptr, int32_t width,
+                               int32_t *n_tail_rows, int64_t *tail_nnz, void *scratch,
+                               size_t scratch_bytes, void *stream);
 
 /* Splits a CSR matrix (device arrays) into HYB of width `width`.  Outputs
  * (device, caller-allocated): ell_col / ell_val [width * n_rows],
  * tail_rows [n_tail_rows], tail_rp [n_tail_rows + 1], tail_col / tail_val
  * [tail_nnz].  n_tail_rows / tail_nnz must be the sizes this width gives
- * (spmv_hyb_width; SPMV_ERR_INVALID_VALUE otherwise).  Checks the matrix
+ * (spmv_hyb_width or spmv_hyb_tail_size; SPMV_ERR_INVALID_VALUE otherwise,
+ * before anything is written).  scratch: device, >=
+ * spmv_scratch_size(n_rows) bytes.  Checks the matrix
  * (SPMV_ERR_INVALID_MATRIX).  Synchronises. */
 spmv_status spmv_hyb_from_csr(int32_t n_rows, int32_t n_cols, int32_t nnz, const int32_t *row_ptr,
                               const int32_t *col_idx, const float *vals, int32_t width,
                               int32_t *ell_col, float *ell_val, int32_t n_tail_rows,
                               int64_t tail_nnz, int32_t *tail_rows, int32_t *tail_rp,
-                              int32_t *tail_col, float *tail_val, void *stream);
+                              int32_t *tail_col, float *tail_val, void *scratch,
+                              size_t scratch_bytes, void *stream);
 
 /* y = alpha * A * x + beta * y for a HYB matrix: the ELL part writes
  * alpha * (ELL part) x + beta * y, then each tail row adds alpha * its tail
@@ -225,15 +261,17 @@ typedef struct {
 
 typedef struct spmv_auto *spmv_auto_t;
 
-/* Row statistics and the choice (device row_ptr; plan: host).  Synchronises. */
+/* Row statistics and the choice (device row_ptr; plan: host; scratch:
+ * device, >= spmv_scratch_size(n_rows) bytes).  Synchronises. */
 spmv_status spmv_auto_plan(int32_t n_rows, int32_t n_cols, int32_t nnz, const int32_t *row_ptr,
-                           spmv_auto_plan_t *plan, void *stream);
+                           spmv_auto_plan_t *plan, void *scratch, size_t scratch_bytes, void *stream);
 
 /* Builds the planned format in `workspace` (device, 256-byte aligned, at
  * least plan->workspace_bytes).  The handle borrows the CSR arrays when the
  * format is CSR; ELL and HYB keep their own copy in the workspace (for HYB
  * also a binned CSR plan of the tail, which spmv_auto_apply runs through
- * spmv_csr_apply_rows).  Synchronises. */
+ * spmv_csr_apply_rows), and the conversion's scratch is part of it.
+ * Synchronises. */
 spmv_status spmv_auto_create(spmv_auto_t *h, const spmv_auto_plan_t *plan, int32_t n_rows,
                              int32_t n_cols, int32_t nnz, const int32_t *row_ptr,
                              const int32_t *col_idx, const float *vals, void *workspace,
@@ -353,19 +391,26 @@ spmv_status fem_matvec_threestage(int32_t n_elem, int32_t n_dof, const int32_t *
 /* preconditioned CG around the fused matvec, with an iteration cap;        */
 /* section 4.1: the condition number of K by power iteration).  The        */
 /* operator arguments (n_elem, n_dof, edof, rho, penalty, Ke) are those of  */
-/* fem_matvec_apply, with the same validation.  Vectors are fp32 device     */
-/* arrays of n_dof entries; inner products are accumulated in fp64.  The    */
+/* fem_matvec_apply, with the same validation.  The caller's vectors (f, u, */
+/* v0) are fp32 device arrays of n_dof entries; the iteration keeps its     */
+/* vectors in fp64 in the workspace, accumulates inner products in fp64,    */
+/* and sums each matvec in 64-bit fixed point (element products in fp64,    */
+/* integer atomic adds, scale set per product from max|x|), so that results */
+/* and iteration counts are the same bit for bit from run to run.  The      */
 /* workspace is device memory, 256-byte aligned, of at least the size       */
 /* fem_solver_workspace_size returns; it is not freed by these calls.       */
 /* ======================================================================== */
 
 /* diag[d] = sum of rho_e^penalty * Ke[a][a] over the elements e and local
- * DOFs a with edof[e][a] = d: the Jacobi preconditioner.  Asynchronous. */
+ * DOFs a with edof[e][a] = d: the Jacobi preconditioner, summed with fp32
+ * atomic adds (the solver computes its own copy in fixed point).
+ * Asynchronous. */
 spmv_status fem_jacobi_diagonal(int32_t n_elem, int32_t n_dof, const int32_t *edof, const float *rho,
                                 int32_t penalty, const float *Ke, float *diag, void *stream);
 
-/* Workspace bytes for the calls below; max_history >= the `iterations` of
- * fem_lambda_max / fem_lambda_min (0 for fem_pcg_solve alone). */
+/* Workspace bytes for the calls below (about 64 bytes per DOF plus 64 KB);
+ * max_history >= the `iterations` of fem_lambda_max / fem_lambda_min (0 for
+ * fem_pcg_solve alone). */
 spmv_status fem_solver_workspace_size(int32_t n_dof, int32_t max_history, size_t *bytes);
 
 /* Solves K u = f by Jacobi-PCG from the initial guess in u (device, fp32,
@@ -414,10 +459,12 @@ typedef struct spgemm *spgemm_t;
 
 /* Workspace bytes for spgemm_create on these A and B (device arrays).
  * Validates both (SPMV_ERR_INVALID_MATRIX for a row_ptr that is not
- * monotone from 0 to nnz or a column out of range).  Synchronises. */
+ * monotone from 0 to nnz or a column out of range).  scratch: device, >=
+ * spmv_scratch_size(m) bytes.  Synchronises. */
 spmv_status spgemm_workspace_size(int32_t m, int32_t k, int32_t n, int32_t nnz_a, const int32_t *rp_a,
                                   const int32_t *ci_a, int32_t nnz_b, const int32_t *rp_b,
-                                  const int32_t *ci_b, size_t *bytes, void *stream);
+                                  const int32_t *ci_b, size_t *bytes, void *scratch,
+                                  size_t scratch_bytes, void *stream);
 
 /* Grouping and allocation phase: validates, counts the distinct columns of
  * every row of C and their offsets.  The handle borrows A, B and the

@@ -22,13 +22,15 @@ from . import _lib
 __all__ = [
     "SpmvError", "STATUS", "CSR_AUTO", "CSR_SCALAR", "CSR_VECTOR", "CSR_BINNED",
     "FORMAT_ELL", "FORMAT_HYB", "FORMAT_CSR", "lib",
-    "spmv_csr_row_stats", "spmv_format_recommend", "spmv_csr_plan_size", "spmv_csr_create",
+    "spmv_scratch_size", "spmv_csr_row_stats", "spmv_format_recommend", "spmv_csr_plan_size", "spmv_csr_create",
     "spmv_csr_apply", "spmv_csr_get_plan", "spmv_csr_info", "spmv_csr_destroy",
     "spmv_ell_from_csr", "spmv_ell_apply", "macko_encode_size", "macko_encode", "macko_spmv",
     "macko_quantize_i8", "macko_spmv_i8", "macko_decode_columns", "dense_gemv_f16", "fem_matvec_apply", "fem_threestage_size",
     "fem_matvec_threestage", "fem_jacobi_diagonal", "fem_solver_workspace_size", "fem_pcg_solve",
     "fem_lambda_max", "fem_lambda_min", "spgemm_workspace_size", "spgemm_create", "spgemm_info",
-    "spgemm_compute", "spgemm_destroy", "SpGEMM", "CSRMatrix",
+    "spgemm_compute", "spgemm_destroy", "SpGEMM", "CSRMatrix", "spmv_hyb_width", "spmv_hyb_tail_size",
+    "spmv_hyb_from_csr", "spmv_hyb_apply", "HYBMatrix", "spmv_auto_plan", "spmv_auto_create", "spmv_auto_apply",
+    "spmv_auto_destroy", "AutoMatrix",
 ]
 
 STATUS = {0: "SPMV_OK", 1: "SPMV_ERR_INVALID_VALUE", 2: "SPMV_ERR_INVALID_MATRIX",
@@ -116,14 +118,33 @@ def _u32_dtype():
 
 
 # ---------------------------------------------------------------------------
+# Device scratch of the synchronous calls
+# ---------------------------------------------------------------------------
+def spmv_scratch_size(n_rows) -> int:
+    out = ctypes.c_size_t()
+    _call("spmv_scratch_size", int(n_rows), ctypes.byref(out))
+    return out.value
+
+
+def _scratch(scratch, n_rows, like):
+    """(pointer, bytes) of the caller's scratch tensor, or of a new one of
+    spmv_scratch_size(n_rows) bytes on like's device (torch allocates it)."""
+    if scratch is None:
+        import torch
+        scratch = torch.empty(spmv_scratch_size(n_rows), dtype=torch.uint8, device=like.device)
+    return scratch, scratch.data_ptr(), scratch.numel() * scratch.element_size()
+
+
+# ---------------------------------------------------------------------------
 # Row statistics and format choice
 # ---------------------------------------------------------------------------
-def spmv_csr_row_stats(row_ptr, stream=None):
+def spmv_csr_row_stats(row_ptr, stream=None, scratch=None):
     """(max_len, sum_len, sum_len_sq) of a device int32 row_ptr."""
     n = row_ptr.numel() - 1
     m, s, q = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    keep, sp, sb = _scratch(scratch, n, row_ptr)
     _call("spmv_csr_row_stats", n, _dev(row_ptr, _i32_dtype(), "row_ptr"), ctypes.byref(m),
-          ctypes.byref(s), ctypes.byref(q), _stream(stream, row_ptr))
+          ctypes.byref(s), ctypes.byref(q), sp, sb, _stream(stream, row_ptr))
     return m.value, s.value, q.value
 
 
@@ -202,10 +223,10 @@ class CSRMatrix:
         import torch
         self.n_rows, self.n_cols = int(n_rows), int(n_cols)
         self._arrays = (row_ptr, col_idx, vals)          # borrowed by the handle: keep alive
-        self.workspace = None
-        if variant in (CSR_AUTO, CSR_BINNED):
-            nb = spmv_csr_plan_size(n_rows, col_idx.numel(), thresholds)
-            self.workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=row_ptr.device)
+        # BINNED / AUTO keep their plan here; SCALAR / VECTOR use 256 bytes
+        # of it while the handle is created
+        nb = spmv_csr_plan_size(n_rows, col_idx.numel(), thresholds) if variant in (CSR_AUTO, CSR_BINNED) else 256
+        self.workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=row_ptr.device)
         self.handle = spmv_csr_create(n_rows, n_cols, row_ptr, col_idx, vals, variant, thresholds,
                                       self.workspace, stream)
 
@@ -238,11 +259,12 @@ class CSRMatrix:
 # ---------------------------------------------------------------------------
 # ELL
 # ---------------------------------------------------------------------------
-def spmv_ell_from_csr(n_rows, n_cols, row_ptr, col_idx, vals, width, ell_col, ell_val, stream=None):
+def spmv_ell_from_csr(n_rows, n_cols, row_ptr, col_idx, vals, width, ell_col, ell_val, stream=None, scratch=None):
+    keep, sp, sb = _scratch(scratch, n_rows, row_ptr)
     _call("spmv_ell_from_csr", int(n_rows), int(n_cols), int(col_idx.numel()),
           _dev(row_ptr, _i32_dtype(), "row_ptr"), _dev(col_idx, _i32_dtype(), "col_idx"),
           _dev(vals, _f32_dtype(), "vals"), int(width), _dev(ell_col, _i32_dtype(), "ell_col"),
-          _dev(ell_val, _f32_dtype(), "ell_val"), _stream(stream, row_ptr))
+          _dev(ell_val, _f32_dtype(), "ell_val"), sp, sb, _stream(stream, row_ptr))
 
 
 def spmv_ell_apply(n_rows, n_cols, width, ell_col, ell_val, alpha, x, beta, y, stream=None):
@@ -258,22 +280,33 @@ def spmv_ell_apply(n_rows, n_cols, width, ell_col, ell_val, alpha, x, beta, y, s
 HYB_ELL_NUM, HYB_ELL_DEN = 7, 10
 
 
-def spmv_hyb_width(n_rows, row_ptr, num=HYB_ELL_NUM, den=HYB_ELL_DEN, stream=None):
+def spmv_hyb_width(n_rows, row_ptr, num=HYB_ELL_NUM, den=HYB_ELL_DEN, stream=None, scratch=None):
     """(width, n_tail_rows, tail_nnz) of the width rule.  Synchronises."""
     w, r, t = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    keep, sp, sb = _scratch(scratch, n_rows, row_ptr)
     _call("spmv_hyb_width", int(n_rows), _dev(row_ptr, _i32_dtype(), "row_ptr"), int(num), int(den),
-          ctypes.byref(w), ctypes.byref(r), ctypes.byref(t), _stream(stream, row_ptr))
+          ctypes.byref(w), ctypes.byref(r), ctypes.byref(t), sp, sb, _stream(stream, row_ptr))
     return w.value, r.value, t.value
 
 
+def spmv_hyb_tail_size(n_rows, row_ptr, width, stream=None, scratch=None):
+    """(n_tail_rows, tail_nnz) of the HYB split at an explicit width.  Synchronises."""
+    r, t = ctypes.c_int32(), ctypes.c_int64()
+    keep, sp, sb = _scratch(scratch, n_rows, row_ptr)
+    _call("spmv_hyb_tail_size", int(n_rows), _dev(row_ptr, _i32_dtype(), "row_ptr"), int(width),
+          ctypes.byref(r), ctypes.byref(t), sp, sb, _stream(stream, row_ptr))
+    return r.value, t.value
+
+
 def spmv_hyb_from_csr(n_rows, n_cols, row_ptr, col_idx, vals, width, n_tail_rows, tail_nnz,
-                      ell_col, ell_val, tail_rows, tail_rp, tail_col, tail_val, stream=None):
+                      ell_col, ell_val, tail_rows, tail_rp, tail_col, tail_val, stream=None, scratch=None):
+    keep, sp, sb = _scratch(scratch, n_rows, row_ptr)
     _call("spmv_hyb_from_csr", int(n_rows), int(n_cols), int(col_idx.numel()),
           _dev(row_ptr, _i32_dtype(), "row_ptr"), _dev(col_idx, _i32_dtype(), "col_idx"),
           _dev(vals, _f32_dtype(), "vals"), int(width), _dev(ell_col, _i32_dtype(), "ell_col"),
           _dev(ell_val, _f32_dtype(), "ell_val"), int(n_tail_rows), int(tail_nnz),
           _dev(tail_rows, _i32_dtype(), "tail_rows"), _dev(tail_rp, _i32_dtype(), "tail_rp"),
-          _dev(tail_col, _i32_dtype(), "tail_col"), _dev(tail_val, _f32_dtype(), "tail_val"),
+          _dev(tail_col, _i32_dtype(), "tail_col"), _dev(tail_val, _f32_dtype(), "tail_val"), sp, sb,
           _stream(stream, row_ptr))
 
 
@@ -294,10 +327,12 @@ class HYBMatrix:
                  stream=None):
         import torch
         self.n_rows, self.n_cols = int(n_rows), int(n_cols)
-        w, r, t = spmv_hyb_width(n_rows, row_ptr, num, den, stream)
-        if width is not None and int(width) != w:
+        scratch = torch.empty(spmv_scratch_size(n_rows), dtype=torch.uint8, device=row_ptr.device)
+        if width is None:
+            w, r, t = spmv_hyb_width(n_rows, row_ptr, num, den, stream, scratch)
+        else:
             w = int(width)
-            r, t = _tail_size(row_ptr, w)
+            r, t = spmv_hyb_tail_size(n_rows, row_ptr, w, stream, scratch)
         self.width, self.n_tail_rows, self.tail_nnz = w, r, t
         d = row_ptr.device
         self.ell_col = torch.empty(w * self.n_rows, dtype=torch.int32, device=d)
@@ -307,7 +342,7 @@ class HYBMatrix:
         self.tail_col = torch.empty(t, dtype=torch.int32, device=d)
         self.tail_val = torch.empty(t, dtype=torch.float32, device=d)
         spmv_hyb_from_csr(n_rows, n_cols, row_ptr, col_idx, vals, w, r, t, self.ell_col, self.ell_val,
-                          self.tail_rows, self.tail_rp, self.tail_col, self.tail_val, stream)
+                          self.tail_rows, self.tail_rp, self.tail_col, self.tail_val, stream, scratch)
 
     def apply(self, x, y, alpha=1.0, beta=0.0, stream=None):
         spmv_hyb_apply(self.n_rows, self.n_cols, self.width, self.ell_col, self.ell_val, self.n_tail_rows,
@@ -316,18 +351,12 @@ class HYBMatrix:
         return y
 
 
-def _tail_size(row_ptr, width):
-    """Tail sizes for an explicit width (host computation on the row lengths)."""
-    lens = np.diff(row_ptr.cpu().numpy().astype(np.int64))
-    over = lens > width
-    return int(over.sum()), int((lens[over] - width).sum())
-
-
-def spmv_auto_plan(n_rows, n_cols, nnz, row_ptr, stream=None):
+def spmv_auto_plan(n_rows, n_cols, nnz, row_ptr, stream=None, scratch=None):
     """The CV rule's choice for this matrix: an AutoPlan (format, width, tail sizes, workspace bytes)."""
     p = _lib.AutoPlan()
+    keep, sp, sb = _scratch(scratch, n_rows, row_ptr)
     _call("spmv_auto_plan", int(n_rows), int(n_cols), int(nnz), _dev(row_ptr, _i32_dtype(), "row_ptr"),
-          ctypes.byref(p), _stream(stream, row_ptr))
+          ctypes.byref(p), sp, sb, _stream(stream, row_ptr))
     return p
 
 
@@ -385,11 +414,12 @@ class AutoMatrix:
 # ---------------------------------------------------------------------------
 # SpGEMM C = A * B (hash-based, multi-phase)
 # ---------------------------------------------------------------------------
-def spgemm_workspace_size(m, k, n, rp_a, ci_a, rp_b, ci_b, stream=None) -> int:
+def spgemm_workspace_size(m, k, n, rp_a, ci_a, rp_b, ci_b, stream=None, scratch=None) -> int:
     out = ctypes.c_size_t()
+    keep, sp, sb = _scratch(scratch, m, rp_a)
     _call("spgemm_workspace_size", int(m), int(k), int(n), int(ci_a.numel()), _dev(rp_a, _i32_dtype(), "rp_a"),
           _dev(ci_a, _i32_dtype(), "ci_a"), int(ci_b.numel()), _dev(rp_b, _i32_dtype(), "rp_b"),
-          _dev(ci_b, _i32_dtype(), "ci_b"), ctypes.byref(out), _stream(stream, rp_a))
+          _dev(ci_b, _i32_dtype(), "ci_b"), ctypes.byref(out), sp, sb, _stream(stream, rp_a))
     return out.value
 
 

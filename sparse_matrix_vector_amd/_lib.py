@@ -31,7 +31,8 @@ P_plan = ctypes.POINTER(AutoPlan)
 
 # name -> argument types (every function returns spmv_status, an int)
 SIGNATURES = {
-    "spmv_csr_row_stats": [c_i32, vp, P_i32, P_i64, P_i64, vp],
+    "spmv_scratch_size": [c_i32, P_sz],
+    "spmv_csr_row_stats": [c_i32, vp, P_i32, P_i64, P_i64, vp, c_sz, vp],
     "spmv_format_recommend": [c_i64, c_i64, c_i64, P_i32],
     "spmv_csr_plan_size": [c_i32, c_i32, vp, P_sz],
     "spmv_csr_create": [P_vp, c_i32, c_i32, c_i32, vp, vp, vp, c_i32, vp, vp, c_sz, vp],
@@ -40,12 +41,14 @@ SIGNATURES = {
     "spmv_csr_get_plan": [vp, P_i32, vp, vp],
     "spmv_csr_info": [vp, P_i32, P_i32, P_i32],
     "spmv_csr_destroy": [vp],
-    "spmv_ell_from_csr": [c_i32, c_i32, c_i32, vp, vp, vp, c_i32, vp, vp, vp],
+    "spmv_ell_from_csr": [c_i32, c_i32, c_i32, vp, vp, vp, c_i32, vp, vp, vp, c_sz, vp],
     "spmv_ell_apply": [c_i32, c_i32, c_i32, vp, vp, c_f32, vp, c_f32, vp, vp],
-    "spmv_hyb_width": [c_i32, vp, c_i32, c_i32, P_i32, P_i32, P_i64, vp],
-    "spmv_hyb_from_csr": [c_i32, c_i32, c_i32, vp, vp, vp, c_i32, vp, vp, c_i32, c_i64, vp, vp, vp, vp, vp],
+    "spmv_hyb_width": [c_i32, vp, c_i32, c_i32, P_i32, P_i32, P_i64, vp, c_sz, vp],
+    "spmv_hyb_tail_size": [c_i32, vp, c_i32, P_i32, P_i64, vp, c_sz, vp],
+    "spmv_hyb_from_csr": [c_i32, c_i32, c_i32, vp, vp, vp, c_i32, vp, vp, c_i32, c_i64, vp, vp, vp, vp, vp, c_sz,
+                          vp],
     "spmv_hyb_apply": [c_i32, c_i32, c_i32, vp, vp, c_i32, c_i64, vp, vp, vp, vp, c_f32, vp, c_f32, vp, vp],
-    "spmv_auto_plan": [c_i32, c_i32, c_i32, vp, P_plan, vp],
+    "spmv_auto_plan": [c_i32, c_i32, c_i32, vp, P_plan, vp, c_sz, vp],
     "spmv_auto_create": [P_vp, P_plan, c_i32, c_i32, c_i32, vp, vp, vp, vp, c_sz, vp],
     "spmv_auto_apply": [vp, c_f32, vp, c_f32, vp, vp],
     "spmv_auto_destroy": [vp],
@@ -59,7 +62,7 @@ SIGNATURES = {
     "fem_matvec_apply": [c_i32, c_i32, vp, vp, c_i32, vp, c_f32, vp, c_f32, vp, vp],
     "fem_threestage_size": [c_i32, P_sz],
     "fem_matvec_threestage": [c_i32, c_i32, vp, vp, c_i32, vp, c_f32, vp, c_f32, vp, vp, c_sz, vp],
-    "spgemm_workspace_size": [c_i32, c_i32, c_i32, c_i32, vp, vp, c_i32, vp, vp, P_sz, vp],
+    "spgemm_workspace_size": [c_i32, c_i32, c_i32, c_i32, vp, vp, c_i32, vp, vp, P_sz, vp, c_sz, vp],
     "spgemm_create": [P_vp, c_i32, c_i32, c_i32, c_i32, vp, vp, vp, c_i32, vp, vp, vp, vp, c_sz, vp],
     "spgemm_info": [vp, P_i64, P_i64, P_i32],
     "spgemm_compute": [vp, vp, vp, vp, vp],

@@ -33,9 +33,24 @@ int device_cu_count() {
     return cached[dev];
 }
 
+spmv_status check_scratch(const void *scratch, size_t bytes, int64_t n_rows) {
+    const size_t need = scratch_bytes(n_rows);
+    if (!scratch) return fail(SPMV_ERR_INVALID_VALUE, "scratch is NULL (spmv_scratch_size gives its size)");
+    if (reinterpret_cast<uintptr_t>(scratch) & 255u) return fail(SPMV_ERR_INVALID_VALUE, "scratch must be 256-byte aligned");
+    if (bytes < need) return fail(SPMV_ERR_INVALID_VALUE, "scratch of %zu bytes is smaller than %zu", bytes, need);
+    return SPMV_OK;
+}
+
 }  // namespace spmv
 
 extern "C" const char *spmv_last_error(void) { return spmv::g_last_error.c_str(); }
+
+extern "C" spmv_status spmv_scratch_size(int32_t n_rows, size_t *bytes) {
+    if (!bytes) return spmv::fail(SPMV_ERR_INVALID_VALUE, "bytes is NULL");
+    if (n_rows < 0) return spmv::fail(SPMV_ERR_INVALID_VALUE, "n_rows < 0");
+    *bytes = spmv::scratch_bytes(n_rows);
+    return SPMV_OK;
+}
 
 // Coefficient-of-variation rule ("Why SpMV needs CUDA optimisation", section
 // 2.2) in exact integer arithmetic: with S1 = sum of lengths, S2 = sum of

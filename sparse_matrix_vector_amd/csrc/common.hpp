@@ -52,6 +52,29 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int device_cu_count();
 
 // ---------------------------------------------------------------------------
+// Host: the caller's device scratch of the synchronous statistics, planning
+// and conversion calls (spmv_scratch_size).  A 256-byte head of counters,
+// each call using its own fixed offset, then two int32 counts per
+// 256-row workgroup (the HYB split's compaction).
+// ---------------------------------------------------------------------------
+constexpr size_t SCRATCH_ROW_STATS = 0;     // {u64 sum, u64 sum_sq, i32 max, i32 err}
+constexpr size_t SCRATCH_HYB_COUNTS = 32;   // u64[3]: sum min(len, W), rows > W, entries past W
+constexpr size_t SCRATCH_ERR = 64;          // i32 error flags of a conversion or validation
+constexpr size_t SCRATCH_SG_ERR = 96;       // i32 error flags of the SpGEMM validation
+constexpr size_t SCRATCH_SG_TOTALS = 128;   // SpGEMM intermediate-product totals (<= 128 bytes)
+constexpr size_t SCRATCH_HEAD = 256;
+constexpr int SCRATCH_ROWS_PER_WG = 256;
+
+inline size_t scratch_bytes(int64_t n_rows) {
+    const int64_t nb = (n_rows + SCRATCH_ROWS_PER_WG - 1) / SCRATCH_ROWS_PER_WG;
+    const size_t counts = (size_t)8 * (size_t)(nb > 0 ? nb : 1);
+    return SCRATCH_HEAD + ((counts + 255) & ~size_t(255));
+}
+
+// Checks a caller scratch buffer for a matrix of n_rows rows.
+spmv_status check_scratch(const void *scratch, size_t bytes, int64_t n_rows);
+
+// ---------------------------------------------------------------------------
 // Device: wave64 primitives.
 //
 // DPP controls of the GFX9-family data-parallel-primitives encoding (CDNA

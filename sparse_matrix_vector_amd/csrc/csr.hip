@@ -1039,9 +1039,12 @@ struct spmv_csr_plan {
 };
 
 extern "C" spmv_status spmv_csr_row_stats(int32_t n_rows, const int32_t *row_ptr, int32_t *max_len,
-                                          int64_t *sum_len, int64_t *sum_len_sq, void *stream) {
+                                          int64_t *sum_len, int64_t *sum_len_sq, void *scratch,
+                                          size_t scratch_bytes, void *stream) {
     if (n_rows < 0) return fail(SPMV_ERR_INVALID_VALUE, "n_rows < 0");
     if (!row_ptr || !max_len || !sum_len || !sum_len_sq) return fail(SPMV_ERR_INVALID_VALUE, "NULL pointer");
+    spmv_status cs = check_scratch(scratch, scratch_bytes, n_rows);
+    if (cs != SPMV_OK) return cs;
     if (n_rows == 0) {
         *max_len = 0;
         *sum_len = 0;
@@ -1053,15 +1056,13 @@ extern "C" spmv_status spmv_csr_row_stats(int32_t n_rows, const int32_t *row_ptr
         unsigned long long sum, sq;
         int mx, err;
     };
-    Out *d = nullptr;
-    SPMV_HIP(hipMallocAsync(reinterpret_cast<void **>(&d), sizeof(Out), st));
+    Out *d = reinterpret_cast<Out *>(static_cast<char *>(scratch) + SCRATCH_ROW_STATS);
     SPMV_HIP(hipMemsetAsync(d, 0, sizeof(Out), st));
     const int grid = (int)std::min<int64_t>(ceil_div(n_rows, WG), 4 * device_cu_count());
     k_row_stats<<<grid, WG, 0, st>>>(n_rows, row_ptr, &d->mx, &d->sum, &d->sq, &d->err);
     SPMV_LAUNCHED("k_row_stats");
     Out h{};
     SPMV_HIP(hipMemcpyAsync(&h, d, sizeof(Out), hipMemcpyDeviceToHost, st));
-    SPMV_HIP(hipFreeAsync(d, st));
     SPMV_HIP(hipStreamSynchronize(st));
     if (h.err) return fail(SPMV_ERR_INVALID_MATRIX, "row_ptr decreases somewhere");
     *max_len = h.mx;
@@ -1196,14 +1197,14 @@ extern "C" spmv_status spmv_csr_create(spmv_csr_t *out, int32_t n_rows, int32_t 
     if (s != SPMV_OK) return s;
     const int var = variant == SPMV_CSR_AUTO ? SPMV_CSR_BINNED : variant;
     Layout L = make_layout(n_rows, nnz, t[0]);
-    if (var == SPMV_CSR_BINNED) {
-        if (!workspace) return fail(SPMV_ERR_INVALID_VALUE, "workspace is NULL");
-        if (workspace_bytes < L.total)
-            return fail(SPMV_ERR_INVALID_VALUE, "workspace of %zu bytes is smaller than %zu", workspace_bytes,
-                        L.total);
-        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-            return fail(SPMV_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
-    }
+    // BINNED keeps its plan in the workspace; SCALAR and VECTOR use only its
+    // first 256 bytes, for the validation flags, during this call
+    const size_t need = var == SPMV_CSR_BINNED ? L.total : SCRATCH_HEAD;
+    if (!workspace) return fail(SPMV_ERR_INVALID_VALUE, "workspace is NULL");
+    if (workspace_bytes < need)
+        return fail(SPMV_ERR_INVALID_VALUE, "workspace of %zu bytes is smaller than %zu", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(SPMV_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
     spmv_csr_plan *h = new spmv_csr_plan();
     h->n_rows = n_rows;
     h->n_cols = n_cols;
@@ -1224,23 +1225,14 @@ extern "C" spmv_status spmv_csr_create(spmv_csr_t *out, int32_t n_rows, int32_t 
         h->group_lanes = g;
     }
     hipStream_t st = as_stream(stream);
-    // validation needs 4 bytes of device scratch: the workspace if there is
-    // one, otherwise a short-lived allocation
-    int *d_err = nullptr;
-    bool own = false;
-    if (var == SPMV_CSR_BINNED) {
-        d_err = &reinterpret_cast<Meta *>(static_cast<char *>(workspace) + L.meta)->err;
-    } else {
-        if (hipMallocAsync(reinterpret_cast<void **>(&d_err), sizeof(int), st) != hipSuccess) {
-            delete h;
-            return fail(SPMV_ERR_HIP, "hipMallocAsync failed");
-        }
-        own = true;
-    }
+    // validation flags: in the plan's header (BINNED) or the workspace's
+    // first bytes (SCALAR, VECTOR)
+    int *d_err = var == SPMV_CSR_BINNED
+                     ? &reinterpret_cast<Meta *>(static_cast<char *>(workspace) + L.meta)->err
+                     : reinterpret_cast<int *>(static_cast<char *>(workspace) + SCRATCH_ERR);
     spmv_status r = SPMV_OK;
     if (hipMemsetAsync(d_err, 0, sizeof(int), st) != hipSuccess) r = fail(SPMV_ERR_HIP, "hipMemsetAsync failed");
     if (r == SPMV_OK) r = validate_matrix(h, st, d_err);
-    if (own) (void)hipFreeAsync(d_err, st);
     if (r == SPMV_OK && var == SPMV_CSR_BINNED) r = build_binned_plan(h, static_cast<char *>(workspace), L, st);
     if (r != SPMV_OK) {
         (void)hipStreamSynchronize(st);

@@ -228,7 +228,8 @@ using namespace spmv;
 
 extern "C" spmv_status spmv_ell_from_csr(int32_t n_rows, int32_t n_cols, int32_t nnz, const int32_t *row_ptr,
                                          const int32_t *col_idx, const float *vals, int32_t width,
-                                         int32_t *ell_col, float *ell_val, void *stream) {
+                                         int32_t *ell_col, float *ell_val, void *scratch, size_t scratch_bytes,
+                                         void *stream) {
     if (n_rows < 0 || n_cols < 0 || nnz < 0 || width < 0) return fail(SPMV_ERR_INVALID_VALUE, "negative size");
     if ((int64_t)n_rows * width > INT32_MAX)
         return fail(SPMV_ERR_OVERFLOW, "width * n_rows = %lld exceeds int32", (long long)n_rows * width);
@@ -240,7 +241,7 @@ extern "C" spmv_status spmv_ell_from_csr(int32_t n_rows, int32_t n_cols, int32_t
         return fail(SPMV_ERR_INVALID_VALUE, "NULL pointer");
     int32_t max_len = 0;
     int64_t s1 = 0, s2 = 0;
-    spmv_status s = spmv_csr_row_stats(n_rows, row_ptr, &max_len, &s1, &s2, stream);
+    spmv_status s = spmv_csr_row_stats(n_rows, row_ptr, &max_len, &s1, &s2, scratch, scratch_bytes, stream);
     if (s != SPMV_OK) return s;
     if (s1 != nnz) return fail(SPMV_ERR_INVALID_MATRIX, "row lengths sum to %lld, not nnz = %d", (long long)s1, nnz);
     if (max_len > width) return fail(SPMV_ERR_INVALID_VALUE, "width %d is shorter than the longest row (%d)", width, max_len);
@@ -251,15 +252,13 @@ extern "C" spmv_status spmv_ell_from_csr(int32_t n_rows, int32_t n_cols, int32_t
     SPMV_HIP(hipMemcpyAsync(&rp0, row_ptr, sizeof(int), hipMemcpyDeviceToHost, st));
     SPMV_HIP(hipStreamSynchronize(st));
     if (rp0 != 0) return fail(SPMV_ERR_INVALID_MATRIX, "row_ptr[0] != 0");
-    int *d_err = nullptr;
-    SPMV_HIP(hipMallocAsync(reinterpret_cast<void **>(&d_err), sizeof(int), st));
+    int *d_err = reinterpret_cast<int *>(static_cast<char *>(scratch) + SCRATCH_ERR);
     SPMV_HIP(hipMemsetAsync(d_err, 0, sizeof(int), st));
     k_ell_from_csr<<<(int)ceil_div(n_rows, WG), WG, 0, st>>>(n_rows, n_cols, nnz, width, row_ptr, col_idx, vals,
                                                              ell_col, ell_val, d_err);
     SPMV_LAUNCHED("k_ell_from_csr");
     int err = 0;
     SPMV_HIP(hipMemcpyAsync(&err, d_err, sizeof(int), hipMemcpyDeviceToHost, st));
-    SPMV_HIP(hipFreeAsync(d_err, st));
     SPMV_HIP(hipStreamSynchronize(st));
     if (err) return fail(SPMV_ERR_INVALID_MATRIX, "row_ptr inconsistent or a column outside [0, n_cols)");
     return SPMV_OK;

@@ -29,6 +29,7 @@ namespace {
 constexpr int WG = 256;
 constexpr int WAVES = WG / 64;
 constexpr int SCAN_WG = 1024;
+static_assert(WG == SCRATCH_ROWS_PER_WG, "the HYB split keeps one count pair per 256-row workgroup in the scratch");
 
 // Block sums over rows of min(len, W), [len > W] and max(len - W, 0), added
 // into out[0..2] (exact 64-bit integers).
@@ -209,10 +210,13 @@ spmv_status hyb_counts(int n, const int *rp, int W, hipStream_t st, unsigned lon
 using namespace spmv;
 
 extern "C" spmv_status spmv_hyb_width(int32_t n_rows, const int32_t *row_ptr, int32_t num, int32_t den,
-                                      int32_t *width, int32_t *n_tail_rows, int64_t *tail_nnz, void *stream) {
+                                      int32_t *width, int32_t *n_tail_rows, int64_t *tail_nnz, void *scratch,
+                                      size_t scratch_bytes, void *stream) {
     if (n_rows < 0) return fail(SPMV_ERR_INVALID_VALUE, "n_rows < 0");
     if (!width || !n_tail_rows || !tail_nnz) return fail(SPMV_ERR_INVALID_VALUE, "NULL output pointer");
     if (den <= 0 || num < 0 || num > den) return fail(SPMV_ERR_INVALID_VALUE, "need 0 <= num <= den, den > 0");
+    spmv_status s = check_scratch(scratch, scratch_bytes, n_rows);
+    if (s != SPMV_OK) return s;
     *width = 0;
     *n_tail_rows = 0;
     *tail_nnz = 0;
@@ -220,11 +224,10 @@ extern "C" spmv_status spmv_hyb_width(int32_t n_rows, const int32_t *row_ptr, in
     if (!row_ptr) return fail(SPMV_ERR_INVALID_VALUE, "row_ptr is NULL");
     int32_t max_len = 0;
     int64_t s1 = 0, s2 = 0;
-    spmv_status s = spmv_csr_row_stats(n_rows, row_ptr, &max_len, &s1, &s2, stream);
+    s = spmv_csr_row_stats(n_rows, row_ptr, &max_len, &s1, &s2, scratch, scratch_bytes, stream);
     if (s != SPMV_OK) return s;
     hipStream_t st = as_stream(stream);
-    unsigned long long *d_out = nullptr;
-    SPMV_HIP(hipMallocAsync(reinterpret_cast<void **>(&d_out), 3 * sizeof(unsigned long long), st));
+    auto *d_out = reinterpret_cast<unsigned long long *>(static_cast<char *>(scratch) + SCRATCH_HYB_COUNTS);
     // smallest W in [0, max_len] with den * count(W) >= num * nnz; the
     // condition is monotone in W and holds at W = max_len (count = nnz)
     int lo = 0, hi = max_len;
@@ -241,9 +244,34 @@ extern "C" spmv_status spmv_hyb_width(int32_t n_rows, const int32_t *row_ptr, in
         }
     }
     if (s == SPMV_OK) s = hyb_counts(n_rows, row_ptr, lo, st, d_out, h);
-    (void)hipFreeAsync(d_out, st);
     if (s != SPMV_OK) return s;
     *width = lo;
+    *n_tail_rows = (int32_t)h[1];
+    *tail_nnz = (int64_t)h[2];
+    return SPMV_OK;
+}
+
+extern "C" spmv_status spmv_hyb_tail_size(int32_t n_rows, const int32_t *row_ptr, int32_t width,
+                                          int32_t *n_tail_rows, int64_t *tail_nnz, void *scratch,
+                                          size_t scratch_bytes, void *stream) {
+    if (n_rows < 0 || width < 0) return fail(SPMV_ERR_INVALID_VALUE, "negative size");
+    if (!n_tail_rows || !tail_nnz) return fail(SPMV_ERR_INVALID_VALUE, "NULL output pointer");
+    spmv_status s = check_scratch(scratch, scratch_bytes, n_rows);
+    if (s != SPMV_OK) return s;
+    *n_tail_rows = 0;
+    *tail_nnz = 0;
+    if (n_rows == 0) return SPMV_OK;
+    if (!row_ptr) return fail(SPMV_ERR_INVALID_VALUE, "row_ptr is NULL");
+    // row lengths must be non-negative for the counts to mean anything
+    int32_t max_len = 0;
+    int64_t s1 = 0, s2 = 0;
+    s = spmv_csr_row_stats(n_rows, row_ptr, &max_len, &s1, &s2, scratch, scratch_bytes, stream);
+    if (s != SPMV_OK) return s;
+    unsigned long long h[3] = {0, 0, 0};
+    s = hyb_counts(n_rows, row_ptr, width, as_stream(stream),
+                   reinterpret_cast<unsigned long long *>(static_cast<char *>(scratch) + SCRATCH_HYB_COUNTS), h);
+    if (s != SPMV_OK) return s;
+    if (h[1] > (unsigned long long)INT32_MAX) return fail(SPMV_ERR_OVERFLOW, "tail rows exceed int32");
     *n_tail_rows = (int32_t)h[1];
     *tail_nnz = (int64_t)h[2];
     return SPMV_OK;
@@ -253,17 +281,20 @@ extern "C" spmv_status spmv_hyb_from_csr(int32_t n_rows, int32_t n_cols, int32_t
                                          const int32_t *col_idx, const float *vals, int32_t width,
                                          int32_t *ell_col, float *ell_val, int32_t n_tail_rows,
                                          int64_t tail_nnz, int32_t *tail_rows, int32_t *tail_rp,
-                                         int32_t *tail_col, float *tail_val, void *stream) {
+                                         int32_t *tail_col, float *tail_val, void *scratch, size_t scratch_bytes,
+                                         void *stream) {
     if (n_rows < 0 || n_cols < 0 || nnz < 0 || width < 0 || n_tail_rows < 0 || tail_nnz < 0)
         return fail(SPMV_ERR_INVALID_VALUE, "negative size");
     if ((int64_t)n_rows * width > INT32_MAX) return fail(SPMV_ERR_OVERFLOW, "width * n_rows exceeds int32");
+    spmv_status s = check_scratch(scratch, scratch_bytes, n_rows);
+    if (s != SPMV_OK) return s;
     if (n_rows == 0) return SPMV_OK;
     if (!row_ptr || !tail_rp || (nnz > 0 && (!col_idx || !vals)) || (width > 0 && (!ell_col || !ell_val)) ||
         (n_tail_rows > 0 && !tail_rows) || (tail_nnz > 0 && (!tail_col || !tail_val)))
         return fail(SPMV_ERR_INVALID_VALUE, "NULL pointer");
     int32_t max_len = 0;
     int64_t s1 = 0, s2 = 0;
-    spmv_status s = spmv_csr_row_stats(n_rows, row_ptr, &max_len, &s1, &s2, stream);
+    s = spmv_csr_row_stats(n_rows, row_ptr, &max_len, &s1, &s2, scratch, scratch_bytes, stream);
     if (s != SPMV_OK) return s;
     if (s1 != nnz) return fail(SPMV_ERR_INVALID_MATRIX, "row lengths sum to %lld, not nnz = %d", (long long)s1, nnz);
     hipStream_t st = as_stream(stream);
@@ -271,50 +302,38 @@ extern "C" spmv_status spmv_hyb_from_csr(int32_t n_rows, int32_t n_cols, int32_t
     SPMV_HIP(hipMemcpyAsync(&rp0, row_ptr, sizeof(int), hipMemcpyDeviceToHost, st));
     SPMV_HIP(hipStreamSynchronize(st));
     if (rp0 != 0) return fail(SPMV_ERR_INVALID_MATRIX, "row_ptr[0] != 0");
-    // the tail sizes the caller allocated for must be those of this width
-    int *d = nullptr;   // err, then per-block row and entry counts
-    const int nb = (int)ceil_div(n_rows, WG);
-    SPMV_HIP(hipMallocAsync(reinterpret_cast<void **>(&d), sizeof(int) * (1 + 2 * (size_t)nb), st));
-    int *d_err = d, *brows = d + 1, *bents = d + 1 + nb;
-    s = SPMV_OK;
-    if (hipMemsetAsync(d_err, 0, sizeof(int), st) != hipSuccess) s = fail(SPMV_ERR_HIP, "hipMemsetAsync failed");
-    if (s == SPMV_OK) {
-        if (width > 0) {
-            k_hyb_ell<<<nb, WG, 0, st>>>(n_rows, n_cols, width, row_ptr, col_idx, vals, ell_col, ell_val, d_err);
-            SPMV_LAUNCHED("k_hyb_ell");
-        }
-        k_hyb_tail_count<<<nb, WG, 0, st>>>(n_rows, row_ptr, width, brows, bents);
-        SPMV_LAUNCHED("k_hyb_tail_count");
-        k_hyb_scan<<<1, SCAN_WG, 0, st>>>(nb, brows, bents);
-        SPMV_LAUNCHED("k_hyb_scan");
-        // totals = last exclusive offset + last block's count: recomputed on
-        // the host from the counts kernel instead, which also checks them
-        unsigned long long h[3] = {0, 0, 0};
-        unsigned long long *d_out = nullptr;
-        if (hipMallocAsync(reinterpret_cast<void **>(&d_out), 3 * sizeof(unsigned long long), st) != hipSuccess)
-            s = fail(SPMV_ERR_HIP, "hipMallocAsync failed");
-        if (s == SPMV_OK) s = hyb_counts(n_rows, row_ptr, width, st, d_out, h);
-        if (d_out) (void)hipFreeAsync(d_out, st);
-        if (s == SPMV_OK && ((int64_t)h[1] != n_tail_rows || (int64_t)h[2] != tail_nnz))
-            s = fail(SPMV_ERR_INVALID_VALUE, "width %d gives %llu tail rows / %llu tail entries, not %d / %lld",
-                     width, h[1], h[2], n_tail_rows, (long long)tail_nnz);
-        if (s == SPMV_OK) {
-            k_hyb_tail_write<<<nb, WG, 0, st>>>(n_rows, n_cols, row_ptr, col_idx, vals, width, brows, bents,
-                                                tail_rows, tail_rp, tail_col, tail_val, d_err);
-            SPMV_LAUNCHED("k_hyb_tail_write");
-            k_set_int<<<1, 1, 0, st>>>(tail_rp + n_tail_rows, (int)tail_nnz);
-            SPMV_LAUNCHED("k_set_int");
-        }
+    // the tail sizes the caller allocated for must be those of this width;
+    // checked before any kernel writes the caller's arrays
+    unsigned long long h[3] = {0, 0, 0};
+    s = hyb_counts(n_rows, row_ptr, width, st,
+                   reinterpret_cast<unsigned long long *>(static_cast<char *>(scratch) + SCRATCH_HYB_COUNTS), h);
+    if (s != SPMV_OK) return s;
+    if ((int64_t)h[1] != n_tail_rows || (int64_t)h[2] != tail_nnz)
+        return fail(SPMV_ERR_INVALID_VALUE, "width %d gives %llu tail rows / %llu tail entries, not %d / %lld", width,
+                    h[1], h[2], n_tail_rows, (long long)tail_nnz);
+    char *sc = static_cast<char *>(scratch);
+    int *d_err = reinterpret_cast<int *>(sc + SCRATCH_ERR);
+    const int nb = (int)ceil_div(n_rows, WG);   // WG == SCRATCH_ROWS_PER_WG rows per count
+    int *brows = reinterpret_cast<int *>(sc + SCRATCH_HEAD), *bents = brows + nb;
+    SPMV_HIP(hipMemsetAsync(d_err, 0, sizeof(int), st));
+    if (width > 0) {
+        k_hyb_ell<<<nb, WG, 0, st>>>(n_rows, n_cols, width, row_ptr, col_idx, vals, ell_col, ell_val, d_err);
+        SPMV_LAUNCHED("k_hyb_ell");
     }
+    k_hyb_tail_count<<<nb, WG, 0, st>>>(n_rows, row_ptr, width, brows, bents);
+    SPMV_LAUNCHED("k_hyb_tail_count");
+    k_hyb_scan<<<1, SCAN_WG, 0, st>>>(nb, brows, bents);
+    SPMV_LAUNCHED("k_hyb_scan");
+    k_hyb_tail_write<<<nb, WG, 0, st>>>(n_rows, n_cols, row_ptr, col_idx, vals, width, brows, bents, tail_rows,
+                                        tail_rp, tail_col, tail_val, d_err);
+    SPMV_LAUNCHED("k_hyb_tail_write");
+    k_set_int<<<1, 1, 0, st>>>(tail_rp + n_tail_rows, (int)tail_nnz);
+    SPMV_LAUNCHED("k_set_int");
     int err = 0;
-    if (s == SPMV_OK) {
-        if (hipMemcpyAsync(&err, d_err, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess)
-            s = fail(SPMV_ERR_HIP, "hipMemcpyAsync failed");
-    }
-    (void)hipFreeAsync(d, st);
-    if (hipStreamSynchronize(st) != hipSuccess && s == SPMV_OK) s = fail(SPMV_ERR_HIP, "hipStreamSynchronize failed");
-    if (s == SPMV_OK && err) s = fail(SPMV_ERR_INVALID_MATRIX, "a column index is outside [0, n_cols)");
-    return s;
+    SPMV_HIP(hipMemcpyAsync(&err, d_err, sizeof(int), hipMemcpyDeviceToHost, st));
+    SPMV_HIP(hipStreamSynchronize(st));
+    if (err) return fail(SPMV_ERR_INVALID_MATRIX, "a column index is outside [0, n_cols)");
+    return SPMV_OK;
 }
 
 extern "C" spmv_status spmv_hyb_apply(int32_t n_rows, int32_t n_cols, int32_t width, const int32_t *ell_col,
@@ -366,7 +385,8 @@ namespace {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct AutoLayout {
-    size_t ell_col, ell_val, tail_rows, tail_rp, tail_col, tail_val, tail_plan, tail_plan_bytes, total;
+    size_t ell_col, ell_val, tail_rows, tail_rp, tail_col, tail_val, tail_plan, tail_plan_bytes, scratch,
+        scratch_bytes, total;
 };
 
 AutoLayout auto_layout(const spmv_auto_plan_t &p, int32_t n_rows) {
@@ -388,6 +408,9 @@ AutoLayout auto_layout(const spmv_auto_plan_t &p, int32_t n_rows) {
     if (p.n_tail_rows > 0 && spmv_csr_plan_size(p.n_tail_rows, (int32_t)p.tail_nnz, nullptr, &L.tail_plan_bytes) != SPMV_OK)
         L.tail_plan_bytes = 0;
     L.tail_plan = take(L.tail_plan_bytes);
+    // the conversion's own scratch (spmv_scratch_size), used during create only
+    L.scratch_bytes = scratch_bytes(n_rows);
+    L.scratch = take(L.scratch_bytes);
     L.total = off;
     return L;
 }
@@ -395,16 +418,18 @@ AutoLayout auto_layout(const spmv_auto_plan_t &p, int32_t n_rows) {
 }  // namespace
 
 extern "C" spmv_status spmv_auto_plan(int32_t n_rows, int32_t n_cols, int32_t nnz, const int32_t *row_ptr,
-                                      spmv_auto_plan_t *plan, void *stream) {
+                                      spmv_auto_plan_t *plan, void *scratch, size_t scratch_bytes, void *stream) {
     if (!plan) return fail(SPMV_ERR_INVALID_VALUE, "plan is NULL");
     if (n_rows < 0 || n_cols < 0 || nnz < 0) return fail(SPMV_ERR_INVALID_VALUE, "negative size");
+    spmv_status cs = check_scratch(scratch, scratch_bytes, n_rows);
+    if (cs != SPMV_OK) return cs;
     spmv_auto_plan_t p{};
     p.format = SPMV_FORMAT_CSR;
     int32_t max_len = 0;
     int64_t s1 = 0, s2 = 0;
     if (n_rows > 0) {
         if (!row_ptr) return fail(SPMV_ERR_INVALID_VALUE, "row_ptr is NULL");
-        spmv_status s = spmv_csr_row_stats(n_rows, row_ptr, &max_len, &s1, &s2, stream);
+        spmv_status s = spmv_csr_row_stats(n_rows, row_ptr, &max_len, &s1, &s2, scratch, scratch_bytes, stream);
         if (s != SPMV_OK) return s;
         if (s1 != nnz)
             return fail(SPMV_ERR_INVALID_MATRIX, "row lengths sum to %lld, not nnz = %d", (long long)s1, nnz);
@@ -421,7 +446,7 @@ extern "C" spmv_status spmv_auto_plan(int32_t n_rows, int32_t n_cols, int32_t nn
         p.width = max_len;
     } else if (p.format == SPMV_FORMAT_HYB) {
         spmv_status s = spmv_hyb_width(n_rows, row_ptr, SPMV_HYB_ELL_NUM, SPMV_HYB_ELL_DEN, &p.width,
-                                       &p.n_tail_rows, &p.tail_nnz, stream);
+                                       &p.n_tail_rows, &p.tail_nnz, scratch, scratch_bytes, stream);
         if (s != SPMV_OK) return s;
         if ((int64_t)p.width * n_rows > INT32_MAX) p.format = SPMV_FORMAT_CSR;
     }
@@ -472,11 +497,11 @@ extern "C" spmv_status spmv_auto_create(spmv_auto_t *out, const spmv_auto_plan_t
         h->tail_val = reinterpret_cast<float *>(ws + L.tail_val);
         if (p.format == SPMV_FORMAT_ELL)
             s = spmv_ell_from_csr(n_rows, n_cols, nnz, row_ptr, col_idx, vals, p.width, h->ell_col, h->ell_val,
-                                  stream);
+                                  ws + L.scratch, L.scratch_bytes, stream);
         else
             s = spmv_hyb_from_csr(n_rows, n_cols, nnz, row_ptr, col_idx, vals, p.width, h->ell_col, h->ell_val,
                                   p.n_tail_rows, p.tail_nnz, h->tail_rows, h->tail_rp, h->tail_col, h->tail_val,
-                                  stream);
+                                  ws + L.scratch, L.scratch_bytes, stream);
         // the tail as a CSR matrix over the tail rows, with its own plan
         if (s == SPMV_OK && p.format == SPMV_FORMAT_HYB && p.n_tail_rows > 0)
             s = spmv_csr_create(&h->csr, p.n_tail_rows, n_cols, (int32_t)p.tail_nnz, h->tail_rp, h->tail_col,

@@ -932,19 +932,20 @@ using namespace spmv;
 
 extern "C" spmv_status spgemm_workspace_size(int32_t m, int32_t k, int32_t n, int32_t nnz_a, const int32_t *rp_a,
                                              const int32_t *ci_a, int32_t nnz_b, const int32_t *rp_b,
-                                             const int32_t *ci_b, size_t *bytes, void *stream) {
+                                             const int32_t *ci_b, size_t *bytes, void *scratch,
+                                             size_t scratch_bytes, void *stream) {
+    static_assert(sizeof(IpTotals) <= SCRATCH_HEAD - SCRATCH_SG_TOTALS, "IpTotals must fit the scratch head");
     if (!bytes) return fail(SPMV_ERR_INVALID_VALUE, "bytes is NULL");
     spmv_status s = sg_check_args(m, k, n, nnz_a, rp_a, ci_a, nnz_b, rp_b, ci_b);
     if (s != SPMV_OK) return s;
+    s = check_scratch(scratch, scratch_bytes, m);
+    if (s != SPMV_OK) return s;
     hipStream_t st = as_stream(stream);
-    void *scratch = nullptr;
-    SPMV_HIP(hipMallocAsync(&scratch, 256 + sizeof(IpTotals), st));
-    int *err = static_cast<int *>(scratch);
-    IpTotals *tot = reinterpret_cast<IpTotals *>(static_cast<char *>(scratch) + 256);
+    int *err = reinterpret_cast<int *>(static_cast<char *>(scratch) + SCRATCH_SG_ERR);
+    IpTotals *tot = reinterpret_cast<IpTotals *>(static_cast<char *>(scratch) + SCRATCH_SG_TOTALS);
     IpTotals h{};
     s = sg_validate(m, k, n, nnz_a, rp_a, ci_a, nnz_b, rp_b, ci_b, err, st);
     if (s == SPMV_OK) s = sg_ip(m, rp_a, ci_a, rp_b, nullptr, nullptr, tot, &h, st);
-    (void)hipFreeAsync(scratch, st);
     if (s != SPMV_OK) return s;
     *bytes = sg_layout(m, h.counts[SG_NBIN - 1], (int64_t)h.g3_slots).total;
     return SPMV_OK;

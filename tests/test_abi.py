@@ -185,10 +185,47 @@ def test_host_validation_before_any_gpu_call():
     assert L.spgemm_create(ctypes.byref(h), 2, 2, 2, 3, 16, None, 16, 0, 16, None, None, 16, 1 << 20, None) == 1
     assert L.spgemm_info(None, None, None, None) == 1
     assert L.spgemm_compute(None, None, None, None, None) == 1
-    assert L.spgemm_workspace_size(1, 1, 1, 0, None, None, 0, 16, None, ctypes.byref(ctypes.c_size_t()), None) == 1
+    assert L.spgemm_workspace_size(1, 1, 1, 0, None, None, 0, 16, None, ctypes.byref(ctypes.c_size_t()), 256, 512,
+                                   None) == 1
     assert L.spgemm_destroy(None) == 0
     # n_rows == 0 applies are no-ops that succeed without touching the GPU
     assert L.macko_spmv(0, 4, 4, None, None, None, 1.0, None, 0.0, None, None) == 0
     assert L.macko_spmv_i8(0, 4, 1, None, None, None, None, 1.0, None, 0.0, None, None) == 0
     assert L.spmv_ell_apply(0, 4, 2, None, None, 1.0, None, 0.0, None, None) == 0
     assert L.dense_gemv_f16(0, 4, None, None, 1.0, 0.0, None, None) == 0
+
+
+def test_scratch_size_and_validation():
+    """The synchronous calls take their device scratch from the caller: its
+    size follows the documented formula and a missing, misaligned or short
+    buffer is rejected on the host before any GPU call."""
+    import ctypes
+    L = S.lib()
+    for n, want in [(0, 512), (1, 512), (256, 512), (257, 512), (8192, 512), (8193, 768),
+                    (1_000_000, 256 + 31488), (2**31 - 1, 256 + 67108864)]:
+        assert S.spmv_scratch_size(n) == want, n
+    assert L.spmv_scratch_size(-1, ctypes.byref(ctypes.c_size_t())) == 1
+    m, s1, s2 = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    args = (ctypes.byref(m), ctypes.byref(s1), ctypes.byref(s2))
+    assert L.spmv_csr_row_stats(10, 4096, *args, None, 512, None) == 1          # no scratch
+    assert b"scratch" in L.spmv_last_error()
+    assert L.spmv_csr_row_stats(10, 4096, *args, 4096 + 64, 512, None) == 1     # misaligned
+    assert L.spmv_csr_row_stats(10, 4096, *args, 4096, 256, None) == 1          # too small
+    r, t = ctypes.c_int32(), ctypes.c_int64()
+    assert L.spmv_hyb_tail_size(10, 4096, -1, ctypes.byref(r), ctypes.byref(t), 4096, 512, None) == 1
+    assert L.spmv_hyb_tail_size(10, 4096, 2, ctypes.byref(r), ctypes.byref(t), None, 512, None) == 1
+    assert L.spmv_hyb_width(10, 4096, 7, 10, ctypes.byref(m), ctypes.byref(r), ctypes.byref(t), 4096, 64,
+                            None) == 1
+    assert L.spmv_ell_from_csr(10, 10, 0, 4096, None, None, 2, 4096, 4096, None, 512, None) == 1
+    assert L.spmv_hyb_from_csr(10, 10, 0, 4096, None, None, 2, 4096, 4096, 0, 0, None, 4096, None, None,
+                               4096, 8, None) == 1
+    p = S._lib.AutoPlan()
+    assert L.spmv_auto_plan(10, 10, 0, 4096, ctypes.byref(p), 4096, 100, None) == 1
+    # zero rows: valid scratch, nothing to do, no GPU call
+    assert L.spmv_csr_row_stats(0, 4096, *args, 4096, 512, None) == 0
+    assert (m.value, s1.value, s2.value) == (0, 0, 0)
+    assert L.spmv_hyb_tail_size(0, 4096, 3, ctypes.byref(r), ctypes.byref(t), 4096, 512, None) == 0
+    # SCALAR / VECTOR handles need a workspace of 256 bytes for the validation flags
+    h = ctypes.c_void_p()
+    assert L.spmv_csr_create(ctypes.byref(h), 4, 4, 4, 4096, 4096, 4096, 1, None, None, 0, None) == 1
+    assert L.spmv_csr_create(ctypes.byref(h), 4, 4, 4, 4096, 4096, 4096, 1, None, 4096, 128, None) == 1

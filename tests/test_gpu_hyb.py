@@ -57,7 +57,8 @@ def _split(A, W=None):
     w, r, t = S.spmv_hyb_width(A.n_rows, dev(A.row_ptr))
     if W is not None and W != w:
         w = W
-        r, t = oracle.hyb_tail_size(A.row_ptr, w)
+        r, t = S.spmv_hyb_tail_size(A.n_rows, dev(A.row_ptr), w)
+        assert (r, t) == oracle.hyb_tail_size(A.row_ptr, w)
     arrs = dict(ec=torch.empty(w * A.n_rows, dtype=torch.int32, device="cuda"),
                 ev=torch.empty(w * A.n_rows, dtype=torch.float32, device="cuda"),
                 tr=torch.empty(r, dtype=torch.int32, device="cuda"),
@@ -172,15 +173,28 @@ def test_all_rows_empty():
     assert np.array_equal(host(y), np.full(100, 3.0, np.float32))
 
 
+def test_tail_size_matches_oracle():
+    """spmv_hyb_tail_size at explicit widths, bit-exact with the oracle's
+    count, on the moderate-CV and power-law matrices."""
+    for name in ("varlen", "powerlaw"):
+        A = _case(name)
+        mx = oracle.row_stats(A.row_ptr)[0]
+        for W in (0, 1, 3, 7, 33, mx - 1, mx, mx + 5):
+            assert S.spmv_hyb_tail_size(A.n_rows, dev(A.row_ptr), W) == oracle.hyb_tail_size(A.row_ptr, W), (name, W)
+
+
 def test_rejects_wrong_tail_sizes_and_bad_columns():
     A = gen.random_csr(64, 64, np.arange(64) % 7, 3)
     w, r, t = S.spmv_hyb_width(64, dev(A.row_ptr))
-    bufs = [torch.empty(max(n, 1), dtype=d, device="cuda") for n, d in
+    bufs = [torch.full((max(n, 1),), 77, dtype=d, device="cuda") for n, d in
             [(w * 64, torch.int32), (w * 64, torch.float32), (r + 1, torch.int32), (r + 2, torch.int32),
              (t + 1, torch.int32), (t + 1, torch.float32)]]
     with pytest.raises(S.SpmvError) as e:
         S.spmv_hyb_from_csr(64, 64, dev(A.row_ptr), dev(A.col_idx), dev(A.vals), w, r + 1, t, *bufs)
     assert e.value.status == 1
+    # sizes are checked before any kernel writes the caller's arrays
+    for b in bufs:
+        assert bool((b == 77).all())
     bad = A.col_idx.copy()
     bad[-1] = 64                                   # last entry of the last nonempty row
     with pytest.raises(S.SpmvError) as e:
