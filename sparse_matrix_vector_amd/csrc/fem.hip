@@ -103,7 +103,8 @@ __global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const
         for (int b = 0; b < NDOF_E; ++b) f = fmaf(Ke[a * NDOF_E + b], u[b], f);
         fa[a] = s * f;
     }
-    fe_scatter_lines(d, fa, n_dof, y, line_dof[threadIdx.x >> 6], line_val[threadIdx.x >> 6]);
+    fe_scatter_lines(d, fa, n_dof, [y](int i, float v) { atomicAdd(y + i, v); }, line_dof[threadIdx.x >> 6],
+                     line_val[threadIdx.x >> 6]);
 }
 
 // ---- three-stage comparator ----

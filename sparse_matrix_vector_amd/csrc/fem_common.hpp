@@ -19,9 +19,12 @@ namespace spmv {
 // lane i taking entries i, 64 + i, ...  Consecutive lanes then add to
 // consecutive DOFs, so one memory-side atomic request carries ~16 lanes,
 // against ~5 when each lane adds its own element's DOFs, and half the adds
-// disappear.
-template <typename T>
-__device__ __forceinline__ void fe_scatter_lines(const int (&d)[24], const T (&f)[24], int n_dof, T *y, int *sd,
+// disappear.  `add(dof, value)` performs one global accumulation (an
+// atomic add of the value, or of a fixed-point image of it).  Which values
+// meet in a slot depends only on the lanes' elements, and each is added in
+// a fixed order, so the values passed to `add` are deterministic.
+template <typename T, typename Add>
+__device__ __forceinline__ void fe_scatter_lines(const int (&d)[24], const T (&f)[24], int n_dof, Add add, int *sd,
                                                  T *sv) {
     constexpr int P0[4] = {0, 3, 4, 7}, P1[4] = {1, 2, 5, 6};
     const int lane = __lane_id();
@@ -51,7 +54,7 @@ __device__ __forceinline__ void fe_scatter_lines(const int (&d)[24], const T (&f
                 else if (lane == 63)
                     sd[j] = da, sv[j] = f[3 * P1[k] + c];
                 else
-                    atomicAdd(y + da, f[3 * P1[k] + c]);
+                    add(da, f[3 * P1[k] + c]);
             }
         }
         wave_sync();
@@ -60,7 +63,7 @@ __device__ __forceinline__ void fe_scatter_lines(const int (&d)[24], const T (&f
             const int i = 64 * r + lane;
             if (i < 3 * 65) {
                 const int dd = sd[i];
-                if ((unsigned)dd < (unsigned)n_dof) atomicAdd(y + dd, sv[i]);
+                if ((unsigned)dd < (unsigned)n_dof) add(dd, sv[i]);
             }
         }
         wave_sync();

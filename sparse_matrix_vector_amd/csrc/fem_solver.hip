@@ -9,16 +9,34 @@
 // on K and the smallest from the same iteration on K^-1, each step of which
 // is a Jacobi-PCG solve.
 //
-// Vectors are fp32, every inner product is accumulated in fp64 and the
-// scalars of the iteration are fp64, so an iteration needs no host round
-// trip.  The matvec inside the solver (k_fe_matvec64) is the fused one with
-// fp64 element products and fp64 atomic adds into an fp64 accumulator: a
-// stiffness operator applied to a smooth vector cancels most of each sum
-// (the element matrix annihilates rigid motions), and with fp32 sums that
-// cancellation error more than doubles the iteration count already at
-// kappa ~ 2e4; with fp64 sums the fp32 iteration tracks the fp64 one.  The
-// kernel that consumes K p next reads the accumulator, rounds it to fp32
-// and clears it for the following product.
+// The operator's data (edof, rho, Ke) are those of the fp32 matvec; the
+// iteration's vectors (u, r, z, p, q and the Jacobi scaling) are fp64, every
+// inner product is accumulated in fp64 and the scalars are fp64, so an
+// iteration needs no host round trip.  The matvec inside the solver
+// (k_fe_matvec64) is the fused one with fp64 element products: a stiffness
+// operator applied to a smooth vector cancels most of each sum (the element
+// matrix annihilates rigid motions), and with fp32 sums that cancellation
+// error more than doubles the iteration count already at kappa ~ 2e4.  With
+// fp32 vectors the iteration still lost conjugacy at kappa ~ 1e6 (the
+// rounding of r and p each step is ~1e-7 against kappa * 1e-16 for fp64)
+// and needed 1.0x-1.6x the fp64 count depending on rounding details; with
+// fp64 vectors it follows the fp64 iteration.  The caller's f and u stay
+// fp32: u is read once at the start and written once at the end.
+//
+// Its scatter adds 64-bit fixed-point integers, not floating-point values:
+// each contribution v becomes round(v * 2^k) and is added with an integer
+// atomic, and integer addition does not depend on the order of the adds.
+// The product K x is therefore the same bit for bit in every run, and so is
+// the whole iteration, its count included.  The scale 2^k is set per
+// product from a bound on |(K x)_i|: G * max|x|, with G = (most elements on
+// one DOF) * max_e rho_e^p * max_a sum_b |Ke_ab| computed once per operator,
+// and k chosen so that the bound times 2^k stays below 2^62.  The rounding
+// of one contribution is at most 2^-(k+1) <= G max|x| 2^-63, below the
+// rounding of an fp64 running sum of the same terms.  Every kernel that
+// produces a vector the matvec takes next also stores per-workgroup maxima
+// of |x|; the matvec reduces them, and the kernel that consumes K x reads
+// the accumulator back with the same k, rounds it to fp32 and clears it.
+// The Jacobi diagonal is summed the same way.
 //
 // Inner products: every workgroup stores its partial sums; the next kernel
 // in the stream, in every one of its workgroups, adds all partials in the
@@ -32,9 +50,8 @@
 // k_pcg_update (alpha = r.z(k-1) / p.q; u, r, z = D^-1 r; partial r.z, r.r
 // into slot k & 1); k_pcg_direction (convergence test, beta, p = z + beta p).
 // Once the state says "done", these kernels return at once; the host checks
-// the state every PCG_CHECK iterations.  The reductions are deterministic;
-// the matvec's atomic adds are not (their order varies), so two solves
-// agree to rounding, not bit for bit.
+// the state every PCG_CHECK iterations.  Reductions and matvecs are both
+// deterministic, so two solves of the same system agree bit for bit.
 #include "common.hpp"
 #include "fem_common.hpp"
 
@@ -57,20 +74,24 @@ struct SolverState {
     double ff;          // f . f
     double rr;          // r . r of the last residual
     double rtol2;       // rtol^2
+    double op_bound;    // G: |(K x)_i| <= G max|x| for every i
     int iter, max_iter;
     int done;           // converged, capped or broken down
     int bad;            // 1: diagonal entry not positive, 2: p.Kp <= 0, 4: zero vector
+    int acc_exp;        // k of the accumulator's fixed point (value = acc * 2^-k)
 };
 
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 // Workspace: state | partials: 2 slots x SV_NQ x SV_MAX_BLOCKS doubles, then
-// SV_MAX_BLOCKS more for p.q | lambda history (max_history doubles) |
-// vectors of n_dof floats: dinv r z p q (PCG) and v w (eigenvalue
-// iterations) | the fp64 matvec accumulator (n_dof doubles, all zero
-// between uses).
+// SV_MAX_BLOCKS more for p.q and SV_MAX_BLOCKS for the maxima of |x| of the
+// next matvec's input | lambda history (max_history doubles) | vectors of
+// n_dof doubles: dinv r z p q u (PCG) | vectors of n_dof floats: v w
+// (eigenvalue iterations) | the fixed-point matvec accumulator (n_dof
+// int64, all zero between uses).
+constexpr int NVEC64 = 6, NVEC32 = 2;
 struct Layout {
-    size_t state, partials, hist, vec[7], acc, total;
+    size_t state, partials, hist, vec64[NVEC64], vec32[NVEC32], acc, total;
 };
 
 Layout layout(int64_t n_dof, int64_t max_history) {
@@ -79,15 +100,19 @@ Layout layout(int64_t n_dof, int64_t max_history) {
     L.state = at;
     at += round256(sizeof(SolverState));
     L.partials = at;
-    at += round256(sizeof(double) * (2 * SV_NQ + 1) * SV_MAX_BLOCKS);
+    at += round256(sizeof(double) * (2 * SV_NQ + 2) * SV_MAX_BLOCKS);
     L.hist = at;
     at += round256(sizeof(double) * (size_t)std::max<int64_t>(max_history, 1));
-    for (int k = 0; k < 7; ++k) {
-        L.vec[k] = at;
+    for (int k = 0; k < NVEC64; ++k) {
+        L.vec64[k] = at;
+        at += round256(sizeof(double) * (size_t)std::max<int64_t>(n_dof, 1));
+    }
+    for (int k = 0; k < NVEC32; ++k) {
+        L.vec32[k] = at;
         at += round256(sizeof(float) * (size_t)std::max<int64_t>(n_dof, 1));
     }
     L.acc = at;
-    at += round256(sizeof(double) * (size_t)std::max<int64_t>(n_dof, 1));
+    at += round256(sizeof(long long) * (size_t)std::max<int64_t>(n_dof, 1));
     L.total = at;
     return L;
 }
@@ -109,6 +134,13 @@ __device__ __forceinline__ const double *slot(const double *partials, int s, int
 }
 __device__ __forceinline__ double *pq_slot(double *partials) {
     return partials + (size_t)2 * SV_NQ * SV_MAX_BLOCKS;
+}
+// Per-workgroup maxima of |x| of the vector the next matvec takes.
+__device__ __forceinline__ double *xmax_slot(double *partials) {
+    return partials + (size_t)(2 * SV_NQ + 1) * SV_MAX_BLOCKS;
+}
+__device__ __forceinline__ const double *xmax_slot(const double *partials) {
+    return partials + (size_t)(2 * SV_NQ + 1) * SV_MAX_BLOCKS;
 }
 
 // Sum over the workgroup of NQ values per thread, in a fixed order; the
@@ -136,6 +168,28 @@ __device__ void block_sum(double (&v)[NQ]) {
     }
 }
 
+// Maximum over the workgroup, returned in every thread.
+__device__ double block_max(double v) {
+    __shared__ double red[SV_WG / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double m = red[0];
+    for (int k = 1; k < SV_WG / 64; ++k) m = fmax(m, red[k]);
+    return m;
+}
+
+// This workgroup's max |x| (m: this thread's) into the xmax slot.
+__device__ void store_xmax(double m, double *partials) {
+    m = block_max(m);
+    if (threadIdx.x == 0) xmax_slot(partials)[blockIdx.x] = m;
+}
+
+// 2^-k as a double (k may be negative).
+__device__ __forceinline__ double fix_unit(int k) { return ldexp(1.0, -k); }
+
 // This workgroup's sums of v, one per quantity, into dst[q][blockIdx.x].
 template <int NQ>
 __device__ void store_partials(double (&v)[NQ], double *const (&dst)[NQ]) {
@@ -161,24 +215,101 @@ __global__ void k_sv_fill(int n, float v, float *__restrict__ y) {
     for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) y[i] = v;
 }
 
-__global__ void k_sv_zero64(int n, double *__restrict__ y) {
-    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) y[i] = 0.0;
+__global__ void k_sv_zero64(int n, long long *__restrict__ y) {
+    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) y[i] = 0;
 }
 
-// acc += sum_e rho_e^p P_e^T Ke P_e x, with the element product and the
-// scatter in fp64 (products of fp32 values are exact in fp64).  The fused
+// Per-workgroup maxima of |x| into the xmax slot (for a matvec whose input
+// was not produced by one of the iteration kernels).
+template <typename X>
+__global__ void k_sv_absmax(int n, const X *__restrict__ x, double *__restrict__ partials) {
+    double m = 0.0;
+    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) m = fmax(m, fabs((double)x[i]));
+    store_xmax(m, partials);
+}
+
+// The operator bound G (see the file comment), in three steps.  1: counts
+// of elements per DOF into cnt (int32, zero on entry).
+__global__ void k_op_count(int n_elem, int n_dof, const int *__restrict__ edof, int *__restrict__ cnt) {
+    const int64_t k = (int64_t)blockIdx.x * SV_WG + threadIdx.x;
+    if (k >= (int64_t)n_elem * NDOF_E) return;
+    const int d = edof[k];
+    if ((unsigned)d < (unsigned)n_dof) atomicAdd(cnt + d, 1);
+}
+
+// 2: per-workgroup maxima of the counts (cleared for the accumulator again)
+// into slot 0 quantity 0 and of rho_e^p into slot 0 quantity 1.
+__global__ void k_op_partials(int n_elem, int n_dof, const float *__restrict__ rho, int penalty,
+                              int *__restrict__ cnt, double *__restrict__ partials) {
+    double mc = 0.0, ms = 0.0;
+    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n_dof; i += gridDim.x * SV_WG) {
+        mc = fmax(mc, (double)cnt[i]);
+        cnt[i] = 0;
+    }
+    for (int e = blockIdx.x * SV_WG + threadIdx.x; e < n_elem; e += gridDim.x * SV_WG) {
+        double sv = 1.0;
+        for (int k = 0; k < penalty; ++k) sv *= (double)rho[e];
+        ms = fmax(ms, fabs(sv));
+    }
+    mc = block_max(mc);
+    ms = block_max(ms);
+    if (threadIdx.x == 0) {
+        slot(partials, 0, 0)[blockIdx.x] = mc;
+        slot(partials, 0, 1)[blockIdx.x] = ms;
+    }
+}
+
+// 3 (one workgroup): G = max count * max rho^p * max_a sum_b |Ke_ab|.
+__global__ void k_op_bound(int nb, const double *__restrict__ partials, const float *__restrict__ Ke,
+                           SolverState *st) {
+    double mc = 0.0, ms = 0.0, mk = 0.0;
+    for (int b = threadIdx.x; b < nb; b += SV_WG) {
+        mc = fmax(mc, slot(partials, 0, 0)[b]);
+        ms = fmax(ms, slot(partials, 0, 1)[b]);
+    }
+    if (threadIdx.x < NDOF_E) {
+        for (int b = 0; b < NDOF_E; ++b) mk += fabs((double)Ke[threadIdx.x * NDOF_E + b]);
+    }
+    mc = block_max(mc);
+    ms = block_max(ms);
+    mk = block_max(mk);
+    if (threadIdx.x == 0) st->op_bound = mc * ms * mk;
+}
+
+// Fixed-point exponent for a product whose input has max|x| = xm: the
+// largest k with G * xm * 2^k < 2^62 (0 when the bound is 0, i.e. K x = 0).
+__device__ __forceinline__ int fix_exponent(double G, double xm) {
+    const double b = G * xm;
+    if (!(b > 0.0) || !(b < INFINITY)) return 0;
+    int e;
+    (void)frexp(b, &e);   // b < 2^e
+    return 62 - e;
+}
+
+// acc += sum_e rho_e^p P_e^T Ke P_e x in fixed point, with the element
+// product in fp64 (products of fp32 values are exact in fp64).  The fused
 // shape of fem_matvec_apply: one lane per element, Ke through the scalar
 // cache, 24 gathers, and the contributions merged along x-lines of nodes in
-// LDS before the fp64 atomic adds.  Does nothing when `st` says the
-// iteration is done.
+// LDS before the integer atomic adds.  The scale comes from the nb maxima
+// of |x| in the xmax slot and the operator bound; workgroup 0 records its
+// exponent for the consumer.  x is fp32 (power iteration, the initial
+// guess) or fp64 (the PCG direction).  Does nothing when `check_done` and
+// the state says the iteration is done.
+template <typename X>
 __global__ __launch_bounds__(SV_WG) void k_fe_matvec64(int n_elem, int n_dof, const int *__restrict__ edof,
                                                        const float *__restrict__ rho, int penalty,
-                                                       const float *__restrict__ Ke, const float *__restrict__ x,
-                                                       double *__restrict__ acc, const SolverState *st) {
+                                                       const float *__restrict__ Ke, const X *__restrict__ x,
+                                                       long long *__restrict__ acc, const double *__restrict__ partials,
+                                                       int nb, SolverState *st, int check_done) {
     typedef int i32x4 __attribute__((ext_vector_type(4)));
-    if (st && st->done) return;   // uniform
+    if (check_done && st->done) return;   // uniform
     __shared__ int line_dof[SV_WG / 64][3 * 65];
     __shared__ double line_val[SV_WG / 64][3 * 65];
+    double xm = 0.0;
+    for (int b = threadIdx.x; b < nb; b += SV_WG) xm = fmax(xm, xmax_slot(partials)[b]);
+    const int kx = fix_exponent(st->op_bound, block_max(xm));
+    if (blockIdx.x == 0 && threadIdx.x == 0) st->acc_exp = kx;
+    const double unit = ldexp(1.0, kx);
     // lanes past the last element stay for the wave exchange, with index -1
     const int e = blockIdx.x * SV_WG + threadIdx.x;
     const bool live = e < n_elem;
@@ -195,11 +326,11 @@ __global__ __launch_bounds__(SV_WG) void k_fe_matvec64(int n_elem, int n_dof, co
     }
 #pragma unroll
     for (int b = 0; b < NDOF_E; ++b) d[b] = live ? d[b] : -1;
-    float u[NDOF_E];
+    X u[NDOF_E];
 #pragma unroll
     for (int b = 0; b < NDOF_E; ++b) u[b] = x[(unsigned)d[b] < (unsigned)n_dof ? d[b] : 0];
 #pragma unroll
-    for (int b = 0; b < NDOF_E; ++b) u[b] = (unsigned)d[b] < (unsigned)n_dof ? u[b] : 0.0f;
+    for (int b = 0; b < NDOF_E; ++b) u[b] = (unsigned)d[b] < (unsigned)n_dof ? u[b] : X(0);
     double s = 1.0;
     for (int k = 0; k < penalty; ++k) s *= (double)rho[ec];
     double fa[NDOF_E];
@@ -210,7 +341,12 @@ __global__ __launch_bounds__(SV_WG) void k_fe_matvec64(int n_elem, int n_dof, co
         for (int b = 0; b < NDOF_E; ++b) f = fma((double)Ke[a * NDOF_E + b], (double)u[b], f);
         fa[a] = s * f;
     }
-    fe_scatter_lines(d, fa, n_dof, acc, line_dof[threadIdx.x >> 6], line_val[threadIdx.x >> 6]);
+    fe_scatter_lines(
+        d, fa, n_dof,
+        [acc, unit](int i, double v) {
+            atomicAdd(reinterpret_cast<unsigned long long *>(acc + i), (unsigned long long)__double2ll_rn(v * unit));
+        },
+        line_dof[threadIdx.x >> 6], line_val[threadIdx.x >> 6]);
 }
 
 // diag[edof[e][a]] += rho_e^p Ke[a][a] over the element's free DOFs.
@@ -227,37 +363,67 @@ __global__ void k_fe_diag(int n_elem, int n_dof, const int *__restrict__ edof, c
     }
 }
 
-// dinv = 1 / diag, flagging an entry that is not positive and finite.
-__global__ void k_pcg_dinv(int n, const float *__restrict__ diag, float *__restrict__ dinv, SolverState *st) {
+// The solver's diagonal in fixed point: acc[edof[e][a]] += rho_e^p Ke[a][a]
+// scaled by 2^k with k from the operator bound (Ke_aa <= sum_b |Ke_ab|, so
+// each DOF's sum is within G), added with integer atomics.
+__global__ void k_fe_diag_fixed(int n_elem, int n_dof, const int *__restrict__ edof, const float *__restrict__ rho,
+                                int penalty, const float *__restrict__ Ke, long long *__restrict__ acc,
+                                const SolverState *st) {
+    const int e = blockIdx.x * SV_WG + threadIdx.x;
+    if (e >= n_elem) return;
+    const double unit = ldexp(1.0, fix_exponent(st->op_bound, 1.0));
+    double s = 1.0;
+    for (int k = 0; k < penalty; ++k) s *= (double)rho[e];
+#pragma unroll 4
+    for (int a = 0; a < NDOF_E; ++a) {
+        const int d = edof[(size_t)e * NDOF_E + a];
+        if ((unsigned)d < (unsigned)n_dof)
+            atomicAdd(reinterpret_cast<unsigned long long *>(acc + d),
+                      (unsigned long long)__double2ll_rn(s * (double)Ke[a * NDOF_E + a] * unit));
+    }
+}
+
+// dinv = 1 / diag with diag read from the fixed-point accumulator (which is
+// cleared), flagging an entry that is not positive and finite.
+__global__ void k_pcg_dinv(int n, long long *__restrict__ acc, double *__restrict__ dinv, SolverState *st) {
+    const double inv_unit = fix_unit(fix_exponent(st->op_bound, 1.0));
     bool ok = true;
     for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) {
-        const float d = diag[i];
-        ok = ok && (d > 0.0f) && (d < INFINITY);
-        dinv[i] = 1.0f / d;
+        const double d = (double)acc[i] * inv_unit;
+        acc[i] = 0;
+        ok = ok && (d > 0.0) && (d < INFINITY);
+        dinv[i] = 1.0 / d;
     }
     if (!ok) atomicOr(&st->bad, 1);
 }
 
-// Start of PCG, with acc = K u: r = f - acc (acc cleared), z = D^-1 r,
-// p = z; partial r.z, r.r, f.f into slot 1 (read as "iteration -1").
-__global__ void k_pcg_start(int n, const float *__restrict__ f, double *__restrict__ acc, float *__restrict__ r,
-                            const float *__restrict__ dinv, float *__restrict__ z, float *__restrict__ p,
-                            double *__restrict__ partials) {
+// Start of PCG, with acc = K u: u64 = u, r = f - acc (acc cleared),
+// z = D^-1 r, p = z; partial r.z, r.r, f.f into slot 1 (read as
+// "iteration -1"), and the maxima of |p| for the first matvec.
+__global__ void k_pcg_start(int n, const float *__restrict__ f, const float *__restrict__ u, long long *__restrict__ acc,
+                            double *__restrict__ u64, double *__restrict__ r, const double *__restrict__ dinv,
+                            double *__restrict__ z, double *__restrict__ p, double *__restrict__ partials,
+                            const SolverState *st) {
+    const double inv_unit = fix_unit(st->acc_exp);
     double v[3] = {0.0, 0.0, 0.0};
+    double m = 0.0;
     for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) {
-        const float fi = f[i];
-        const float ri = (float)((double)fi - acc[i]);
-        acc[i] = 0.0;
-        const float zi = dinv[i] * ri;
+        const double fi = f[i];
+        const double ri = fi - (double)acc[i] * inv_unit;
+        acc[i] = 0;
+        const double zi = dinv[i] * ri;
+        u64[i] = u[i];
         r[i] = ri;
         z[i] = zi;
         p[i] = zi;
-        v[0] += (double)ri * zi;
-        v[1] += (double)ri * ri;
-        v[2] += (double)fi * fi;
+        v[0] += ri * zi;
+        v[1] += ri * ri;
+        v[2] += fi * fi;
+        m = fmax(m, fabs(zi));
     }
     double *const dst[3] = {slot(partials, 1, 0), slot(partials, 1, 1), slot(partials, 1, 2)};
     store_partials<3>(v, dst);
+    store_xmax(m, partials);
 }
 
 // One workgroup: f.f and r.r of the start, and whether there is anything to do.
@@ -274,15 +440,16 @@ __global__ void k_pcg_start_fin(int nb, const double *__restrict__ partials, Sol
 }
 
 // q = acc = K p (acc cleared); partial p.q.
-__global__ void k_pcg_pq(int n, const float *__restrict__ p, double *__restrict__ acc, float *__restrict__ q,
+__global__ void k_pcg_pq(int n, const double *__restrict__ p, long long *__restrict__ acc, double *__restrict__ q,
                          double *__restrict__ partials, const SolverState *st) {
     if (st->done) return;   // uniform: set by an earlier launch
+    const double inv_unit = fix_unit(st->acc_exp);
     double v[1] = {0.0};
     for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) {
-        const float qi = (float)acc[i];
-        acc[i] = 0.0;
+        const double qi = (double)acc[i] * inv_unit;
+        acc[i] = 0;
         q[i] = qi;
-        v[0] += (double)p[i] * qi;
+        v[0] += p[i] * qi;
     }
     double *const dst[1] = {pq_slot(partials)};
     store_partials<1>(v, dst);
@@ -291,9 +458,9 @@ __global__ void k_pcg_pq(int n, const float *__restrict__ p, double *__restrict_
 // Iteration k: alpha = r.z (slot (k+1)&1) / p.q; u += alpha p,
 // r -= alpha q, z = D^-1 r; partial r.z, r.r into slot k&1.  A p.q that is
 // not positive stops the iteration (the operator is not SPD).
-__global__ void k_pcg_update(int n, int k, const float *__restrict__ p, const float *__restrict__ q,
-                             const float *__restrict__ dinv, float *__restrict__ u, float *__restrict__ r,
-                             float *__restrict__ z, double *__restrict__ partials, SolverState *st) {
+__global__ void k_pcg_update(int n, int k, const double *__restrict__ p, const double *__restrict__ q,
+                             const double *__restrict__ dinv, double *__restrict__ u, double *__restrict__ r,
+                             double *__restrict__ z, double *__restrict__ partials, SolverState *st) {
     if (st->done) return;
     const double *const src[2] = {pq_slot(partials), slot(partials, (k + 1) & 1, 0)};
     double t[2];
@@ -305,16 +472,16 @@ __global__ void k_pcg_update(int n, int k, const float *__restrict__ p, const fl
         }
         return;
     }
-    const float a = (float)(t[1] / t[0]);
+    const double a = t[1] / t[0];
     double v[2] = {0.0, 0.0};
     for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) {
-        u[i] = fmaf(a, p[i], u[i]);
-        const float ri = fmaf(-a, q[i], r[i]);
+        u[i] = fma(a, p[i], u[i]);
+        const double ri = fma(-a, q[i], r[i]);
         r[i] = ri;
-        const float zi = dinv[i] * ri;
+        const double zi = dinv[i] * ri;
         z[i] = zi;
-        v[0] += (double)ri * zi;
-        v[1] += (double)ri * ri;
+        v[0] += ri * zi;
+        v[1] += ri * ri;
     }
     double *const dst[2] = {slot(partials, k & 1, 0), slot(partials, k & 1, 1)};
     store_partials<2>(v, dst);
@@ -322,8 +489,8 @@ __global__ void k_pcg_update(int n, int k, const float *__restrict__ p, const fl
 
 // Iteration k: stop when r.r <= rtol^2 f.f or the cap is reached, else
 // beta = r.z (slot k&1) / r.z (slot (k+1)&1) and p = z + beta p.
-__global__ void k_pcg_direction(int n, int k, const float *__restrict__ z, float *__restrict__ p,
-                                const double *__restrict__ partials, SolverState *st) {
+__global__ void k_pcg_direction(int n, int k, const double *__restrict__ z, double *__restrict__ p,
+                                double *__restrict__ partials, SolverState *st) {
     if (st->done) return;
     const double *const src[3] = {slot(partials, k & 1, 0), slot(partials, k & 1, 1),
                                   slot(partials, (k + 1) & 1, 0)};
@@ -336,8 +503,19 @@ __global__ void k_pcg_direction(int n, int k, const float *__restrict__ z, float
         if (stop) st->done = 1;
     }
     if (stop) return;
-    const float b = (float)(t[0] / t[2]);
-    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) p[i] = fmaf(b, p[i], z[i]);
+    const double b = t[0] / t[2];
+    double m = 0.0;
+    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) {
+        const double pi = fma(b, p[i], z[i]);
+        p[i] = pi;
+        m = fmax(m, fabs(pi));
+    }
+    store_xmax(m, partials);
+}
+
+// The solution back into the caller's fp32 u.
+__global__ void k_pcg_store_u(int n, const double *__restrict__ u64, float *__restrict__ u) {
+    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) u[i] = (float)u64[i];
 }
 
 // Partial ||v||^2 into slot 0.
@@ -349,25 +527,32 @@ __global__ void k_sv_norm(int n, const float *__restrict__ v, double *__restrict
 }
 
 // dst = src / ||src|| with ||src||^2 from slot 0 (a zero vector is flagged
-// and gives zeros).
+// and gives zeros); the maxima of |dst| for the next matvec.
 __global__ void k_sv_scale(int n, const float *__restrict__ src, float *__restrict__ dst,
-                           const double *__restrict__ partials, SolverState *st) {
+                           double *__restrict__ partials, SolverState *st) {
     const double *const in[1] = {slot(partials, 0, 0)};
     double t[1];
     total_partials<1>(in, gridDim.x, t);
     if (!(t[0] > 0.0) && blockIdx.x == 0 && threadIdx.x == 0) st->bad |= 4;
     const float s = t[0] > 0.0 ? (float)(1.0 / sqrt(t[0])) : 0.0f;
-    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) dst[i] = src[i] * s;
+    double m = 0.0;
+    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) {
+        const float di = src[i] * s;
+        dst[i] = di;
+        m = fmax(m, fabs((double)di));
+    }
+    store_xmax(m, partials);
 }
 
 // Power-iteration step after acc = K v (v of unit length): w = acc (acc
 // cleared); partial v.w, w.w into slot 0.
-__global__ void k_pow_dots(int n, const float *__restrict__ v, double *__restrict__ acc, float *__restrict__ w,
-                           double *__restrict__ partials) {
+__global__ void k_pow_dots(int n, const float *__restrict__ v, long long *__restrict__ acc, float *__restrict__ w,
+                           double *__restrict__ partials, const SolverState *st) {
+    const double inv_unit = fix_unit(st->acc_exp);
     double s[2] = {0.0, 0.0};
     for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) {
-        const double wi = acc[i];
-        acc[i] = 0.0;
+        const double wi = (double)acc[i] * inv_unit;
+        acc[i] = 0;
         w[i] = (float)wi;
         s[0] += (double)v[i] * wi;
         s[1] += wi * wi;
@@ -377,9 +562,9 @@ __global__ void k_pow_dots(int n, const float *__restrict__ v, double *__restric
 }
 
 // v = w / ||w||, and the Rayleigh quotient v.w of the previous v into
-// hist[k] (both from slot 0).
+// hist[k] (both from slot 0); the maxima of |v| for the next matvec.
 __global__ void k_pow_next(int n, int k, const float *__restrict__ w, float *__restrict__ v,
-                           const double *__restrict__ partials, double *__restrict__ hist, SolverState *st) {
+                           double *__restrict__ partials, double *__restrict__ hist, SolverState *st) {
     const double *const in[2] = {slot(partials, 0, 0), slot(partials, 0, 1)};
     double t[2];
     total_partials<2>(in, gridDim.x, t);
@@ -388,16 +573,23 @@ __global__ void k_pow_next(int n, int k, const float *__restrict__ w, float *__r
         if (!(t[1] > 0.0)) st->bad |= 4;
     }
     const float s = t[1] > 0.0 ? (float)(1.0 / sqrt(t[1])) : 0.0f;
-    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) v[i] = w[i] * s;
+    double m = 0.0;
+    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) {
+        const float vi = w[i] * s;
+        v[i] = vi;
+        m = fmax(m, fabs((double)vi));
+    }
+    store_xmax(m, partials);
 }
 
 // Partial v.acc (acc = K v; acc cleared) into slot 0.
-__global__ void k_rayleigh(int n, const float *__restrict__ v, double *__restrict__ acc,
-                           double *__restrict__ partials) {
+__global__ void k_rayleigh(int n, const float *__restrict__ v, long long *__restrict__ acc,
+                           double *__restrict__ partials, const SolverState *st) {
+    const double inv_unit = fix_unit(st->acc_exp);
     double s[1] = {0.0};
     for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) {
-        s[0] += (double)v[i] * acc[i];
-        acc[i] = 0.0;
+        s[0] += (double)v[i] * ((double)acc[i] * inv_unit);
+        acc[i] = 0;
     }
     double *const dst[1] = {slot(partials, 0, 0)};
     store_partials<1>(s, dst);
@@ -423,8 +615,10 @@ struct Operator {
 
 struct Work {
     SolverState *st;
-    double *partials, *hist, *acc;
-    float *dinv, *r, *z, *p, *q, *v, *w;
+    double *partials, *hist;
+    long long *acc;
+    double *dinv, *r, *z, *p, *q, *u;   // PCG
+    float *v, *w;                       // eigenvalue iterations
 };
 
 Work carve(void *ws, const Layout &L) {
@@ -433,9 +627,11 @@ Work carve(void *ws, const Layout &L) {
     W.st = reinterpret_cast<SolverState *>(b + L.state);
     W.partials = reinterpret_cast<double *>(b + L.partials);
     W.hist = reinterpret_cast<double *>(b + L.hist);
-    W.acc = reinterpret_cast<double *>(b + L.acc);
-    float **v[7] = {&W.dinv, &W.r, &W.z, &W.p, &W.q, &W.v, &W.w};
-    for (int k = 0; k < 7; ++k) *v[k] = reinterpret_cast<float *>(b + L.vec[k]);
+    W.acc = reinterpret_cast<long long *>(b + L.acc);
+    double **v64[NVEC64] = {&W.dinv, &W.r, &W.z, &W.p, &W.q, &W.u};
+    for (int k = 0; k < NVEC64; ++k) *v64[k] = reinterpret_cast<double *>(b + L.vec64[k]);
+    float **v32[NVEC32] = {&W.v, &W.w};
+    for (int k = 0; k < NVEC32; ++k) *v32[k] = reinterpret_cast<float *>(b + L.vec32[k]);
     return W;
 }
 
@@ -457,14 +653,40 @@ spmv_status check_ws(const Layout &L, void *ws, size_t bytes) {
     return SPMV_OK;
 }
 
-// acc += K x (acc must hold zeros, or a sum to add to); skipped once
-// `state` (if given) says done.
-spmv_status matvec64(const Operator &A, const float *x, double *acc, hipStream_t st,
-                     const SolverState *state = nullptr) {
-    if (A.n_elem == 0) return SPMV_OK;
-    k_fe_matvec64<<<(int)ceil_div(A.n_elem, SV_WG), SV_WG, 0, st>>>(A.n_elem, A.n_dof, A.edof, A.rho, A.penalty,
-                                                                    A.Ke, x, acc, state);
+// acc = K x in fixed point (acc must hold zeros).  The maxima of |x| must
+// be in the xmax slot (from the kernel that wrote x) unless `find_max`, in
+// which case they are computed first.  With `check_done`, skipped once the
+// state says done.
+template <typename X>
+spmv_status matvec64(const Operator &A, const Work &W, const X *x, hipStream_t st, bool find_max,
+                     bool check_done) {
+    const int nb = vec_blocks(A.n_dof);
+    if (find_max) {
+        k_sv_absmax<X><<<nb, SV_WG, 0, st>>>(A.n_dof, x, W.partials);
+        SPMV_LAUNCHED("k_sv_absmax");
+    }
+    if (A.n_elem == 0) return SPMV_OK;   // K x = 0: the accumulator holds zeros at any exponent
+    k_fe_matvec64<X><<<(int)ceil_div(A.n_elem, SV_WG), SV_WG, 0, st>>>(A.n_elem, A.n_dof, A.edof, A.rho,
+                                                                       A.penalty, A.Ke, x, W.acc, W.partials, nb,
+                                                                       W.st, check_done ? 1 : 0);
     SPMV_LAUNCHED("k_fe_matvec64");
+    return SPMV_OK;
+}
+
+// The operator bound G into the state (the accumulator must hold zeros;
+// it does again afterwards).
+spmv_status prepare_bound(const Operator &A, const Work &W, hipStream_t st) {
+    const int nb = vec_blocks(std::max(A.n_dof, A.n_elem));
+    if (A.n_elem > 0) {
+        k_op_count<<<(int)ceil_div((int64_t)A.n_elem * NDOF_E, SV_WG), SV_WG, 0, st>>>(
+            A.n_elem, A.n_dof, A.edof, reinterpret_cast<int *>(W.acc));
+        SPMV_LAUNCHED("k_op_count");
+    }
+    k_op_partials<<<nb, SV_WG, 0, st>>>(A.n_elem, A.n_dof, A.rho, A.penalty, reinterpret_cast<int *>(W.acc),
+                                       W.partials);
+    SPMV_LAUNCHED("k_op_partials");
+    k_op_bound<<<1, SV_WG, 0, st>>>(nb, W.partials, A.Ke, W.st);
+    SPMV_LAUNCHED("k_op_bound");
     return SPMV_OK;
 }
 
@@ -491,11 +713,15 @@ spmv_status diag_into(const Operator &A, float *diag, hipStream_t st) {
     return SPMV_OK;
 }
 
-// Sets up D^-1 (once per operator) in W.dinv, using W.q as scratch.
+// Sets up D^-1 (once per operator) in W.dinv from the fixed-point
+// diagonal; the operator bound must be in the state.
 spmv_status prepare_dinv(const Operator &A, const Work &W, hipStream_t st) {
-    spmv_status s = diag_into(A, W.q, st);
-    if (s != SPMV_OK) return s;
-    k_pcg_dinv<<<vec_blocks(A.n_dof), SV_WG, 0, st>>>(A.n_dof, W.q, W.dinv, W.st);
+    if (A.n_elem > 0) {
+        k_fe_diag_fixed<<<(int)ceil_div(A.n_elem, SV_WG), SV_WG, 0, st>>>(A.n_elem, A.n_dof, A.edof, A.rho,
+                                                                          A.penalty, A.Ke, W.acc, W.st);
+        SPMV_LAUNCHED("k_fe_diag_fixed");
+    }
+    k_pcg_dinv<<<vec_blocks(A.n_dof), SV_WG, 0, st>>>(A.n_dof, W.acc, W.dinv, W.st);
     SPMV_LAUNCHED("k_pcg_dinv");
     return SPMV_OK;
 }
@@ -515,9 +741,9 @@ spmv_status pcg_run(const Operator &A, const Work &W, const float *f, float *u, 
     s = write_state(W, h, st);
     if (s != SPMV_OK) return s;
     // r = f - K u
-    s = matvec64(A, u, W.acc, st);
+    s = matvec64(A, W, u, st, true, false);
     if (s != SPMV_OK) return s;
-    k_pcg_start<<<nb, SV_WG, 0, st>>>(n, f, W.acc, W.r, W.dinv, W.z, W.p, W.partials);
+    k_pcg_start<<<nb, SV_WG, 0, st>>>(n, f, u, W.acc, W.u, W.r, W.dinv, W.z, W.p, W.partials, W.st);
     SPMV_LAUNCHED("k_pcg_start");
     k_pcg_start_fin<<<1, SV_WG, 0, st>>>(nb, W.partials, W.st);
     SPMV_LAUNCHED("k_pcg_start_fin");
@@ -527,11 +753,11 @@ spmv_status pcg_run(const Operator &A, const Work &W, const float *f, float *u, 
     while (!h.done && k < max_iter) {
         const int batch = std::min(PCG_CHECK, max_iter - k);
         for (int j = 0; j < batch; ++j, ++k) {
-            s = matvec64(A, W.p, W.acc, st, W.st);
+            s = matvec64(A, W, W.p, st, false, true);
             if (s != SPMV_OK) return s;
             k_pcg_pq<<<nb, SV_WG, 0, st>>>(n, W.p, W.acc, W.q, W.partials, W.st);
             SPMV_LAUNCHED("k_pcg_pq");
-            k_pcg_update<<<nb, SV_WG, 0, st>>>(n, k, W.p, W.q, W.dinv, u, W.r, W.z, W.partials, W.st);
+            k_pcg_update<<<nb, SV_WG, 0, st>>>(n, k, W.p, W.q, W.dinv, W.u, W.r, W.z, W.partials, W.st);
             SPMV_LAUNCHED("k_pcg_update");
             k_pcg_direction<<<nb, SV_WG, 0, st>>>(n, k, W.z, W.p, W.partials, W.st);
             SPMV_LAUNCHED("k_pcg_direction");
@@ -539,6 +765,8 @@ spmv_status pcg_run(const Operator &A, const Work &W, const float *f, float *u, 
         s = read_state(W, &h, st);
         if (s != SPMV_OK) return s;
     }
+    k_pcg_store_u<<<nb, SV_WG, 0, st>>>(n, W.u, u);
+    SPMV_LAUNCHED("k_pcg_store_u");
     if (h.bad & 1) return fail(SPMV_ERR_INVALID_MATRIX, "a diagonal entry of the operator is not positive");
     if (h.bad & 2) return fail(SPMV_ERR_INVALID_MATRIX, "p.Kp <= 0: the operator is not positive definite");
     if (iters) *iters = h.iter;
@@ -546,11 +774,15 @@ spmv_status pcg_run(const Operator &A, const Work &W, const float *f, float *u, 
     return SPMV_OK;
 }
 
-// Clears the state and the fp64 accumulator.
-spmv_status reset_state(const Work &W, int n, hipStream_t st) {
+// Clears the state and the accumulator, then puts the operator bound in
+// the state.
+spmv_status reset_state(const Operator &A, const Work &W, hipStream_t st) {
+    const int n = A.n_dof;
     k_sv_zero64<<<vec_blocks(n), SV_WG, 0, st>>>(n, W.acc);
     SPMV_LAUNCHED("k_sv_zero64");
-    return write_state(W, SolverState{}, st);
+    spmv_status s = write_state(W, SolverState{}, st);
+    if (s != SPMV_OK) return s;
+    return prepare_bound(A, W, st);
 }
 
 // dst = src / ||src||.
@@ -604,7 +836,7 @@ extern "C" spmv_status fem_pcg_solve(int32_t n_elem, int32_t n_dof, const int32_
     if (s != SPMV_OK) return s;
     hipStream_t st = as_stream(stream);
     const Work W = carve(workspace, L);
-    s = reset_state(W, n_dof, st);
+    s = reset_state(A, W, st);
     if (s != SPMV_OK) return s;
     s = prepare_dinv(A, W, st);
     if (s != SPMV_OK) return s;
@@ -625,14 +857,14 @@ extern "C" spmv_status fem_lambda_max(int32_t n_elem, int32_t n_dof, const int32
     hipStream_t st = as_stream(stream);
     const Work W = carve(workspace, L);
     const int n = n_dof, nb = vec_blocks(n);
-    s = reset_state(W, n_dof, st);
+    s = reset_state(A, W, st);
     if (s != SPMV_OK) return s;
     s = normalise_into(W, n, v0, W.v, st);
     if (s != SPMV_OK) return s;
     for (int k = 0; k < iterations; ++k) {
-        s = matvec64(A, W.v, W.acc, st);
+        s = matvec64(A, W, W.v, st, false, false);
         if (s != SPMV_OK) return s;
-        k_pow_dots<<<nb, SV_WG, 0, st>>>(n, W.v, W.acc, W.w, W.partials);
+        k_pow_dots<<<nb, SV_WG, 0, st>>>(n, W.v, W.acc, W.w, W.partials, W.st);
         SPMV_LAUNCHED("k_pow_dots");
         k_pow_next<<<nb, SV_WG, 0, st>>>(n, k, W.w, W.v, W.partials, W.hist, W.st);
         SPMV_LAUNCHED("k_pow_next");
@@ -664,7 +896,7 @@ extern "C" spmv_status fem_lambda_min(int32_t n_elem, int32_t n_dof, const int32
     hipStream_t st = as_stream(stream);
     const Work W = carve(workspace, L);
     const int n = n_dof, nb = vec_blocks(n);
-    s = reset_state(W, n_dof, st);
+    s = reset_state(A, W, st);
     if (s != SPMV_OK) return s;
     s = prepare_dinv(A, W, st);
     if (s != SPMV_OK) return s;
@@ -681,9 +913,9 @@ extern "C" spmv_status fem_lambda_min(int32_t n_elem, int32_t n_dof, const int32
         // v = w / ||w||, then the Rayleigh quotient v.Kv
         s = normalise_into(W, n, W.w, W.v, st);
         if (s != SPMV_OK) return s;
-        s = matvec64(A, W.v, W.acc, st);
+        s = matvec64(A, W, W.v, st, false, false);
         if (s != SPMV_OK) return s;
-        k_rayleigh<<<nb, SV_WG, 0, st>>>(n, W.v, W.acc, W.partials);
+        k_rayleigh<<<nb, SV_WG, 0, st>>>(n, W.v, W.acc, W.partials, W.st);
         SPMV_LAUNCHED("k_rayleigh");
         k_hist_fin<<<1, SV_WG, 0, st>>>(nb, k, W.partials, W.hist);
         SPMV_LAUNCHED("k_hist_fin");

@@ -6,10 +6,14 @@ inverse iteration) against the oracle, through the C ABI.
 * PCG on elasticity cantilevers: the reported residual is below rtol; the
   true residual ||f - K u|| / ||f||, recomputed by the oracle in fp64, is
   below 10 (rtol + floor), floor being the true residual of the exact
-  solution rounded to fp32 (what fp32 storage of u alone leaves); the compliance f.u is within 1e-4 of the fp64 solution's
-  (the page reports fp32 within 0.2% of fp64 for its solver); iteration
-  counts within 20% of the fp64 oracle's; the cap, a converged initial
-  guess, f = 0, a non-positive diagonal, and two solves agreeing;
+  solution rounded to fp32 (what fp32 storage of u alone leaves); the
+  compliance f.u is within 1e-4 of the fp64 solution's (the page reports
+  fp32 within 0.2% of fp64 for its solver); the iteration is fp64 PCG on
+  the same operator, so its count is within 2 (or 2%) of the fp64
+  oracle's, and within 5% at 64k and 216k elements; the cap, a converged
+  initial guess, f = 0, a non-positive diagonal; two solves of one system
+  agree bit for bit (the matvec adds fixed-point integers, whose sum does
+  not depend on the order of the atomic adds);
 * largest / smallest eigenvalue of small cantilevers against LAPACK, and the
   power-iteration sequence against the fp64 oracle's from the same start.
 """
@@ -36,6 +40,13 @@ def _K(m):
     return sp.csr_matrix((v, ci, rp), shape=(m.n_dof, m.n_dof))
 
 
+def _Kmv(m):
+    """x -> K x with K assembled by the oracle in fp64 and applied by the
+    oracle's fp64 CSR product."""
+    rp, ci, v = oracle.fe_assemble(m.edof, m.rho, m.Ke, m.n_dof, m.penalty)
+    return lambda x: oracle.csr_spmv_f64v(rp, ci, v, np.asarray(x, np.float64))
+
+
 @pytest.mark.parametrize("which", ["bench_mesh", "cantilever"])
 def test_jacobi_diagonal(which):
     m = gen.fe_mesh(40, 20, 10) if which == "bench_mesh" else gen.fe_cantilever(30, 10, 6)
@@ -55,35 +66,33 @@ def _solve(m, rtol, max_iter=20000, u0=None, f=None):
 @pytest.mark.parametrize("dims", [(4, 2, 2), (12, 6, 3), (24, 12, 6), (40, 20, 10)])
 def test_pcg_cantilever(dims):
     m = gen.fe_cantilever(*dims)
-    K = _K(m)
+    Kx = _Kmv(m)
     d = oracle.fe_diagonal(m.edof, m.rho, m.Ke, m.n_dof, m.penalty)
     f64 = m.f.astype(np.float64)
     rtol = 1e-6
     u, it, rr = _solve(m, rtol)
-    ur, itr, rrr = oracle.pcg_jacobi(lambda x: K @ x, d, f64, rtol=rtol, max_iter=20000)
-    uex, _, _ = oracle.pcg_jacobi(lambda x: K @ x, d, f64, rtol=1e-12, max_iter=50000)
-    true_res = np.linalg.norm(f64 - K @ u.astype(np.float64)) / np.linalg.norm(f64)
+    ur, itr, rrr = oracle.pcg_jacobi(Kx, d, f64, rtol=rtol, max_iter=20000)
+    uex, _, _ = oracle.pcg_jacobi(Kx, d, f64, rtol=1e-12, max_iter=50000)
+    true_res = np.linalg.norm(f64 - Kx(u.astype(np.float64))) / np.linalg.norm(f64)
     # what storing the exact solution in fp32 alone leaves: the floor of any fp32 u
-    floor = np.linalg.norm(f64 - K @ uex.astype(np.float32).astype(np.float64)) / np.linalg.norm(f64)
+    floor = np.linalg.norm(f64 - Kx(uex.astype(np.float32).astype(np.float64))) / np.linalg.norm(f64)
     c, cex = f64 @ u, f64 @ uex
     print(f"[pcg] {dims} n_dof={m.n_dof} it={it} (fp64 {itr}) reported={rr:.3g} true={true_res:.3g} "
           f"fp32 floor={floor:.3g} compliance rel err={abs(c - cex) / abs(cex):.3g}", flush=True)
     assert rr <= rtol
     assert true_res <= 10 * (rtol + floor)
     assert abs(c - cex) <= 1e-4 * abs(cex)
-    assert abs(it - itr) <= max(3, 0.2 * itr)
+    assert abs(it - itr) <= max(2, 0.02 * itr)
 
 
 def test_pcg_cap_initial_guess_zero_rhs_and_reproducible():
     m = gen.fe_cantilever(12, 6, 3)
     u, it, rr = _solve(m, 0.0, max_iter=5)
     assert it == 5 and rr > 0
-    # the matvec's atomic adds land in any order, so two solves agree to
-    # rounding, not bit for bit
-    a, ita, _ = _solve(m, 1e-6)
-    b, itb, _ = _solve(m, 1e-6)
-    f64 = m.f.astype(np.float64)
-    assert abs(ita - itb) <= 1 and abs(f64 @ a - f64 @ b) <= 1e-6 * abs(f64 @ a)
+    # the matvec adds fixed-point integers, so two solves agree bit for bit
+    a, ita, ra = _solve(m, 1e-6)
+    b, itb, rb = _solve(m, 1e-6)
+    assert ita == itb and ra == rb and np.array_equal(a.view(np.uint32), b.view(np.uint32))
     # a solution as the initial guess: converged before the first iteration
     u2, it2, rr2 = _solve(m, 1e-3, u0=a)
     assert it2 == 0 and rr2 <= 1e-3 and np.array_equal(u2, a)
@@ -111,7 +120,7 @@ def test_extreme_eigenvalues_small(dims):
     w = np.linalg.eigvalsh(K.toarray())
     v0 = np.random.default_rng(5).standard_normal(m.n_dof).astype(np.float32)
     lam = S.fem_lambda_max(*_op(m), dev(v0), 3000)
-    ref = oracle.power_lambda_max(lambda x: K @ x, v0.astype(np.float64), 3000)
+    ref = oracle.power_lambda_max(_Kmv(m), v0.astype(np.float64), 3000)
     print(f"[eig] {dims} lmax gpu={lam[-1]:.9g} oracle={ref[-1]:.9g} lapack={w[-1]:.9g}", flush=True)
     assert abs(lam[-1] - w[-1]) <= 2e-3 * w[-1]
     assert np.all(np.abs(lam[:50] - ref[:50]) <= 1e-5 * ref[:50])
@@ -134,14 +143,13 @@ PAGE_KAPPA = {"80x40x20": 6.1e5, "120x60x30": 1.3e6, "160x80x40": 2.3e6}
 
 @pytest.mark.parametrize("dims", [(80, 40, 20), (120, 60, 30)])
 def test_full_size_pcg_and_kappa(dims):
-    """The 64k- and 216k-element cantilevers: PCG iterations between 0.9x
-    and 2x the fp64 oracle's (with fp32 vectors at kappa ~ 1e6 the iteration
-    loses orthogonality and needs more steps than in fp64, by an amount that
-    varies with the order of the matvec's atomic adds: 715 to 1113 against
-    709 in runs of the same build at 216k elements), compliance within
-    1e-4 of the oracle's tight solve; the extreme eigenvalues within 1e-4 of
-    the oracle's from the same start vector; and kappa within 10% of the
-    page's value."""
+    """The 64k- and 216k-element cantilevers: PCG iterations within 5% of
+    the fp64 oracle's (the iteration runs in fp64 on the same operator;
+    with the former fp32 vectors the count drifted up to 1.6x at kappa ~
+    1e6), the same count and the same u bit for bit in a second solve,
+    compliance within 1e-4 of the oracle's tight solve; the extreme
+    eigenvalues within 1e-4 of the oracle's from the same start vector; and
+    kappa within 10% of the page's value."""
     key = "x".join(map(str, dims))
     g = _golden()[key]
     m = gen.fe_cantilever(*dims)
@@ -149,6 +157,9 @@ def test_full_size_pcg_and_kappa(dims):
     ws = torch.empty(S.fem_solver_workspace_size(m.n_dof, 400), dtype=torch.uint8, device="cuda")
     u = torch.zeros(m.n_dof, device="cuda")
     it, rr = S.fem_pcg_solve(*op, dev(m.f), u, 1e-6, 20000, workspace=ws)
+    u2 = torch.zeros(m.n_dof, device="cuda")
+    it2, rr2 = S.fem_pcg_solve(*op, dev(m.f), u2, 1e-6, 20000, workspace=ws)
+    assert it2 == it and rr2 == rr and torch.equal(u, u2), (it, it2)
     c = float(m.f.astype(np.float64) @ host(u).astype(np.float64))
     v0 = np.random.default_rng(5).standard_normal(m.n_dof).astype(np.float32)
     lam = S.fem_lambda_max(*op, dev(v0), 400, workspace=ws)
@@ -159,7 +170,7 @@ def test_full_size_pcg_and_kappa(dims):
           f"lmin={mu[-1]:.9g} ({g['lambda_min_inverse'][-1]:.9g}) kappa={kappa:.4g} page={PAGE_KAPPA[key]:.2g}",
           flush=True)
     assert rr <= 1e-6
-    assert 0.9 * g["pcg_iterations_rtol_1e-6"] <= it <= 2.0 * g["pcg_iterations_rtol_1e-6"]
+    assert abs(it - g["pcg_iterations_rtol_1e-6"]) <= 0.05 * g["pcg_iterations_rtol_1e-6"]
     assert abs(c - g["compliance"]) <= 1e-4 * abs(g["compliance"])
     assert abs(lam[99] - g["lambda_max_power_100"]) <= 1e-4 * g["lambda_max_power_100"]
     assert abs(lam[-1] - g["lambda_max_power_400"]) <= 1e-4 * g["lambda_max_power_400"]
