@@ -58,6 +58,7 @@ def lib():
             "oracle_half_to_double": (c_double, [ctypes.c_uint16]),
             "oracle_csr_spmv": (None, [c_int, i32p, i32p, f32p, f32p, c_double, c_double, vp, f64p, f64p]),
             "oracle_csr_spmv_f64": (None, [c_int, i32p, i32p, f64p, f32p, c_double, c_double, vp, f64p, f64p]),
+            "oracle_csr_spmv_f64v": (None, [c_int, i32p, i32p, f64p, f64p, f64p]),
             "oracle_row_stats": (None, [c_int, i32p, ctypes.POINTER(ctypes.c_int32),
                                         ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]),
             "oracle_row_bin": (c_int, [ctypes.c_int32, i32p]),
@@ -132,6 +133,15 @@ def csr_spmv_f64(row_ptr, col_idx, vals64, x, alpha=1.0, beta=0.0, y_in=None):
     lib().oracle_csr_spmv_f64(n, rp, _c(col_idx, np.int32), _c(vals64, np.float64), _c(x, np.float32),
                               float(alpha), float(beta), yp, y, s)
     return y, s
+
+
+def csr_spmv_f64v(row_ptr, col_idx, vals64, x64):
+    """y = A x with fp64 values and an fp64 vector (rows summed in storage order)."""
+    rp = _c(row_ptr, np.int32)
+    y = np.empty(len(rp) - 1, np.float64)
+    lib().oracle_csr_spmv_f64v(len(rp) - 1, rp, _c(col_idx, np.int32), _c(vals64, np.float64),
+                               _c(x64, np.float64), y)
+    return y
 
 
 def row_stats(row_ptr):

@@ -89,6 +89,19 @@ void oracle_csr_spmv_f64(int n_rows, const int32_t *rp, const int32_t *ci,
     }
 }
 
+/* The same definition with fp64 values and an fp64 vector, alpha = 1 and
+ * beta = 0: y = A x, each row summed in storage order (the matvec of the
+ * fp64 reference solver on the assembled FE operator). */
+void oracle_csr_spmv_f64v(int n_rows, const int32_t *rp, const int32_t *ci,
+                          const double *v, const double *x, double *y_out)
+{
+    for (int i = 0; i < n_rows; ++i) {
+        double s = 0.0;
+        for (int32_t k = rp[i]; k < rp[i + 1]; ++k) s += v[k] * x[ci[k]];
+        y_out[i] = s;
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Row statistics: max row length, sum and sum of squares (int64).          */
 /* ------------------------------------------------------------------------ */

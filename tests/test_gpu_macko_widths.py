@@ -31,20 +31,28 @@ def _encoded(s, b, n_rows=12288, n_cols=None, seed=3):
     if key not in _CACHE:
         W = gen.pruned_weight(s, n_rows=n_rows, n_cols=n_cols, seed=seed)
         enc = S.macko_encode(W.n_rows, W.n_cols, W.row_ptr, W.col_idx, W.vals_f16, bdelta=b)
+        oenc = oracle.macko_encode(W.n_cols, W.row_ptr, W.col_idx, W.vals_f16, bdelta=b)
+        for name, x, y in zip(("mrow_ptr", "codes", "values"), enc, oenc):
+            assert np.array_equal(x, y), f"encoder differs from the oracle in {name} ({key})"
         _CACHE.clear()
         _CACHE[key] = (W, enc)
     return _CACHE[key]
 
 
 def _run(n_rows, n_cols, b, enc, x16, i8, alpha=1.0, beta=0.0, y_in=None, xdev=None):
+    """GPU result and the oracle's (y, scale).  enc is asserted equal to the
+    oracle's encoding where it is built, so the reference uses the same
+    arrays; the int8 values are checked against the oracle's quantiser here."""
     mrp, codes, mv = enc
     y = dev(y_in) if beta else torch.full((n_rows,), float("nan"), device="cuda")
     xd = dev(x16) if xdev is None else xdev
     if i8:
         q, sc = S.macko_quantize_i8(n_rows, mrp, mv)
+        oq, osc = oracle.macko_quantize_i8(mrp, mv)
+        assert np.array_equal(q, oq) and np.array_equal(sc.view(np.uint32), osc.view(np.uint32))
         S.macko_spmv_i8(n_rows, n_cols, dev(mrp), dev(codes), dev(q), dev(sc), alpha, xd, beta, y, bdelta=b)
         torch.cuda.synchronize()
-        yr, s = oracle.macko_spmv_i8(n_cols, mrp, codes, q, sc, x16, alpha, beta, y_in, bdelta=b)
+        yr, s = oracle.macko_spmv_i8(n_cols, mrp, codes, oq, osc, x16, alpha, beta, y_in, bdelta=b)
     else:
         S.macko_spmv(n_rows, n_cols, dev(mrp), dev(codes), dev(mv), alpha, xd, beta, y, bdelta=b)
         torch.cuda.synchronize()
@@ -70,6 +78,10 @@ def test_full_size(b, s, i8):
     y, yr, sc = _run(W.n_rows, W.n_cols, b, enc, W.x_f16, i8)
     err = assert_close(y, yr, sc, TAU_F16, f"macko b={b} s={s} int8={i8}")
     assert err < 1e-5
+    if not i8:
+        # and against the dense fp16 oracle on the densified matrix
+        yd, scd = oracle.gemv_f16(W.dense_f16(), W.x_f16)
+        assert_close(y, yd, scd, TAU_F16, f"macko b={b} s={s} against the dense oracle")
 
 
 SHAPES = [(37, 1000, 0.5), (5, 17, 0.0), (64, 40000, 0.9), (300, 2049, 0.7), (3, 33000, 0.999)]

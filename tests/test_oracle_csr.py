@@ -118,3 +118,34 @@ def test_f64_valued_csr_matches_dense():
     rows = np.repeat(np.arange(50), np.diff(A.row_ptr))
     np.add.at(D, (rows, A.col_idx), v64)
     assert np.all(np.abs(y - 1.5 * D @ A.x.astype(np.float64)) <= 1e-13 * s + 1e-300)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_f64_vector_csr_matches_dense(seed):
+    """y = A x with fp64 values and an fp64 x (the fp64 solver's matvec):
+    NumPy dense brute force with duplicate columns and empty rows, and an
+    exact closed form: the 1-D Laplacian (2, -1) applied to i^2 gives -2
+    inside (second difference), exactly in fp64 for these small integers."""
+    rng = np.random.default_rng(200 + seed)
+    n_rows, n_cols = int(rng.integers(1, 200)), int(rng.integers(1, 200))
+    lens = rng.integers(0, 12, n_rows)
+    A = gen.random_csr(n_rows, n_cols, lens, seed=seed, sorted_cols=bool(seed % 2))
+    ci = A.col_idx.copy()
+    if A.nnz > 2:
+        ci[-1] = ci[0]
+    v64 = rng.standard_normal(A.nnz)
+    x64 = rng.standard_normal(n_cols)
+    y = oracle.csr_spmv_f64v(A.row_ptr, ci, v64, x64)
+    D = np.zeros((n_rows, n_cols))
+    rows = np.repeat(np.arange(n_rows), np.diff(A.row_ptr))
+    np.add.at(D, (rows, ci), v64)
+    scale = np.abs(D) @ np.abs(x64)
+    assert np.all(np.abs(y - D @ x64) <= 1e-13 * scale + 1e-300)
+    n = 50
+    rp = np.arange(0, 3 * n + 1, 3, dtype=np.int32)
+    cols = np.stack([np.arange(n) - 1, np.arange(n), np.arange(n) + 1], 1).clip(0, n - 1).astype(np.int32).ravel()
+    vals = np.tile([-1.0, 2.0, -1.0], n)
+    vals[0] = 0.0
+    vals[-1] = 0.0
+    y = oracle.csr_spmv_f64v(rp, cols, vals, np.arange(n, dtype=np.float64) ** 2)
+    assert np.array_equal(y[1:-1], np.full(n - 2, -2.0))
