@@ -386,6 +386,23 @@ spmv_status fem_matvec_threestage(int32_t n_elem, int32_t n_dof, const int32_t *
                                   float alpha, const float *x, float beta, float *y,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * three-stage comparator with its per-element vectors in a library-owned
+ * static device array instead of a workspace.  The array holds 65,536
+ * elements' U and F (12 MiB per GPU, kept until the process ends); larger
+ * meshes run as consecutive chunks of 65,536 elements on `stream`, so no
+ * size is rejected.  Same arguments, validation and result as
+ * fem_matvec_threestage (up to the order of the atomic adds).  Every call
+ * on one GPU uses that GPU's one array: calls that overlap on one GPU (on
+ * different streams or threads) race and give wrong results.  The stream
+ * must belong to the current device.  Nothing is allocated, no memset is
+ * issued; only kernels are launched.  Asynchronous. */
+spmv_status fem_matvec_threestage_noalloc(int32_t n_elem, int32_t n_dof, const int32_t *edof,
+                                          const float *rho, int32_t penalty, const float *Ke,
+                                          float alpha, const float *x, float beta, float *y,
+                                          void *stream);
+
 /* ======================================================================== */
 /* FE solver ("Fused GPU SpMV kernel optimisation", section 6.1: Jacobi-     */
 /* preconditioned CG around the fused matvec, with an iteration cap;        */

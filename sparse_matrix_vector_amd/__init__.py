@@ -26,7 +26,7 @@ __all__ = [
     "spmv_csr_apply", "spmv_csr_get_plan", "spmv_csr_info", "spmv_csr_destroy",
     "spmv_ell_from_csr", "spmv_ell_apply", "macko_encode_size", "macko_encode", "macko_spmv",
     "macko_quantize_i8", "macko_spmv_i8", "macko_decode_columns", "dense_gemv_f16", "fem_matvec_apply", "fem_threestage_size",
-    "fem_matvec_threestage", "fem_jacobi_diagonal", "fem_solver_workspace_size", "fem_pcg_solve",
+    "fem_matvec_threestage", "fem_matvec_threestage_noalloc", "fem_jacobi_diagonal", "fem_solver_workspace_size", "fem_pcg_solve",
     "fem_lambda_max", "fem_lambda_min", "spgemm_workspace_size", "spgemm_create", "spgemm_info",
     "spgemm_compute", "spgemm_destroy", "SpGEMM", "CSRMatrix", "spmv_hyb_width", "spmv_hyb_tail_size",
     "spmv_hyb_from_csr", "spmv_hyb_apply", "HYBMatrix", "spmv_auto_plan", "spmv_auto_create", "spmv_auto_apply",
@@ -631,3 +631,11 @@ def fem_matvec_threestage(n_elem, n_dof, edof, rho, penalty, Ke, alpha, x, beta,
           _dev(rho, _f32_dtype(), "rho"), int(penalty), _dev(Ke, _f32_dtype(), "Ke"), float(alpha),
           _dev(x, _f32_dtype(), "x"), float(beta), _dev(y, _f32_dtype(), "y"), workspace.data_ptr(),
           ws_bytes, _stream(stream, y))
+
+
+def fem_matvec_threestage_noalloc(n_elem, n_dof, edof, rho, penalty, Ke, alpha, x, beta, y, stream=None):
+    """The three-stage FE matvec with the library's static device scratch
+    (no workspace, no allocation); calls overlapping on one GPU race."""
+    _call("fem_matvec_threestage_noalloc", int(n_elem), int(n_dof), _dev(edof, _i32_dtype(), "edof"),
+          _dev(rho, _f32_dtype(), "rho"), int(penalty), _dev(Ke, _f32_dtype(), "Ke"), float(alpha),
+          _dev(x, _f32_dtype(), "x"), float(beta), _dev(y, _f32_dtype(), "y"), _stream(stream, y))

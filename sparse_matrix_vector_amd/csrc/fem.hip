@@ -30,6 +30,16 @@
 #include "fem_common.hpp"
 
 #include <algorithm>
+#include <mutex>
+
+// Device scratch of fem_matvec_threestage_noalloc: the per-element vectors U
+// and F of one chunk of at most FE_NOALLOC_CHUNK elements (2 * 65536 * 24
+// floats = 12 MiB).  Each GPU the library runs on holds its own copy until
+// the process ends.  Host code never uses this name as an address: the
+// entry point takes the device address from hipGetSymbolAddress once per
+// device.
+constexpr int FE_NOALLOC_CHUNK = 65536;
+static __device__ __align__(256) float scratch[2 * FE_NOALLOC_CHUNK * 24];
 
 namespace spmv {
 namespace {
@@ -162,6 +172,42 @@ __global__ void k_fe_scatter(int n_elem, int n_dof, const int *__restrict__ edof
     if ((unsigned)d < (unsigned)n_dof) atomicAdd(y + d, F[k]);
 }
 
+// The three launches of the unfused form for elements [0, n_elem) of the
+// given arrays (already offset to a chunk), U and F holding n_elem * 24
+// floats each.
+spmv_status threestage_launch(int n_elem, int n_dof, const int32_t *edof, const float *rho, int penalty,
+                              const float *Ke, float alpha, const float *x, float *y, float *U, float *F,
+                              hipStream_t st) {
+    const int entries = n_elem * NDOF_E;
+    k_fe_gather<<<(int)ceil_div(entries, 256), 256, 0, st>>>(n_elem, n_dof, edof, x, U);
+    SPMV_LAUNCHED("k_fe_gather");
+    k_fe_elem<<<(int)ceil_div(n_elem, FE_WG), FE_WG, 0, st>>>(n_elem, rho, penalty, Ke, alpha, U, F);
+    SPMV_LAUNCHED("k_fe_elem");
+    k_fe_scatter<<<(int)ceil_div(entries, 256), 256, 0, st>>>(n_elem, n_dof, edof, F, y);
+    SPMV_LAUNCHED("k_fe_scatter");
+    return SPMV_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+spmv_status scratch_address(float **out) {
+    static std::mutex mu;
+    static float *addr[64] = {};
+    int dev = -1;
+    SPMV_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= 64) return fail(SPMV_ERR_UNSUPPORTED, "device %d: at most 64 devices", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(SPMV_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        addr[dev] = static_cast<float *>(p);
+    }
+    *out = addr[dev];
+    return SPMV_OK;
+}
+
 spmv_status check_fe(int32_t n_elem, int32_t n_dof, const int32_t *edof, const float *rho, int32_t penalty,
                      const float *Ke, const float *x, float *y) {
     if (n_elem < 0 || n_dof < 0) return fail(SPMV_ERR_INVALID_VALUE, "negative size");
@@ -222,12 +268,30 @@ extern "C" spmv_status fem_matvec_threestage(int32_t n_elem, int32_t n_dof, cons
     if (n_elem == 0) return SPMV_OK;
     float *U = static_cast<float *>(workspace);
     float *F = U + (size_t)n_elem * NDOF_E;
-    const int entries = n_elem * NDOF_E;
-    k_fe_gather<<<(int)ceil_div(entries, 256), 256, 0, st>>>(n_elem, n_dof, edof, x, U);
-    SPMV_LAUNCHED("k_fe_gather");
-    k_fe_elem<<<(int)ceil_div(n_elem, FE_WG), FE_WG, 0, st>>>(n_elem, rho, penalty, Ke, alpha, U, F);
-    SPMV_LAUNCHED("k_fe_elem");
-    k_fe_scatter<<<(int)ceil_div(entries, 256), 256, 0, st>>>(n_elem, n_dof, edof, F, y);
-    SPMV_LAUNCHED("k_fe_scatter");
+    return threestage_launch(n_elem, n_dof, edof, rho, penalty, Ke, alpha, x, y, U, F, st);
+}
+
+extern "C" spmv_status fem_matvec_threestage_noalloc(int32_t n_elem, int32_t n_dof, const int32_t *edof,
+                                                     const float *rho, int32_t penalty, const float *Ke, float alpha,
+                                                     const float *x, float beta, float *y, void *stream) {
+    spmv_status s = check_fe(n_elem, n_dof, edof, rho, penalty, Ke, x, y);
+    if (s != SPMV_OK) return s;
+    if (n_dof == 0) return SPMV_OK;
+    float *U = nullptr;
+    s = scratch_address(&U);
+    if (s != SPMV_OK) return s;
+    float *F = U + (size_t)FE_NOALLOC_CHUNK * NDOF_E;
+    hipStream_t st = as_stream(stream);
+    if (beta != 1.0f) {
+        k_fe_beta<<<(int)ceil_div(n_dof, 256), 256, 0, st>>>(n_dof, beta, y);
+        SPMV_LAUNCHED("k_fe_beta");
+    }
+    // chunks of elements one after another on the stream: a chunk's gather
+    // overwrites U only after the previous chunk's kernels have used it
+    for (int off = 0; off < n_elem; off += FE_NOALLOC_CHUNK) {
+        const int m = std::min(FE_NOALLOC_CHUNK, n_elem - off);
+        s = threestage_launch(m, n_dof, edof + (size_t)off * NDOF_E, rho + off, penalty, Ke, alpha, x, y, U, F, st);
+        if (s != SPMV_OK) return s;
+    }
     return SPMV_OK;
 }
