@@ -1,27 +1,35 @@
 #!/usr/bin/env python3
 """Benchmark of the MI355X SpMV library: y = alpha * A * x + beta * y.
 
-Default run (N = 1): the 2-D 5-point Laplacian on a 1000 x 1000 grid
-(1,000,000 rows, 4,996,000 nonzeros, fp32), CSR path with the row-grouping
-planner (spmv_csr_apply, AUTO variant).  One step = one apply.
+Default run (N = 1): every configuration in one JSON line.  The headline is
+the 2-D 5-point Laplacian on a 1000 x 1000 grid (1,000,000 rows, 4,996,000
+nonzeros, fp32), CSR path with the row-grouping planner (spmv_csr_apply,
+AUTO variant); one step = one apply, and exactly --steps of them are timed.
+Under "configs" the line then carries, with the same step count, its own
+parity check and a short oracle timing: the Laplacian's ELL path, the tiny
+CSR, the power-law CSR, the pruned 12288 x 12288 weights at 50 / 70 / 90 %
+sparsity (MACKO) and the dense fp16 GEMV comparator, and the FE matvec
+(fused and three-stage).
 
 Cold-cache protocol ("rotate", the default): the inputs are replicated R
 times in HBM so that R copies span >= 1 GiB (4x the 256 MB Infinity Cache
 plus the L2s); step i applies copy i mod R, so every apply streams a matrix
 that was last touched >= 3/4 GiB of traffic earlier, i.e. from HBM.  K steps
 run back to back on one stream between two HIP events recorded on that
-stream (no host synchronisation inside), so per-launch event overhead does
-not enter the per-step time.  "flush" mode instead writes 1 GiB before
-every apply and brackets each apply with its own event pair.  "warm"
-repeats copy 0 (data cached in the Infinity Cache).  Inputs are resident in
-HBM before the timed region.
+stream (no host synchronisation inside), replayed from HIP graphs (one of
+the R copies, one of the first K mod R), so per-launch host cost does not
+enter the per-step time.  "flush" mode instead writes 1 GiB before every
+apply and brackets each apply with its own event pair.  "warm" repeats copy
+0 (data cached in the Infinity Cache).  Inputs are resident in HBM before
+the timed region.
 
 Printed: ONE JSON line with the metric (GFLOP/s), effective GB/s over the
 algorithmic bytes, the roofline of the dominant kernel against the 8 TB/s
-HBM peak, and the CPU oracle timed on the host (serial fp64 C, bounded
-sample).
+HBM peak, the library's reference streams (copy, read) at the same size,
+and the CPU oracle timed on the host (serial fp64 C on one core, bounded
+sample; and the same function on row blocks in one thread per core).
 
-Other workloads (parity-test configs, also used for profiles):
+One workload only (--config, optionally --path; used for the profiles):
   --config tiny | laplacian | powerlaw | varlen | pruned50 | pruned70 | pruned90 | fe | cantilever
   --path   csr | csr-binned | csr-vector | csr-scalar | ell | hyb | auto | macko | dense | fem | fem-3stage
            (MACKO variants: macko-b1 | macko-b2 | macko-b8 for 1-, 2- or 8-bit
@@ -195,6 +203,7 @@ class Workload:
             if path.startswith("macko"):
                 i8, bd = macko_variant(path)
                 mrp, codes, mv = S.macko_encode(P.n_rows, P.n_cols, P.row_ptr, P.col_idx, P.vals_f16, bdelta=bd)
+                self.enc = (mrp, codes, mv)
                 E = int(mrp[-1])
                 # codes + values (+ row scales) + row pointers + x + y
                 self.bytes = (E * bd // 8 + (E + 4 * P.n_rows if i8 else 2 * E) + 4 * (P.n_rows + 1)
@@ -312,6 +321,10 @@ def macko_variant(path):
 
 
 def parity(w, ref_fn):
+    """The GPU result of one apply against the oracle, element by element:
+    |y - y_ref| <= tau * scale (tau 1e-5 for fp32 values, 4e-3 for fp16
+    values), and for MACKO the library's encoding bit-exact with the
+    oracle's."""
     np = w.np
     w.torch.cuda.synchronize()
     w.launch()
@@ -323,23 +336,106 @@ def parity(w, ref_fn):
     err = np.abs(y - yr)
     worst = float(np.max(err[nz] / sc[nz])) if nz.any() else 0.0
     ok = bool(np.all(err <= tau * sc))
-    return {"ok": ok, "tau": tau, "max_err_over_scale": worst}
+    out = {"ok": ok, "tau": tau, "max_err_over_scale": worst, "outputs": int(len(y))}
+    if getattr(w, "enc", None) is not None:
+        import oracle
+        i8, bd = macko_variant(w.path)
+        P = w.P
+        oenc = oracle.macko_encode(P.n_cols, P.row_ptr, P.col_idx, P.vals_f16, bdelta=bd)
+        same = all(np.array_equal(a, b) for a, b in zip(w.enc, oenc))
+        out["encoding_bit_exact"] = bool(same)
+        out["ok"] = bool(ok and same)
+    return out
 
 
-def cpu_baseline(w, fn, seconds):
-    """The oracle as it stands (serial C, fp64), repeated on the full input
-    until `seconds` of CPU time have passed (at least one call)."""
-    reps = 0
-    t0 = time.perf_counter()
+def _rate(w, per_call_s):
+    """CPU rate in the metric's unit (GFLOP/s) and per-call milliseconds."""
+    return round(w.flops / per_call_s / 1e9, 4), round(per_call_s * 1e3, 3)
+
+
+def _repeat(fn, seconds):
+    """Calls fn until `seconds` have passed (at least once); seconds per call."""
+    reps, t0 = 0, time.perf_counter()
     while True:
         fn()
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
-    per = el / reps
-    return {"value": round(w.flops / per / 1e9, 4), "unit": "GFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full applies of the same {w.workload} input ({el:.1f} s, {per * 1e3:.2f} ms each)"}
+            return el / reps, reps, el
+
+
+def rowpar_oracle(w):
+    """(callable, threads) running the oracle's serial C function on T
+    nonzero-balanced row blocks in T threads at once (ctypes releases the
+    GIL), T = the host cores this process may use; every row is still summed
+    serially, so the result equals the serial oracle's bit for bit.  None
+    for paths without independent rows (ELL's slot-major layout, the FE
+    element loop)."""
+    import concurrent.futures
+    import oracle
+    np = w.np
+    L = oracle.lib()
+    T = len(os.sched_getaffinity(0))
+    if w.config in CSR_CONFIGS and w.path.startswith("csr"):
+        A = w.A
+        rp, ci, v, x = (np.ascontiguousarray(a) for a in (A.row_ptr, A.col_idx, A.vals, A.x))
+        n, weight = A.n_rows, rp.astype(np.int64) + np.arange(A.n_rows + 1)
+
+        def part(r0, r1, y, s):
+            L.oracle_csr_spmv(r1 - r0, rp[r0:r1 + 1], ci, v, x, 1.0, 0.0, None, y[r0:r1], s[r0:r1])
+    elif w.config.startswith("pruned") and w.path.startswith("macko") and not macko_variant(w.path)[0]:
+        P = w.P
+        i8, bd = macko_variant(w.path)
+        mrp, codes, mv = oracle.macko_encode(P.n_cols, P.row_ptr, P.col_idx, P.vals_f16, bdelta=bd)
+        x = np.ascontiguousarray(P.x_f16)
+        n, weight = P.n_rows, mrp.astype(np.int64)
+
+        def part(r0, r1, y, s):
+            L.oracle_macko_spmv(r1 - r0, P.n_cols, bd, mrp[r0:r1 + 1], codes, mv, x, 1.0, 0.0, None, y[r0:r1],
+                                s[r0:r1])
+    elif w.config.startswith("pruned") and w.path == "dense":
+        P = w.P
+        D = np.ascontiguousarray(P.dense_f16())
+        x = np.ascontiguousarray(P.x_f16)
+        n, weight = P.n_rows, np.arange(P.n_rows + 1, dtype=np.int64)
+
+        def part(r0, r1, y, s):
+            L.oracle_gemv_f16(r1 - r0, P.n_cols, D[r0:r1].reshape(-1), x, 1.0, 0.0, None, y[r0:r1], s[r0:r1])
+    else:
+        return None, 0
+    cuts = np.searchsorted(weight, np.linspace(0, weight[-1], T + 1), side="left").clip(0, n)
+    cuts[0], cuts[-1] = 0, n
+    blocks = [(int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+    y, s = np.empty(n), np.empty(n)
+    pool = concurrent.futures.ThreadPoolExecutor(T)
+
+    def run():
+        list(pool.map(lambda b: part(b[0], b[1], y, s), blocks))
+        return y, s
+    return run, T
+
+
+def cpu_baseline(w, fn, seconds, par_seconds=None):
+    """The oracle as it stands (serial C, fp64, one core) on the full input,
+    repeated for `seconds`; and, where the path has independent rows, the
+    same function on row blocks in one thread per host core (the identical
+    result is checked)."""
+    per, reps, el = _repeat(fn, seconds)
+    value, ms = _rate(w, per)
+    out = {"value": value, "unit": "GFLOP/s", "cores": 1, "kind": "oracle", "ms_per_apply": ms,
+           "sample": f"{reps} full applies of the same {w.workload} input ({el:.1f} s, {ms:.2f} ms each)"}
+    run, T = rowpar_oracle(w)
+    if run is not None:
+        np = w.np
+        ys, _ = fn()
+        yp, _ = run()
+        per_p, reps_p, el_p = _repeat(run, par_seconds if par_seconds is not None else seconds / 2)
+        v2, ms2 = _rate(w, per_p)
+        out["row_parallel"] = {"value": v2, "unit": "GFLOP/s", "cores": T, "kind": "oracle", "ms_per_apply": ms2,
+                               "identical_to_serial": bool(np.array_equal(ys, yp)),
+                               "sample": f"{reps_p} full applies on {T} threads, nonzero-balanced row blocks "
+                                         f"({el_p:.1f} s)"}
+    return out
 
 
 def traffic_record(w):
@@ -356,46 +452,58 @@ def traffic_record(w):
     return int(r["bytes_per_launch"])
 
 
+def _capture(torch, launches):
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for L in launches:
+            L()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for L in launches:
+            L()
+    return g.replay
+
+
 def timed_rotate(w, steps, warmup, launches, graph=True):
-    """`steps` applies back to back, step i on launches[i % R], between one
-    pair of HIP events on the launch stream, with a device synchronisation
-    on both sides.  With `graph`, one pass over the R launches is captured
-    in a HIP graph and replayed, so host launch cost does not throttle the
-    GPU; the captured kernels are the same launches."""
-    import math
+    """Exactly `steps` applies back to back, step i on launches[i % R],
+    between one pair of HIP events on the launch stream, with a device
+    synchronisation on both sides.  With `graph`, one pass over the R
+    launches is captured in a HIP graph (and the first steps % R launches
+    in a second one) and replayed, so host launch cost does not throttle
+    the GPU; the captured kernels are the same launches."""
     torch = w.torch
     R = len(launches)
-    reps = max(1, math.ceil(steps / R))
+    full_passes, rest = divmod(steps, R)
     if graph:
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for L in launches:
-                L()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            for L in launches:
-                L()
-        run = g.replay
+        run_all = _capture(torch, launches)
+        run_rest = _capture(torch, launches[:rest]) if rest else None
     else:
-        def run():
+        def run_all():
             for L in launches:
                 L()
-    for _ in range(max(1, math.ceil(warmup / R))):
-        run()
+
+        def run_rest():
+            for L in launches[:rest]:
+                L()
+    for _ in range(max(1, -(-warmup // R))):
+        run_all()
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    a.record()
-    for _ in range(reps):
-        run()
-    b.record()
+    a.record(stream)
+    for _ in range(full_passes):
+        run_all()
+    if rest:
+        run_rest()
+    b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    n = reps * R
-    return {"ms_per_apply": a.elapsed_time(b) / n, "wall_ms_per_apply": wall * 1e3 / n, "applies": n,
+    n = max(steps, 1)
+    return {"ms_per_apply": a.elapsed_time(b) / n, "wall_ms_per_apply": wall * 1e3 / n, "applies": steps,
             "copies": R, "graph": graph}
 
 
@@ -415,7 +523,7 @@ def timed_flush(w, steps, warmup):
         b.record()
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
-    return {"ms_per_apply": sum(ms) / len(ms), "median_ms": ms[len(ms) // 2]}
+    return {"ms_per_apply": sum(ms) / len(ms), "median_ms": ms[len(ms) // 2], "applies": steps}
 
 
 def launch_spread(w, launches, n=200):
@@ -438,25 +546,36 @@ def launch_spread(w, launches, n=200):
     return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "launches": n}
 
 
-def copy_reference(nbytes, steps=400):
-    """Bandwidth of torch's device copy (nbytes/2 read + nbytes/2 written)
-    under the same rotation protocol: what a plain streaming kernel reaches
-    at this size on this GPU."""
-    import math
+def stream_reference(nbytes, steps=400):
+    """The library's own reference streams (spmv_stream_copy, spmv_stream_read)
+    at the workload's size, under the same rotation protocol and graph
+    replay: what a plain streaming kernel of this size reaches on this GPU.
+    copy: nbytes / 2 read + nbytes / 2 written; read: nbytes read."""
     import torch
-    half = max(nbytes // 2 // 4, 1)
-    R = max(2, math.ceil(ROTATE_BYTES / (8 * half)))
-    pairs = [(torch.ones(half, dtype=torch.float32, device="cuda"),
-              torch.empty(half, dtype=torch.float32, device="cuda")) for _ in range(R)]
-    launches = [(lambda p=p: p[1].copy_(p[0])) for p in pairs]
+    import sparse_matrix_vector_amd as S
+    out = {}
+    for kind in ("copy", "read"):
+        elems = max(((nbytes // 2 if kind == "copy" else nbytes) // 4) // 4 * 4, 4)
+        moved = 4 * elems * (2 if kind == "copy" else 1)
+        R = max(2, -(-ROTATE_BYTES // moved))
+        bufs = [(torch.ones(elems, dtype=torch.float32, device="cuda"),
+                 torch.empty(elems if kind == "copy" else 4096, dtype=torch.float32, device="cuda"))
+                for _ in range(R)]
+        if kind == "copy":
+            launches = [(lambda b=b: S.spmv_stream_copy(b[0], b[1])) for b in bufs]
+        else:
+            launches = [(lambda b=b: S.spmv_stream_read(b[0], b[1])) for b in bufs]
 
-    class _W:
-        pass
-    w = _W()
-    w.torch = torch
-    r = timed_rotate(w, steps, 2 * R, launches, graph=True)
-    return {"bytes": 8 * half, "copies": R, "ms": round(r["ms_per_apply"], 6),
-            "gbs": round(8 * half / (r["ms_per_apply"] * 1e-3) / 1e9, 1)}
+        class _W:
+            pass
+        w = _W()
+        w.torch = torch
+        r = timed_rotate(w, steps, 2 * R, launches, graph=True)
+        out[kind] = {"bytes": moved, "copies": R, "us": round(r["ms_per_apply"] * 1e3, 3),
+                     "gbs": round(moved / (r["ms_per_apply"] * 1e-3) / 1e9, 1),
+                     "kernel": "k_stream_" + kind}
+        del bufs, launches
+    return out
 
 
 def pmc_calibration_copies(nbytes=256 << 20, reps=3):
@@ -666,12 +785,72 @@ def bench_spgemm(args):
     print(json.dumps(line), flush=True)
 
 
+# The default run: the headline (Laplacian CSR) in full detail, then every
+# other path the five configurations name, each with its own parity check,
+# timing over the same number of steps, and a short oracle timing.  Targets
+# are % of the 8 TB/s HBM peak over the algorithmic bytes.
+HEADLINE = ("laplacian", "csr", 60.0, None)
+SUITE = [
+    ("laplacian", "ell", 60.0, "the Laplacian config's ELL path (width 5)"),
+    ("tiny", "csr", None, "parity config: 311 KB, launch-bound, no % target"),
+    ("powerlaw", "csr", 35.0, None),
+    ("pruned50", "macko", 60.0, None),
+    ("pruned70", "macko", 60.0, None),
+    ("pruned90", "macko", 60.0, None),
+    ("pruned50", "dense", None, "dense fp16 GEMV comparator of the MACKO configs (same W densified)"),
+    ("fe", "fem", None, "fused FE matvec: parity config, atomic-bound, no % target"),
+    ("fe", "fem-3stage", None, "unfused three-stage comparator of the fused FE matvec"),
+]
+
+
+def measure(config, path, args, target=None, note=None, detail=False, cpu_seconds=0.0, par_seconds=None):
+    """One path of one config: parity, timing over args.steps applies, the
+    oracle on the host; returns the result record."""
+    import torch
+    w = Workload(config, path, args.copies if args.protocol == "rotate" else 1)
+    ref_fn = w.oracle_call() if (not args.no_parity or cpu_seconds > 0) else None
+    par = None
+    if not args.no_parity:
+        par = parity(w, ref_fn)
+        log(f"[bench] parity {config}/{path} {par}")
+    graph = not args.no_graph
+    if args.protocol == "rotate":
+        meas = timed_rotate(w, args.steps, args.warmup, w.launches, graph)
+    elif args.protocol == "flush":
+        meas = timed_flush(w, args.steps, args.warmup)
+    else:
+        meas = timed_rotate(w, args.steps, args.warmup, [w.launches[0]] * min(len(w.launches), 16), graph)
+    ms = meas["ms_per_apply"]
+    gbs = w.bytes / (ms * 1e-3) / 1e9
+    pct = 100 * gbs / HBM_PEAK_GBS
+    rec = {"workload": w.workload, "path": path, "kernel": getattr(w, "kernel", None) or KERNEL[path],
+           "us_per_apply": round(ms * 1e3, 3), "algorithmic_bytes": w.bytes, "flops": w.flops,
+           "gflops": round(w.flops / (ms * 1e-3) / 1e9, 3), "effective_gbs": round(gbs, 2),
+           "pct_hbm_peak": round(pct, 2), "target_pct": target,
+           "target_met": None if target is None else bool(pct >= target),
+           "traffic": traffic_record(w), "parity": par, "shape": w.shape,
+           "timing_ms": {k: (round(v, 6) if isinstance(v, float) else v) for k, v in meas.items()}}
+    if note:
+        rec["note"] = note
+    if detail:
+        warm = timed_rotate(w, args.steps, args.warmup, [w.launches[0]] * min(len(w.launches), 16), graph)
+        rec["warm_timing_ms"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in warm.items()}
+        rec["single_launch_us"] = launch_spread(w, w.launches)
+    if cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(w, ref_fn, cpu_seconds, par_seconds)
+    log(f"[bench] {config}/{path}: {rec['us_per_apply']} us per apply, {rec['pct_hbm_peak']}% of peak")
+    del w
+    torch.cuda.empty_cache()
+    return rec, meas
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", default="laplacian", choices=sorted(DEFAULT_PATH))
+    ap.add_argument("--config", default=None, choices=sorted(DEFAULT_PATH),
+                    help="one configuration only (default: all of them, headline first)")
     ap.add_argument("--path", default=None, choices=sorted(KERNEL))
     ap.add_argument("--protocol", default="rotate", choices=["rotate", "flush", "warm"],
                     help="cold-cache protocol (see the module docstring)")
@@ -680,9 +859,9 @@ def main():
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="first run known-size device copies (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="CPU time spent on the oracle baseline (0 = skip)")
+                    help="CPU time spent on the headline's serial oracle baseline (0 = skip every CPU timing)")
     ap.add_argument("--no-parity", action="store_true")
-    ap.add_argument("--no-copy-ref", action="store_true", help="skip the plain-copy bandwidth reference")
+    ap.add_argument("--no-copy-ref", action="store_true", help="skip the reference-stream bandwidth")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -690,92 +869,79 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1:
+        raise SystemExit("--steps must be >= 1")
 
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(2)
-    path = args.path or DEFAULT_PATH[args.config]
+    config = args.config or HEADLINE[0]
+    path = args.path or (DEFAULT_PATH[config] if args.config else HEADLINE[1])
     if path == "spgemm":
-        if args.config not in ("powerlaw", "laplacian"):
+        if config not in ("powerlaw", "laplacian"):
             raise SystemExit("the spgemm path runs on the powerlaw and laplacian configs")
+        args.config = config
         bench_spgemm(args)
         return
-    if args.config == "cantilever" or path == "fem-pcg":
-        if args.config != "cantilever" or path != "fem-pcg":
+    if config == "cantilever" or path == "fem-pcg":
+        if config != "cantilever" or path != "fem-pcg":
             raise SystemExit("the fem-pcg path runs on the cantilever config only")
         bench_pcg(args)
         return
     if args.pmc_calibrate:
         pmc_calibration_copies()
-    w = Workload(args.config, path, args.copies if args.protocol == "rotate" else 1)
-
-    par = None
-    ref_fn = w.oracle_call() if (not args.no_parity or args.cpu_seconds > 0) else None
-    if not args.no_parity:
-        par = parity(w, ref_fn)
-        log(f"[bench] parity {par}")
-
-    graph = not args.no_graph
-    warm_launches = [w.launches[0]] * min(len(w.launches), 16)
-    if args.protocol == "rotate":
-        meas = timed_rotate(w, args.steps, args.warmup, w.launches, graph)
-    elif args.protocol == "flush":
-        meas = timed_flush(w, args.steps, args.warmup)
-    else:
-        meas = timed_rotate(w, args.steps, args.warmup, warm_launches, graph)
-    warm = timed_rotate(w, args.steps, args.warmup, warm_launches, graph)
-    spread = launch_spread(w, w.launches)
+    suite = args.config is None and args.path is None
+    target = HEADLINE[2] if (config, path) == HEADLINE[:2] else None
+    head, meas = measure(config, path, args, target=target, detail=True, cpu_seconds=args.cpu_seconds,
+                         par_seconds=args.cpu_seconds / 2)
     ms = meas["ms_per_apply"]
-    gflops = w.flops / (ms * 1e-3) / 1e9
-    gbs = w.bytes / (ms * 1e-3) / 1e9
-    traffic = traffic_record(w)
     line = {
         "metric": METRIC,
-        "value": round(gflops, 3),
+        "value": head["gflops"],
         "unit": "GFLOP/s",
         "n_gpus": 1,
-        "steps": meas.get("applies", args.steps),
+        "steps": meas["applies"],
         "warmup": args.warmup,
         "ms_per_step": round(ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16xf16->f32" if args.config.startswith("pruned") else "f32",
+        "dtype": "f16xf16->f32" if config.startswith("pruned") else "f32",
         "data": "synthetic (seeded generators in gen/)",
-        "config": {"workload": w.workload, "path": path, **w.shape, "alpha": w.alpha, "beta": w.beta,
-                   "protocol": args.protocol, "copies": len(w.launches),
-                   "timing": "HIP events on the launch stream around the timed steps"
-                             + (", replayed from a HIP graph" if graph and args.protocol != "flush" else ""),
-                   "algorithmic_bytes": w.bytes, "flops": w.flops},
-        "effective_gbs": round(gbs, 2),
-        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": getattr(w, "kernel", None) or KERNEL[path]},
-        "timing_ms": {k: round(v, 6) for k, v in meas.items()},
-        "warm_timing_ms": {k: round(v, 6) for k, v in warm.items()},
-        "single_launch_us": spread,
-        "parity": par,
-        "copy_reference": copy_reference(w.bytes) if not args.no_copy_ref else None,
+        "config": {"workload": head["workload"], "path": path, **head["shape"], "alpha": 1.0, "beta": 0.0,
+                   "protocol": args.protocol, "copies": meas.get("copies", 1),
+                   "timing": "HIP events on the launch stream around exactly `steps` applies"
+                             + (", replayed from HIP graphs" if not args.no_graph and args.protocol != "flush"
+                                else ""),
+                   "algorithmic_bytes": head["algorithmic_bytes"], "flops": head["flops"]},
+        "effective_gbs": head["effective_gbs"],
+        "pct_hbm_peak": head["pct_hbm_peak"],
+        "roofline": {"bound": "hbm", "achieved": head["effective_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(head["effective_gbs"] / HBM_PEAK_GBS, 4), "traffic": head["traffic"],
+                     "kernel": head["kernel"]},
+        "timing_ms": head["timing_ms"],
+        "warm_timing_ms": head["warm_timing_ms"],
+        "single_launch_us": head["single_launch_us"],
+        "parity": head["parity"],
+        "target_pct": head["target_pct"],
+        "target_met": head["target_met"],
     }
-    if args.cpu_seconds > 0:
-        line["cpu_baseline"] = cpu_baseline(w, ref_fn, args.cpu_seconds)
-    if args.path is None and args.config in OTHER_PATHS:
-        others = {}
-        del w
-        torch.cuda.empty_cache()
-        for op in OTHER_PATHS[args.config]:
-            w2 = Workload(args.config, op, args.copies)
-            p2 = None if args.no_parity else parity(w2, w2.oracle_call())
-            m2 = timed_rotate(w2, args.steps, args.warmup, w2.launches, graph)
-            g2 = w2.bytes / (m2["ms_per_apply"] * 1e-3) / 1e9
-            others[op] = {"ms_per_apply": round(m2["ms_per_apply"], 6), "algorithmic_bytes": w2.bytes,
-                          "effective_gbs": round(g2, 2), "pct_hbm_peak": round(100 * g2 / HBM_PEAK_GBS, 2),
-                          "kernel": KERNEL[op], "traffic": traffic_record(w2), "parity": p2, "shape": w2.shape}
-            del w2
-            torch.cuda.empty_cache()
-        line["other_paths"] = others
+    if not args.no_copy_ref:
+        line["stream_reference"] = stream_reference(head["algorithmic_bytes"])
+    if "cpu_baseline" in head:
+        line["cpu_baseline"] = head["cpu_baseline"]
+    if suite:
+        configs = {f"{config}/{path}": {k: v for k, v in head.items()
+                                        if k not in ("warm_timing_ms", "single_launch_us", "cpu_baseline")}}
+        for c, p, tgt, note in SUITE:
+            rec, _ = measure(c, p, args, target=tgt, note=note,
+                             cpu_seconds=min(args.cpu_seconds, 1.5), par_seconds=min(args.cpu_seconds, 1.0))
+            configs[f"{c}/{p}"] = rec
+        line["configs"] = configs
+        met = [r["target_met"] for r in configs.values() if r["target_met"] is not None]
+        line["targets_met"] = f"{sum(met)} of {len(met)}"
+        line["parity_all_ok"] = all((r["parity"] or {}).get("ok", False) for r in configs.values())
     print(json.dumps(line), flush=True)
 
 

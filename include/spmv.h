@@ -509,6 +509,21 @@ spmv_status spgemm_compute(spgemm_t h, int32_t *rp_c, int32_t *ci_c, float *v_c,
 /* Releases the handle (not the workspace or the borrowed arrays). */
 spmv_status spgemm_destroy(spgemm_t h);
 
+/* ======================================================================== */
+/* Reference streams: the measured bandwidth a plain kernel reaches, beside  */
+/* the HBM peak, as the second denominator of the roofline figures.          */
+/* ======================================================================== */
+
+/* dst[0 .. bytes) = src[0 .. bytes) with 16-byte non-temporal loads and
+ * stores (bytes read + bytes written).  bytes: a multiple of 16; src and
+ * dst device, 16-byte aligned, not overlapping.  Asynchronous. */
+spmv_status spmv_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/* Reads src[0 .. bytes) once with 16-byte non-temporal loads and writes one
+ * fp32 sum per workgroup to partial (device, at least 4 * CUs floats: 1024
+ * on MI355X).  Same size and alignment rules.  Asynchronous. */
+spmv_status spmv_stream_read(const void *src, size_t bytes, float *partial, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,8 @@ __all__ = [
     "spmv_csr_apply", "spmv_csr_get_plan", "spmv_csr_info", "spmv_csr_destroy",
     "spmv_ell_from_csr", "spmv_ell_apply", "macko_encode_size", "macko_encode", "macko_spmv",
     "macko_quantize_i8", "macko_spmv_i8", "macko_decode_columns", "dense_gemv_f16", "fem_matvec_apply", "fem_threestage_size",
-    "fem_matvec_threestage", "fem_matvec_threestage_noalloc", "fem_jacobi_diagonal", "fem_solver_workspace_size", "fem_pcg_solve",
+    "fem_matvec_threestage", "fem_matvec_threestage_noalloc", "spmv_stream_copy", "spmv_stream_read",
+    "fem_jacobi_diagonal", "fem_solver_workspace_size", "fem_pcg_solve",
     "fem_lambda_max", "fem_lambda_min", "spgemm_workspace_size", "spgemm_create", "spgemm_info",
     "spgemm_compute", "spgemm_destroy", "SpGEMM", "CSRMatrix", "spmv_hyb_width", "spmv_hyb_tail_size",
     "spmv_hyb_from_csr", "spmv_hyb_apply", "HYBMatrix", "spmv_auto_plan", "spmv_auto_create", "spmv_auto_apply",
@@ -639,3 +640,20 @@ def fem_matvec_threestage_noalloc(n_elem, n_dof, edof, rho, penalty, Ke, alpha, 
     _call("fem_matvec_threestage_noalloc", int(n_elem), int(n_dof), _dev(edof, _i32_dtype(), "edof"),
           _dev(rho, _f32_dtype(), "rho"), int(penalty), _dev(Ke, _f32_dtype(), "Ke"), float(alpha),
           _dev(x, _f32_dtype(), "x"), float(beta), _dev(y, _f32_dtype(), "y"), _stream(stream, y))
+
+
+# ---------------------------------------------------------------------------
+# Reference streams (the measured bandwidth denominator)
+# ---------------------------------------------------------------------------
+def spmv_stream_copy(src, dst, stream=None):
+    """dst = src byte for byte (CUDA tensors of equal size, multiple of 16 bytes)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst must have the same size in bytes")
+    _call("spmv_stream_copy", src.data_ptr(), dst.data_ptr(), n, _stream(stream, dst))
+
+
+def spmv_stream_read(src, partial, stream=None):
+    """Reads src once; one fp32 sum per workgroup into partial (>= 1024 floats)."""
+    _call("spmv_stream_read", src.data_ptr(), src.numel() * src.element_size(),
+          _dev(partial, _f32_dtype(), "partial"), _stream(stream, partial))
