@@ -424,7 +424,7 @@ int oracle_macko_encode(int n_rows, int n_cols, int b, const int32_t *rp, const 
     int64_t total = oracle_macko_size(n_rows, n_cols, b, rp, ci);
     if (total < 0 || total > INT32_MAX) return -1;
     const int64_t span = (int64_t)1 << b, align = 1024 / b;
-    memset(codes, 0, (size_t)(total * b / 32) * sizeof(uint32_t));
+    if (total > 0) memset(codes, 0, (size_t)(total * b / 32) * sizeof(uint32_t));
     int64_t e = 0;
     for (int i = 0; i < n_rows; ++i) {
         mrow_ptr[i] = (int32_t)e;
