@@ -32,6 +32,7 @@ sample; and the same function on row blocks in one thread per core).
 One workload only (--config, optionally --path; used for the profiles):
   --config tiny | laplacian | powerlaw | varlen | pruned50 | pruned70 | pruned90 | fe | cantilever
   --path   csr | csr-binned | csr-vector | csr-scalar | ell | hyb | auto | macko | dense | fem | fem-3stage
+           | fem-csr (the assembled stiffness matrix through the binned CSR path)
            (MACKO variants: macko-b1 | macko-b2 | macko-b8 for 1-, 2- or 8-bit
            codes instead of 4, macko-i8 and macko-i8-bN for int8 values)
   (varlen: 1M rows of 2..10 entries in a +-1000 band, CV 0.43, the HYB range
@@ -73,14 +74,16 @@ OTHER_PATHS = {"laplacian": ("ell",)}
 # kernel (as rocprofv3 names it) that dominates each path
 KERNEL = {"csr": "k_csr_tasks", "csr-binned": "k_csr_tasks", "csr-vector": "k_csr_vector",
           "csr-scalar": "k_csr_scalar", "ell": "k_ell_apply4t", "macko": "k_macko_spmv",
-          "dense": "k_gemv_f16", "fem": "k_fe_fused", "fem-3stage": "k_fe_elem", "hyb": "k_ell_apply",
+          "dense": "k_gemv_f16", "fem": "k_fe_fused", "fem-3stage": "k_fe_elem", "fem-csr": "k_csr_tasks",
+          "hyb": "k_ell_apply",
           "auto": None, "fem-pcg": "k_fe_matvec64 + k_pcg_pq + k_pcg_update + k_pcg_direction",
           "spgemm": "k_sg_* (grouping, allocation, accumulation)"}
 
 # source file of each path's kernels (for the traffic-record freshness check)
 SOURCE = {"csr": ("csr.hip",), "csr-binned": ("csr.hip",), "csr-vector": ("csr.hip",),
           "csr-scalar": ("csr.hip",), "ell": ("ell.hip",), "macko": ("macko.hip",), "dense": ("dense.hip",),
-          "fem": ("fem.hip", "fem_common.hpp"), "fem-3stage": ("fem.hip",), "hyb": ("ell.hip", "hyb.hip"),
+          "fem": ("fem.hip", "fem_common.hpp"), "fem-3stage": ("fem.hip",), "fem-csr": ("csr.hip",),
+          "hyb": ("ell.hip", "hyb.hip"),
           "auto": ("csr.hip", "ell.hip", "hyb.hip"), "fem-pcg": ("fem_solver.hip", "fem_common.hpp"), "spgemm": ("spgemm.hip",)}
 for _v in ("b1", "b2", "b8", "i8", "i8-b1", "i8-b2", "i8-b8"):
     KERNEL["macko-" + _v] = "k_macko_spmv"
@@ -246,8 +249,27 @@ class Workload:
             self.workload = "fe_hex8_cantilever_120x60x30"
             self.bytes = 96 * M.n_elem + 4 * M.n_elem + 2304 + 8 * M.n_dof
             self.flops = 1176 * M.n_elem
-            if path not in ("fem", "fem-3stage"):
+            if path not in ("fem", "fem-3stage", "fem-csr"):
                 raise SystemExit(f"path {path} does not apply to config {config}")
+            if path == "fem-csr":
+                # the assembled K, built by the library on the GPU once, then the binned CSR apply
+                rp, ci, v = S.fem_assemble_csr(M.n_elem, M.n_dof, dev(M.edof.reshape(-1)), dev(M.rho), M.penalty,
+                                               dev(M.Ke.reshape(-1)))
+                nnz = int(ci.numel())
+                self.bytes = 8 * nnz + 4 * (M.n_dof + 1) + 8 * M.n_dof
+                self.flops = 2 * nnz
+
+                def make_csr(arrs):
+                    rp_, ci_, v_, x = arrs
+                    A = S.CSRMatrix(M.n_dof, M.n_dof, rp_, ci_, v_)
+                    y = torch.zeros(M.n_dof, device="cuda")
+                    return (lambda: A.apply(x, y, self.alpha, self.beta)), y, A
+                self._setup((rp, ci, v, dev(M.x)), make_csr, copies)
+                self.shape = {"n_elem": M.n_elem, "n_dof": M.n_dof, "assembled_nnz": nnz,
+                              "note": "K assembled by fem_assemble_pattern / fem_assemble_values"}
+                torch.cuda.synchronize()
+                log(f"[bench] setup {config}/{path}: {len(self.launches)} copies, {time.time() - t0:.1f}s")
+                return
             ws = None
             if path == "fem-3stage":
                 ws = torch.empty(S.fem_threestage_size(M.n_elem), dtype=torch.uint8, device="cuda")
@@ -800,6 +822,7 @@ SUITE = [
     ("pruned50", "dense", None, "dense fp16 GEMV comparator of the MACKO configs (same W densified)"),
     ("fe", "fem", None, "fused FE matvec: parity config, atomic-bound, no % target"),
     ("fe", "fem-3stage", None, "unfused three-stage comparator of the fused FE matvec"),
+    ("fe", "fem-csr", None, "the assembled K (53.1M nonzeros, built on the GPU) through the binned CSR path"),
 ]
 
 

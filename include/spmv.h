@@ -386,6 +386,29 @@ spmv_status fem_matvec_threestage(int32_t n_elem, int32_t n_dof, const int32_t *
                                   float alpha, const float *x, float beta, float *y,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
+/* The assembled stiffness matrix K = sum_e rho_e^penalty P_e^T Ke P_e in CSR
+ * (section 2.1: the conventional route the fused kernel is measured
+ * against: assemble K once, then run a CSR SpMV on it).  Row and column d
+ * are DOF d; each row lists its distinct columns in increasing order; an
+ * entry is the sum of its element terms rho_e^penalty Ke[a][b], taken in a
+ * fixed order in fp64 and rounded to fp32.  Constrained edof entries (-1 or
+ * outside [0, n_dof)) are dropped.  Two synchronous calls that share a
+ * device workspace (256-byte aligned, >= fem_assemble_size bytes, about
+ * 100 bytes per element; keep it between the calls):
+ * fem_assemble_pattern writes row_ptr (device int32[n_dof + 1]) and *nnz
+ * (host); fem_assemble_values then writes col_idx (device int32[nnz]) and
+ * vals (device fp32[nnz]) for the given rho, penalty and Ke (the layout of
+ * fem_matvec_apply).  A row may collect at most 256 (element, column)
+ * candidates (24 per element reaching the DOF: 10 elements per node),
+ * else SPMV_ERR_UNSUPPORTED; nnz beyond int32 gives SPMV_ERR_OVERFLOW. */
+spmv_status fem_assemble_size(int32_t n_elem, int32_t n_dof, size_t *bytes);
+spmv_status fem_assemble_pattern(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t *row_ptr,
+                                 int64_t *nnz, void *workspace, size_t workspace_bytes, void *stream);
+spmv_status fem_assemble_values(int32_t n_elem, int32_t n_dof, const int32_t *edof, const float *rho,
+                                int32_t penalty, const float *Ke, const int32_t *row_ptr,
+                                int32_t *col_idx, float *vals, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the
  * three-stage comparator with its per-element vectors in a library-owned

@@ -27,6 +27,7 @@ __all__ = [
     "spmv_ell_from_csr", "spmv_ell_apply", "macko_encode_size", "macko_encode", "macko_spmv",
     "macko_quantize_i8", "macko_spmv_i8", "macko_decode_columns", "dense_gemv_f16", "fem_matvec_apply", "fem_threestage_size",
     "fem_matvec_threestage", "fem_matvec_threestage_noalloc", "spmv_stream_copy", "spmv_stream_read",
+    "fem_assemble_size", "fem_assemble_pattern", "fem_assemble_values", "fem_assemble_csr",
     "fem_jacobi_diagonal", "fem_solver_workspace_size", "fem_pcg_solve",
     "fem_lambda_max", "fem_lambda_min", "spgemm_workspace_size", "spgemm_create", "spgemm_info",
     "spgemm_compute", "spgemm_destroy", "SpGEMM", "CSRMatrix", "spmv_hyb_width", "spmv_hyb_tail_size",
@@ -657,3 +658,42 @@ def spmv_stream_read(src, partial, stream=None):
     """Reads src once; one fp32 sum per workgroup into partial (>= 1024 floats)."""
     _call("spmv_stream_read", src.data_ptr(), src.numel() * src.element_size(),
           _dev(partial, _f32_dtype(), "partial"), _stream(stream, partial))
+
+
+# ---------------------------------------------------------------------------
+# Assembled stiffness matrix (CSR) of the FE operator
+# ---------------------------------------------------------------------------
+def fem_assemble_size(n_elem, n_dof) -> int:
+    out = ctypes.c_size_t()
+    _call("fem_assemble_size", int(n_elem), int(n_dof), ctypes.byref(out))
+    return out.value
+
+
+def fem_assemble_pattern(n_elem, n_dof, edof, row_ptr, workspace, stream=None) -> int:
+    """Fills row_ptr (CUDA int32[n_dof + 1]); returns nnz.  Synchronises."""
+    nnz = ctypes.c_int64()
+    _call("fem_assemble_pattern", int(n_elem), int(n_dof), _dev(edof, _i32_dtype(), "edof"),
+          _dev(row_ptr, _i32_dtype(), "row_ptr"), ctypes.byref(nnz), workspace.data_ptr(),
+          workspace.numel() * workspace.element_size(), _stream(stream, row_ptr))
+    return nnz.value
+
+
+def fem_assemble_values(n_elem, n_dof, edof, rho, penalty, Ke, row_ptr, col_idx, vals, workspace, stream=None):
+    _call("fem_assemble_values", int(n_elem), int(n_dof), _dev(edof, _i32_dtype(), "edof"),
+          _dev(rho, _f32_dtype(), "rho"), int(penalty), _dev(Ke, _f32_dtype(), "Ke"),
+          _dev(row_ptr, _i32_dtype(), "row_ptr"), _dev(col_idx, _i32_dtype(), "col_idx"),
+          _dev(vals, _f32_dtype(), "vals"), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+          _stream(stream, row_ptr))
+
+
+def fem_assemble_csr(n_elem, n_dof, edof, rho, penalty, Ke, stream=None):
+    """(row_ptr, col_idx, vals) of the assembled K as new CUDA tensors."""
+    import torch
+    dev = edof.device
+    ws = torch.empty(max(fem_assemble_size(n_elem, n_dof), 256), dtype=torch.uint8, device=dev)
+    rp = torch.empty(int(n_dof) + 1, dtype=torch.int32, device=dev)
+    nnz = fem_assemble_pattern(n_elem, n_dof, edof, rp, ws, stream)
+    ci = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)[:nnz]
+    v = torch.empty(max(nnz, 1), dtype=torch.float32, device=dev)[:nnz]
+    fem_assemble_values(n_elem, n_dof, edof, rho, penalty, Ke, rp, ci, v, ws, stream)
+    return rp, ci, v

@@ -63,6 +63,9 @@ SIGNATURES = {
     "fem_threestage_size": [c_i32, P_sz],
     "fem_matvec_threestage": [c_i32, c_i32, vp, vp, c_i32, vp, c_f32, vp, c_f32, vp, vp, c_sz, vp],
     "fem_matvec_threestage_noalloc": [c_i32, c_i32, vp, vp, c_i32, vp, c_f32, vp, c_f32, vp, vp],
+    "fem_assemble_size": [c_i32, c_i32, P_sz],
+    "fem_assemble_pattern": [c_i32, c_i32, vp, vp, P_i64, vp, c_sz, vp],
+    "fem_assemble_values": [c_i32, c_i32, vp, vp, c_i32, vp, vp, vp, vp, vp, c_sz, vp],
     "spmv_stream_copy": [vp, vp, c_sz, vp],
     "spmv_stream_read": [vp, c_sz, vp, vp],
     "spgemm_workspace_size": [c_i32, c_i32, c_i32, c_i32, vp, vp, c_i32, vp, vp, P_sz, vp, c_sz, vp],
