@@ -814,34 +814,29 @@ __global__ __launch_bounds__(TWG) void k_csr_tasks(TaskArgs a, const i32x4 *__re
     // a wave without a block (XT only) still helps stage the tile: it loads
     // a dummy task (the first entries of the arrays)
     const i32x4 d = have ? tasks[t] : i32x4{0, 0, 0, 0};
-    // start of each row (lane l: rows l + 64 j; entry nr is the block's end),
-    // loaded together with the streams, ahead of the gathers
-    int rs[SHORT_RMAX / 64];
-    const int nr = max(d.y, 0);
-#pragma unroll
-    for (int j = 0; j < SHORT_RMAX / 64; ++j) rs[j] = rg[d.x + min(lane + 64 * j, nr)];
-    stage_streams<VEC>(a, m, d, lane, cur);
-    __builtin_amdgcn_sched_barrier(0);
+    // the window of x (XT) from the X_SEG-float boundary below the
+    // workgroup's smallest column (a workgroup without entries stages
+    // x[0..3]); its loads depend only on the plan, so they are issued
+    // before the row starts and streams: the in-order load counter then
+    // lets the LDS stores and the barrier below complete while the streams
+    // are still in flight.
+    // XTR rounds of 16-byte loads: enough for the widest window of the
+    // matrix; threads past a window's end load and store its last vector
+    // again.  Only segments holding a column of the workgroup's entries are
+    // read (a banded matrix touches a few bands of its window): the other
+    // lanes get a buffer offset past the end of x, which the hardware
+    // answers with zeros and no memory access, so the loads need no branch.
+    // Round u of wave wv covers vectors 64 wv + u TWG .. + 63, i.e. the 8
+    // segments from 8 wv + 32 u TWAVES / 4: one mask word for the wave,
+    // picked without per-lane selects, and one bit per 8 lanes.  Threads
+    // past the window's end re-load its last vector, which holds the
+    // largest column and must be read.
+    static_assert(X_SEG == 32 && TWAVES % 4 == 0, "segment word layout");
+    __builtin_assume(wv >= 0 && wv < TWAVES);
+    const int tb = XT && sp.hi >= 0 ? (sp.lo & ~(X_SEG - 1)) : 0;
+    const int nvec = XT && sp.hi >= 0 ? (sp.hi + 4 - tb) >> 2 : 1;
+    f32x4 tv[XTR > 0 ? XTR : 1];
     if (XT) {
-        // the workgroup's window of x, from the X_SEG-float boundary below
-        // its smallest column (a workgroup without entries stages x[0..3])
-        const int tb = sp.hi >= 0 ? (sp.lo & ~(X_SEG - 1)) : 0;
-        const int nvec = sp.hi >= 0 ? (sp.hi + 4 - tb) >> 2 : 1;
-        // XTR rounds of 16-byte loads: enough for the widest window of the
-        // matrix; threads past a window's end load and store its last
-        // vector again.  Only segments holding a column of the workgroup's
-        // entries are read (a banded matrix touches a few bands of its
-        // window): the other lanes get a buffer offset past the end of x,
-        // which the hardware answers with zeros and no memory access, so
-        // the loads need no branch.
-        // Round u of wave wv covers vectors 64 wv + u TWG .. + 63, i.e. the
-        // 8 segments from 8 wv + 32 u TWAVES / 4: one mask word for the
-        // wave, picked without per-lane selects, and one bit per 8 lanes.
-        // Threads past the window's end re-load its last vector, which holds
-        // the largest column and must be read.
-        static_assert(X_SEG == 32 && TWAVES % 4 == 0, "segment word layout");
-        __builtin_assume(wv >= 0 && wv < TWAVES);
-        f32x4 tv[XTR > 0 ? XTR : 1];
 #pragma unroll
         for (int u = 0; u < XTR; ++u) {
             const int iu = (int)threadIdx.x + u * TWG;
@@ -851,6 +846,16 @@ __global__ __launch_bounds__(TWG) void k_csr_tasks(TaskArgs a, const i32x4 *__re
             const int off = need ? (int)(4u * (unsigned)(tb + 4 * i)) : X_OOB;
             tv[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xg.r, off, 0, 0));
         }
+    }
+    // start of each row (lane l: rows l + 64 j; entry nr is the block's end),
+    // loaded together with the streams, ahead of the gathers
+    int rs[SHORT_RMAX / 64];
+    const int nr = max(d.y, 0);
+#pragma unroll
+    for (int j = 0; j < SHORT_RMAX / 64; ++j) rs[j] = rg[d.x + min(lane + 64 * j, nr)];
+    stage_streams<VEC>(a, m, d, lane, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    if (XT) {
 #pragma unroll
         for (int u = 0; u < XTR; ++u)
             *reinterpret_cast<f32x4 *>(xtile + 4 * min((int)threadIdx.x + u * TWG, nvec - 1)) = tv[u];
