@@ -9,7 +9,8 @@ Under "configs" the line then carries, with the same step count, its own
 parity check and a short oracle timing: the Laplacian's ELL path, the tiny
 CSR, the power-law CSR, the pruned 12288 x 12288 weights at 50 / 70 / 90 %
 sparsity (MACKO) and the dense fp16 GEMV comparator, and the FE matvec
-(fused and three-stage).
+(fused, three-stage, and the assembled stiffness matrix through the binned
+CSR path).
 
 Cold-cache protocol ("rotate", the default): the inputs are replicated R
 times in HBM so that R copies span >= 1 GiB (4x the 256 MB Infinity Cache

@@ -543,9 +543,12 @@ spmv_status spgemm_destroy(spgemm_t h);
 spmv_status spmv_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 /* Reads src[0 .. bytes) once with 16-byte non-temporal loads and writes one
- * fp32 sum per workgroup to partial (device, at least 4 * CUs floats: 1024
- * on MI355X).  Same size and alignment rules.  Asynchronous. */
-spmv_status spmv_stream_read(const void *src, size_t bytes, float *partial, void *stream);
+ * fp32 sum per workgroup to partial (device, partial_count floats).  The
+ * kernel runs min(ceil(bytes / 4096), 8 * CUs) workgroups (at most 2048 on
+ * MI355X); a partial_count below that is rejected (SPMV_ERR_INVALID_VALUE)
+ * before anything is launched, and entries past it are not written.  Same
+ * size and alignment rules as the copy.  Asynchronous. */
+spmv_status spmv_stream_read(const void *src, size_t bytes, float *partial, size_t partial_count, void *stream);
 
 #ifdef __cplusplus
 }

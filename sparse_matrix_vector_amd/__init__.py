@@ -655,9 +655,9 @@ def spmv_stream_copy(src, dst, stream=None):
 
 
 def spmv_stream_read(src, partial, stream=None):
-    """Reads src once; one fp32 sum per workgroup into partial (>= 1024 floats)."""
+    """Reads src once; one fp32 sum per workgroup into partial (2048 floats always suffice)."""
     _call("spmv_stream_read", src.data_ptr(), src.numel() * src.element_size(),
-          _dev(partial, _f32_dtype(), "partial"), _stream(stream, partial))
+          _dev(partial, _f32_dtype(), "partial"), partial.numel(), _stream(stream, partial))
 
 
 # ---------------------------------------------------------------------------

@@ -67,7 +67,7 @@ SIGNATURES = {
     "fem_assemble_pattern": [c_i32, c_i32, vp, vp, P_i64, vp, c_sz, vp],
     "fem_assemble_values": [c_i32, c_i32, vp, vp, c_i32, vp, vp, vp, vp, vp, c_sz, vp],
     "spmv_stream_copy": [vp, vp, c_sz, vp],
-    "spmv_stream_read": [vp, c_sz, vp, vp],
+    "spmv_stream_read": [vp, c_sz, vp, c_sz, vp],
     "spgemm_workspace_size": [c_i32, c_i32, c_i32, c_i32, vp, vp, c_i32, vp, vp, P_sz, vp, c_sz, vp],
     "spgemm_create": [P_vp, c_i32, c_i32, c_i32, c_i32, vp, vp, vp, c_i32, vp, vp, vp, vp, c_sz, vp],
     "spgemm_info": [vp, P_i64, P_i64, P_i32],

@@ -1,6 +1,6 @@
 """GPU check of the reference streaming kernels (the bench's measured
 bandwidth denominator), through the C ABI: the copy is byte-exact, including
-a size that is not a multiple of the unrolled grid step, and the read pass's
+a size that is not a multiple of the grid step, and the read pass's
 per-workgroup sums add up to the fp64 sum of the input within fp32
 rounding; bad sizes and alignment are rejected on the host."""
 import ctypes
@@ -36,5 +36,6 @@ def test_rejects_bad_arguments():
     L = S.lib()
     assert L.spmv_stream_copy(4096, 8192, 20, None) == 1          # not a multiple of 16
     assert L.spmv_stream_copy(4100, 8192, 32, None) == 1          # misaligned source
-    assert L.spmv_stream_read(4096, 32, None, None) == 1          # no partial buffer
+    assert L.spmv_stream_read(4096, 32, None, 4096, None) == 1    # no partial buffer
+    assert L.spmv_stream_read(4096, 1 << 20, 8192, 16, None) == 1  # fewer partials than workgroups
     assert L.spmv_stream_copy(None, None, 0, None) == 0           # nothing to do
