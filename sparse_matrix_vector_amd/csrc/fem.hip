@@ -21,11 +21,12 @@
 // 24 DOF indices are read with six 16-byte loads, 24 gathers of x,
 // 576 FMAs, then the wave's contributions are merged along x-lines of
 // nodes in LDS (the face shared with the next lane's element is summed
-// there) and go out as fp32 atomic adds (hardware global_atomic_add_f32)
-// with consecutive lanes on consecutive DOFs: 12 instead of 24 adds per
-// element when elements are numbered x-fastest, ~16 lanes per memory-side
-// request.  The beta pass runs first as a separate small kernel, because
-// atomics only add.
+// there, all four node lines in one pass) and go out as fp32 atomic adds
+// (hardware buffer atomics, issued unconditionally with out-of-range
+// offsets where there is nothing to add) with consecutive lanes on
+// consecutive DOFs: 12 instead of 24 adds per element when elements are
+// numbered x-fastest, ~16 lanes per memory-side request.  The beta pass
+// runs first as a separate small kernel, because atomics only add.
 #include "common.hpp"
 #include "fem_common.hpp"
 
@@ -82,12 +83,23 @@ __device__ __forceinline__ void load_edof(const int *__restrict__ edof, int e, i
     }
 }
 
+// Buffer resources for x and y (byte offsets below 2 GiB): an offset of
+// FE_OOB is out of range, so a load there returns 0 and an atomic there is
+// dropped, with no memory access and no branch.
+constexpr int FE_BUF_DWORD3 = 0x00020000;   // gfx9-family buffer resource word 3 (raw 32-bit data)
+constexpr int FE_OOB = 0x7FFFFFF0;
+
+// BUF: x and y are addressed through buffer resources (4 * n_dof <= FE_OOB),
+// so every gather and every atomic add is issued unconditionally, with an
+// out-of-range offset where a DOF is constrained or has nothing to add;
+// otherwise through pointers with the same results.
+template <bool BUF>
 __global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const int *__restrict__ edof,
                                                     const float *__restrict__ rho, int penalty,
                                                     const float *__restrict__ Ke, float alpha,
                                                     const float *__restrict__ x, float *__restrict__ y) {
-    __shared__ int line_dof[FE_WG / 64][3 * 65];
-    __shared__ float line_val[FE_WG / 64][3 * 65];
+    __shared__ int line_dof[FE_WG / 64][4 * 3 * 65];
+    __shared__ float line_val[FE_WG / 64][4 * 3 * 65];
     // lanes past the last element stay (the wave exchange below needs all
     // 64) with every DOF index -1
     const int e = blockIdx.x * FE_WG + threadIdx.x;
@@ -97,13 +109,22 @@ __global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const
     load_edof(edof, ec, d);
 #pragma unroll
     for (int b = 0; b < NDOF_E; ++b) d[b] = live ? d[b] : -1;
-    // 24 gathers issued together (a constrained DOF reads x[0] and is zeroed
-    // after), rather than one masked load at a time
+    // 24 gathers issued together; a constrained DOF contributes 0
     float u[NDOF_E];
+    __amdgpu_buffer_rsrc_t xr, yr;
+    if (BUF) {
+        xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(x), 0, 4 * n_dof, FE_BUF_DWORD3);
+        yr = __builtin_amdgcn_make_buffer_rsrc(y, 0, 4 * n_dof, FE_BUF_DWORD3);
 #pragma unroll
-    for (int b = 0; b < NDOF_E; ++b) u[b] = x[(unsigned)d[b] < (unsigned)n_dof ? d[b] : 0];
+        for (int b = 0; b < NDOF_E; ++b)
+            u[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 xr, (unsigned)d[b] < (unsigned)n_dof ? 4 * d[b] : FE_OOB, 0, 0));
+    } else {
 #pragma unroll
-    for (int b = 0; b < NDOF_E; ++b) u[b] = (unsigned)d[b] < (unsigned)n_dof ? u[b] : 0.0f;
+        for (int b = 0; b < NDOF_E; ++b) u[b] = x[(unsigned)d[b] < (unsigned)n_dof ? d[b] : 0];
+#pragma unroll
+        for (int b = 0; b < NDOF_E; ++b) u[b] = (unsigned)d[b] < (unsigned)n_dof ? u[b] : 0.0f;
+    }
     const float s = alpha * simp(rho[ec], penalty);
     float fa[NDOF_E];
 #pragma unroll
@@ -113,8 +134,26 @@ __global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const
         for (int b = 0; b < NDOF_E; ++b) f = fmaf(Ke[a * NDOF_E + b], u[b], f);
         fa[a] = s * f;
     }
-    fe_scatter_lines(d, fa, n_dof, [y](int i, float v) { atomicAdd(y + i, v); }, line_dof[threadIdx.x >> 6],
-                     line_val[threadIdx.x >> 6]);
+    // all 24 products are finished here: left to itself the compiler sinks
+    // them into the scatter, where Ke no longer fits the scalar registers and
+    // is spilled to vector-register lanes and reloaded around every add
+#pragma unroll
+    for (int a = 0; a < NDOF_E; ++a) asm volatile("" : "+v"(fa[a]));
+    const int w = threadIdx.x >> 6;
+    if (BUF)
+        fe_scatter_lines4(
+            d, fa, n_dof,
+            [yr](int i, bool on, float v) {
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, yr, on ? 4 * i : FE_OOB, 0, 0);
+            },
+            line_dof[w], line_val[w]);
+    else
+        fe_scatter_lines4(
+            d, fa, n_dof,
+            [y](int i, bool on, float v) {
+                if (on) atomicAdd(y + i, v);
+            },
+            line_dof[w], line_val[w]);
 }
 
 // ---- three-stage comparator ----
@@ -237,7 +276,11 @@ extern "C" spmv_status fem_matvec_apply(int32_t n_elem, int32_t n_dof, const int
         SPMV_LAUNCHED("k_fe_beta");
     }
     if (n_elem == 0) return SPMV_OK;
-    k_fe_fused<<<(int)ceil_div(n_elem, FE_WG), FE_WG, 0, st>>>(n_elem, n_dof, edof, rho, penalty, Ke, alpha, x, y);
+    const int grid = (int)ceil_div(n_elem, FE_WG);
+    if (4 * (int64_t)n_dof <= FE_OOB)
+        k_fe_fused<true><<<grid, FE_WG, 0, st>>>(n_elem, n_dof, edof, rho, penalty, Ke, alpha, x, y);
+    else
+        k_fe_fused<false><<<grid, FE_WG, 0, st>>>(n_elem, n_dof, edof, rho, penalty, Ke, alpha, x, y);
     SPMV_LAUNCHED("k_fe_fused");
     return SPMV_OK;
 }

@@ -70,4 +70,73 @@ __device__ __forceinline__ void fe_scatter_lines(const int (&d)[24], const T (&f
     }
 }
 
+// The same merge for all four node lines at once, for kernels whose adds
+// are issued unconditionally: lane l writes its first nodes of the four
+// pairs into slot l of the four lines (sd/sv: 4 x 195 entries for this
+// wave), one wave sync, every lane reads slot l + 1 of the four lines and
+// merges its second nodes there (or, where the DOFs differ, adds them to y
+// itself), one wave sync, and the 780 entries go out with lane i taking
+// entries i, 64 + i, ...  `add(dof, on, value)` is called the same number
+// of times in every lane (on = false for an entry with nothing to add), so
+// the caller can issue it as one memory instruction per call with no
+// branch around it.  A final wave sync lets the caller reuse sd/sv.
+template <typename Add>
+__device__ __forceinline__ void fe_scatter_lines4(const int (&d)[24], const float (&f)[24], int n_dof, Add add,
+                                                  int *sd, float *sv) {
+    constexpr int P0[4] = {0, 3, 4, 7}, P1[4] = {1, 2, 5, 6};
+    constexpr int LS = 3 * 65;                 // entries per line
+    constexpr int R = (4 * LS + 63) / 64;      // entries per lane in the final pass
+    const int lane = __lane_id();
+    auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            sd[k * LS + 3 * lane + c] = d[3 * P0[k] + c];
+            sv[k * LS + 3 * lane + c] = f[3 * P0[k] + c];
+        }
+    if (lane == 63)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int c = 0; c < 3; ++c) sd[k * LS + 3 * 64 + c] = -1;
+    wave_sync();
+    int nd[12];
+    float nv[12];
+#pragma unroll
+    for (int q = 0; q < 12; ++q) {
+        nd[q] = sd[(q / 3) * LS + 3 * (lane + 1) + q % 3];
+        nv[q] = sv[(q / 3) * LS + 3 * (lane + 1) + q % 3];
+    }
+#pragma unroll
+    for (int q = 0; q < 12; ++q) {
+        const int k = q / 3, c = q % 3;
+        const int j = k * LS + 3 * (lane + 1) + c;
+        const int da = d[3 * P1[k] + c];
+        const float fv = f[3 * P1[k] + c];
+        const bool valid = (unsigned)da < (unsigned)n_dof;
+        const bool same = valid && nd[q] == da;
+        const bool open = valid && !same && lane == 63;   // slot 64: past the wave's last element
+        if (same || open) sv[j] = same ? nv[q] + fv : fv;
+        if (open) sd[j] = da;
+        add(da, valid && !same && lane != 63, fv);
+    }
+    wave_sync();
+    int od[R];
+    float ov[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = 64 * r + lane;
+        od[r] = i < 4 * LS ? sd[i] : -1;
+        ov[r] = i < 4 * LS ? sv[i] : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) add(od[r], (unsigned)od[r] < (unsigned)n_dof, ov[r]);
+    wave_sync();
+}
+
 }  // namespace spmv
