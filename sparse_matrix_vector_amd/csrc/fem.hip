@@ -141,14 +141,14 @@ __global__ __launch_bounds__(FE_WG) void k_fe_fused(int n_elem, int n_dof, const
     for (int a = 0; a < NDOF_E; ++a) asm volatile("" : "+v"(fa[a]));
     const int w = threadIdx.x >> 6;
     if (BUF)
-        fe_scatter_lines4(
+        fe_scatter_lines(
             d, fa, n_dof,
             [yr](int i, bool on, float v) {
                 __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, yr, on ? 4 * i : FE_OOB, 0, 0);
             },
             line_dof[w], line_val[w]);
     else
-        fe_scatter_lines4(
+        fe_scatter_lines(
             d, fa, n_dof,
             [y](int i, bool on, float v) {
                 if (on) atomicAdd(y + i, v);

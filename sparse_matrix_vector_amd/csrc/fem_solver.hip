@@ -303,8 +303,8 @@ __global__ __launch_bounds__(SV_WG) void k_fe_matvec64(int n_elem, int n_dof, co
                                                        int nb, SolverState *st, int check_done) {
     typedef int i32x4 __attribute__((ext_vector_type(4)));
     if (check_done && st->done) return;   // uniform
-    __shared__ int line_dof[SV_WG / 64][3 * 65];
-    __shared__ double line_val[SV_WG / 64][3 * 65];
+    __shared__ int line_dof[SV_WG / 64][4 * 3 * 65];
+    __shared__ double line_val[SV_WG / 64][4 * 3 * 65];
     double xm = 0.0;
     for (int b = threadIdx.x; b < nb; b += SV_WG) xm = fmax(xm, xmax_slot(partials)[b]);
     const int kx = fix_exponent(st->op_bound, block_max(xm));
@@ -341,10 +341,16 @@ __global__ __launch_bounds__(SV_WG) void k_fe_matvec64(int n_elem, int n_dof, co
         for (int b = 0; b < NDOF_E; ++b) f = fma((double)Ke[a * NDOF_E + b], (double)u[b], f);
         fa[a] = s * f;
     }
+    // products finished before the scatter (else the compiler sinks them
+    // into it and spills Ke from the scalar registers to vector lanes)
+#pragma unroll
+    for (int a = 0; a < NDOF_E; ++a) asm volatile("" : "+v"(fa[a]));
     fe_scatter_lines(
         d, fa, n_dof,
-        [acc, unit](int i, double v) {
-            atomicAdd(reinterpret_cast<unsigned long long *>(acc + i), (unsigned long long)__double2ll_rn(v * unit));
+        [acc, unit](int i, bool on, double v) {
+            if (on)
+                atomicAdd(reinterpret_cast<unsigned long long *>(acc + i),
+                          (unsigned long long)__double2ll_rn(v * unit));
         },
         line_dof[threadIdx.x >> 6], line_val[threadIdx.x >> 6]);
 }
