@@ -11,7 +11,11 @@ oracle's element loop, through the C ABI.
   CSR form, under the element-wise scale (the required bound) and under the
   assembled scale sum_j |K_ij x_j|;
 * run to run the atomic order may change the last bits only: two runs agree
-  within the same tolerance.
+  within the same tolerance;
+* other numberings of the same mesh (elements shuffled, elements numbered
+  y-fastest, DOFs relabelled at random): the node-line merge then finds few
+  or no matching neighbours and falls back to direct adds DOF by DOF, with
+  the same bound against the oracle on the renumbered input.
 """
 import numpy as np
 import pytest
@@ -110,3 +114,42 @@ def test_no_elements_scales_y():
     S.fem_matvec_apply(0, 2, torch.zeros(0, dtype=torch.int32, device="cuda"), torch.zeros(0, device="cuda"),
                        3, torch.zeros(576, device="cuda"), 1.0, torch.zeros(2, device="cuda"), 3.0, y)
     assert host(y).tolist() == [3.0, 6.0]
+
+
+def _renumbered(M, how, seed=21):
+    """The same mesh and operator under another numbering (inputs only):
+    returns (edof, rho, x, n_dof) and the map from the renumbered y back to
+    the original DOF order."""
+    rng = np.random.default_rng(seed)
+    edof, rho, x = M.edof, M.rho, M.x
+    if how == "elements_shuffled":
+        p = rng.permutation(M.n_elem)
+        return edof[p], rho[p], x, None
+    if how == "elements_y_fastest":
+        e = np.arange(M.n_elem).reshape(M.nz, M.ny, M.nx)        # e = ix + nx (iy + ny iz)
+        p = e.transpose(0, 2, 1).reshape(-1)                     # iy fastest, then ix, then iz
+        return edof[p], rho[p], x, None
+    q = rng.permutation(M.n_dof)                                 # DOF d -> q[d]
+    ed = np.where(edof >= 0, q[np.maximum(edof, 0)], -1).astype(np.int32)
+    xq = np.empty_like(x)
+    xq[q] = x
+    return ed, rho, xq, q
+
+
+@pytest.mark.parametrize("kind", ["fused", "threestage"])
+@pytest.mark.parametrize("how", ["elements_shuffled", "elements_y_fastest", "dofs_relabelled"])
+@pytest.mark.parametrize("dims", [(13, 7, 5), (40, 20, 10)])
+def test_other_numberings(kind, how, dims):
+    M = _mesh(dims, clamp=True)
+    ed, rho, x, q = _renumbered(M, how)
+    print(f"[fem] {dims} {how} {kind}", flush=True)
+    R = type(M)(M.nx, M.ny, M.nz, M.n_elem, M.n_dof, np.ascontiguousarray(ed), np.ascontiguousarray(rho),
+                M.Ke, np.ascontiguousarray(x), M.penalty)
+    y_in = np.random.default_rng(5).uniform(-1, 1, M.n_dof).astype(np.float32)
+    y = _apply(R, kind, 0.5, -2.0, y_in)
+    yr, sc = oracle.fe_matvec(R.edof, R.rho, R.Ke, R.x, R.n_dof, R.penalty, 0.5, -2.0, y_in)
+    assert_close(y, yr, sc, TAU_F32, f"fem {dims} {how} {kind}")
+    if q is not None:
+        # the relabelled product is the original one, permuted
+        y0, sc0 = oracle.fe_matvec(M.edof, M.rho, M.Ke, M.x, M.n_dof, M.penalty, 0.5, -2.0, y_in[q])
+        assert_close(y[q], y0, sc0, TAU_F32, f"fem {dims} relabelled vs original")

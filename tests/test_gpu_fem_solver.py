@@ -13,7 +13,8 @@ inverse iteration) against the oracle, through the C ABI.
   oracle's, and within 5% at 64k and 216k elements; the cap, a converged
   initial guess, f = 0, a non-positive diagonal; two solves of one system
   agree bit for bit (the matvec adds fixed-point integers, whose sum does
-  not depend on the order of the atomic adds);
+  not depend on the order of the atomic adds); the same with the elements
+  shuffled (the node-line merge then falls back to direct adds);
 * largest / smallest eigenvalue of small cantilevers against LAPACK, and the
   power-iteration sequence against the fp64 oracle's from the same start.
 """
@@ -83,6 +84,26 @@ def test_pcg_cantilever(dims):
     assert true_res <= 10 * (rtol + floor)
     assert abs(c - cex) <= 1e-4 * abs(cex)
     assert abs(it - itr) <= max(2, 0.02 * itr)
+
+
+def test_pcg_shuffled_elements():
+    """The 24 x 12 x 6 cantilever with its elements in random order: the
+    same operator, so the same iteration count as the fp64 oracle within 2%
+    and the same compliance within 1e-4."""
+    m = gen.fe_cantilever(24, 12, 6)
+    p = np.random.default_rng(17).permutation(m.n_elem)
+    m.edof, m.rho = np.ascontiguousarray(m.edof[p]), np.ascontiguousarray(m.rho[p])
+    Kx = _Kmv(m)
+    d = oracle.fe_diagonal(m.edof, m.rho, m.Ke, m.n_dof, m.penalty)
+    f64 = m.f.astype(np.float64)
+    u, it, rr = _solve(m, 1e-6)
+    ur, itr, _ = oracle.pcg_jacobi(Kx, d, f64, rtol=1e-6, max_iter=20000)
+    print(f"[pcg] shuffled it={it} (fp64 {itr})", flush=True)
+    assert rr <= 1e-6
+    assert abs(it - itr) <= max(2, 0.02 * itr)
+    assert abs(f64 @ u - f64 @ ur) <= 1e-4 * abs(f64 @ ur)
+    a, ita, ra = _solve(m, 1e-6)
+    assert ita == it and ra == rr and np.array_equal(a.view(np.uint32), u.view(np.uint32))
 
 
 def test_pcg_cap_initial_guess_zero_rhs_and_reproducible():
