@@ -628,7 +628,8 @@ struct GatherI {
 
 // Block of short rows r0 .. r0 + nr - 1 (nr = d.y > 1), given its streams,
 // row starts and gathered x: products are staged in the wave's LDS area and
-// lane l sums rows l + 64 j in storage order.  Entries of the staged vectors
+// lane l sums rows l + 64 j in storage order (or, for at most 32 rows, a
+// group of lanes sums each row).  Entries of the staged vectors
 // outside the block (neighbouring rows, re-read vectors) are multiplied too
 // but never read back.
 __device__ __forceinline__ void finish_block(const TaskArgs &a, i32x4 d, const Staged &cur,
@@ -647,6 +648,32 @@ __device__ __forceinline__ void finish_block(const TaskArgs &a, i32x4 d, const S
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (nr <= 32) {   // uniform
+        // Few, longer rows (e.g. ~80 entries of an assembled stiffness row):
+        // G = 64 / 2^ceil(log2 nr) lanes per row, lane j of a row's group
+        // summing entries j, j + G, ... four at a time, then a butterfly
+        // within the group (fixed order, so results stay reproducible).
+        // One lane per row would leave most of the wave idle through a
+        // long serial sum.
+        const int G = 64 >> (32 - __builtin_clz((unsigned)(nr - 1)));
+        const int i_row = lane / G, sub = lane % G;
+        const int start = __shfl(rs[0], i_row < nr ? i_row : 0) - base;
+        const int nxt = __shfl(rs[0], i_row + 1 < nr ? i_row + 1 : 0);
+        const int end = (i_row + 1 < nr ? nxt : d.w) - base;
+        float acc = 0.0f;
+        if (i_row < nr) {
+            for (int k = start + sub; k < end; k += 4 * G) {
+                float vv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) vv[u] = st[min(k + u * G, end - 1)];   // stays inside the row
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc += k + u * G < end ? vv[u] : 0.0f;
+            }
+        }
+        for (int off = G >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+        if (i_row < nr && sub == 0) store_y(y, ymap, d.x + i_row, acc, a.alpha, a.beta);
+        return;
+    }
     // Lane l sums row l + 64 j, reading 8 staged entries per step so their
     // LDS latencies overlap.  Row i's end is row i+1's start: from lane l + 1,
     // or for lane 63 from lane 0 of the next j, or the block's end entry.

@@ -122,6 +122,31 @@ def test_short_rows_near_the_bound(lo, hi):
     assert off[1] == A.n_rows                     # every row is short under the default bounds
 
 
+@pytest.mark.parametrize("lens_kind", ["fe_like", "mixed", "two_rows"])
+def test_blocks_of_few_rows(lens_kind):
+    """Short-row blocks of at most 32 rows, summed by a group of lanes per
+    row (groups of 2 to 32 lanes): rows of ~78 entries as in an assembled
+    stiffness matrix, a mix of lengths 0..127 where blocks hold 2..30 rows,
+    and blocks of exactly two long short rows; alpha, beta, bit-reproducible."""
+    rng = np.random.default_rng(41)
+    if lens_kind == "fe_like":
+        lens = rng.integers(72, 82, 20_000)
+    elif lens_kind == "mixed":
+        lens = rng.choice([0, 1, 5, 17, 33, 64, 100, 127], 20_000)
+    else:
+        lens = np.full(4000, 126)
+        lens[1::2] = 127
+    A = gen.random_csr(len(lens), 30_000, lens, seed=42)
+    y0 = rng.uniform(-1, 1, A.n_rows).astype(np.float32)
+    print(f"[few rows] {lens_kind} n={A.n_rows} nnz={A.nnz}", flush=True)
+    for alpha, beta in [(1.0, 0.0), (-0.5, 2.0)]:
+        M, y = _run(A, S.CSR_BINNED, alpha=alpha, beta=beta, y_in=y0 if beta else None)
+        yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x, alpha, beta, y0 if beta else None)
+        assert_close(y, yr, sc, TAU_F32, f"few rows {lens_kind} {alpha} {beta}")
+    M2, y2 = _run(A, S.CSR_BINNED, alpha=-0.5, beta=2.0, y_in=y0)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
 def test_workgroup_rows_and_chunked_rows():
     """Rows of 2-16 chunks (one workgroup each, no second kernel) next to
     rows of 1 chunk and of more than 16 chunks (chunk partials), from
