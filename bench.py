@@ -816,6 +816,9 @@ HEADLINE = ("laplacian", "csr", 60.0, None)
 SUITE = [
     ("laplacian", "ell", 60.0, "the Laplacian config's ELL path (width 5)"),
     ("tiny", "csr", None, "parity config: 311 KB, launch-bound, no % target"),
+    ("tiny", "csr-scalar", None, "the pages' scalar CSR kernel on the parity config"),
+    ("tiny", "csr-vector", None, "the pages' vector (lanes per row) CSR kernel on the parity config"),
+    ("tiny", "ell", None, "ELL (W = 8) on the parity config"),
     ("powerlaw", "csr", 35.0, None),
     ("pruned50", "macko", 60.0, None),
     ("pruned70", "macko", 60.0, None),
@@ -959,10 +962,17 @@ def main():
         configs = {f"{config}/{path}": {k: v for k, v in head.items()
                                         if k not in ("warm_timing_ms", "single_launch_us", "cpu_baseline")}}
         for c, p, tgt, note in SUITE:
-            rec, _ = measure(c, p, args, target=tgt, note=note,
+            rec, _ = measure(c, p, args, target=tgt, note=note, detail=True,
                              cpu_seconds=min(args.cpu_seconds, 1.5), par_seconds=min(args.cpu_seconds, 1.0))
             configs[f"{c}/{p}"] = rec
         line["configs"] = configs
+        # the MACKO speed-up over the dense fp16 GEMV of the same 12288 x 12288
+        # shape (one dense time serves every sparsity: the dense matrix is the same size)
+        dense = configs.get("pruned50/dense")
+        if dense:
+            line["macko_speedup_vs_dense"] = {
+                c: round(dense["us_per_apply"] / configs[f"{c}/macko"]["us_per_apply"], 3)
+                for c in ("pruned50", "pruned70", "pruned90") if f"{c}/macko" in configs}
         met = [r["target_met"] for r in configs.values() if r["target_met"] is not None]
         line["targets_met"] = f"{sum(met)} of {len(met)}"
         line["parity_all_ok"] = all((r["parity"] or {}).get("ok", False) for r in configs.values())
