@@ -58,9 +58,37 @@ __device__ __forceinline__ float simp(float r, int p) {
     return s;
 }
 
-__global__ void k_fe_beta(int n, float beta, float *__restrict__ y) {
+// y = beta * y, and y = 0 without reading y when beta = 0.  With y 16-byte
+// aligned: 16-byte accesses over a grid-stride loop of 8 workgroups per CU
+// (the streaming kernels' shape; as fast as a device fill at 2.7 MB and
+// 1.5x faster than one float per thread at 43 MB), the last n % 4 entries
+// by block 0; otherwise one float per thread.
+__global__ __launch_bounds__(256) void k_fe_beta(int n, float beta, float *__restrict__ y) {
+    const int n4 = n >> 2;
+    f32x4 *y4 = reinterpret_cast<f32x4 *>(y);
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n4; i += gridDim.x * 256) {
+        f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (beta != 0.0f) v = beta * y4[i];
+        y4[i] = v;
+    }
+    if (blockIdx.x == 0 && (int)threadIdx.x < (n & 3)) {
+        const int i = 4 * n4 + threadIdx.x;
+        y[i] = beta != 0.0f ? beta * y[i] : 0.0f;
+    }
+}
+
+__global__ void k_fe_beta1(int n, float beta, float *__restrict__ y) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) y[i] = beta != 0.0f ? beta * y[i] : 0.0f;
+}
+
+void beta_launch(int n, float beta, float *y, hipStream_t st) {
+    if (aligned16(y)) {
+        const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(n, 1024), 8 * (int64_t)device_cu_count()));
+        k_fe_beta<<<grid, 256, 0, st>>>(n, beta, y);
+    } else {
+        k_fe_beta1<<<(int)ceil_div(n, 256), 256, 0, st>>>(n, beta, y);
+    }
 }
 
 // Ke (576 floats, 16-byte aligned) into LDS: 144 16-byte vectors, all loads
@@ -272,7 +300,7 @@ extern "C" spmv_status fem_matvec_apply(int32_t n_elem, int32_t n_dof, const int
     if (n_dof == 0) return SPMV_OK;
     hipStream_t st = as_stream(stream);
     if (beta != 1.0f) {
-        k_fe_beta<<<(int)ceil_div(n_dof, 256), 256, 0, st>>>(n_dof, beta, y);
+        beta_launch(n_dof, beta, y, st);
         SPMV_LAUNCHED("k_fe_beta");
     }
     if (n_elem == 0) return SPMV_OK;
@@ -305,7 +333,7 @@ extern "C" spmv_status fem_matvec_threestage(int32_t n_elem, int32_t n_dof, cons
     if (n_dof == 0) return SPMV_OK;
     hipStream_t st = as_stream(stream);
     if (beta != 1.0f) {
-        k_fe_beta<<<(int)ceil_div(n_dof, 256), 256, 0, st>>>(n_dof, beta, y);
+        beta_launch(n_dof, beta, y, st);
         SPMV_LAUNCHED("k_fe_beta");
     }
     if (n_elem == 0) return SPMV_OK;
@@ -326,7 +354,7 @@ extern "C" spmv_status fem_matvec_threestage_noalloc(int32_t n_elem, int32_t n_d
     float *F = U + (size_t)FE_NOALLOC_CHUNK * NDOF_E;
     hipStream_t st = as_stream(stream);
     if (beta != 1.0f) {
-        k_fe_beta<<<(int)ceil_div(n_dof, 256), 256, 0, st>>>(n_dof, beta, y);
+        beta_launch(n_dof, beta, y, st);
         SPMV_LAUNCHED("k_fe_beta");
     }
     // chunks of elements one after another on the stream: a chunk's gather

@@ -116,6 +116,31 @@ def test_no_elements_scales_y():
     assert host(y).tolist() == [3.0, 6.0]
 
 
+@pytest.mark.parametrize("kind", ["fused", "threestage"])
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1_000_003])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_beta_pass_sizes_and_alignment(kind, n, offset):
+    """The beta pass alone (no elements) over y of every length mod 4, 16-byte
+    aligned (vector pass plus tail) and not (one float per thread); beta = 0
+    must not read y (NaN in, 0 out)."""
+    buf = torch.empty(n + 1, device="cuda")
+    y = buf[offset:offset + n]
+    y0 = np.random.default_rng(n).uniform(-1, 1, n).astype(np.float32)
+    no_e = (torch.zeros(0, dtype=torch.int32, device="cuda"), torch.zeros(0, device="cuda"), 3,
+            torch.zeros(576, device="cuda"))
+    x = torch.zeros(n, device="cuda")
+    for beta in (-1.5, 0.0):
+        y.copy_(dev(y0) if beta else torch.full((n,), float("nan"), device="cuda"))
+        if kind == "fused":
+            S.fem_matvec_apply(0, n, *no_e, 1.0, x, beta, y)
+        else:
+            ws = torch.empty(max(S.fem_threestage_size(0), 1), dtype=torch.uint8, device="cuda")
+            S.fem_matvec_threestage(0, n, *no_e, 1.0, x, beta, y, ws)
+        torch.cuda.synchronize()
+        want = (np.float32(beta) * y0).astype(np.float32) if beta else np.zeros(n, np.float32)
+        assert np.array_equal(host(y), want), (kind, n, offset, beta)
+
+
 def _renumbered(M, how, seed=21):
     """The same mesh and operator under another numbering (inputs only):
     returns (edof, rho, x, n_dof) and the map from the renumbered y back to
