@@ -10,7 +10,9 @@ parity check and a short oracle timing: the Laplacian's ELL path, the tiny
 CSR, the power-law CSR, the pruned 12288 x 12288 weights at 50 / 70 / 90 %
 sparsity (MACKO) and the dense fp16 GEMV comparator, and the FE matvec
 (fused, three-stage, and the assembled stiffness matrix through the binned
-CSR path).
+CSR path).  Under "next_rows": the moderate-CV matrix through the CV-driven
+choice (HYB), Jacobi-PCG on the elasticity cantilever, and the hash SpGEMM
+C = A * A of the power-law matrix (at most 20 whole products).
 
 Cold-cache protocol ("rotate", the default): the inputs are replicated R
 times in HBM so that R copies span >= 1 GiB (4x the 256 MB Infinity Cache
@@ -615,8 +617,9 @@ def pmc_calibration_copies(nbytes=256 << 20, reps=3):
     log(f"[bench] calibration copies: {reps} x {nbytes} bytes read and written")
 
 
-def bench_pcg(args):
-    """One JSON line for Jacobi-PCG on the cantilever (see the module docstring)."""
+def bench_pcg(args, emit=True):
+    """One JSON line for Jacobi-PCG on the cantilever (see the module docstring);
+    returns it (and prints it when `emit`)."""
     import numpy as np
     import torch
     import gen
@@ -698,11 +701,14 @@ def bench_pcg(args):
         line["cpu_baseline"] = {"value": round(flops * k / el / 1e9, 3), "unit": "GFLOP/s", "cores": 1,
                                 "kind": "oracle", "ms_per_step": round(1e3 * el / k, 3),
                                 "sample": f"{k} fp64 PCG iterations on the assembled CSR (oracle matvec), same mesh"}
-    print(json.dumps(line), flush=True)
+    if emit:
+        print(json.dumps(line), flush=True)
+    return line
 
 
-def bench_spgemm(args):
-    """One JSON line for C = A * A (see the module docstring)."""
+def bench_spgemm(args, emit=True):
+    """One JSON line for C = A * A (see the module docstring); returns it
+    (and prints it when `emit`)."""
     import numpy as np
     import torch
     import gen
@@ -805,7 +811,9 @@ def bench_spgemm(args):
         line["cpu_baseline"] = {"value": round(2 * ip_s / el / 1e9, 4), "unit": "GFLOP/s", "cores": 1,
                                 "kind": "oracle", "sample": f"rows 0..{n_sample} of the same product "
                                 f"({ip_s} intermediate products, {el:.1f} s)"}
-    print(json.dumps(line), flush=True)
+    if emit:
+        print(json.dumps(line), flush=True)
+    return line
 
 
 # The default run: the headline (Laplacian CSR) in full detail, then every
@@ -975,7 +983,24 @@ def main():
                 for c in ("pruned50", "pruned70", "pruned90") if f"{c}/macko" in configs}
         met = [r["target_met"] for r in configs.values() if r["target_met"] is not None]
         line["targets_met"] = f"{sum(met)} of {len(met)}"
-        line["parity_all_ok"] = all((r["parity"] or {}).get("ok", False) for r in configs.values())
+        # the adjacent rows built beside the hot path: HYB chosen by the CV
+        # rule, Jacobi-PCG on the elasticity cantilever, hash SpGEMM (C = A * A)
+        import copy
+        nxt = {}
+        rec, _ = measure("varlen", "auto", args, note="HYB chosen by the CV rule (CV 0.43, W = 5)", detail=True,
+                         cpu_seconds=min(args.cpu_seconds, 1.5), par_seconds=min(args.cpu_seconds, 1.0))
+        nxt["varlen/auto"] = rec
+        drop = ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data")
+        a = copy.copy(args)
+        a.config, a.cpu_seconds = "cantilever", min(args.cpu_seconds, 1.5)
+        nxt["cantilever/fem-pcg"] = {k: v for k, v in bench_pcg(a, emit=False).items() if k not in drop}
+        a = copy.copy(args)
+        a.config, a.steps, a.warmup = "powerlaw", min(args.steps, 20), min(args.warmup, 3)
+        a.cpu_seconds = min(args.cpu_seconds, 1.5)
+        nxt["powerlaw/spgemm"] = {k: v for k, v in bench_spgemm(a, emit=False).items() if k not in drop}
+        line["next_rows"] = nxt
+        line["parity_all_ok"] = (all((r["parity"] or {}).get("ok", False) for r in configs.values())
+                                 and all((r.get("parity") or {}).get("ok", False) for r in nxt.values()))
     print(json.dumps(line), flush=True)
 
 
