@@ -115,8 +115,11 @@ def test_macko_and_dense_replay():
     _replay_and_compare("dense", fd, x, xs, y, y0, _bitwise_vs_eager(fd, x, y, y0))
 
 
-def test_fe_fused_replay():
-    M = gen.fe_mesh(12, 6, 5, seed=3)
+@pytest.mark.parametrize("dims", [(12, 6, 5), (40, 20, 10)])
+def test_fe_fused_replay(dims):
+    """The beta kernel and the fused kernel in one graph, replayed; an eager
+    call between the replays must agree with the oracle too."""
+    M = gen.fe_mesh(*dims, seed=3)
     ed, rho, Ke = dev(M.edof.reshape(-1)), dev(M.rho), dev(M.Ke.reshape(-1))
     x = dev(M.x)
     y = torch.zeros(M.n_dof, device="cuda")
@@ -128,6 +131,10 @@ def test_fe_fused_replay():
     def check(got, xv):
         yr, sc = oracle.fe_matvec(M.edof, M.rho, M.Ke, xv, M.n_dof, M.penalty, 2.0, -0.5, y0)
         assert_close(got, yr, sc, TAU_F32, "graph fe")
+        y.copy_(dev(y0))
+        fn()                                   # an eager call between the replays
+        torch.cuda.synchronize()
+        assert_close(host(y), yr, sc, TAU_F32, "eager fe between replays")
     _replay_and_compare("fe", fn, x, xs, y, y0, check)
 
 
