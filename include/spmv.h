@@ -268,10 +268,13 @@ spmv_status spmv_auto_plan(int32_t n_rows, int32_t n_cols, int32_t nnz, const in
 
 /* Builds the planned format in `workspace` (device, 256-byte aligned, at
  * least plan->workspace_bytes).  The handle borrows the CSR arrays when the
- * format is CSR; ELL and HYB keep their own copy in the workspace (for HYB
- * also a binned CSR plan of the tail, which spmv_auto_apply runs through
- * spmv_csr_apply_rows), and the conversion's scratch is part of it.
- * Synchronises. */
+ * format is CSR; ELL and HYB keep their own copy in the workspace, and the
+ * conversion's scratch is part of it.  For HYB the tail is kept per tail
+ * row with a binned CSR plan, and per row (one pointer per row): when no
+ * row has more than 16 entries past the width, n_rows and n_cols are
+ * multiples of 4 and x, y are 16-byte aligned, spmv_auto_apply runs the ELL
+ * part and the tail in one kernel; otherwise the ELL kernel, then the tail
+ * through spmv_csr_apply_rows.  Synchronises. */
 spmv_status spmv_auto_create(spmv_auto_t *h, const spmv_auto_plan_t *plan, int32_t n_rows,
                              int32_t n_cols, int32_t nnz, const int32_t *row_ptr,
                              const int32_t *col_idx, const float *vals, void *workspace,

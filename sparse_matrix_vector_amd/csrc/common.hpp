@@ -74,6 +74,16 @@ inline size_t scratch_bytes(int64_t n_rows) {
 // Checks a caller scratch buffer for a matrix of n_rows rows.
 spmv_status check_scratch(const void *scratch, size_t bytes, int64_t n_rows);
 
+// HYB in one launch (ell.hip): the ELL part and a tail stored per row (entries
+// of row r at [trp[r], trp[r + 1]) of tcol / tval) summed into one store per
+// row.  ell_tail_fits: the shape and alignments the kernel needs of the
+// matrix (width 1..8, n_rows and n_cols multiples of 4, 16-byte aligned
+// arrays); x and y must be 16-byte aligned too.
+bool ell_tail_fits(int32_t n_rows, int32_t n_cols, int32_t width, const void *ec, const void *ev, const void *trp);
+spmv_status ell_tail_apply(int32_t n_rows, int32_t width, const int32_t *ell_col, const float *ell_val,
+                           const int32_t *trp, const int32_t *tcol, const float *tval, float alpha, const float *x,
+                           float beta, float *y, hipStream_t st);
+
 // ---------------------------------------------------------------------------
 // Device: wave64 primitives.
 //

@@ -114,14 +114,48 @@ __global__ __launch_bounds__(WG) void k_ell_apply4(int n, int width, const int *
 // through the texture addresser, a gather one).  Wider windows gather from
 // memory as in k_ell_apply4.  Every thread takes part in the barriers; rows
 // past n only load the matrix's first slot vector.
+//
+// TAIL: the rows also carry the overflow of a HYB split, stored per row
+// (entries of row r at [trp[r], trp[r + 1])), and each row is finished here
+// in one store.  A wave's 256 rows own one contiguous run of tail entries:
+// its 64 lanes load up to TAIL_BATCH * 64 of them together (issued with the
+// x-window loads), take x from the window where the column falls in it
+// (else from memory), and leave the products in the wave's LDS buffer, from
+// which every lane sums its four rows' share; a longer run takes further
+// rounds of the same.
 constexpr int XT_ROUNDS = 3;
+constexpr int TAIL_BATCH = 8;    // tail entries per lane per round: 512 per wave
 
-template <int U>
-__global__ __launch_bounds__(WG) void k_ell_apply4t(int n, const int *__restrict__ ec, const float *__restrict__ ev,
+struct EllTail {
+    const int *trp;     // int32[n + 1], 16-byte aligned
+    const int *tcol;
+    const float *tval;
+};
+
+// One round of a wave's tail: the products of entries [base, base +
+// TAIL_BATCH * 64) (clipped to te) are in buf; the lane's rows cover entries
+// [b[0], b[4]), row t from b[t].
+__device__ __forceinline__ void tail_sum(const float *buf, int base, int te, const int (&b)[5], float (&tacc)[4]) {
+    const int lo = max(b[0], base), hi = min(b[4], min(te, base + TAIL_BATCH * 64));
+    for (int k = lo; k < hi; ++k) {
+        const float v = buf[k - base];
+        const int t = (k >= b[1]) + (k >= b[2]) + (k >= b[3]);
+        tacc[0] += t == 0 ? v : 0.0f;
+        tacc[1] += t == 1 ? v : 0.0f;
+        tacc[2] += t == 2 ? v : 0.0f;
+        tacc[3] += t == 3 ? v : 0.0f;
+    }
+}
+
+// TAIL with width <= 5: held to 128 registers, so that four waves per SIMD
+// stay resident (the whole grid of a 1M-row matrix at once)
+template <int U, bool TAIL>
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(TAIL && U <= 5 ? 4 : 1))) void k_ell_apply4t(int n, const int *__restrict__ ec, const float *__restrict__ ev,
                                                     float alpha, const float *__restrict__ x, float beta,
-                                                    float *__restrict__ y) {
+                                                    float *__restrict__ y, EllTail tl) {
     __shared__ __attribute__((aligned(16))) float xt[XT_ROUNDS * 4 * WG];
     __shared__ int red[2][WG / 64];
+    __shared__ float tbuf[TAIL ? WG / 64 : 1][TAIL ? TAIL_BATCH * 64 : 1];
     const int w = xcd_contiguous(blockIdx.x, gridDim.x);
     const int i0 = 4 * (w * WG + (int)threadIdx.x);
     const bool live = i0 < n;
@@ -133,6 +167,24 @@ __global__ __launch_bounds__(WG) void k_ell_apply4t(int n, const int *__restrict
         const size_t slot = (size_t)u * (size_t)n + (size_t)ib;
         c[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(ec + slot));
         f[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(ev + slot));
+    }
+    // TAIL: the lane's row bounds in the tail, and the wave's run [tb, te)
+    int tb_ = 0, te_ = 0;
+    int b[5] = {0, 0, 0, 0, 0};
+    const int lane = __lane_id();
+    if (TAIL) {
+        if (live) {
+            const i32x4 q = *reinterpret_cast<const i32x4 *>(tl.trp + i0);
+            b[0] = q.x;
+            b[1] = q.y;
+            b[2] = q.z;
+            b[3] = q.w;
+            b[4] = tl.trp[i0 + 4];
+        }
+        // live lanes are a prefix of the wave (rows grow with the lane)
+        const int nl = __popcll(__ballot(live));
+        tb_ = __builtin_amdgcn_readfirstlane(b[0]);
+        te_ = nl > 0 ? __builtin_amdgcn_readlane(b[4], max(nl - 1, 0)) : tb_;
     }
     // the workgroup's column window (padding, -1, and dead rows excluded)
     int mn = INT_MAX, mx = -1;
@@ -160,8 +212,23 @@ __global__ __launch_bounds__(WG) void k_ell_apply4t(int n, const int *__restrict
     }
     const int tb = mx >= 0 ? (mn & ~3) : 0;
     const int nvec = mx >= 0 ? (mx + 4 - tb) >> 2 : 1;
+    // TAIL: the first round's entries, loaded with the window (clamped to
+    // the run, zero value past its end)
+    int tc[TAIL ? TAIL_BATCH : 1];
+    float tv_[TAIL ? TAIL_BATCH : 1];
+    auto tail_load = [&](int base) {
+#pragma unroll
+        for (int j = 0; j < TAIL_BATCH; ++j) {
+            const int k = base + j * 64 + lane;
+            const int kk = min(k, te_ - 1);
+            tc[j] = tl.tcol[kk];
+            tv_[j] = k < te_ ? tl.tval[kk] : 0.0f;
+        }
+    };
+    if (TAIL && te_ > tb_) tail_load(tb_);
     float xv[U][4];
-    if (nvec <= XT_ROUNDS * WG) {   // uniform over the workgroup
+    const bool win = nvec <= XT_ROUNDS * WG;
+    if (win) {   // uniform over the workgroup
         f32x4 tv[XT_ROUNDS];
 #pragma unroll
         for (int r = 0; r < XT_ROUNDS; ++r)
@@ -185,12 +252,39 @@ __global__ __launch_bounds__(WG) void k_ell_apply4t(int n, const int *__restrict
 #pragma unroll
         for (int u = 0; u < U; ++u) issue_together(xv[u][0], xv[u][1], xv[u][2], xv[u][3]);
     }
+    float tacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (TAIL && te_ > tb_) {   // uniform over the wave
+        float *buf = tbuf[threadIdx.x / 64];
+        for (int base = tb_; base < te_; base += TAIL_BATCH * 64) {
+            if (base != tb_) tail_load(base);
+            // x from the workgroup's window where the column falls in it
+            float g[TAIL_BATCH];
+#pragma unroll
+            for (int j = 0; j < TAIL_BATCH; ++j) {
+                const unsigned o = (unsigned)(tc[j] - tb);
+                g[j] = win && o < 4u * (unsigned)nvec ? xt[o] : x[tc[j]];
+            }
+#pragma unroll
+            for (int j = 0; j < TAIL_BATCH; ++j) buf[j * 64 + lane] = tv_[j] * g[j];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            tail_sum(buf, base, te_, b, tacc);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    }
     if (!live) return;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[t] = c[u][t] >= 0 ? fmaf(f[u][t], xv[u][t], acc[t]) : acc[t];
+    if (TAIL) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] += tacc[t];
+    }
     f32x4 yo = {0.0f, 0.0f, 0.0f, 0.0f};
     if (beta != 0.0f) yo = *reinterpret_cast<const f32x4 *>(y + i0);
     f32x4 r;
@@ -222,6 +316,32 @@ __global__ void k_scale(int n, float beta, float *__restrict__ y) {
 }
 
 }  // namespace
+
+bool ell_tail_fits(int32_t n_rows, int32_t n_cols, int32_t width, const void *ec, const void *ev, const void *trp) {
+    return n_rows > 0 && n_rows % 4 == 0 && n_cols > 0 && n_cols % 4 == 0 && width >= 1 && width <= 8 && ec && ev &&
+           trp && aligned16(ec) && aligned16(ev) && aligned16(trp);
+}
+
+spmv_status ell_tail_apply(int32_t n_rows, int32_t width, const int32_t *ell_col, const float *ell_val,
+                           const int32_t *trp, const int32_t *tcol, const float *tval, float alpha, const float *x,
+                           float beta, float *y, hipStream_t st) {
+    const int grid = (int)ceil_div(n_rows / 4, WG);
+    const EllTail tl{trp, tcol, tval};
+    switch (width) {
+#define SPMV_ELL_TT(W)                                                                               \
+    case W:                                                                                          \
+        k_ell_apply4t<W, true><<<grid, WG, 0, st>>>(n_rows, ell_col, ell_val, alpha, x, beta, y, tl); \
+        break;
+        SPMV_ELL_TT(1) SPMV_ELL_TT(2) SPMV_ELL_TT(3) SPMV_ELL_TT(4) SPMV_ELL_TT(5) SPMV_ELL_TT(6) SPMV_ELL_TT(7)
+        SPMV_ELL_TT(8)
+#undef SPMV_ELL_TT
+    default:
+        return fail(SPMV_ERR_INVALID_VALUE, "width %d outside 1..8", width);
+    }
+    SPMV_LAUNCHED("k_ell_apply4t");
+    return SPMV_OK;
+}
+
 }  // namespace spmv
 
 using namespace spmv;
@@ -284,7 +404,7 @@ extern "C" spmv_status spmv_ell_apply(int32_t n_rows, int32_t n_cols, int32_t wi
         switch (width) {
 #define SPMV_ELL_T(W)                                                                                   \
     case W:                                                                                             \
-        k_ell_apply4t<W><<<grid, WG, 0, st>>>(n_rows, ell_col, ell_val, alpha, x, beta, y);           \
+        k_ell_apply4t<W, false><<<grid, WG, 0, st>>>(n_rows, ell_col, ell_val, alpha, x, beta, y, EllTail{}); \
         break;
             SPMV_ELL_T(1) SPMV_ELL_T(2) SPMV_ELL_T(3) SPMV_ELL_T(4) SPMV_ELL_T(5) SPMV_ELL_T(6) SPMV_ELL_T(7)
             SPMV_ELL_T(8)

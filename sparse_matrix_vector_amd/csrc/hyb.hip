@@ -173,6 +173,23 @@ __global__ __launch_bounds__(WG) void k_hyb_tail_write(int n, int n_cols, const 
 
 __global__ void k_set_int(int *p, int v) { *p = v; }
 
+// The tail per row: tfull[r] = first tail entry of row r or of the next tail
+// row after it (tail_rp[number of tail rows < r]), r = 0..n.
+__global__ __launch_bounds__(WG) void k_hyb_row_tail(int n, int n_tail, const int *__restrict__ trows,
+                                                     const int *__restrict__ trp, int *__restrict__ tfull) {
+    const int r = blockIdx.x * WG + threadIdx.x;
+    if (r > n) return;
+    int lo = 0, hi = n_tail;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (trows[mid] < r)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    tfull[r] = trp[lo];
+}
+
 // y[tail_rows[t]] += alpha * (tail row t) . x, G lanes per tail row.
 template <int G>
 __global__ __launch_bounds__(WG) void k_hyb_tail(int n_tail, const int *__restrict__ trows,
@@ -377,6 +394,8 @@ struct spmv_auto {
     float *ell_val = nullptr;
     int32_t *tail_rows = nullptr, *tail_rp = nullptr, *tail_col = nullptr;
     float *tail_val = nullptr;
+    int32_t *tail_full = nullptr;   // HYB: the tail's entries per row (n_rows + 1 pointers)
+    bool one_launch = false;        // HYB: short tails, ELL and tail in one kernel when x and y allow
     spmv_csr_t csr = nullptr;    // CSR format, or the HYB tail's binned plan
 };
 
@@ -384,8 +403,13 @@ namespace {
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// HYB tails of at most this many entries per row run in the ELL kernel
+// (each wave then sums at most 256 * HYB_ONE_LAUNCH_TAIL entries); longer
+// ones go through the binned CSR plan of the tail.
+constexpr int HYB_ONE_LAUNCH_TAIL = 16;
+
 struct AutoLayout {
-    size_t ell_col, ell_val, tail_rows, tail_rp, tail_col, tail_val, tail_plan, tail_plan_bytes, scratch,
+    size_t ell_col, ell_val, tail_rows, tail_rp, tail_col, tail_val, tail_full, tail_plan, tail_plan_bytes, scratch,
         scratch_bytes, total;
 };
 
@@ -404,6 +428,7 @@ AutoLayout auto_layout(const spmv_auto_plan_t &p, int32_t n_rows) {
     L.tail_rp = take(4 * ((size_t)p.n_tail_rows + 1));
     L.tail_col = take(4 * (size_t)p.tail_nnz);
     L.tail_val = take(4 * (size_t)p.tail_nnz);
+    L.tail_full = take(p.format == SPMV_FORMAT_HYB ? 4 * ((size_t)n_rows + 1) : 0);
     L.tail_plan_bytes = 0;
     if (p.n_tail_rows > 0 && spmv_csr_plan_size(p.n_tail_rows, (int32_t)p.tail_nnz, nullptr, &L.tail_plan_bytes) != SPMV_OK)
         L.tail_plan_bytes = 0;
@@ -506,6 +531,23 @@ extern "C" spmv_status spmv_auto_create(spmv_auto_t *out, const spmv_auto_plan_t
         if (s == SPMV_OK && p.format == SPMV_FORMAT_HYB && p.n_tail_rows > 0)
             s = spmv_csr_create(&h->csr, p.n_tail_rows, n_cols, (int32_t)p.tail_nnz, h->tail_rp, h->tail_col,
                                 h->tail_val, SPMV_CSR_BINNED, nullptr, ws + L.tail_plan, L.tail_plan_bytes, stream);
+        // and per row, for the one-launch apply when every tail is short
+        if (s == SPMV_OK && p.format == SPMV_FORMAT_HYB) {
+            int32_t max_len = 0;
+            int64_t s1 = 0, s2 = 0;
+            s = spmv_csr_row_stats(n_rows, row_ptr, &max_len, &s1, &s2, ws + L.scratch, L.scratch_bytes, stream);
+            if (s == SPMV_OK) {
+                h->tail_full = reinterpret_cast<int32_t *>(ws + L.tail_full);
+                hipStream_t st = as_stream(stream);
+                k_hyb_row_tail<<<(int)ceil_div((int64_t)n_rows + 1, WG), WG, 0, st>>>(n_rows, p.n_tail_rows,
+                                                                                      h->tail_rows, h->tail_rp,
+                                                                                      h->tail_full);
+                SPMV_LAUNCHED("k_hyb_row_tail");
+                h->one_launch = max_len - p.width <= HYB_ONE_LAUNCH_TAIL &&
+                                ell_tail_fits(n_rows, n_cols, p.width, h->ell_col, h->ell_val, h->tail_full);
+                if (hipStreamSynchronize(st) != hipSuccess) s = fail(SPMV_ERR_HIP, "hipStreamSynchronize failed");
+            }
+        }
     }
     if (s != SPMV_OK) {
         delete h;
@@ -525,8 +567,12 @@ extern "C" spmv_status spmv_auto_apply(spmv_auto_t h, float alpha, const float *
         return spmv_ell_apply(h->n_rows, h->n_cols, h->plan.width, h->ell_col, h->ell_val, alpha, x, beta, y,
                               stream);
     default: {
-        // ELL part, then the tail rows added in place (beta = 1) through the
-        // binned CSR kernels with the tail's row map
+        // short tails: ELL part and tail in one kernel, one store per row
+        if (h->one_launch && x && y && aligned16(x) && aligned16(y))
+            return ell_tail_apply(h->n_rows, h->plan.width, h->ell_col, h->ell_val, h->tail_full, h->tail_col,
+                                  h->tail_val, alpha, x, beta, y, as_stream(stream));
+        // else the ELL part, then the tail rows added in place (beta = 1)
+        // through the binned CSR kernels with the tail's row map
         spmv_status s = spmv_ell_apply(h->n_rows, h->n_cols, h->plan.width, h->ell_col, h->ell_val, alpha, x,
                                        beta, y, stream);
         if (s != SPMV_OK || !h->csr) return s;

@@ -62,12 +62,16 @@ def _bitwise_vs_eager(fn, x, y, y0):
     return check
 
 
-@pytest.mark.parametrize("kind", ["csr-binned", "csr-vector", "ell", "auto-hyb"])
+@pytest.mark.parametrize("kind", ["csr-binned", "csr-vector", "ell", "auto-hyb", "auto-hyb-short"])
 def test_spmv_paths_replay(kind):
+    """auto-hyb: tails up to ~25 entries (ELL kernel, then the binned tail);
+    auto-hyb-short: tails of at most 16 (ELL and tail in one kernel)."""
     rng = np.random.default_rng(5)
     if kind == "auto-hyb":
         lens = rng.integers(1, 13, 20_000)
         lens[rng.choice(20_000, 100, replace=False)] = 30
+    elif kind == "auto-hyb-short":
+        lens = rng.integers(1, 13, 20_000)
     else:
         lens = rng.integers(0, 40, 20_000)
         lens[::997] = 700                       # rows of several chunks

@@ -160,6 +160,53 @@ def test_auto_hyb_shapes(n, misaligned_y):
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
 
 
+@pytest.mark.parametrize("n,x_off,y_off", [(8192, 0, 0), (4 * 1024 * 3 + 4, 0, 0), (8190, 0, 0), (8192, 1, 0),
+                                           (8192, 0, 1)])
+def test_auto_hyb_one_launch(n, x_off, y_off):
+    """HYB with short tails (every row at most 16 entries past the width):
+    with n % 4 == 0 and x, y 16-byte aligned the ELL part and the tail run in
+    one kernel, each wave summing its rows' run of tail entries in rounds of
+    640; otherwise (n % 4 != 0, x or y misaligned) the ELL kernel and then
+    the binned tail.  Rows of 1..12 entries, one wave of 256 rows with 17
+    each (a run of several rounds), waves without tail rows, tail rows at
+    wave and workgroup edges; alpha / beta against the oracle, and the two
+    forms against each other."""
+    rng = np.random.default_rng(n + 7 * x_off + 3 * y_off)
+    lens = rng.integers(1, 13, n)
+    lens[2048:2048 + 256] = 17                      # one wave's rows (ELL rows 4 per lane)
+    lens[4096:4096 + 512] = rng.integers(1, 4, 512)  # two waves without tails
+    lens[[0, 255, 256, 1023, 1024, 4095, n - 1]] = 16
+    A = gen.random_csr(n, 3000, lens, seed=n + 5)
+    s1, s2 = int(lens.sum()), int((lens.astype(np.int64) ** 2).sum())
+    assert oracle.format_choice(n, s1, s2) == 1
+    M = S.AutoMatrix(A.n_rows, A.n_cols, dev(A.row_ptr), dev(A.col_idx), dev(A.vals))
+    assert M.format == 1
+    W = int(M.plan.width)
+    heavy = int(np.maximum(lens[2048:2048 + 256] - W, 0).sum())
+    print(f"[auto hyb 1-launch] n={n} x_off={x_off} y_off={y_off} W={W} heaviest wave run {heavy}", flush=True)
+    assert lens.max() - W <= 16 and heavy > 640
+    y_in = rng.uniform(-1, 1, n).astype(np.float32)
+    xb = torch.zeros(A.n_cols + 4, device="cuda")
+    x = xb[x_off:x_off + A.n_cols]
+    x.copy_(dev(A.x))
+    yb = torch.zeros(n + 4, device="cuda")
+    y = yb[y_off:y_off + n]
+    for alpha, beta in [(1.0, 0.0), (0.5, 2.0)]:
+        y.copy_(dev(y_in) if beta else torch.full((n,), float("nan"), device="cuda"))
+        M.apply(x, y, alpha, beta)
+        torch.cuda.synchronize()
+        yr, sc = oracle.csr_spmv(A.row_ptr, A.col_idx, A.vals, A.x, alpha, beta, y_in)
+        assert_close(host(y), yr, sc, TAU_F32, f"auto hyb 1-launch n={n} {alpha} {beta}")
+    # the same handle with a misaligned x (ELL kernel, then the binned tail)
+    xm = torch.zeros(A.n_cols + 4, device="cuda")[1:1 + A.n_cols]
+    xm.copy_(dev(A.x))
+    y2 = torch.zeros(n, device="cuda")
+    y2.copy_(dev(y_in))
+    M.apply(xm, y2, 0.5, 2.0)
+    torch.cuda.synchronize()
+    assert_close(host(y2), host(y).astype(np.float64), sc, 2 * TAU_F32, "one launch vs two")
+
+
 def test_auto_ell_padding_guard():
     """CV < 0.3 but one long row: padding every row to it would more than
     double the storage, so HYB is used instead of ELL."""
