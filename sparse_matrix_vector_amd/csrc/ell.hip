@@ -136,14 +136,11 @@ struct EllTail {
 // TAIL_BATCH * 64) (clipped to te) are in buf; the lane's rows cover entries
 // [b[0], b[4]), row t from b[t].
 __device__ __forceinline__ void tail_sum(const float *buf, int base, int te, const int (&b)[5], float (&tacc)[4]) {
-    const int lo = max(b[0], base), hi = min(b[4], min(te, base + TAIL_BATCH * 64));
-    for (int k = lo; k < hi; ++k) {
-        const float v = buf[k - base];
-        const int t = (k >= b[1]) + (k >= b[2]) + (k >= b[3]);
-        tacc[0] += t == 0 ? v : 0.0f;
-        tacc[1] += t == 1 ? v : 0.0f;
-        tacc[2] += t == 2 ? v : 0.0f;
-        tacc[3] += t == 3 ? v : 0.0f;
+    const int end = min(te, base + TAIL_BATCH * 64);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int lo = max(b[t], base), hi = min(b[t + 1], end);
+        for (int k = lo; k < hi; ++k) tacc[t] += buf[k - base];
     }
 }
 
