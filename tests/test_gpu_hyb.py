@@ -160,14 +160,15 @@ def test_auto_hyb_shapes(n, misaligned_y):
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
 
 
-@pytest.mark.parametrize("n,x_off,y_off", [(8192, 0, 0), (4 * 1024 * 3 + 4, 0, 0), (8190, 0, 0), (8192, 1, 0),
-                                           (8192, 0, 1)])
-def test_auto_hyb_one_launch(n, x_off, y_off):
+@pytest.mark.parametrize("n,x_off,y_off,n_cols", [(8192, 0, 0, 3000), (4 * 1024 * 3 + 4, 0, 0, 3000),
+                                                  (8190, 0, 0, 3000), (8192, 1, 0, 3000), (8192, 0, 1, 3000),
+                                                  (8192, 0, 0, 3001)])
+def test_auto_hyb_one_launch(n, x_off, y_off, n_cols):
     """HYB with short tails (every row at most 16 entries past the width):
     with n % 4 == 0 and x, y 16-byte aligned the ELL part and the tail run in
     one kernel, each wave summing its rows' run of tail entries in rounds of
-    640; otherwise (n % 4 != 0, x or y misaligned) the ELL kernel and then
-    the binned tail.  Rows of 1..12 entries, one wave of 256 rows with 17
+    512; otherwise (n or n_cols not a multiple of 4, x or y misaligned) the
+    ELL kernel and then the binned tail.  Rows of 1..12 entries, one wave of 256 rows with 17
     each (a run of several rounds), waves without tail rows, tail rows at
     wave and workgroup edges; alpha / beta against the oracle, and the two
     forms against each other."""
@@ -176,15 +177,16 @@ def test_auto_hyb_one_launch(n, x_off, y_off):
     lens[2048:2048 + 256] = 17                      # one wave's rows (ELL rows 4 per lane)
     lens[4096:4096 + 512] = rng.integers(1, 4, 512)  # two waves without tails
     lens[[0, 255, 256, 1023, 1024, 4095, n - 1]] = 16
-    A = gen.random_csr(n, 3000, lens, seed=n + 5)
+    A = gen.random_csr(n, n_cols, lens, seed=n + 5)
     s1, s2 = int(lens.sum()), int((lens.astype(np.int64) ** 2).sum())
     assert oracle.format_choice(n, s1, s2) == 1
     M = S.AutoMatrix(A.n_rows, A.n_cols, dev(A.row_ptr), dev(A.col_idx), dev(A.vals))
     assert M.format == 1
     W = int(M.plan.width)
     heavy = int(np.maximum(lens[2048:2048 + 256] - W, 0).sum())
-    print(f"[auto hyb 1-launch] n={n} x_off={x_off} y_off={y_off} W={W} heaviest wave run {heavy}", flush=True)
-    assert lens.max() - W <= 16 and heavy > 640
+    print(f"[auto hyb 1-launch] n={n} n_cols={n_cols} x_off={x_off} y_off={y_off} W={W} heaviest wave run {heavy}",
+          flush=True)
+    assert lens.max() - W <= 16 and heavy > 512
     y_in = rng.uniform(-1, 1, n).astype(np.float32)
     xb = torch.zeros(A.n_cols + 4, device="cuda")
     x = xb[x_off:x_off + A.n_cols]
