@@ -79,7 +79,7 @@ KERNEL = {"csr": "k_csr_tasks", "csr-binned": "k_csr_tasks", "csr-vector": "k_cs
           "csr-scalar": "k_csr_scalar", "ell": "k_ell_apply4t", "macko": "k_macko_spmv",
           "dense": "k_gemv_f16", "fem": "k_fe_fused", "fem-3stage": "k_fe_elem", "fem-csr": "k_csr_tasks",
           "hyb": "k_ell_apply",
-          "auto": None, "fem-pcg": "k_fe_matvec64 + k_pcg_pq + k_pcg_update + k_pcg_direction",
+          "auto": None, "fem-pcg": "k_fe_matvec64 + k_cg_dot + k_cg_step",
           "spgemm": "k_sg_* (grouping, allocation, accumulation)"}
 
 # source file of each path's kernels (for the traffic-record freshness check)
@@ -633,10 +633,11 @@ def bench_pcg(args, emit=True):
     ws = torch.empty(S.fem_solver_workspace_size(n, 400), dtype=torch.uint8, device="cuda")
     u = torch.zeros(n, device="cuda")
     stream = torch.cuda.current_stream()
-    # per iteration (fp64 vectors, int64 fixed-point accumulator): matvec (edof 96 B + rho 4 B per element;
-    # p 8 B, accumulator read + write 16 B per DOF), alpha (p, acc in; q, cleared acc out: 32 B), update
-    # (p q dinv u r in, u r z out: 64 B), direction (z p in, p out: 24 B)
-    nbytes = 100 * E + 144 * n
+    # per iteration (fp64 vectors, int64 fixed-point accumulator; the one-reduction CG form): matvec
+    # w = K z (edof 96 B + rho 4 B per element; z 8 B, accumulator read + write 16 B per DOF), w.z
+    # (accumulator and z in: 16 B), step (accumulator, p, s, x, r, dinv in; p, s, x, r, z and the cleared
+    # accumulator out: 96 B)
+    nbytes = 100 * E + 136 * n
     flops = 2 * 576 * E + 13 * n
     S.fem_pcg_solve(*op, f, u, 0.0, max(args.warmup, 1), workspace=ws)
     u.zero_()

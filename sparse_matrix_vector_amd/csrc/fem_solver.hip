@@ -45,10 +45,15 @@
 // XCDs' L2 caches; no device-scope fence, which on gfx950 writes back and
 // invalidates the L2, is issued inside a kernel.  Partials of consecutive
 // iterations alternate between two slots, so a kernel never overwrites
-// sums that a workgroup of the same kernel still reads.  One PCG iteration
-// k is: the matvec acc = K p; k_pcg_pq (q = acc, partial p.q);
-// k_pcg_update (alpha = r.z(k-1) / p.q; u, r, z = D^-1 r; partial r.z, r.r
-// into slot k & 1); k_pcg_direction (convergence test, beta, p = z + beta p).
+// sums that a workgroup of the same kernel still reads.  The CG recurrences
+// are taken in the one-reduction form of Chronopoulos and Gear (the same
+// iterates as the textbook form in exact arithmetic): besides r and
+// z = D^-1 r it carries w = K z and s = K p, so that r.z and w.z, the only
+// inner products of an iteration, are both known before the vector
+// updates.  One iteration i is three launches: the matvec acc = K z_i;
+// k_cg_dot (convergence test on r_i.r_i, partial w.z); k_cg_step (beta,
+// alpha, p = z + beta p, s = w + beta s, x += alpha p, r -= alpha s,
+// z = D^-1 r; partial r.z, r.r into slot (i + 1) & 1).
 // Once the state says "done", these kernels return at once; the host checks
 // the state every PCG_CHECK iterations.  Reductions and matvecs are both
 // deterministic, so two solves of the same system agree bit for bit.
@@ -79,14 +84,16 @@ struct SolverState {
     int done;           // converged, capped or broken down
     int bad;            // 1: diagonal entry not positive, 2: p.Kp <= 0, 4: zero vector
     int acc_exp;        // k of the accumulator's fixed point (value = acc * 2^-k)
+    double cg_gamma[2]; // r.z of CG step i, in slot i & 1 (read by step i + 1)
+    double cg_alpha[2]; // alpha of CG step i, in slot i & 1
 };
 
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 // Workspace: state | partials: 2 slots x SV_NQ x SV_MAX_BLOCKS doubles, then
-// SV_MAX_BLOCKS more for p.q and SV_MAX_BLOCKS for the maxima of |x| of the
+// SV_MAX_BLOCKS more for w.z (CG) and SV_MAX_BLOCKS for the maxima of |x| of the
 // next matvec's input | lambda history (max_history doubles) | vectors of
-// n_dof doubles: dinv r z p q u (PCG) | vectors of n_dof floats: v w
+// n_dof doubles: dinv r z p kp u (PCG; kp = K p) | vectors of n_dof floats: v w
 // (eigenvalue iterations) | the fixed-point matvec accumulator (n_dof
 // int64, all zero between uses).
 constexpr int NVEC64 = 6, NVEC32 = 2;
@@ -132,7 +139,8 @@ __device__ __forceinline__ double *slot(double *partials, int s, int q) {
 __device__ __forceinline__ const double *slot(const double *partials, int s, int q) {
     return partials + (size_t)(s * SV_NQ + q) * SV_MAX_BLOCKS;
 }
-__device__ __forceinline__ double *pq_slot(double *partials) {
+// The partials of w.z = (K z).z of a CG iteration.
+__device__ __forceinline__ double *wz_slot(double *partials) {
     return partials + (size_t)2 * SV_NQ * SV_MAX_BLOCKS;
 }
 // Per-workgroup maxima of |x| of the vector the next matvec takes.
@@ -404,12 +412,11 @@ __global__ void k_pcg_dinv(int n, long long *__restrict__ acc, double *__restric
 }
 
 // Start of PCG, with acc = K u: u64 = u, r = f - acc (acc cleared),
-// z = D^-1 r, p = z; partial r.z, r.r, f.f into slot 1 (read as
-// "iteration -1"), and the maxima of |p| for the first matvec.
+// z = D^-1 r; partial r.z, r.r, f.f into slot 0 (read by CG step 0), and the
+// maxima of |z| for the first matvec.
 __global__ void k_pcg_start(int n, const float *__restrict__ f, const float *__restrict__ u, long long *__restrict__ acc,
                             double *__restrict__ u64, double *__restrict__ r, const double *__restrict__ dinv,
-                            double *__restrict__ z, double *__restrict__ p, double *__restrict__ partials,
-                            const SolverState *st) {
+                            double *__restrict__ z, double *__restrict__ partials, const SolverState *st) {
     const double inv_unit = fix_unit(st->acc_exp);
     double v[3] = {0.0, 0.0, 0.0};
     double m = 0.0;
@@ -421,20 +428,19 @@ __global__ void k_pcg_start(int n, const float *__restrict__ f, const float *__r
         u64[i] = u[i];
         r[i] = ri;
         z[i] = zi;
-        p[i] = zi;
         v[0] += ri * zi;
         v[1] += ri * ri;
         v[2] += fi * fi;
         m = fmax(m, fabs(zi));
     }
-    double *const dst[3] = {slot(partials, 1, 0), slot(partials, 1, 1), slot(partials, 1, 2)};
+    double *const dst[3] = {slot(partials, 0, 0), slot(partials, 0, 1), slot(partials, 0, 2)};
     store_partials<3>(v, dst);
     store_xmax(m, partials);
 }
 
 // One workgroup: f.f and r.r of the start, and whether there is anything to do.
 __global__ void k_pcg_start_fin(int nb, const double *__restrict__ partials, SolverState *st) {
-    const double *const src[2] = {slot(partials, 1, 1), slot(partials, 1, 2)};
+    const double *const src[2] = {slot(partials, 0, 1), slot(partials, 0, 2)};
     double t[2];
     total_partials<2>(src, nb, t);
     if (threadIdx.x == 0) {
@@ -445,77 +451,88 @@ __global__ void k_pcg_start_fin(int nb, const double *__restrict__ partials, Sol
     }
 }
 
-// q = acc = K p (acc cleared); partial p.q.
-__global__ void k_pcg_pq(int n, const double *__restrict__ p, long long *__restrict__ acc, double *__restrict__ q,
-                         double *__restrict__ partials, const SolverState *st) {
+// CG iteration i, first part (acc = K z_i from the matvec, left in place):
+// stop when r_i.r_i <= rtol^2 f.f or i reached the cap (i steps taken so
+// far), clearing the accumulator, else partial w.z with w = acc.
+__global__ void k_cg_dot(int n, int i, long long *__restrict__ acc, const double *__restrict__ z,
+                         double *__restrict__ partials, SolverState *st) {
     if (st->done) return;   // uniform: set by an earlier launch
+    const double *const src[1] = {slot(partials, i & 1, 1)};
+    double t[1];
+    total_partials<1>(src, gridDim.x, t);
+    const bool stop = t[0] <= st->rtol2 * st->ff || i >= st->max_iter;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        st->iter = i;
+        st->rr = t[0];
+        if (stop) st->done = 1;
+    }
+    if (stop) {   // uniform: every workgroup has the same totals; the accumulator is left all zero
+        for (int j = blockIdx.x * SV_WG + threadIdx.x; j < n; j += gridDim.x * SV_WG) acc[j] = 0;
+        return;
+    }
     const double inv_unit = fix_unit(st->acc_exp);
     double v[1] = {0.0};
-    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) {
-        const double qi = (double)acc[i] * inv_unit;
-        acc[i] = 0;
-        q[i] = qi;
-        v[0] += p[i] * qi;
-    }
-    double *const dst[1] = {pq_slot(partials)};
+    for (int j = blockIdx.x * SV_WG + threadIdx.x; j < n; j += gridDim.x * SV_WG)
+        v[0] += ((double)acc[j] * inv_unit) * z[j];
+    double *const dst[1] = {wz_slot(partials)};
     store_partials<1>(v, dst);
 }
 
-// Iteration k: alpha = r.z (slot (k+1)&1) / p.q; u += alpha p,
-// r -= alpha q, z = D^-1 r; partial r.z, r.r into slot k&1.  A p.q that is
-// not positive stops the iteration (the operator is not SPD).
-__global__ void k_pcg_update(int n, int k, const double *__restrict__ p, const double *__restrict__ q,
-                             const double *__restrict__ dinv, double *__restrict__ u, double *__restrict__ r,
-                             double *__restrict__ z, double *__restrict__ partials, SolverState *st) {
+// CG iteration i, second part: gamma = r_i.z_i (slot i & 1), delta = w.z;
+// beta = gamma / gamma_{i-1}, alpha = gamma / (delta - beta gamma /
+// alpha_{i-1}) (step 0: beta = 0, alpha = gamma / delta, p = z, s = w);
+// p = z + beta p, s = w + beta s (w = acc, which is cleared), x += alpha p,
+// r -= alpha s, z = D^-1 r; partial r.z and r.r into slot (i + 1) & 1 and
+// the maxima of |z| for the next matvec.  A denominator that is not
+// positive stops the iteration (the operator is not SPD).
+__global__ void k_cg_step(int n, int i, long long *__restrict__ acc, const double *__restrict__ dinv,
+                          double *__restrict__ x, double *__restrict__ r, double *__restrict__ z,
+                          double *__restrict__ p, double *__restrict__ s, double *__restrict__ partials,
+                          SolverState *st) {
     if (st->done) return;
-    const double *const src[2] = {pq_slot(partials), slot(partials, (k + 1) & 1, 0)};
+    const double *const src[2] = {slot(partials, i & 1, 0), wz_slot(partials)};
     double t[2];
     total_partials<2>(src, gridDim.x, t);
-    if (!(t[0] > 0.0)) {   // uniform: every workgroup has the same totals
+    const double g = t[0], d = t[1];
+    double beta = 0.0, den = d;
+    if (i > 0) {
+        beta = g / st->cg_gamma[(i - 1) & 1];
+        den = d - beta * g / st->cg_alpha[(i - 1) & 1];
+    }
+    if (!(den > 0.0)) {   // uniform; the accumulator is left all zero
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             st->bad |= 2;
             st->done = 1;
         }
+        for (int j = blockIdx.x * SV_WG + threadIdx.x; j < n; j += gridDim.x * SV_WG) acc[j] = 0;
         return;
     }
-    const double a = t[1] / t[0];
-    double v[2] = {0.0, 0.0};
-    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) {
-        u[i] = fma(a, p[i], u[i]);
-        const double ri = fma(-a, q[i], r[i]);
-        r[i] = ri;
-        const double zi = dinv[i] * ri;
-        z[i] = zi;
-        v[0] += ri * zi;
-        v[1] += ri * ri;
-    }
-    double *const dst[2] = {slot(partials, k & 1, 0), slot(partials, k & 1, 1)};
-    store_partials<2>(v, dst);
-}
-
-// Iteration k: stop when r.r <= rtol^2 f.f or the cap is reached, else
-// beta = r.z (slot k&1) / r.z (slot (k+1)&1) and p = z + beta p.
-__global__ void k_pcg_direction(int n, int k, const double *__restrict__ z, double *__restrict__ p,
-                                double *__restrict__ partials, SolverState *st) {
-    if (st->done) return;
-    const double *const src[3] = {slot(partials, k & 1, 0), slot(partials, k & 1, 1),
-                                  slot(partials, (k + 1) & 1, 0)};
-    double t[3];
-    total_partials<3>(src, gridDim.x, t);
-    const bool stop = t[1] <= st->rtol2 * st->ff || k + 1 >= st->max_iter;
+    const double alpha = g / den;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
-        st->iter = k + 1;
-        st->rr = t[1];
-        if (stop) st->done = 1;
+        st->cg_gamma[i & 1] = g;
+        st->cg_alpha[i & 1] = alpha;
     }
-    if (stop) return;
-    const double b = t[0] / t[2];
+    const double inv_unit = fix_unit(st->acc_exp);
+    double v[2] = {0.0, 0.0};
     double m = 0.0;
-    for (int i = blockIdx.x * SV_WG + threadIdx.x; i < n; i += gridDim.x * SV_WG) {
-        const double pi = fma(b, p[i], z[i]);
-        p[i] = pi;
-        m = fmax(m, fabs(pi));
+    for (int j = blockIdx.x * SV_WG + threadIdx.x; j < n; j += gridDim.x * SV_WG) {
+        const double wj = (double)acc[j] * inv_unit;
+        acc[j] = 0;
+        const double pj = i > 0 ? fma(beta, p[j], z[j]) : z[j];
+        const double sj = i > 0 ? fma(beta, s[j], wj) : wj;
+        p[j] = pj;
+        s[j] = sj;
+        x[j] = fma(alpha, pj, x[j]);
+        const double rj = fma(-alpha, sj, r[j]);
+        r[j] = rj;
+        const double zj = dinv[j] * rj;
+        z[j] = zj;
+        v[0] += rj * zj;
+        v[1] += rj * rj;
+        m = fmax(m, fabs(zj));
     }
+    double *const dst[2] = {slot(partials, (i + 1) & 1, 0), slot(partials, (i + 1) & 1, 1)};
+    store_partials<2>(v, dst);
     store_xmax(m, partials);
 }
 
@@ -623,7 +640,7 @@ struct Work {
     SolverState *st;
     double *partials, *hist;
     long long *acc;
-    double *dinv, *r, *z, *p, *q, *u;   // PCG
+    double *dinv, *r, *z, *p, *kp, *u;  // PCG (kp: K p, the CG recurrence's s)
     float *v, *w;                       // eigenvalue iterations
 };
 
@@ -634,7 +651,7 @@ Work carve(void *ws, const Layout &L) {
     W.partials = reinterpret_cast<double *>(b + L.partials);
     W.hist = reinterpret_cast<double *>(b + L.hist);
     W.acc = reinterpret_cast<long long *>(b + L.acc);
-    double **v64[NVEC64] = {&W.dinv, &W.r, &W.z, &W.p, &W.q, &W.u};
+    double **v64[NVEC64] = {&W.dinv, &W.r, &W.z, &W.p, &W.kp, &W.u};
     for (int k = 0; k < NVEC64; ++k) *v64[k] = reinterpret_cast<double *>(b + L.vec64[k]);
     float **v32[NVEC32] = {&W.v, &W.w};
     for (int k = 0; k < NVEC32; ++k) *v32[k] = reinterpret_cast<float *>(b + L.vec32[k]);
@@ -749,7 +766,7 @@ spmv_status pcg_run(const Operator &A, const Work &W, const float *f, float *u, 
     // r = f - K u
     s = matvec64(A, W, u, st, true, false);
     if (s != SPMV_OK) return s;
-    k_pcg_start<<<nb, SV_WG, 0, st>>>(n, f, u, W.acc, W.u, W.r, W.dinv, W.z, W.p, W.partials, W.st);
+    k_pcg_start<<<nb, SV_WG, 0, st>>>(n, f, u, W.acc, W.u, W.r, W.dinv, W.z, W.partials, W.st);
     SPMV_LAUNCHED("k_pcg_start");
     k_pcg_start_fin<<<1, SV_WG, 0, st>>>(nb, W.partials, W.st);
     SPMV_LAUNCHED("k_pcg_start_fin");
@@ -759,15 +776,19 @@ spmv_status pcg_run(const Operator &A, const Work &W, const float *f, float *u, 
     while (!h.done && k < max_iter) {
         const int batch = std::min(PCG_CHECK, max_iter - k);
         for (int j = 0; j < batch; ++j, ++k) {
-            s = matvec64(A, W, W.p, st, false, true);
+            s = matvec64(A, W, W.z, st, false, true);   // w = K z_k
             if (s != SPMV_OK) return s;
-            k_pcg_pq<<<nb, SV_WG, 0, st>>>(n, W.p, W.acc, W.q, W.partials, W.st);
-            SPMV_LAUNCHED("k_pcg_pq");
-            k_pcg_update<<<nb, SV_WG, 0, st>>>(n, k, W.p, W.q, W.dinv, W.u, W.r, W.z, W.partials, W.st);
-            SPMV_LAUNCHED("k_pcg_update");
-            k_pcg_direction<<<nb, SV_WG, 0, st>>>(n, k, W.z, W.p, W.partials, W.st);
-            SPMV_LAUNCHED("k_pcg_direction");
+            k_cg_dot<<<nb, SV_WG, 0, st>>>(n, k, W.acc, W.z, W.partials, W.st);
+            SPMV_LAUNCHED("k_cg_dot");
+            k_cg_step<<<nb, SV_WG, 0, st>>>(n, k, W.acc, W.dinv, W.u, W.r, W.z, W.p, W.kp, W.partials, W.st);
+            SPMV_LAUNCHED("k_cg_step");
         }
+        s = read_state(W, &h, st);
+        if (s != SPMV_OK) return s;
+    }
+    if (!h.done) {   // the cap: the last residual's norm and the count (the accumulator is already clear)
+        k_cg_dot<<<nb, SV_WG, 0, st>>>(n, k, W.acc, W.z, W.partials, W.st);
+        SPMV_LAUNCHED("k_cg_dot");
         s = read_state(W, &h, st);
         if (s != SPMV_OK) return s;
     }
