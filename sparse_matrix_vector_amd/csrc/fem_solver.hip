@@ -66,6 +66,9 @@
 namespace spmv {
 namespace {
 
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef long long i64x2 __attribute__((ext_vector_type(2)));
+
 constexpr int SV_WG = 256;
 constexpr int SV_MAX_BLOCKS = 1024;
 constexpr int SV_NQ = 3;                 // inner products per partial slot
@@ -472,8 +475,17 @@ __global__ void k_cg_dot(int n, int i, long long *__restrict__ acc, const double
     }
     const double inv_unit = fix_unit(st->acc_exp);
     double v[1] = {0.0};
-    for (int j = blockIdx.x * SV_WG + threadIdx.x; j < n; j += gridDim.x * SV_WG)
-        v[0] += ((double)acc[j] * inv_unit) * z[j];
+    // two DOFs per thread and step, 16-byte loads (the workspace vectors are 256-byte aligned)
+    const int n2 = n >> 1;
+    const i64x2 *acc2 = reinterpret_cast<const i64x2 *>(acc);
+    const f64x2 *z2 = reinterpret_cast<const f64x2 *>(z);
+    for (int j = blockIdx.x * SV_WG + threadIdx.x; j < n2; j += gridDim.x * SV_WG) {
+        const i64x2 a = acc2[j];
+        const f64x2 zz = z2[j];
+        v[0] += ((double)a.x * inv_unit) * zz.x;
+        v[0] += ((double)a.y * inv_unit) * zz.y;
+    }
+    if ((n & 1) && blockIdx.x == 0 && threadIdx.x == 0) v[0] += ((double)acc[n - 1] * inv_unit) * z[n - 1];
     double *const dst[1] = {wz_slot(partials)};
     store_partials<1>(v, dst);
 }
@@ -515,21 +527,49 @@ __global__ void k_cg_step(int n, int i, long long *__restrict__ acc, const doubl
     const double inv_unit = fix_unit(st->acc_exp);
     double v[2] = {0.0, 0.0};
     double m = 0.0;
-    for (int j = blockIdx.x * SV_WG + threadIdx.x; j < n; j += gridDim.x * SV_WG) {
-        const double wj = (double)acc[j] * inv_unit;
-        acc[j] = 0;
-        const double pj = i > 0 ? fma(beta, p[j], z[j]) : z[j];
-        const double sj = i > 0 ? fma(beta, s[j], wj) : wj;
-        p[j] = pj;
-        s[j] = sj;
-        x[j] = fma(alpha, pj, x[j]);
-        const double rj = fma(-alpha, sj, r[j]);
-        r[j] = rj;
-        const double zj = dinv[j] * rj;
-        z[j] = zj;
+    // one DOF: w = acc (cleared), p, s, x, r, z updated; r.z, r.r, max|z| collected
+    auto dof = [&](long long a, double &pj, double &sj, double &xj, double &rj, double dj, double &zj) {
+        const double wj = (double)a * inv_unit;
+        pj = i > 0 ? fma(beta, pj, zj) : zj;
+        sj = i > 0 ? fma(beta, sj, wj) : wj;
+        xj = fma(alpha, pj, xj);
+        rj = fma(-alpha, sj, rj);
+        zj = dj * rj;
         v[0] += rj * zj;
         v[1] += rj * rj;
         m = fmax(m, fabs(zj));
+    };
+    // two DOFs per thread and step, 16-byte accesses (the workspace vectors are 256-byte aligned)
+    const int n2 = n >> 1;
+    for (int j = blockIdx.x * SV_WG + threadIdx.x; j < n2; j += gridDim.x * SV_WG) {
+        const i64x2 a = reinterpret_cast<const i64x2 *>(acc)[j];
+        const f64x2 pv = reinterpret_cast<const f64x2 *>(p)[j];
+        const f64x2 sv = i > 0 ? reinterpret_cast<const f64x2 *>(s)[j] : f64x2{0.0, 0.0};
+        const f64x2 xv = reinterpret_cast<const f64x2 *>(x)[j];
+        const f64x2 rv = reinterpret_cast<const f64x2 *>(r)[j];
+        const f64x2 dv = reinterpret_cast<const f64x2 *>(dinv)[j];
+        const f64x2 zv = reinterpret_cast<const f64x2 *>(z)[j];
+        double pp[2] = {pv.x, pv.y}, ss[2] = {sv.x, sv.y}, xx[2] = {xv.x, xv.y}, rr[2] = {rv.x, rv.y},
+               zz[2] = {zv.x, zv.y};
+        dof(a.x, pp[0], ss[0], xx[0], rr[0], dv.x, zz[0]);
+        dof(a.y, pp[1], ss[1], xx[1], rr[1], dv.y, zz[1]);
+        reinterpret_cast<i64x2 *>(acc)[j] = i64x2{0, 0};
+        reinterpret_cast<f64x2 *>(p)[j] = f64x2{pp[0], pp[1]};
+        reinterpret_cast<f64x2 *>(s)[j] = f64x2{ss[0], ss[1]};
+        reinterpret_cast<f64x2 *>(x)[j] = f64x2{xx[0], xx[1]};
+        reinterpret_cast<f64x2 *>(r)[j] = f64x2{rr[0], rr[1]};
+        reinterpret_cast<f64x2 *>(z)[j] = f64x2{zz[0], zz[1]};
+    }
+    if ((n & 1) && blockIdx.x == 0 && threadIdx.x == 0) {
+        const int j = n - 1;
+        double pj = p[j], sj = i > 0 ? s[j] : 0.0, xj = x[j], rj = r[j], zj = z[j];
+        dof(acc[j], pj, sj, xj, rj, dinv[j], zj);
+        acc[j] = 0;
+        p[j] = pj;
+        s[j] = sj;
+        x[j] = xj;
+        r[j] = rj;
+        z[j] = zj;
     }
     double *const dst[2] = {slot(partials, (i + 1) & 1, 0), slot(partials, (i + 1) & 1, 1)};
     store_partials<2>(v, dst);
