@@ -50,7 +50,7 @@ typedef enum {
     SPMV_ERR_INVALID_MATRIX = 2,  /* row_ptr not monotone / inconsistent, column out of range */
     SPMV_ERR_UNSORTED = 3,        /* MACKO input: columns not strictly increasing in a row */
     SPMV_ERR_OVERFLOW = 4,        /* a count does not fit int32 */
-    SPMV_ERR_UNSUPPORTED = 5,     /* valid request this build does not support */
+    SPMV_ERR_UNSUPPORTED = 5,     /* valid request the library does not support */
     SPMV_ERR_HIP = 6              /* a HIP runtime call failed */
 } spmv_status;
 
