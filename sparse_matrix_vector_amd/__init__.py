@@ -25,7 +25,8 @@ __all__ = [
     "spmv_scratch_size", "spmv_csr_row_stats", "spmv_format_recommend", "spmv_csr_plan_size", "spmv_csr_create",
     "spmv_csr_apply", "spmv_csr_get_plan", "spmv_csr_info", "spmv_csr_destroy",
     "spmv_ell_from_csr", "spmv_ell_apply", "macko_encode_size", "macko_encode", "macko_spmv",
-    "macko_quantize_i8", "macko_spmv_i8", "macko_decode_columns", "dense_gemv_f16", "fem_matvec_apply", "fem_threestage_size",
+    "macko_quantize_i8", "macko_spmv_i8", "macko_decode_columns", "dense_gemv_f16", "fem_matvec_apply", "fem_threestage_size", "fem_blocks_size", "fem_blocks_plan_host", "FEBlocks",
+    "fem_blocks_create", "fem_blocks_apply", "fem_blocks_info", "fem_blocks_destroy",
     "fem_matvec_threestage", "fem_matvec_threestage_noalloc", "spmv_stream_copy", "spmv_stream_read",
     "fem_assemble_size", "fem_assemble_pattern", "fem_assemble_values", "fem_assemble_csr",
     "fem_jacobi_diagonal", "fem_solver_workspace_size", "fem_pcg_solve",
@@ -563,6 +564,98 @@ def fem_matvec_apply(n_elem, n_dof, edof, rho, penalty, Ke, alpha, x, beta, y, s
     _call("fem_matvec_apply", int(n_elem), int(n_dof), _dev(edof, _i32_dtype(), "edof"),
           _dev(rho, _f32_dtype(), "rho"), int(penalty), _dev(Ke, _f32_dtype(), "Ke"), float(alpha),
           _dev(x, _f32_dtype(), "x"), float(beta), _dev(y, _f32_dtype(), "y"), _stream(stream, y))
+
+
+def fem_blocks_size(n_elem, n_dof) -> int:
+    out = ctypes.c_size_t()
+    _call("fem_blocks_size", int(n_elem), int(n_dof), ctypes.byref(out))
+    return out.value
+
+
+def fem_blocks_plan_host(n_elem, n_dof, edof, group=0):
+    """The element-block plan from a host (NumPy) edof: a dict of NumPy
+    arrays (blk_elem_off, perm, blk_dof_off, ldof, ldst, cend, lidx, lpos,
+    shr_ptr, shr_dof, shr_cnt) and the counts.  group: 0 (3 when the numbering has
+    the node structure, else 1), 1 or 3.  For inspection and tests."""
+    import numpy as np
+    E, n = int(n_elem), int(n_dof)
+    ed = np.ascontiguousarray(edof, dtype=np.int32).reshape(-1)
+    counts = np.zeros(8, np.int32)
+    ent = max(24 * E, 1)
+    names = ("blk_elem_off", "perm", "blk_dof_off", "ldof", "ldst", "cend", "lidx", "lpos", "shr_ptr", "shr_dof",
+             "shr_cnt")
+    a = {"blk_elem_off": np.zeros(E + 1, np.int32), "perm": np.zeros(max(E, 1), np.int32),
+         "blk_dof_off": np.zeros(E + 1, np.int32), "ldof": np.zeros(ent, np.int32), "ldst": np.zeros(ent, np.int32),
+         "cend": np.zeros(ent, np.uint16), "lidx": np.zeros(ent, np.uint16), "lpos": np.zeros(ent, np.uint16),
+         "shr_ptr": np.zeros(n + 1, np.int32), "shr_dof": np.zeros(max(n, 1), np.int32),
+         "shr_cnt": np.zeros(max(n, 1), np.int32)}
+    _call("fem_blocks_plan_host", E, n, ed.ctypes.data, int(group), counts.ctypes.data,
+          *[a[k].ctypes.data for k in names])
+    nb, sum_l, n_sh, n_slots, lmax, pmax, G, planes = (int(c) for c in counts)
+    U = 24 // G
+    return {"group": G, "n_blocks": nb, "Lmax": lmax, "Pmax": pmax, "n_slots": n_slots, "planes": planes,
+            "blk_elem_off": a["blk_elem_off"][:nb + 1], "perm": a["perm"][:E],
+            "blk_dof_off": a["blk_dof_off"][:nb + 1], "ldof": a["ldof"][:sum_l], "ldst": a["ldst"][:sum_l],
+            "cend": a["cend"][:sum_l], "lidx": a["lidx"][:U * E], "lpos": a["lpos"][:U * E],
+            "shr_ptr": a["shr_ptr"][:n_sh + 1], "shr_dof": a["shr_dof"][:n_sh], "shr_cnt": a["shr_cnt"][:n_sh]}
+
+
+def fem_blocks_create(n_elem, n_dof, edof, workspace, stream=None, group=0):
+    """Opaque handle (int) of the element-block plan, kept in `workspace` (a
+    CUDA uint8 tensor of at least fem_blocks_size() bytes); group as for
+    fem_blocks_plan_host."""
+    h = ctypes.c_void_p()
+    _call("fem_blocks_create", ctypes.byref(h), int(n_elem), int(n_dof), _dev(edof, _i32_dtype(), "edof"), int(group),
+          workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream, edof))
+    return h.value
+
+
+def fem_blocks_apply(handle, rho, penalty, Ke, alpha, x, beta, y, stream=None):
+    _call("fem_blocks_apply", handle, _dev(rho, _f32_dtype(), "rho"), int(penalty), _dev(Ke, _f32_dtype(), "Ke"),
+          float(alpha), _dev(x, _f32_dtype(), "x"), float(beta), _dev(y, _f32_dtype(), "y"), _stream(stream, y))
+    return y
+
+
+def fem_blocks_info(handle):
+    import numpy as np
+    c = np.zeros(6, np.int32)
+    _call("fem_blocks_info", handle, c.ctypes.data)
+    return {"n_blocks": int(c[0]), "Lmax": int(c[1]), "n_shared": int(c[2]), "Pmax": int(c[3]), "group": int(c[4]),
+            "planes": int(c[5])}
+
+
+def fem_blocks_destroy(handle):
+    _call("fem_blocks_destroy", handle)
+
+
+class FEBlocks:
+    """The element-block plan of one mesh (edof: a device int32 tensor of
+    n_elem * 24 entries), built once; apply() runs the two-kernel matvec.
+    group: 0 (per node when the numbering allows it), 1 or 3."""
+
+    def __init__(self, n_elem, n_dof, edof, stream=None, group=0):
+        import torch
+        self.n_elem, self.n_dof = int(n_elem), int(n_dof)
+        self.workspace = torch.empty(max(fem_blocks_size(n_elem, n_dof), 256), dtype=torch.uint8,
+                                     device=edof.device)
+        self.handle = fem_blocks_create(n_elem, n_dof, edof, self.workspace, stream, group)
+
+    def info(self):
+        return fem_blocks_info(self.handle)
+
+    def apply(self, rho, penalty, Ke, alpha, x, beta, y, stream=None):
+        return fem_blocks_apply(self.handle, rho, penalty, Ke, alpha, x, beta, y, stream)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            fem_blocks_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def fem_threestage_size(n_elem) -> int:

@@ -61,6 +61,12 @@ SIGNATURES = {
     "dense_gemv_f16": [c_i32, c_i32, vp, vp, c_f32, c_f32, vp, vp],
     "fem_matvec_apply": [c_i32, c_i32, vp, vp, c_i32, vp, c_f32, vp, c_f32, vp, vp],
     "fem_threestage_size": [c_i32, P_sz],
+    "fem_blocks_size": [c_i32, c_i32, P_sz],
+    "fem_blocks_create": [vp, c_i32, c_i32, vp, c_i32, vp, c_sz, vp],
+    "fem_blocks_apply": [vp, vp, c_i32, vp, c_f32, vp, c_f32, vp, vp],
+    "fem_blocks_info": [vp, vp],
+    "fem_blocks_destroy": [vp],
+    "fem_blocks_plan_host": [c_i32, c_i32, vp, c_i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
     "fem_matvec_threestage": [c_i32, c_i32, vp, vp, c_i32, vp, c_f32, vp, c_f32, vp, vp, c_sz, vp],
     "fem_matvec_threestage_noalloc": [c_i32, c_i32, vp, vp, c_i32, vp, c_f32, vp, c_f32, vp, vp],
     "fem_assemble_size": [c_i32, c_i32, P_sz],
