@@ -840,6 +840,7 @@ SUITE = [
     ("pruned90", "macko", 60.0, None),
     ("pruned50", "dense", None, "dense fp16 GEMV comparator of the MACKO configs (same W densified)"),
     ("fe", "fem", None, "fused FE matvec: parity config, atomic-bound, no % target"),
+    ("fe", "fem-blocks", None, "element-block FE matvec: plan built once per copy, no atomics, fixed-order sums"),
     ("fe", "fem-3stage", None, "unfused three-stage comparator of the fused FE matvec"),
     ("fe", "fem-csr", None, "the assembled K (53.1M nonzeros, built on the GPU) through the binned CSR path"),
 ]

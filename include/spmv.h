@@ -396,7 +396,7 @@ spmv_status fem_matvec_apply(int32_t n_elem, int32_t n_dof, const int32_t *edof,
  * Same operator and arguments as fem_matvec_apply; the result agrees with it
  * up to the order of additions.
  *   fem_blocks_size: device workspace bytes for the shape (an upper bound,
- *     about 450 bytes per element + 44 per DOF).
+ *     about 500 bytes per element + 44 per DOF).
  *   fem_blocks_create: copies edof (device) to the host, builds the plan and
  *     uploads it into `workspace` (device, 256-byte aligned, >= the size,
  *     kept until destroy).  group: 0 picks 3 when the numbering allows it,
@@ -406,25 +406,27 @@ spmv_status fem_matvec_apply(int32_t n_elem, int32_t n_dof, const int32_t *edof,
  *     Ke as for fem_matvec_apply.  Two launches.  Asynchronous; calls that
  *     overlap on one plan race on its partial sums.
  *   fem_blocks_info: counts[0] blocks, [1] most local units of a block, [2]
- *     units finished by the second kernel, [3] most products of a block,
+ *     units finished by the second kernel, [3] largest product buffer of a
+ *     block (products and padding words),
  *     [4] G, [5] rank planes of the partial sums.
  *   fem_blocks_plan_host: the same plan from a host edof into host buffers
  *     (NULL buffers are skipped).  Upper-bound sizes: blk_elem_off,
- *     blk_dof_off n_elem + 1; perm n_elem; ldof, ldst, cend, lidx, lpos
+ *     blk_dof_off n_elem + 1; perm n_elem; ldof, ldst, crun, lidx, lpos
  *     24 n_elem; shr_ptr n_dof + 1; shr_dof, shr_cnt n_dof.  Per block b:
  *     elements perm[blk_elem_off[b] ..], local units at blk_dof_off[b] + l
  *     with first DOF ldof (increasing), destination ldst of the first
  *     component (the DOF itself if private, else ~slot; component c at that
- *     + c) and run end cend (the run starts at the previous local unit's end,
- *     or 0); lidx / lpos [k * (24 / G) + j]: local unit and product position
+ *     + c) and its run crun = start | end << 16 in the block's product
+ *     buffer (runs in local-unit order, a run of even length followed by
+ *     one unused word); lidx / lpos [k * (24 / G) + j]: local unit and product position
  *     of entry j of the block list's k-th element (0xFFFF where constrained;
  *     component c of the entry at lpos + c).  Second-kernel units shr_dof
  *     (first DOF, increasing), each touched by shr_cnt blocks; the partial
  *     sum of the r-th of them sits, for r < planes, at slot
  *     (r * n_shared + i) * G, else at planes * n_shared * G + shr_ptr[i] +
  *     (r - planes) * G.  counts = {blocks, local units in all, second-kernel
- *     units, slots, most local units of a block, most products of a block,
- *     G, planes}.  For inspection and tests. */
+ *     units, slots, most local units of a block, largest product buffer of a
+ *     block, G, planes}.  For inspection and tests. */
 typedef struct fem_blocks *fem_blocks_t;
 spmv_status fem_blocks_size(int32_t n_elem, int32_t n_dof, size_t *bytes);
 spmv_status fem_blocks_create(fem_blocks_t *plan, int32_t n_elem, int32_t n_dof, const int32_t *edof,
@@ -436,7 +438,7 @@ spmv_status fem_blocks_destroy(fem_blocks_t plan);
 spmv_status fem_blocks_plan_host(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t group,
                                  int32_t *counts,
                                  int32_t *blk_elem_off, int32_t *perm, int32_t *blk_dof_off, int32_t *ldof,
-                                 int32_t *ldst, uint16_t *cend, uint16_t *lidx, uint16_t *lpos,
+                                 int32_t *ldst, uint32_t *crun, uint16_t *lidx, uint16_t *lpos,
                                  int32_t *shr_ptr, int32_t *shr_dof, int32_t *shr_cnt);
 
 /* Workspace bytes of the three-stage comparator (2 * n_elem * 24 floats). */

@@ -574,7 +574,7 @@ def fem_blocks_size(n_elem, n_dof) -> int:
 
 def fem_blocks_plan_host(n_elem, n_dof, edof, group=0):
     """The element-block plan from a host (NumPy) edof: a dict of NumPy
-    arrays (blk_elem_off, perm, blk_dof_off, ldof, ldst, cend, lidx, lpos,
+    arrays (blk_elem_off, perm, blk_dof_off, ldof, ldst, crun, lidx, lpos,
     shr_ptr, shr_dof, shr_cnt) and the counts.  group: 0 (3 when the numbering has
     the node structure, else 1), 1 or 3.  For inspection and tests."""
     import numpy as np
@@ -582,11 +582,11 @@ def fem_blocks_plan_host(n_elem, n_dof, edof, group=0):
     ed = np.ascontiguousarray(edof, dtype=np.int32).reshape(-1)
     counts = np.zeros(8, np.int32)
     ent = max(24 * E, 1)
-    names = ("blk_elem_off", "perm", "blk_dof_off", "ldof", "ldst", "cend", "lidx", "lpos", "shr_ptr", "shr_dof",
+    names = ("blk_elem_off", "perm", "blk_dof_off", "ldof", "ldst", "crun", "lidx", "lpos", "shr_ptr", "shr_dof",
              "shr_cnt")
     a = {"blk_elem_off": np.zeros(E + 1, np.int32), "perm": np.zeros(max(E, 1), np.int32),
          "blk_dof_off": np.zeros(E + 1, np.int32), "ldof": np.zeros(ent, np.int32), "ldst": np.zeros(ent, np.int32),
-         "cend": np.zeros(ent, np.uint16), "lidx": np.zeros(ent, np.uint16), "lpos": np.zeros(ent, np.uint16),
+         "crun": np.zeros(ent, np.uint32), "lidx": np.zeros(ent, np.uint16), "lpos": np.zeros(ent, np.uint16),
          "shr_ptr": np.zeros(n + 1, np.int32), "shr_dof": np.zeros(max(n, 1), np.int32),
          "shr_cnt": np.zeros(max(n, 1), np.int32)}
     _call("fem_blocks_plan_host", E, n, ed.ctypes.data, int(group), counts.ctypes.data,
@@ -596,7 +596,7 @@ def fem_blocks_plan_host(n_elem, n_dof, edof, group=0):
     return {"group": G, "n_blocks": nb, "Lmax": lmax, "Pmax": pmax, "n_slots": n_slots, "planes": planes,
             "blk_elem_off": a["blk_elem_off"][:nb + 1], "perm": a["perm"][:E],
             "blk_dof_off": a["blk_dof_off"][:nb + 1], "ldof": a["ldof"][:sum_l], "ldst": a["ldst"][:sum_l],
-            "cend": a["cend"][:sum_l], "lidx": a["lidx"][:U * E], "lpos": a["lpos"][:U * E],
+            "crun": a["crun"][:sum_l], "lidx": a["lidx"][:U * E], "lpos": a["lpos"][:U * E],
             "shr_ptr": a["shr_ptr"][:n_sh + 1], "shr_dof": a["shr_dof"][:n_sh], "shr_cnt": a["shr_cnt"][:n_sh]}
 
 

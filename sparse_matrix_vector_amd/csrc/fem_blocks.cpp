@@ -15,9 +15,11 @@
 //     16-bit local indices;
 //   - each element entry gets a 16-bit position in the block's product
 //     buffer, so that the entries of one local unit form a run (ordered by
-//     element, then by the element's entry, G products each): the apply
-//     then sums each run in a fixed order instead of adding into shared
-//     memory with atomics;
+//     element, then by the element's entry, G products each; a run of even
+//     length is followed by one unused word, which keeps the lanes that sum
+//     neighbouring runs on different LDS banks): the apply then sums each
+//     run in a fixed order instead of adding into shared memory with
+//     atomics;
 //   - a unit whose elements all lie in one block is private to it: the block
 //     writes y there with plain stores.  Every other unit (shared by several
 //     blocks, or touched by none) is finished by a second kernel that adds
@@ -167,12 +169,10 @@ bool fb_plan_build(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t g
                 const int32_t u = unit_of(P.perm[k], j);
                 if (u >= 0) loc.push_back(u);
             }
-        const int32_t products = G * (int32_t)loc.size();
         std::sort(loc.begin(), loc.end());
         loc.erase(std::unique(loc.begin(), loc.end()), loc.end());
-        if ((int)loc.size() > FB_NONE || products > FB_NONE) return false;   // cannot happen: at most 256 * 24
+        if ((int)loc.size() > FB_NONE) return false;   // cannot happen: at most 256 * 24
         P.Lmax = std::max<int32_t>(P.Lmax, (int32_t)loc.size());
-        P.Pmax = std::max<int32_t>(P.Pmax, products);
         run.assign(loc.size(), 0);
         for (int32_t k = k0; k < k1; ++k)
             for (int j = 0; j < U; ++j) {
@@ -182,7 +182,7 @@ bool fb_plan_build(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t g
                 P.lidx[(size_t)k * U + j] = (uint16_t)l;
                 ++run[l];
             }
-        int32_t at = 0;   // run l starts where run l - 1 ends
+        int32_t at = 0;   // run l starts after run l - 1 and its padding word, if any
         for (size_t l = 0; l < loc.size(); ++l) {
             const int32_t u = loc[l];
             P.ldof.push_back(G * u);
@@ -192,9 +192,11 @@ bool fb_plan_build(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t g
                 P.ldst.push_back(~slot_of(u, rank[u]++));   // blocks come in increasing order
             const int32_t c = G * run[l];
             run[l] = at;   // next free position in the run
-            at += c;
-            P.cend.push_back((uint16_t)at);
+            P.crun.push_back((uint32_t)at | (uint32_t)(at + c) << 16);
+            at += c + (c % 2 == 0 ? 1 : 0);
         }
+        if (at > FB_NONE) return false;   // cannot happen: at most 256 * 24 products and as many pads
+        P.Pmax = std::max<int32_t>(P.Pmax, at);
         for (int32_t k = k0; k < k1; ++k)
             for (int j = 0; j < U; ++j) {
                 const uint16_t l = P.lidx[(size_t)k * U + j];
@@ -214,7 +216,7 @@ using namespace spmv;
 
 extern "C" spmv_status fem_blocks_plan_host(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t group,
                                             int32_t *counts, int32_t *blk_elem_off, int32_t *perm,
-                                            int32_t *blk_dof_off, int32_t *ldof, int32_t *ldst, uint16_t *cend,
+                                            int32_t *blk_dof_off, int32_t *ldof, int32_t *ldst, uint32_t *crun,
                                             uint16_t *lidx, uint16_t *lpos, int32_t *shr_ptr, int32_t *shr_dof,
                                             int32_t *shr_cnt) {
     if (n_elem < 0 || n_dof < 0 || !counts) return fail(SPMV_ERR_INVALID_VALUE, "bad size or NULL counts");
@@ -243,7 +245,7 @@ extern "C" spmv_status fem_blocks_plan_host(int32_t n_elem, int32_t n_dof, const
     put(blk_dof_off, P.blk_dof_off);
     put(ldof, P.ldof);
     put(ldst, P.ldst);
-    put(cend, P.cend);
+    put(crun, P.crun);
     put(lidx, P.lidx);
     put(lpos, P.lpos);
     put(shr_ptr, P.shr_ptr);

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(FB_BLOCK) void k_fe_block(const int *__restrict__ b
                                                       const int *__restrict__ perm,
                                                       const int *__restrict__ blk_dof_off,
                                                       const int *__restrict__ ldof, const int *__restrict__ ldst,
-                                                      const uint16_t *__restrict__ cend,
+                                                      const unsigned *__restrict__ crun,
                                                       const uint16_t *__restrict__ lidx,
                                                       const uint16_t *__restrict__ lpos, int Lmax,
                                                       const float *__restrict__ rho, int penalty,
@@ -104,9 +104,9 @@ __global__ __launch_bounds__(FB_BLOCK) void k_fe_block(const int *__restrict__ b
             const int l = min(j * FB_BLOCK + t, L - 1);
             g[j] = ldof[d0 + l];
             dst[j] = ldst[d0 + l];
-            c1[j] = cend[d0 + l];
-            const int q = cend[d0 + max(l - 1, 0)];
-            c0[j] = l > 0 ? q : 0;
+            const unsigned q = crun[d0 + l];
+            c0[j] = q & 0xFFFFu;
+            c1[j] = q >> 16;
         }
         float xv[PER][G];
 #pragma unroll
@@ -175,7 +175,10 @@ __global__ __launch_bounds__(FB_BLOCK) void k_fe_block(const int *__restrict__ b
 #pragma unroll
     for (int j = 0; j < PER; ++j)
         if (j * FB_BLOCK + t < L) put(dst[j], c0[j], c1[j]);
-    for (int l = PER * FB_BLOCK + t; l < L; l += FB_BLOCK) put(ldst[d0 + l], cend[d0 + l - 1], cend[d0 + l]);
+    for (int l = PER * FB_BLOCK + t; l < L; l += FB_BLOCK) {
+        const unsigned q = crun[d0 + l];
+        put(ldst[d0 + l], q & 0xFFFFu, q >> 16);
+    }
 }
 
 // y = beta y + the unit's partial sums (G per block, in increasing block
@@ -224,7 +227,7 @@ size_t fb_align(size_t v) { return (v + 255) & ~size_t(255); }
 // take at most FB_PLANES planes of n_dof + 2 words plus one overflow slot
 // per local unit).
 struct FbLayout {
-    size_t blk_elem_off, perm, blk_dof_off, ldof, ldst, cend, lidx, lpos, slots, shr_ptr, shr_dof, shr_cnt, total;
+    size_t blk_elem_off, perm, blk_dof_off, ldof, ldst, crun, lidx, lpos, slots, shr_ptr, shr_dof, shr_cnt, total;
 };
 
 FbLayout fb_layout(int64_t E, int64_t n) {
@@ -241,7 +244,7 @@ FbLayout fb_layout(int64_t E, int64_t n) {
     L.blk_dof_off = take(4 * ((size_t)E + 1));
     L.ldof = take(4 * ent);
     L.ldst = take(4 * ent);
-    L.cend = take(2 * ent);
+    L.crun = take(4 * ent);
     L.lidx = take(2 * ent);
     L.lpos = take(2 * ent);
     L.slots = take(4 * (ent + (size_t)FB_PLANES * ((size_t)n + 2)));
@@ -267,7 +270,8 @@ struct fem_blocks {
     int32_t n_elem = 0, n_dof = 0, group = 1, n_blocks = 0, Lmax = 0, Pmax = 0, n_shared = 0, planes = 0;
     int32_t *blk_elem_off = nullptr, *perm = nullptr, *blk_dof_off = nullptr, *ldof = nullptr, *ldst = nullptr;
     int32_t *shr_ptr = nullptr, *shr_dof = nullptr, *shr_cnt = nullptr;
-    uint16_t *cend = nullptr, *lidx = nullptr, *lpos = nullptr;
+    uint32_t *crun = nullptr;
+    uint16_t *lidx = nullptr, *lpos = nullptr;
     float *slots = nullptr;
 };
 
@@ -319,7 +323,7 @@ extern "C" spmv_status fem_blocks_create(fem_blocks_t *out, int32_t n_elem, int3
     h->blk_dof_off = reinterpret_cast<int32_t *>(ws + L.blk_dof_off);
     h->ldof = reinterpret_cast<int32_t *>(ws + L.ldof);
     h->ldst = reinterpret_cast<int32_t *>(ws + L.ldst);
-    h->cend = reinterpret_cast<uint16_t *>(ws + L.cend);
+    h->crun = reinterpret_cast<uint32_t *>(ws + L.crun);
     h->lidx = reinterpret_cast<uint16_t *>(ws + L.lidx);
     h->lpos = reinterpret_cast<uint16_t *>(ws + L.lpos);
     h->slots = reinterpret_cast<float *>(ws + L.slots);
@@ -338,7 +342,7 @@ extern "C" spmv_status fem_blocks_create(fem_blocks_t *out, int32_t n_elem, int3
     chk(put(h->blk_dof_off, P.blk_dof_off.data(), P.blk_dof_off.size() * 4));
     chk(put(h->ldof, P.ldof.data(), P.ldof.size() * 4));
     chk(put(h->ldst, P.ldst.data(), P.ldst.size() * 4));
-    chk(put(h->cend, P.cend.data(), P.cend.size() * 2));
+    chk(put(h->crun, P.crun.data(), P.crun.size() * 4));
     chk(put(h->lidx, P.lidx.data(), P.lidx.size() * 2));
     chk(put(h->lpos, P.lpos.data(), P.lpos.size() * 2));
     chk(put(h->shr_ptr, P.shr_ptr.data(), P.shr_ptr.size() * 4));
@@ -369,11 +373,11 @@ extern "C" spmv_status fem_blocks_apply(fem_blocks_t h, const float *rho, int32_
         const size_t lds = sizeof(float) * ((size_t)h->group * lmax + pmax);
         if (h->group == 3)
             k_fe_block<3><<<h->n_blocks, FB_BLOCK, lds, st>>>(h->blk_elem_off, h->perm, h->blk_dof_off, h->ldof,
-                                                             h->ldst, h->cend, h->lidx, h->lpos, lmax, rho, penalty,
+                                                             h->ldst, h->crun, h->lidx, h->lpos, lmax, rho, penalty,
                                                              Ke, alpha, x, beta, y, h->slots);
         else
             k_fe_block<1><<<h->n_blocks, FB_BLOCK, lds, st>>>(h->blk_elem_off, h->perm, h->blk_dof_off, h->ldof,
-                                                             h->ldst, h->cend, h->lidx, h->lpos, lmax, rho, penalty,
+                                                             h->ldst, h->crun, h->lidx, h->lpos, lmax, rho, penalty,
                                                              Ke, alpha, x, beta, y, h->slots);
         SPMV_LAUNCHED("k_fe_block");
     }

@@ -25,8 +25,10 @@ constexpr uint16_t FB_NONE = 0xFFFF;          // local index / position of a con
 //   local units l = 0..L-1 at blk_dof_off[b] + l: first DOF ldof (increasing),
 //     destination ldst of the first component (the DOF itself when every
 //     element on the unit lies in this block, else ~slot; component c goes
-//     to that + c), and cend, the end of the unit's run in the block's
-//     product buffer (its start is the previous local unit's cend, or 0)
+//     to that + c), and crun = start | end << 16, the unit's run in the
+//     block's product buffer (runs follow the local units; a run of even
+//     length is followed by one unused word, so that neighbouring lanes
+//     summing neighbouring runs read different LDS banks)
 //   lidx[k * U + j]: local unit of entry j of element k
 //   lpos[k * U + j]: where that entry's G products go in the block's product
 //     buffer (component c at lpos + c): a unit's run holds its entries in
@@ -39,13 +41,15 @@ constexpr uint16_t FB_NONE = 0xFFFF;          // local index / position of a con
 // units and the second kernel reading unit after unit both touch
 // consecutive words; ranks r >= planes (only when a unit lies in more than
 // FB_PLANES blocks) at planes * n_shared * G + shr_ptr[i] + (r - planes) * G + c.
-// Lmax: the most local units of a block; Pmax: the most products of one.
+// Lmax: the most local units of a block; Pmax: the largest product buffer
+// of one (products and padding words).
 constexpr int FB_PLANES = 8;   // most rank planes of the partial sums (a hexahedral node lies in <= 8 blocks)
 
 struct FbPlanHost {
     int32_t group = 1, n_blocks = 0, Lmax = 0, Pmax = 0, planes = 0, n_slots = 0;
     std::vector<int32_t> blk_elem_off, perm, blk_dof_off, ldof, ldst, shr_ptr, shr_dof, shr_cnt;
-    std::vector<uint16_t> cend, lidx, lpos;
+    std::vector<uint32_t> crun;
+    std::vector<uint16_t> lidx, lpos;
 };
 
 // True when every element corner is three constrained DOFs or the three DOFs

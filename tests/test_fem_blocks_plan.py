@@ -10,8 +10,9 @@ its destination is the DOF itself; the private DOFs and the second kernel's
 DOFs partition all DOFs (untouched DOFs go to the second kernel); each
 second-kernel DOF owns one slot per block that touches it, numbered in
 increasing block order, and each of those blocks writes its own slot; the
-product positions of a block are a permutation of its products, each local
-DOF's run holds exactly its entries in (element, DOF) order; and the product
+product positions of a block fill its runs, each local unit's run holds
+exactly its entries in (element, entry) order and is followed by a padding
+word when its length is even; and the product
 rebuilt from these arrays equals the oracle within the FE tolerance.
 """
 import numpy as np
@@ -45,7 +46,8 @@ def _check(ed, n_dof, group=0):
     U = 24 // G
     nb = P["n_blocks"]
     beo, perm, bdo = P["blk_elem_off"], P["perm"], P["blk_dof_off"]
-    g, dst, cend = P["ldof"].astype(np.int64), P["ldst"].astype(np.int64), P["cend"].astype(np.int64)
+    g, dst = P["ldof"].astype(np.int64), P["ldst"].astype(np.int64)
+    starts, ends = (P["crun"] & 0xFFFF).astype(np.int64), (P["crun"] >> 16).astype(np.int64)
     # unit of each element entry (the entry's first DOF / G), -1 if constrained
     first = ed.reshape(E, U, G)[:, :, 0].astype(np.int64)
     unit = np.where((first >= 0) & (first < n_dof), first // G, -1)
@@ -75,14 +77,16 @@ def _check(ed, n_dof, group=0):
         assert np.all((L[rows] == NONE) == ~valid) and np.all((Q[rows] == NONE) == ~valid)
         assert np.array_equal(loc[L[rows][valid]] // G, up[rows][valid])
         li, q = L[rows][valid], Q[rows][valid]   # flattened in (element, entry) order
-        n_p = G * len(li)
-        assert np.array_equal(np.sort(q), np.arange(0, n_p, G))
-        ends = cend[bdo[b]:bdo[b + 1]]
-        starts = np.concatenate([[0], ends[:-1]])
-        assert len(ends) == 0 or ends[-1] == n_p
+        # runs in local-unit order, each followed by one padding word when its
+        # length is even, starting at 0; each holds its unit's entries
+        s_b, e_b = starts[bdo[b]:bdo[b + 1]], ends[bdo[b]:bdo[b + 1]]
+        size = 0
         for l in range(len(loc)):
-            assert np.array_equal(q[li == l], np.arange(starts[l], ends[l], G)), (b, l)
-        lmax, pmax = max(lmax, len(loc)), max(pmax, n_p)
+            assert s_b[l] == size
+            assert np.array_equal(q[li == l], np.arange(s_b[l], e_b[l], G)), (b, l)
+            size = e_b[l] + (1 if (e_b[l] - s_b[l]) % 2 == 0 else 0)
+        assert G * len(li) == (e_b - s_b).sum()
+        lmax, pmax = max(lmax, len(loc)), max(pmax, size)
     assert P["Lmax"] == lmax and P["Pmax"] == pmax
     # private units against the set of blocks per unit
     n_units = (n_dof + G - 1) // G
@@ -121,7 +125,8 @@ def _emulate(P, ed, n_dof, rho, Ke, x, alpha, beta, y_in, penalty=3):
     G = P["group"]
     U = 24 // G
     beo, perm, bdo = P["blk_elem_off"], P["perm"], P["blk_dof_off"]
-    g, dst, cend = P["ldof"].astype(np.int64), P["ldst"].astype(np.int64), P["cend"].astype(np.int64)
+    g, dst = P["ldof"].astype(np.int64), P["ldst"].astype(np.int64)
+    starts, ends = (P["crun"] & 0xFFFF).astype(np.int64), (P["crun"] >> 16).astype(np.int64)
     slots = np.zeros(P["n_slots"])
     y = np.array(y_in, np.float64) if beta != 0 else np.zeros(n_dof)
     Kd = Ke.astype(np.float64).reshape(24, 24)
@@ -142,7 +147,7 @@ def _emulate(P, ed, n_dof, rho, Ke, x, alpha, beta, y_in, penalty=3):
         for l in range(len(loc)):
             j = bdo[b] + l
             v = np.zeros(G)
-            for q in range(cend[j - 1] if l > 0 else 0, cend[j], G):
+            for q in range(starts[j], ends[j], G):
                 v += pb[q:q + G]
             for c in range(G):
                 if dst[j] >= 0:
@@ -260,15 +265,18 @@ def test_plan_edge_cases():
     P = S.fem_blocks_plan_host(1, 6, ed, 1)
     assert P["group"] == 1 and len(P["ldof"]) == 6
     assert np.array_equal(P["lidx"].astype(np.int64), ed.astype(np.int64))
-    # ... and each local DOF's run holds its four entries in DOF order
-    assert list(P["cend"]) == [4, 8, 12, 16, 20, 24] and P["Pmax"] == 24
-    assert np.array_equal(P["lpos"].astype(np.int64), 4 * (ed % 6) + np.arange(24) // 6)
+    # ... and each local DOF's run holds its four entries in DOF order, each
+    # run of four followed by a padding word
+    assert list(P["crun"] & 0xFFFF) == [0, 5, 10, 15, 20, 25] and list(P["crun"] >> 16) == [4, 9, 14, 19, 24, 29]
+    assert P["Pmax"] == 30
+    assert np.array_equal(P["lpos"].astype(np.int64), 5 * (ed % 6) + np.arange(24) // 6)
     # the same with whole nodes (the automatic choice): two nodes, each on
     # four corners
     P = S.fem_blocks_plan_host(1, 6, ed)
-    assert P["group"] == 3 and list(P["ldof"]) == [0, 3] and list(P["cend"]) == [12, 24]
+    assert P["group"] == 3 and list(P["ldof"]) == [0, 3]
+    assert list(P["crun"] & 0xFFFF) == [0, 13] and list(P["crun"] >> 16) == [12, 25] and P["Pmax"] == 26
     assert np.array_equal(P["lidx"].astype(np.int64), np.arange(8) % 2)
-    assert np.array_equal(P["lpos"].astype(np.int64), 12 * (np.arange(8) % 2) + 3 * (np.arange(8) // 2))
+    assert np.array_equal(P["lpos"].astype(np.int64), 13 * (np.arange(8) % 2) + 3 * (np.arange(8) // 2))
     # bad group
     with pytest.raises(S.SpmvError):
         S.fem_blocks_plan_host(1, 6, ed, 2)
