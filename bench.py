@@ -291,7 +291,11 @@ class Workload:
                     return (lambda: S.fem_matvec_apply(*a, self.alpha, x, self.beta, y)), y, None
                 return (lambda: S.fem_matvec_threestage(*a, self.alpha, x, self.beta, y, ws)), y, None
             self._setup((dev(M.edof.reshape(-1)), dev(M.rho), dev(M.Ke.reshape(-1)), dev(M.x)), make, copies)
-            self.shape = {"n_elem": M.n_elem, "n_dof": M.n_dof, "atomics": int((M.edof >= 0).sum())}
+            self.shape = {"n_elem": M.n_elem, "n_dof": M.n_dof}
+            if path in ("fem", "fem-3stage"):
+                self.shape["atomics"] = int((M.edof >= 0).sum())
+            elif path == "fem-blocks":
+                self.shape["plan"] = self.extra[0].info()
         else:
             raise SystemExit(f"unknown config {config}")
         torch.cuda.synchronize()

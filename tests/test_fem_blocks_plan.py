@@ -238,6 +238,30 @@ def test_plan_partial_sums_past_the_rank_planes(group):
     assert_close(y, yr, sc, TAU_F32, f"hub node, G={group}")
 
 
+def _chain_mesh(E=600):
+    """Elements in a chain, each sharing one node with the next: a block of
+    256 holds ~1,800 nodes (~5,400 DOFs), more local units than a lane's
+    registers stage, so the apply's remainder loops run."""
+    M = gen.fe_mesh(1, 1, 1, clamp_x0=False, seed=5)
+    nodes = 7 * np.arange(E)[:, None] + np.arange(8)[None, :]
+    ed = (3 * nodes[:, :, None] + np.arange(3)[None, None, :]).reshape(E, 24).astype(np.int32)
+    n = 3 * (7 * E + 1)
+    rng = np.random.default_rng(11)
+    rho = rng.uniform(0.1, 1.0, E).astype(np.float32)
+    x = rng.uniform(-1, 1, n).astype(np.float32)
+    return M.Ke, ed, n, rho, x
+
+
+@pytest.mark.parametrize("group", [1, 3])
+def test_plan_long_blocks(group):
+    Ke, ed, n, rho, x = _chain_mesh()
+    P = _check(ed, n, group)
+    assert P["Lmax"] > (1792 if group == 1 else 768)
+    y = _emulate(P, ed, n, rho, Ke, x, 1.0, 0.0, None)
+    yr, sc = oracle.fe_matvec(ed, rho, Ke, x, n)
+    assert_close(y, yr, sc, TAU_F32, f"chain, G={group}")
+
+
 def test_plan_blocks_are_compact_on_the_cantilever_slice():
     """A 40 x 20 x 10 slice: the breadth-first blocks keep about half of the
     DOFs private (a regression guard on the partition, not a correctness pin)."""

@@ -168,3 +168,24 @@ def test_partial_sums_past_the_rank_planes(group):
     assert info["planes"] == 8 and info["n_blocks"] > 8
     yr, sc = oracle.fe_matvec(ed, M.rho, M.Ke, x, n, M.penalty, 0.5, 2.0, y_in)
     assert_close(y, yr, sc, TAU_F32, f"hub node, G={group}")
+
+
+@pytest.mark.parametrize("group", [1, 3])
+def test_long_blocks_chain(group):
+    """Elements in a chain, each sharing one node with the next: ~1,800 nodes
+    per block, past what a lane stages from registers, so the apply's
+    remainder loops (staging and run sums) carry most of the block."""
+    Ke = _mesh((1, 1, 1), False).Ke
+    E = 600
+    nodes = 7 * np.arange(E)[:, None] + np.arange(8)[None, :]
+    ed = (3 * nodes[:, :, None] + np.arange(3)[None, None, :]).reshape(E, 24).astype(np.int32)
+    n = 3 * (7 * E + 1)
+    rng = np.random.default_rng(11)
+    rho = rng.uniform(0.1, 1.0, E).astype(np.float32)
+    x = rng.uniform(-1, 1, n).astype(np.float32)
+    y_in = rng.uniform(-1, 1, n).astype(np.float32)
+    print(f"[blocks] chain, group {group}", flush=True)
+    y, plan = _run(ed, n, rho, Ke, x, 3, 1.5, -0.5, y_in, group=group)
+    assert plan.info()["Lmax"] > (1792 if group == 1 else 768)
+    yr, sc = oracle.fe_matvec(ed, rho, Ke, x, n, 3, 1.5, -0.5, y_in)
+    assert_close(y, yr, sc, TAU_F32, f"chain, G={group}")
