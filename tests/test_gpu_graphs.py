@@ -2,8 +2,9 @@
 (torch.cuda.CUDAGraph on a side stream) and replayed several times, with
 eager work between the replays that changes x and resets y; every replay
 must equal an eager apply on the same inputs (bit for bit on the
-deterministic paths; within the oracle's bound for the FE matvec, whose
-atomics add in a varying order, and for SpGEMM, whose values do too).
+deterministic paths, the element-block FE apply included; within the
+oracle's bound for the fused FE matvec, whose atomics add in a varying
+order, and for SpGEMM, whose values do too).
 
 Nothing in these applies may record a memset or an allocation into the
 graph; a path that did would fail here on a replay after the first.
@@ -140,6 +141,29 @@ def test_fe_fused_replay(dims):
         torch.cuda.synchronize()
         assert_close(host(y), yr, sc, TAU_F32, "eager fe between replays")
     _replay_and_compare("fe", fn, x, xs, y, y0, check)
+
+
+@pytest.mark.parametrize("group", [3, 1])
+def test_fe_blocks_replay(group):
+    """The element-block apply (two kernels, no atomics) in one graph,
+    replayed: every replay bit for bit equal to an eager apply, and within the
+    oracle's bound."""
+    M = gen.fe_mesh(40, 20, 10, seed=3)
+    ed, rho, Ke = dev(M.edof.reshape(-1)), dev(M.rho), dev(M.Ke.reshape(-1))
+    plan = S.FEBlocks(M.n_elem, M.n_dof, ed, group=group)
+    x = dev(M.x)
+    y = torch.zeros(M.n_dof, device="cuda")
+    y0 = np.random.default_rng(2).uniform(-1, 1, M.n_dof).astype(np.float32)
+    rng = np.random.default_rng(10)
+    xs = [rng.uniform(-1, 1, M.n_dof).astype(np.float32) for _ in range(REPLAYS)]
+    fn = lambda: plan.apply(rho, M.penalty, Ke, 2.0, x, -0.5, y)  # noqa: E731
+    bitwise = _bitwise_vs_eager(fn, x, y, y0)
+
+    def check(got, xv):
+        yr, sc = oracle.fe_matvec(M.edof, M.rho, M.Ke, xv, M.n_dof, M.penalty, 2.0, -0.5, y0)
+        assert_close(got, yr, sc, TAU_F32, "graph fe blocks")
+        bitwise(got, xv)
+    _replay_and_compare(f"fe-blocks G={group}", fn, x, xs, y, y0, check)
 
 
 def test_spgemm_compute_replay():
