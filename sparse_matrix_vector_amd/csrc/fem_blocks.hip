@@ -77,7 +77,15 @@ __global__ __launch_bounds__(FB_BLOCK) void k_fe_block(const int *__restrict__ b
     constexpr int U = FbShape<G>::U, PER = FbShape<G>::PER;
     extern __shared__ float fb_lds[];
     float *xs = fb_lds, *pb = fb_lds + G * Lmax;
-    const int b = blockIdx.x, t = threadIdx.x;
+    const int t = threadIdx.x;
+    // the workgroups one XCD receives (workgroup i goes to XCD i % 8) take a
+    // contiguous range of blocks: neighbouring blocks share nodes, whose x
+    // and partial-sum lines then stay in that XCD's L2
+    int b;
+    {
+        const int nw = gridDim.x, w = blockIdx.x, q = nw / 8, r = nw % 8, xcd = w % 8, idx = w / 8;
+        b = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    }
     const int e0 = blk_elem_off[b], ne = blk_elem_off[b + 1] - e0;
     const int d0 = blk_dof_off[b], L = blk_dof_off[b + 1] - d0;
     // the lane's element: local units and product positions of its entries, rho
