@@ -322,7 +322,16 @@ __global__ __launch_bounds__(SV_WG) void k_fe_matvec64(int n_elem, int n_dof, co
     if (blockIdx.x == 0 && threadIdx.x == 0) st->acc_exp = kx;
     const double unit = ldexp(1.0, kx);
     // lanes past the last element stay for the wave exchange, with index -1
-    const int e = blockIdx.x * SV_WG + threadIdx.x;
+    // the workgroups one XCD receives (workgroup i goes to XCD i % 8) take a
+    // contiguous range of elements, whose x and accumulator lines then stay
+    // in that XCD's L2 (0.8 us per PCG iteration; the fused fp32 kernel,
+    // whose memory-side atomics dominate, is slower this way)
+    int wg;
+    {
+        const int nw = gridDim.x, w = blockIdx.x, q = nw / 8, r = nw % 8, xcd = w % 8, idx = w / 8;
+        wg = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    }
+    const int e = wg * SV_WG + threadIdx.x;
     const bool live = e < n_elem;
     const int ec = live ? e : n_elem - 1;
     int d[NDOF_E];
