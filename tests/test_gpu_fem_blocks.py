@@ -5,7 +5,8 @@ Same bound as the fused kernel (|y - y_ref| <= 1e-5 x the element-wise
 scale): the full 120 x 60 x 30 cantilever, small meshes with alpha / beta,
 other numberings (elements shuffled or y-fastest, DOFs relabelled), a mesh
 whose blocks have no free DOF, no elements at all (y = beta y only), a new
-rho on the same plan, and agreement with fem_matvec_apply.  Every addition
+rho on the same plan, agreement with fem_matvec_apply, and the assembled
+form of the oracle at both scales on 40 x 20 x 10.  Every addition
 happens in an order the plan fixes, so a repeated apply must give the same
 bits.
 """
@@ -189,3 +190,24 @@ def test_long_blocks_chain(group):
     assert plan.info()["Lmax"] > (1792 if group == 1 else 768)
     yr, sc = oracle.fe_matvec(ed, rho, Ke, x, n, 3, 1.5, -0.5, y_in)
     assert_close(y, yr, sc, TAU_F32, f"chain, G={group}")
+
+
+@pytest.mark.parametrize("group", [3, 1])
+@pytest.mark.parametrize("clamp", [True, False])
+def test_assembled_form(clamp, group):
+    """The element-block apply against K x with K assembled by the oracle in
+    fp64 (COO sorted, duplicates merged) and applied by the oracle's CSR
+    product, on 40 x 20 x 10 (32 blocks, shared nodes on every block face):
+    within 1e-5 of the element-wise scale, and of the smaller assembled
+    scale sum_j |K_ij x_j| as well."""
+    M = _mesh((40, 20, 10), clamp, seed=12)
+    rp, ci, v = oracle.fe_assemble(M.edof, M.rho, M.Ke, M.n_dof)
+    ya, sa = oracle.csr_spmv_f64(rp, ci, v, M.x)
+    y, _ = _run(M.edof.reshape(M.n_elem, 24), M.n_dof, M.rho, M.Ke, M.x, M.penalty, group=group)
+    _, sc = oracle.fe_matvec(M.edof, M.rho, M.Ke, M.x, M.n_dof)
+    err = assert_close(y, ya, sc, TAU_F32, f"blocks G={group} vs assembled (element scale)")
+    nz = sa > 0
+    worst = float(np.max(np.abs(y[nz] - ya[nz]) / sa[nz]))
+    print(f"[blocks] clamp={clamp} G={group}: max err / element scale {err:.2e}, "
+          f"max err / assembled scale {worst:.2e}", flush=True)
+    assert_close(y, ya, sa, TAU_F32, f"blocks G={group} vs assembled (assembled scale)")
