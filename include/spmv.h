@@ -380,7 +380,8 @@ spmv_status fem_matvec_apply(int32_t n_elem, int32_t n_dof, const int32_t *edof,
 /* Element blocks ("Fused GPU SpMV kernel optimisation", sections 2.2 and
  * 5.2: the fused pass, with what the elements share held in on-chip memory).
  * A plan built once from edof cuts the elements into compact blocks of at
- * most 256 (one workgroup each).  It works on units of G DOFs: a node's
+ * most 512 (256 where a 512-element block's workgroup would need more than
+ * 64 KB of LDS; one workgroup each).  It works on units of G DOFs: a node's
  * three DOFs (G = 3) when every element corner is either three constrained
  * DOFs or the DOFs 3i, 3i+1, 3i+2 of one node, else single DOFs (G = 1).
  * Each block numbers its units locally, stores each element's 24 / G units
@@ -408,7 +409,8 @@ spmv_status fem_matvec_apply(int32_t n_elem, int32_t n_dof, const int32_t *edof,
  *   fem_blocks_info: counts[0] blocks, [1] most local units of a block, [2]
  *     units finished by the second kernel, [3] largest product buffer of a
  *     block (products and padding words),
- *     [4] G, [5] rank planes of the partial sums.
+ *     [4] G, [5] rank planes of the partial sums, [6] most elements per
+ *     block (512 or 256).
  *   fem_blocks_plan_host: the same plan from a host edof into host buffers
  *     (NULL buffers are skipped).  Upper-bound sizes: blk_elem_off,
  *     blk_dof_off n_elem + 1; perm n_elem; ldof, ldst, crun, lidx, lpos
@@ -426,7 +428,7 @@ spmv_status fem_matvec_apply(int32_t n_elem, int32_t n_dof, const int32_t *edof,
  *     (r * n_shared + i) * G, else at planes * n_shared * G + shr_ptr[i] +
  *     (r - planes) * G.  counts = {blocks, local units in all, second-kernel
  *     units, slots, most local units of a block, largest product buffer of a
- *     block, G, planes}.  For inspection and tests. */
+ *     block, G, planes, most elements per block} (counts holds 9).  For inspection and tests. */
 typedef struct fem_blocks *fem_blocks_t;
 spmv_status fem_blocks_size(int32_t n_elem, int32_t n_dof, size_t *bytes);
 spmv_status fem_blocks_create(fem_blocks_t *plan, int32_t n_elem, int32_t n_dof, const int32_t *edof,

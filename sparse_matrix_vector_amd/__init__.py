@@ -580,7 +580,7 @@ def fem_blocks_plan_host(n_elem, n_dof, edof, group=0):
     import numpy as np
     E, n = int(n_elem), int(n_dof)
     ed = np.ascontiguousarray(edof, dtype=np.int32).reshape(-1)
-    counts = np.zeros(8, np.int32)
+    counts = np.zeros(9, np.int32)
     ent = max(24 * E, 1)
     names = ("blk_elem_off", "perm", "blk_dof_off", "ldof", "ldst", "crun", "lidx", "lpos", "shr_ptr", "shr_dof",
              "shr_cnt")
@@ -591,9 +591,10 @@ def fem_blocks_plan_host(n_elem, n_dof, edof, group=0):
          "shr_cnt": np.zeros(max(n, 1), np.int32)}
     _call("fem_blocks_plan_host", E, n, ed.ctypes.data, int(group), counts.ctypes.data,
           *[a[k].ctypes.data for k in names])
-    nb, sum_l, n_sh, n_slots, lmax, pmax, G, planes = (int(c) for c in counts)
+    nb, sum_l, n_sh, n_slots, lmax, pmax, G, planes, block = (int(c) for c in counts)
     U = 24 // G
-    return {"group": G, "n_blocks": nb, "Lmax": lmax, "Pmax": pmax, "n_slots": n_slots, "planes": planes,
+    return {"group": G, "block": block, "n_blocks": nb, "Lmax": lmax, "Pmax": pmax, "n_slots": n_slots,
+            "planes": planes,
             "blk_elem_off": a["blk_elem_off"][:nb + 1], "perm": a["perm"][:E],
             "blk_dof_off": a["blk_dof_off"][:nb + 1], "ldof": a["ldof"][:sum_l], "ldst": a["ldst"][:sum_l],
             "crun": a["crun"][:sum_l], "lidx": a["lidx"][:U * E], "lpos": a["lpos"][:U * E],
@@ -618,10 +619,10 @@ def fem_blocks_apply(handle, rho, penalty, Ke, alpha, x, beta, y, stream=None):
 
 def fem_blocks_info(handle):
     import numpy as np
-    c = np.zeros(6, np.int32)
+    c = np.zeros(7, np.int32)
     _call("fem_blocks_info", handle, c.ctypes.data)
     return {"n_blocks": int(c[0]), "Lmax": int(c[1]), "n_shared": int(c[2]), "Pmax": int(c[3]), "group": int(c[4]),
-            "planes": int(c[5])}
+            "planes": int(c[5]), "block": int(c[6])}
 
 
 def fem_blocks_destroy(handle):

@@ -4,7 +4,8 @@
 // every element's gather, product and scatter on chip, and its cost is the
 // scatter (atomic adds) and the index traffic.  A plan built once from the
 // mesh connectivity (edof) takes most of that off the apply:
-//   - the elements are cut into compact blocks of at most FB_BLOCK elements
+//   - the elements are cut into compact blocks of at most 512 elements (256
+//     when a 512-element block would not fit a workgroup's LDS)
 //     (greedy breadth-first growth over elements that share a DOF, from the
 //     lowest-numbered element not yet taken), one workgroup each;
 //   - the plan works on units of G DOFs: a node's three DOFs (G = 3) when
@@ -50,10 +51,12 @@ bool fb_node_structured(int32_t n_elem, int32_t n_dof, const int32_t *edof) {
     return true;
 }
 
-bool fb_plan_build(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t group, FbPlanHost &P) {
+bool fb_plan_build(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t group, int32_t cap,
+                   FbPlanHost &P) {
     P = FbPlanHost{};
     const int E = n_elem, n = n_dof, G = group, U = FB_NDOF / group;
     P.group = G;
+    P.block = cap;
     auto valid = [n](int32_t d) { return (uint32_t)d < (uint32_t)n; };
     // DOF -> elements (each element listed once per DOF entry, in element order)
     std::vector<int32_t> ptr(n + 1, 0);
@@ -82,13 +85,13 @@ bool fb_plan_build(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t g
         P.perm.push_back(s);
         q.clear();
         q.push_back(s);
-        while (!q.empty() && size < FB_BLOCK) {
+        while (!q.empty() && size < cap) {
             const int32_t e = q.front();
             q.pop_front();
-            for (int a = 0; a < FB_NDOF && size < FB_BLOCK; ++a) {
+            for (int a = 0; a < FB_NDOF && size < cap; ++a) {
                 const int32_t d = edof[(int64_t)e * FB_NDOF + a];
                 if (!valid(d)) continue;
-                for (int32_t k = ptr[d]; k < ptr[d + 1] && size < FB_BLOCK; ++k) {
+                for (int32_t k = ptr[d]; k < ptr[d + 1] && size < cap; ++k) {
                     const int32_t f = elems[k];
                     if (block[f] >= 0) continue;
                     block[f] = b;
@@ -171,7 +174,7 @@ bool fb_plan_build(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t g
             }
         std::sort(loc.begin(), loc.end());
         loc.erase(std::unique(loc.begin(), loc.end()), loc.end());
-        if ((int)loc.size() > FB_NONE) return false;   // cannot happen: at most 256 * 24
+        if ((int)loc.size() > FB_NONE) return false;   // cannot happen: at most 512 * 24
         P.Lmax = std::max<int32_t>(P.Lmax, (int32_t)loc.size());
         run.assign(loc.size(), 0);
         for (int32_t k = k0; k < k1; ++k)
@@ -195,7 +198,7 @@ bool fb_plan_build(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t g
             P.crun.push_back((uint32_t)at | (uint32_t)(at + c) << 16);
             at += c + (c % 2 == 0 ? 1 : 0);
         }
-        if (at > FB_NONE) return false;   // cannot happen: at most 256 * 24 products and as many pads
+        if (at > FB_NONE) return false;   // cannot happen: at most 512 * 24 products and as many pads
         P.Pmax = std::max<int32_t>(P.Pmax, at);
         for (int32_t k = k0; k < k1; ++k)
             for (int j = 0; j < U; ++j) {
@@ -208,6 +211,12 @@ bool fb_plan_build(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t g
     }
     P.n_blocks = nb;
     return true;
+}
+
+bool fb_plan_choose(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t group, FbPlanHost &P) {
+    if (!fb_plan_build(n_elem, n_dof, edof, group, FB_BLOCK_MAX, P)) return false;
+    if (fb_lds_bytes(P) <= FB_LDS_MAX) return true;
+    return fb_plan_build(n_elem, n_dof, edof, group, FB_BLOCK_MIN, P);
 }
 
 }  // namespace spmv
@@ -227,10 +236,11 @@ extern "C" spmv_status fem_blocks_plan_host(int32_t n_elem, int32_t n_dof, const
     if (group == 3 && !nodes)
         return fail(SPMV_ERR_INVALID_VALUE, "group 3 needs every element corner to be one node's DOFs 3i..3i+2");
     FbPlanHost P;
-    if (!fb_plan_build(n_elem, n_dof, edof, group ? group : nodes ? 3 : 1, P))
+    if (!fb_plan_choose(n_elem, n_dof, edof, group ? group : nodes ? 3 : 1, P))
         return fail(SPMV_ERR_UNSUPPORTED, "a block has too many DOFs");
     counts[6] = P.group;
     counts[7] = P.planes;
+    counts[8] = P.block;
     counts[0] = P.n_blocks;
     counts[1] = (int32_t)P.ldof.size();
     counts[2] = (int32_t)P.shr_dof.size();

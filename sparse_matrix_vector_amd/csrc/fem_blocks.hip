@@ -3,7 +3,8 @@
 // "Fused GPU SpMV kernel optimisation", sections 2.2 and 5.2: one fused
 // pass gathers, multiplies and scatters; fast on-chip memory should hold
 // what the elements share.  With the plan of fem_blocks.cpp a block of up to
-// 256 elements is one workgroup:
+// 512 elements (256 where a larger one would overflow the LDS) is one
+// workgroup, a lane per element:
 //   k_fe_block  stages x of the block's local units (G DOFs each: a node's
 //               three, or one) in LDS, one load per DOF instead of one per
 //               element entry; reads each element's 24 / G 16-bit local
@@ -62,8 +63,8 @@ struct FbShape {
     static constexpr int PER = G == 1 ? 7 : 3;
 };
 
-template <int G>
-__global__ __launch_bounds__(FB_BLOCK) void k_fe_block(const int *__restrict__ blk_elem_off,
+template <int G, int NT>
+__global__ __launch_bounds__(NT) void k_fe_block(const int *__restrict__ blk_elem_off,
                                                       const int *__restrict__ perm,
                                                       const int *__restrict__ blk_dof_off,
                                                       const int *__restrict__ ldof, const int *__restrict__ ldst,
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(FB_BLOCK) void k_fe_block(const int *__restrict__ b
     if (L > 0) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const int l = min(j * FB_BLOCK + t, L - 1);
+            const int l = min(j * NT + t, L - 1);
             g[j] = ldof[d0 + l];
             dst[j] = ldst[d0 + l];
             const unsigned q = crun[d0 + l];
@@ -123,13 +124,13 @@ __global__ __launch_bounds__(FB_BLOCK) void k_fe_block(const int *__restrict__ b
             for (int c = 0; c < G; ++c) xv[j][c] = x[(unsigned)g[j] + c];
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const int l = j * FB_BLOCK + t;
+            const int l = j * NT + t;
             if (l < L)
 #pragma unroll
                 for (int c = 0; c < G; ++c) xs[G * l + c] = xv[j][c];
         }
     }
-    for (int l = PER * FB_BLOCK + t; l < L; l += FB_BLOCK)
+    for (int l = PER * NT + t; l < L; l += NT)
 #pragma unroll
         for (int c = 0; c < G; ++c) xs[G * l + c] = x[ldof[d0 + l] + c];
     asm volatile("" ::"v"(ke_touch));
@@ -182,8 +183,8 @@ __global__ __launch_bounds__(FB_BLOCK) void k_fe_block(const int *__restrict__ b
     };
 #pragma unroll
     for (int j = 0; j < PER; ++j)
-        if (j * FB_BLOCK + t < L) put(dst[j], c0[j], c1[j]);
-    for (int l = PER * FB_BLOCK + t; l < L; l += FB_BLOCK) {
+        if (j * NT + t < L) put(dst[j], c0[j], c1[j]);
+    for (int l = PER * NT + t; l < L; l += NT) {
         const unsigned q = crun[d0 + l];
         put(ldst[d0 + l], q & 0xFFFFu, q >> 16);
     }
@@ -275,7 +276,7 @@ spmv_status fb_check_shape(int32_t n_elem, int32_t n_dof) {
 using namespace spmv;
 
 struct fem_blocks {
-    int32_t n_elem = 0, n_dof = 0, group = 1, n_blocks = 0, Lmax = 0, Pmax = 0, n_shared = 0, planes = 0;
+    int32_t n_elem = 0, n_dof = 0, group = 1, block = FB_BLOCK_MIN, n_blocks = 0, Lmax = 0, Pmax = 0, n_shared = 0, planes = 0;
     int32_t *blk_elem_off = nullptr, *perm = nullptr, *blk_dof_off = nullptr, *ldof = nullptr, *ldst = nullptr;
     int32_t *shr_ptr = nullptr, *shr_dof = nullptr, *shr_cnt = nullptr;
     uint32_t *crun = nullptr;
@@ -314,13 +315,14 @@ extern "C" spmv_status fem_blocks_create(fem_blocks_t *out, int32_t n_elem, int3
     if (group == 3 && !nodes)
         return fail(SPMV_ERR_INVALID_VALUE, "group 3 needs every element corner to be one node's DOFs 3i..3i+2");
     FbPlanHost P;
-    if (!fb_plan_build(n_elem, n_dof, h_edof.data(), group ? group : nodes ? 3 : 1, P))
+    if (!fb_plan_choose(n_elem, n_dof, h_edof.data(), group ? group : nodes ? 3 : 1, P))
         return fail(SPMV_ERR_UNSUPPORTED, "a block has too many DOFs");
     fem_blocks *h = new fem_blocks();
     char *ws = static_cast<char *>(workspace);
     h->n_elem = n_elem;
     h->n_dof = n_dof;
     h->group = P.group;
+    h->block = P.block;
     h->n_blocks = P.n_blocks;
     h->Lmax = P.Lmax;
     h->Pmax = P.Pmax;
@@ -379,14 +381,17 @@ extern "C" spmv_status fem_blocks_apply(fem_blocks_t h, const float *rho, int32_
         // stays inside the allocation when no block has a free DOF
         const int lmax = std::max(h->Lmax, 1), pmax = std::max(h->Pmax, 1);
         const size_t lds = sizeof(float) * ((size_t)h->group * lmax + pmax);
+        auto launch = [&](auto kernel, int nt) {
+            kernel<<<h->n_blocks, nt, lds, st>>>(h->blk_elem_off, h->perm, h->blk_dof_off, h->ldof, h->ldst, h->crun,
+                                                 h->lidx, h->lpos, lmax, rho, penalty, Ke, alpha, x, beta, y,
+                                                 h->slots);
+        };
         if (h->group == 3)
-            k_fe_block<3><<<h->n_blocks, FB_BLOCK, lds, st>>>(h->blk_elem_off, h->perm, h->blk_dof_off, h->ldof,
-                                                             h->ldst, h->crun, h->lidx, h->lpos, lmax, rho, penalty,
-                                                             Ke, alpha, x, beta, y, h->slots);
+            h->block == FB_BLOCK_MAX ? launch(k_fe_block<3, FB_BLOCK_MAX>, FB_BLOCK_MAX)
+                                     : launch(k_fe_block<3, FB_BLOCK_MIN>, FB_BLOCK_MIN);
         else
-            k_fe_block<1><<<h->n_blocks, FB_BLOCK, lds, st>>>(h->blk_elem_off, h->perm, h->blk_dof_off, h->ldof,
-                                                             h->ldst, h->crun, h->lidx, h->lpos, lmax, rho, penalty,
-                                                             Ke, alpha, x, beta, y, h->slots);
+            h->block == FB_BLOCK_MAX ? launch(k_fe_block<1, FB_BLOCK_MAX>, FB_BLOCK_MAX)
+                                     : launch(k_fe_block<1, FB_BLOCK_MIN>, FB_BLOCK_MIN);
         SPMV_LAUNCHED("k_fe_block");
     }
     if (h->n_shared > 0) {
@@ -410,6 +415,7 @@ extern "C" spmv_status fem_blocks_info(fem_blocks_t h, int32_t *counts) {
     counts[3] = h->Pmax;
     counts[4] = h->group;
     counts[5] = h->planes;
+    counts[6] = h->block;
     return SPMV_OK;
 }
 

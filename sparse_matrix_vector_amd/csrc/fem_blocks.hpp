@@ -4,12 +4,15 @@
 
 #include "common.hpp"
 
+#include <algorithm>
 #include <cstdint>
 #include <vector>
 
 namespace spmv {
 
-constexpr int FB_BLOCK = 256;                 // elements per block (one workgroup, a lane each)
+constexpr int FB_BLOCK_MAX = 512;             // most elements per block (one workgroup, a lane each)
+constexpr int FB_BLOCK_MIN = 256;             // the size taken when larger blocks overflow the LDS
+constexpr size_t FB_LDS_MAX = 65536;          // LDS bytes a workgroup may take
 constexpr int FB_NDOF = 24;                   // DOFs per element
 constexpr uint16_t FB_NONE = 0xFFFF;          // local index / position of a constrained DOF
 
@@ -46,7 +49,7 @@ constexpr uint16_t FB_NONE = 0xFFFF;          // local index / position of a con
 constexpr int FB_PLANES = 8;   // most rank planes of the partial sums (a hexahedral node lies in <= 8 blocks)
 
 struct FbPlanHost {
-    int32_t group = 1, n_blocks = 0, Lmax = 0, Pmax = 0, planes = 0, n_slots = 0;
+    int32_t group = 1, block = FB_BLOCK_MIN, n_blocks = 0, Lmax = 0, Pmax = 0, planes = 0, n_slots = 0;
     std::vector<int32_t> blk_elem_off, perm, blk_dof_off, ldof, ldst, shr_ptr, shr_dof, shr_cnt;
     std::vector<uint32_t> crun;
     std::vector<uint16_t> lidx, lpos;
@@ -57,10 +60,23 @@ struct FbPlanHost {
 bool fb_node_structured(int32_t n_elem, int32_t n_dof, const int32_t *edof);
 
 // Builds the plan from host edof (int32[n_elem * 24], entries outside
-// [0, n_dof) constrained) for group 1 or 3 (3 only when fb_node_structured).
-// False only if a block had more local units or products than 16-bit
-// indices hold (not possible with FB_BLOCK * 24 < 65535) or the partial
-// sums would need more than 2^31 slots.
-bool fb_plan_build(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t group, FbPlanHost &P);
+// [0, n_dof) constrained) for group 1 or 3 (3 only when fb_node_structured)
+// with blocks of at most `cap` elements.  False only if a block had more
+// local units or products than 16-bit indices hold (not possible with
+// FB_BLOCK_MAX * 48 < 65535) or the partial sums would need more than 2^31
+// slots.
+bool fb_plan_build(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t group, int32_t cap,
+                   FbPlanHost &P);
+
+// LDS bytes a block's workgroup takes: x of its units and its product
+// buffer (at least one word each).
+inline size_t fb_lds_bytes(const FbPlanHost &P) {
+    return sizeof(float) * ((size_t)P.group * std::max(P.Lmax, 1) + std::max(P.Pmax, 1));
+}
+
+// The plan with the largest block size whose workgroups fit the LDS limit:
+// FB_BLOCK_MAX elements (fewer nodes shared between blocks), else
+// FB_BLOCK_MIN, which always fits (at most 256 * 24 units and products).
+bool fb_plan_choose(int32_t n_elem, int32_t n_dof, const int32_t *edof, int32_t group, FbPlanHost &P);
 
 }  // namespace spmv

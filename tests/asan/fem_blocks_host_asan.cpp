@@ -61,7 +61,7 @@ static Mesh hex(int nx, int ny, int nz, bool clamp) {
 // the plan into buffers of exactly the documented upper-bound sizes
 static void plan(const char *name, const Mesh &m, int group, int want_group) {
     const int64_t E = m.n_elem, n = m.n_dof, ent = std::max<int64_t>(24 * E, 1);
-    std::vector<int32_t> counts(8, -7), beo(E + 1), perm(std::max<int64_t>(E, 1)), bdo(E + 1), ldof(ent), ldst(ent);
+    std::vector<int32_t> counts(9, -7), beo(E + 1), perm(std::max<int64_t>(E, 1)), bdo(E + 1), ldof(ent), ldst(ent);
     std::vector<uint32_t> crun(ent);
     std::vector<uint16_t> lidx(ent), lpos(ent);
     std::vector<int32_t> sptr(n + 1), sdof(std::max<int64_t>(n, 1)), scnt(std::max<int64_t>(n, 1));
@@ -80,7 +80,7 @@ static void plan(const char *name, const Mesh &m, int group, int want_group) {
     for (int64_t k = 0; k < E; ++k) CHECK(p[k] == k, "%s: perm", name);
     CHECK(beo[0] == 0 && beo[nb] == E && bdo[0] == 0 && bdo[nb] == sum_l, "%s: offsets", name);
     for (int b = 0; b < nb; ++b) {
-        CHECK(beo[b + 1] - beo[b] >= 1 && beo[b + 1] - beo[b] <= 256, "%s: block size", name);
+        CHECK(beo[b + 1] - beo[b] >= 1 && beo[b + 1] - beo[b] <= counts[8], "%s: block size", name);
         const int L = bdo[b + 1] - bdo[b];
         for (int64_t k = beo[b]; k < beo[b + 1]; ++k)
             for (int j = 0; j < U; ++j) {
@@ -99,7 +99,7 @@ static void plan(const char *name, const Mesh &m, int group, int want_group) {
     }
     for (int i = 0; i < ns; ++i) CHECK(sdof[i] >= 0 && sdof[i] < n && scnt[i] >= 0 && sptr[i] <= sptr[i + 1], "%s: shared", name);
     // NULL buffers: counts only
-    std::vector<int32_t> c2(8, -7);
+    std::vector<int32_t> c2(9, -7);
     CHECK(fem_blocks_plan_host(m.n_elem, m.n_dof, m.edof.data(), group, c2.data(), nullptr, nullptr, nullptr, nullptr,
                                nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) == SPMV_OK &&
               std::equal(c2.begin(), c2.end(), counts.begin()),
@@ -120,7 +120,7 @@ int main() {
         for (auto &d : m.edof)
             if (d >= 0) d = q[d];
         plan("hex relabelled", m, 0, 1);
-        std::vector<int32_t> c(8);
+        std::vector<int32_t> c(9);
         CHECK(fem_blocks_plan_host(m.n_elem, m.n_dof, m.edof.data(), 3, c.data(), nullptr, nullptr, nullptr, nullptr,
                                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) ==
                   SPMV_ERR_INVALID_VALUE,
@@ -137,7 +137,7 @@ int main() {
         plan("chain dofs", m, 1, 1);
     }
     {   // one node in every element: past the rank planes
-        Mesh m = hex(40, 12, 6, true);
+        Mesh m = hex(40, 24, 6, true);
         const int32_t hub = m.n_dof;
         m.n_dof += 3;
         for (int e = 0; e < m.n_elem; ++e)
@@ -162,7 +162,7 @@ int main() {
         plan("no elements", z, 1, 1);
     }
     {   // error paths
-        std::vector<int32_t> c(8), ed(24, 0);
+        std::vector<int32_t> c(9), ed(24, 0);
         CHECK(fem_blocks_plan_host(-1, 5, ed.data(), 0, c.data(), nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                    nullptr, nullptr, nullptr, nullptr, nullptr) == SPMV_ERR_INVALID_VALUE,
               "negative n_elem");

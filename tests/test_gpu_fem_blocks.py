@@ -154,10 +154,10 @@ def test_rejects_bad_arguments():
 
 @pytest.mark.parametrize("group", [1, 3])
 def test_partial_sums_past_the_rank_planes(group):
-    """Every element also lists one extra node, so that node lies in all 12
-    blocks: its partial sums run past the 8 rank planes into the overflow
-    list of the second kernel."""
-    M = gen.fe_mesh(40, 12, 6, clamp_x0=True, seed=6)
+    """Every element also lists one extra node, so that node lies in every
+    block (more than 8): its partial sums run past the 8 rank planes into the
+    overflow list of the second kernel."""
+    M = gen.fe_mesh(40, 24, 6, clamp_x0=True, seed=6)
     ed = M.edof.reshape(M.n_elem, 24).copy()
     n = M.n_dof + 3
     ed[:, 0:3] = [M.n_dof, M.n_dof + 1, M.n_dof + 2]
