@@ -56,7 +56,7 @@ __device__ __forceinline__ void fb_load16(const uint16_t *p, unsigned (&o)[N]) {
 }
 
 // G DOFs per unit: U = 24 / G entries per element, PER local units per
-// thread held in registers (all of them when L <= PER * 256)
+// thread held in registers (all of them when L <= PER * NT, NT the block size)
 template <int G>
 struct FbShape {
     static constexpr int U = FB_NDOF / G;
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(NT) void k_fe_block(const int *__restrict__ blk_ele
     // that chain.  One lane per 64-byte line touches it now, beside the
     // staging loads, and the value is kept until the barrier
     const float ke_touch = t < FB_NDOF * FB_NDOF / 16 ? Ke[16 * t] : 0.0f;
-    // the thread's local units l = j * 256 + t: first DOF, destination and
+    // the thread's local units l = j * NT + t: first DOF, destination and
     // run bounds; x of the block's units into LDS.  The loads take no branch
     // (a lane past the block's last unit reads that unit again and drops
     // it), so that all of them are in flight together instead of one
