@@ -60,3 +60,27 @@ def test_random_plans(c, ab):
         y = _emulate(P, ed, n_dof, rho, KE, x, alpha, beta, y_in)
         yr, sc = oracle.fe_matvec(ed, rho, KE, x, n_dof, 3, alpha, beta, y_in)
         assert_close(y, yr, sc, TAU_F32, f"random plan G={P['group']}")
+
+
+@pytest.mark.parametrize("nodewise", [True, False])
+def test_random_plan_with_several_blocks(nodewise):
+    """A fixed draw of 1,500 elements over 300 nodes (the strategy above may
+    shrink towards small meshes): several blocks, most nodes shared."""
+    rng = np.random.default_rng(42)
+    E, nodes = 1500, 300
+    if nodewise:
+        corner = rng.integers(0, nodes, (E, 8))
+        ed = (3 * corner[:, :, None] + np.arange(3)[None, None, :]).reshape(E, 24)
+        n_dof = 3 * nodes
+    else:
+        n_dof = 3 * nodes
+        ed = np.where(rng.random((E, 24)) < 0.1, -1, rng.integers(0, n_dof, (E, 24)))
+    ed = ed.astype(np.int32)
+    rho = rng.uniform(0.05, 1.0, E).astype(np.float32)
+    x = rng.uniform(-1, 1, n_dof).astype(np.float32)
+    for group in ((0, 1, 3) if nodewise else (0, 1)):
+        P = _check(ed, n_dof, group)
+        assert P["n_blocks"] >= 3
+        y = _emulate(P, ed, n_dof, rho, KE, x, 1.0, 0.0, None)
+        yr, sc = oracle.fe_matvec(ed, rho, KE, x, n_dof)
+        assert_close(y, yr, sc, TAU_F32, f"random plan G={P['group']}")

@@ -211,3 +211,28 @@ def test_assembled_form(clamp, group):
     print(f"[blocks] clamp={clamp} G={group}: max err / element scale {err:.2e}, "
           f"max err / assembled scale {worst:.2e}", flush=True)
     assert_close(y, ya, sa, TAU_F32, f"blocks G={group} vs assembled (assembled scale)")
+
+
+@pytest.mark.parametrize("nodewise", [True, False])
+def test_random_connectivity(nodewise):
+    """1,500 elements on 300 random nodes: every node in ~40 element corners,
+    so the runs are long (up to ~20 entries per block) and most nodes are
+    shared by all blocks."""
+    rng = np.random.default_rng(42)
+    E, nodes = 1500, 300
+    Ke = _mesh((1, 1, 1), False).Ke
+    if nodewise:
+        corner = rng.integers(0, nodes, (E, 8))
+        ed = (3 * corner[:, :, None] + np.arange(3)[None, None, :]).reshape(E, 24)
+    else:
+        ed = np.where(rng.random((E, 24)) < 0.1, -1, rng.integers(0, 3 * nodes, (E, 24)))
+    ed = ed.astype(np.int32)
+    n = 3 * nodes
+    rho = rng.uniform(0.05, 1.0, E).astype(np.float32)
+    x = rng.uniform(-1, 1, n).astype(np.float32)
+    y_in = rng.uniform(-1, 1, n).astype(np.float32)
+    for group in ((3, 1) if nodewise else (1,)):
+        print(f"[blocks] random connectivity, group {group}", flush=True)
+        y, plan = _run(ed, n, rho, Ke, x, 3, 0.75, 0.5, y_in, group=group)
+        yr, sc = oracle.fe_matvec(ed, rho, Ke, x, n, 3, 0.75, 0.5, y_in)
+        assert_close(y, yr, sc, TAU_F32, f"random connectivity G={group}")
