@@ -34,7 +34,8 @@ sample; and the same function on row blocks in one thread per core).
 
 One workload only (--config, optionally --path; used for the profiles):
   --config tiny | laplacian | powerlaw | varlen | pruned50 | pruned70 | pruned90 | fe | cantilever
-  --path   csr | csr-binned | csr-vector | csr-scalar | ell | hyb | auto | macko | dense | fem | fem-blocks | fem-3stage
+  --path   csr | csr-binned | csr-vector | csr-scalar | ell | hyb | auto | macko | dense | fem | fem-blocks
+           | fem-blocks-dof (the element-block plan on single DOFs instead of nodes) | fem-3stage
            | fem-csr (the assembled stiffness matrix through the binned CSR path)
            (MACKO variants: macko-b1 | macko-b2 | macko-b8 for 1-, 2- or 8-bit
            codes instead of 4, macko-i8 and macko-i8-bN for int8 values)
@@ -77,7 +78,8 @@ OTHER_PATHS = {"laplacian": ("ell",)}
 # kernel (as rocprofv3 names it) that dominates each path
 KERNEL = {"csr": "k_csr_tasks", "csr-binned": "k_csr_tasks", "csr-vector": "k_csr_vector",
           "csr-scalar": "k_csr_scalar", "ell": "k_ell_apply4t", "macko": "k_macko_spmv",
-          "dense": "k_gemv_f16", "fem": "k_fe_fused", "fem-blocks": "k_fe_block", "fem-3stage": "k_fe_elem",
+          "dense": "k_gemv_f16", "fem": "k_fe_fused", "fem-blocks": "k_fe_block", "fem-blocks-dof": "k_fe_block",
+          "fem-3stage": "k_fe_elem",
           "fem-csr": "k_csr_tasks",
           "hyb": "k_ell_apply",
           "auto": None, "fem-pcg": "k_fe_matvec64 + k_cg_dot + k_cg_step",
@@ -87,6 +89,7 @@ KERNEL = {"csr": "k_csr_tasks", "csr-binned": "k_csr_tasks", "csr-vector": "k_cs
 SOURCE = {"csr": ("csr.hip",), "csr-binned": ("csr.hip",), "csr-vector": ("csr.hip",),
           "csr-scalar": ("csr.hip",), "ell": ("ell.hip",), "macko": ("macko.hip",), "dense": ("dense.hip",),
           "fem": ("fem.hip", "fem_common.hpp"), "fem-blocks": ("fem_blocks.hip", "fem_blocks.cpp", "fem_blocks.hpp"),
+          "fem-blocks-dof": ("fem_blocks.hip", "fem_blocks.cpp", "fem_blocks.hpp"),
           "fem-3stage": ("fem.hip",), "fem-csr": ("csr.hip",),
           "hyb": ("ell.hip", "hyb.hip"),
           "auto": ("csr.hip", "ell.hip", "hyb.hip"), "fem-pcg": ("fem_solver.hip", "fem_common.hpp"), "spgemm": ("spgemm.hip",)}
@@ -254,7 +257,7 @@ class Workload:
             self.workload = "fe_hex8_cantilever_120x60x30"
             self.bytes = 96 * M.n_elem + 4 * M.n_elem + 2304 + 8 * M.n_dof
             self.flops = 1176 * M.n_elem
-            if path not in ("fem", "fem-blocks", "fem-3stage", "fem-csr"):
+            if path not in ("fem", "fem-blocks", "fem-blocks-dof", "fem-3stage", "fem-csr"):
                 raise SystemExit(f"path {path} does not apply to config {config}")
             if path == "fem-csr":
                 # the assembled K, built by the library on the GPU once, then the binned CSR apply
@@ -283,9 +286,9 @@ class Workload:
                 edof, rho, Ke, x = arrs
                 y = torch.zeros(M.n_dof, device="cuda")
                 a = (M.n_elem, M.n_dof, edof, rho, M.penalty, Ke)
-                if path == "fem-blocks":
+                if path in ("fem-blocks", "fem-blocks-dof"):
                     # the plan is built once per copy, outside the timed region
-                    P = S.FEBlocks(M.n_elem, M.n_dof, edof)
+                    P = S.FEBlocks(M.n_elem, M.n_dof, edof, group=1 if path == "fem-blocks-dof" else 0)
                     return (lambda: P.apply(rho, M.penalty, Ke, self.alpha, x, self.beta, y)), y, P
                 if path == "fem":
                     return (lambda: S.fem_matvec_apply(*a, self.alpha, x, self.beta, y)), y, None
@@ -294,7 +297,7 @@ class Workload:
             self.shape = {"n_elem": M.n_elem, "n_dof": M.n_dof}
             if path in ("fem", "fem-3stage"):
                 self.shape["atomics"] = int((M.edof >= 0).sum())
-            elif path == "fem-blocks":
+            elif path in ("fem-blocks", "fem-blocks-dof"):
                 self.shape["plan"] = self.extra[0].info()
         else:
             raise SystemExit(f"unknown config {config}")
